@@ -1,0 +1,443 @@
+"""Pins of the CPU oracle against facts other than itself.
+
+Each test checks an oracle function against something independent of its
+code: a library routine that computes the same thing another way (a stable
+sort, torch's bf16 conversion, scipy's softmax), a closed form, brute force on
+tiny inputs with plain Python loops, an invariant of the method, a number the
+pages print, or central finite differences of the oracle's own forward in fp64.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import softmax as sp_softmax
+
+import oracle as O
+from moe_inputs import CONFIGS, MoEConfig, expert_weight, make_inputs, \
+    round_robin_topk
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# --------------------------------------------------------------------------
+# rounding
+# --------------------------------------------------------------------------
+def test_round_bf16_matches_torch_conversion_of_fp32_values():
+    rng = np.random.default_rng(1)
+    a = rng.standard_normal(200000).astype(np.float32)
+    a[:1000] *= 1e-38          # subnormal range
+    a[1000:2000] *= 1e30
+    # exact halfway points between neighbouring bf16 values
+    base = torch.from_numpy(rng.standard_normal(1000).astype(np.float32))
+    base = base.to(torch.bfloat16).float().numpy()
+    half = (base.view(np.uint32) | np.uint32(0x8000)).view(np.float32)
+    a = np.concatenate([a, half, np.float32([0.0, -0.0])])
+    ref = torch.from_numpy(a).to(torch.bfloat16).float().numpy()
+    got = O.round_bf16(a.astype(np.float64))
+    assert np.array_equal(got, ref.astype(np.float64))
+
+
+def test_round_bf16_ties_to_even_and_fixed_points():
+    # 1 + 2^-8 lies halfway between 1 and 1 + 2^-7: even mantissa is 1.
+    assert O.round_bf16(1.0 + 2.0 ** -8) == 1.0
+    # 1 + 3*2^-8 lies halfway between 1 + 2^-7 and 1 + 2^-6: even is 1 + 2^-6.
+    assert O.round_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6
+    vals = np.array([1.5, -3.25, 2.0 ** -130, 65280.0])
+    assert np.array_equal(O.round_bf16(vals), vals)
+
+
+def test_round_f32_matches_numpy_cast():
+    a = np.random.default_rng(2).standard_normal(1000) * 1e3
+    assert np.array_equal(O.round_f32(a), a.astype(np.float32).astype(float))
+
+
+# --------------------------------------------------------------------------
+# routing
+# --------------------------------------------------------------------------
+def _sort_select(keys, k, allowed=None):
+    """Independent top-k: a full stable sort by (-key, index) per row."""
+    out = []
+    for t in range(keys.shape[0]):
+        cand = [e for e in range(keys.shape[1])
+                if allowed is None or allowed[t, e]]
+        cand.sort(key=lambda e: (-keys[t, e], e))
+        out.append(cand[:k])
+    return np.array(out, dtype=np.int64)
+
+
+def test_select_topk_matches_stable_sort_with_ties():
+    rng = np.random.default_rng(3)
+    keys = np.round(rng.standard_normal((300, 16)), 1)   # many exact ties
+    for k in (1, 2, 5, 16):
+        assert np.array_equal(O.select_topk(keys, k), _sort_select(keys, k))
+    allowed = rng.random((300, 16)) < 0.6
+    allowed[:, :5] = True
+    assert np.array_equal(O.select_topk(keys, 4, allowed),
+                          _sort_select(keys, 4, allowed))
+
+
+def test_constructed_ties_go_to_lowest_index():
+    l = np.zeros((3, 8), dtype=np.float32)
+    l[1, [2, 5, 7]] = 1.0
+    l[2, :] = -2.0
+    l[2, 6] = 3.0
+    idx, w = O.route_softmax(l, 2)
+    assert idx.tolist() == [[0, 1], [2, 5], [6, 0]]
+    assert np.allclose(w[0], [0.5, 0.5])
+
+
+def test_softmax_top2_gates_closed_form():
+    rng = np.random.default_rng(4)
+    l = rng.standard_normal((200, 8)).astype(np.float32)
+    idx, w = O.route_softmax(l, 2)
+    for t in range(200):
+        l0, l1 = float(l[t, idx[t, 0]]), float(l[t, idx[t, 1]])
+        w0 = 1.0 / (1.0 + math.exp(l1 - l0))
+        assert abs(w[t, 0] - w0) <= 1e-7 and abs(w[t, 1] - (1 - w0)) <= 1e-7
+
+
+def test_softmax_gates_renormalise_and_full_softmax_matches_scipy():
+    rng = np.random.default_rng(5)
+    l = rng.standard_normal((100, 32)).astype(np.float32)
+    idx, w = O.route_softmax(l, 6, renorm=1)
+    assert np.all(np.abs(w.sum(axis=1) - 1.0) <= 6 * 2.0 ** -23)
+    # renormalised gates equal the full softmax renormalised over the picks
+    p = sp_softmax(l.astype(np.float64), axis=1)
+    ps = np.take_along_axis(p, idx.astype(np.int64), axis=1)
+    assert np.allclose(w, ps / ps.sum(axis=1, keepdims=True), rtol=1e-6)
+    idx2, w2 = O.route_softmax(l, 6, renorm=0)
+    assert np.array_equal(idx, idx2)
+    assert np.allclose(w2, ps, rtol=1e-6)
+    # selected keys dominate unselected ones
+    sel = np.take_along_axis(l, idx.astype(np.int64), axis=1)
+    mask = np.ones_like(l, dtype=bool)
+    np.put_along_axis(mask, idx.astype(np.int64), False, axis=1)
+    assert np.all(sel.min(axis=1) >= np.where(mask, l, -np.inf).max(axis=1))
+
+
+def test_sigmoid_single_group_without_bias_is_plain_topk():
+    rng = np.random.default_rng(6)
+    l = (rng.standard_normal((400, 64)) * 1.5).astype(np.float32)
+    idx, w = O.route_sigmoid_grouped(l, 8, 1, 1, None)
+    assert np.array_equal(idx, O.select_topk(l, 8).astype(np.int32))
+    s = 1.0 / (1.0 + np.exp(-l.astype(np.float64)))
+    ss = np.take_along_axis(s, idx.astype(np.int64), axis=1)
+    assert np.allclose(w, ss / ss.sum(axis=1, keepdims=True), rtol=1e-6)
+    assert np.all(np.abs(w.sum(axis=1) - 1.0) <= 8 * 2.0 ** -23)
+
+
+def test_sigmoid_group_limited_routing_brute_force():
+    rng = np.random.default_rng(7)
+    T, E, n_groups, topk_groups, k = 60, 32, 8, 4, 8
+    l = (rng.standard_normal((T, E)) * 1.7).astype(np.float32)
+    bias = (rng.standard_normal(E) * 0.1).astype(np.float32)
+    idx, w = O.route_sigmoid_grouped(l, k, n_groups, topk_groups, bias)
+    G = E // n_groups
+    for t in range(T):
+        s = [np.float32(1.0 / (1.0 + math.exp(-float(v)))) for v in l[t]]
+        key = [np.float32(s[e] + bias[e]) for e in range(E)]
+        gs = []
+        for g in range(n_groups):
+            top = sorted(key[g * G:(g + 1) * G], reverse=True)
+            gs.append(np.float32(top[0] + top[1]))
+        kept = sorted(range(n_groups), key=lambda g: (-gs[g], g))[:topk_groups]
+        cand = [e for e in range(E) if e // G in kept]
+        cand.sort(key=lambda e: (-key[e], e))
+        assert idx[t].tolist() == cand[:k]
+        tot = sum(float(s[e]) for e in cand[:k])
+        assert np.allclose(w[t], [float(s[e]) / tot for e in cand[:k]],
+                           rtol=1e-6)
+        assert len({e // G for e in idx[t]}) <= topk_groups
+
+
+# --------------------------------------------------------------------------
+# permutation
+# --------------------------------------------------------------------------
+def _rand_routing(rng, T, E, k):
+    return np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+
+
+def test_permutation_matches_stable_sort_and_invariants():
+    rng = np.random.default_rng(8)
+    T, E, k, d = 97, 11, 3, 5
+    idx = _rand_routing(rng, T, E, k)
+    idx[:10] = [0, 1, 2]            # a popular expert set
+    w = rng.random((T, k))
+    x = rng.standard_normal((T, d))
+    p = O.permute(x, idx, w, E)
+    # independent: a stable sort of the (t, j) entries by expert id
+    flat = idx.reshape(-1)
+    order = np.argsort(flat, kind="stable")
+    assert np.array_equal(p["row_token"], order // k)
+    assert np.array_equal(p["row_gate"], w.reshape(-1)[order])
+    counts = np.bincount(flat, minlength=E)
+    assert np.array_equal(p["counts"], counts)
+    assert np.array_equal(p["offsets"], np.concatenate([[0], np.cumsum(counts)]))
+    assert p["offsets"][-1] == T * k
+    tr = p["token_row"]
+    for t in range(T):
+        for j in range(k):
+            assert p["row_token"][tr[t, j]] == t
+            assert np.array_equal(p["x_perm"][tr[t, j]], x[t])
+    for e in range(E):
+        seg = p["row_token"][p["offsets"][e]:p["offsets"][e + 1]]
+        assert np.all(np.diff(seg) > 0)
+    assert sorted(tr.reshape(-1).tolist()) == list(range(T * k))
+
+
+def test_round_robin_routing_is_balanced():
+    # The deliberately balanced routing of the Primus blog's imbalance study
+    # gives each expert exactly T*k/E rows, the balanced-routing count
+    # bs*N_r/N of the DeepSeek-V3 memory-model page.
+    for T, E, k in ((256, 8, 2), (8192, 256, 8), (4096, 128, 8)):
+        idx = round_robin_topk(T, E, k).numpy()
+        p = O.permute(None, idx, np.ones((T, k)), E)
+        assert np.all(p["counts"] == T * k // E)
+
+
+def test_permute_then_unpermute_with_unit_gates_is_identity():
+    rng = np.random.default_rng(9)
+    T, E, k, d = 50, 7, 3, 6
+    idx = _rand_routing(rng, T, E, k)
+    x = O.round_bf16(rng.standard_normal((T, d)))
+    p = O.permute(x, idx, np.ones((T, k)), E)
+    # one slot at a time with gate 1 gives back x exactly
+    for j in range(k):
+        onehot = np.zeros((T, k))
+        onehot[:, j] = 1.0
+        y = O.combine(p["x_perm"], p["token_row"], onehot, None, "f64")
+        assert np.array_equal(y, x)
+    # renormalised gates over k copies give x up to fp32 rounding
+    _, w = O.route_softmax(rng.standard_normal((T, E)).astype(np.float32), k)
+    p = O.permute(x, idx, w, E)
+    y = O.combine(p["x_perm"], p["token_row"], w, None, "f32")
+    assert np.allclose(y, x, rtol=1e-6, atol=1e-6)
+
+
+# --------------------------------------------------------------------------
+# FFN + combine: dense brute force (never permutes)
+# --------------------------------------------------------------------------
+def _small_inputs(rng, T, d, E, F, Fs=0, prec="f64"):
+    rnd = O.rounder(prec)
+    inp = dict(
+        x=rnd(rng.standard_normal((T, d))),
+        w_router=rnd(rng.standard_normal((E, d)) * 0.5),
+        w_gate=rnd(rng.standard_normal((E, F, d)) * 0.3),
+        w_up=rnd(rng.standard_normal((E, F, d)) * 0.3),
+        w_down=rnd(rng.standard_normal((E, d, F)) * 0.3),
+        router_bias=None, score_bias=None)
+    if Fs:
+        inp.update(ws_gate=rnd(rng.standard_normal((Fs, d)) * 0.3),
+                   ws_up=rnd(rng.standard_normal((Fs, d)) * 0.3),
+                   ws_down=rnd(rng.standard_normal((d, Fs)) * 0.3))
+    return inp
+
+
+def _loop_ffn(xt, wg, wu, wd, rnd):
+    """Plain-Python SwiGLU FFN of one token vector."""
+    F, d = len(wg), len(xt)
+    h = []
+    for f in range(F):
+        g = sum(xt[i] * wg[f][i] for i in range(d))
+        u = sum(xt[i] * wu[f][i] for i in range(d))
+        h.append(float(rnd(g / (1.0 + math.exp(-g)) * u)))
+    return [float(rnd(sum(h[f] * wd[i][f] for f in range(F))))
+            for i in range(d)]
+
+
+@pytest.mark.parametrize("prec", ["f64", "bf16"])
+@pytest.mark.parametrize("shared", [0, 3])
+def test_forward_matches_dense_bruteforce(prec, shared):
+    rng = np.random.default_rng(10 + shared)
+    T, d, E, k, F = 9, 4, 5, 2, 3
+    inp = _small_inputs(rng, T, d, E, F, shared, prec)
+    cfg = MoEConfig("t", T=T, d=d, E=E, k=k, F=F, F_shared=shared)
+    out = O.forward(inp, cfg, prec=prec)
+    rnd = O.rounder(prec)
+    # dense gate matrix G[t, e] from the routing output
+    G = np.zeros((T, E))
+    for t in range(T):
+        for j in range(k):
+            G[t, out["topk_idx"][t, j]] = out["topk_w"][t, j]
+    x = inp["x"].tolist()
+    for t in range(T):
+        acc = [0.0] * d
+        if shared:
+            ys = _loop_ffn(x[t], inp["ws_gate"].tolist(), inp["ws_up"].tolist(),
+                           inp["ws_down"].tolist(), rnd)
+            acc = [a + b for a, b in zip(acc, ys)]
+        for e in range(E):
+            if G[t, e] == 0.0:
+                continue
+            ye = _loop_ffn(x[t], inp["w_gate"][e].tolist(),
+                           inp["w_up"][e].tolist(), inp["w_down"][e].tolist(),
+                           rnd)
+            acc = [a + G[t, e] * b for a, b in zip(acc, ye)]
+        tol = 1e-12 if prec == "f64" else 1e-6
+        assert np.allclose(out["y"][t], acc, rtol=tol, atol=tol)
+
+
+def test_hand_worked_two_expert_example():
+    """Closed form: x = (1, 2), logits (1, 0), each expert picks one input
+    coordinate for g and the other for u, F = 1.  Then
+    y = (2 sigmoid(1) silu(1), (1 - sigmoid(1)) silu(2))."""
+    inp = dict(x=np.array([[1.0, 2.0]]), w_router=np.eye(2),
+               router_bias=np.array([0.0, -2.0]), score_bias=None,
+               w_gate=np.array([[[1.0, 0.0]], [[0.0, 1.0]]]),
+               w_up=np.array([[[0.0, 1.0]], [[1.0, 0.0]]]),
+               w_down=np.array([[[1.0], [0.0]], [[0.0], [1.0]]]))
+    cfg = MoEConfig("hand", T=1, d=2, E=2, k=2, F=1)
+    logits = np.array([[1.0, 0.0]])
+    out = O.forward(inp, cfg, prec="f64", logits=logits)
+    sig = lambda z: 1.0 / (1.0 + math.exp(-z))
+    assert out["topk_idx"].tolist() == [[0, 1]]
+    assert np.allclose(out["topk_w"], [[sig(1), 1 - sig(1)]], rtol=1e-15)
+    assert np.allclose(out["y"], [[2 * sig(1) * 1 * sig(1),
+                                   (1 - sig(1)) * 2 * sig(2)]], rtol=1e-14)
+    # the oracle's own router reproduces those logits: x . I + (0, -2)
+    assert np.allclose(out["logits"], logits)
+
+
+def test_single_expert_top1_is_a_plain_swiglu_mlp():
+    rng = np.random.default_rng(11)
+    T, d, F = 13, 6, 5
+    inp = _small_inputs(rng, T, d, 1, F)
+    cfg = MoEConfig("mlp", T=T, d=d, E=1, k=1, F=F)
+    out = O.forward(inp, cfg, prec="f64")
+    x = inp["x"]
+    g = np.einsum("td,fd->tf", x, inp["w_gate"][0])
+    u = np.einsum("td,fd->tf", x, inp["w_up"][0])
+    h = g * sp_expit(g) * u
+    y = np.einsum("tf,df->td", h, inp["w_down"][0])
+    assert np.allclose(out["y"], y, rtol=1e-12, atol=1e-14)
+    assert np.all(out["topk_w"] == 1.0)
+
+
+def sp_expit(z):
+    from scipy.special import expit
+    return expit(z)
+
+
+def test_deepseek_v3_expert_parameter_count():
+    vals = {}
+    with open(os.path.join(GOLDEN, "deepseek_v3_expert_params.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                key, v = line.split()
+                vals[key] = int(v)
+    cfg = CONFIGS["deepseek_v3_t8192"]
+    assert (cfg.d, cfg.F) == (vals["hidden"], vals["expert_width"])
+    n = sum(expert_weight(cfg, name, 0).numel()
+            for name in ("w_gate", "w_up", "w_down"))
+    assert n == vals["params_per_expert"] == cfg.expert_params()
+    assert n * vals["expert_stacks_per_device"] == \
+        vals["expert_params_per_device"]
+
+
+# --------------------------------------------------------------------------
+# backward: finite differences of the fp64 forward
+# --------------------------------------------------------------------------
+def _fwd_loss(x, logits, wg, wu, wd, dy, cfg, bias):
+    inp = dict(x=x, w_router=np.zeros((cfg.E, cfg.d)), router_bias=None,
+               score_bias=bias, w_gate=wg, w_up=wu, w_down=wd)
+    out = O.forward(inp, cfg, prec="f64", logits=logits, save_gu=True)
+    return float((out["y"] * dy).sum()), out
+
+
+@pytest.mark.parametrize("score,renorm,groups", [
+    (O.SCORE_SOFTMAX, 1, (1, 1)), (O.SCORE_SOFTMAX, 0, (1, 1)),
+    (O.SCORE_SIGMOID, 1, (2, 1)), (O.SCORE_SIGMOID, 0, (1, 1))])
+def test_backward_matches_central_differences(score, renorm, groups):
+    rng = np.random.default_rng(12 + score * 2 + renorm)
+    T, d, E, k, F = 5, 4, 4, 2, 3
+    cfg = MoEConfig("fd", T=T, d=d, E=E, k=k, F=F, score=score,
+                    renorm=renorm, n_groups=groups[0], topk_groups=groups[1])
+    x = rng.standard_normal((T, d))
+    # well separated logits so that no selection flips under the step
+    logits = np.stack([rng.permutation(E) * 0.7 + rng.random(E) * 0.1
+                       for _ in range(T)]) - 1.2
+    bias = (rng.standard_normal(E) * 0.05) if score == O.SCORE_SIGMOID else None
+    wg = rng.standard_normal((E, F, d)) * 0.5
+    wu = rng.standard_normal((E, F, d)) * 0.5
+    wd = rng.standard_normal((E, d, F)) * 0.5
+    dy = rng.standard_normal((T, d))
+    _, out = _fwd_loss(x, logits, wg, wu, wd, dy, cfg, bias)
+    bw = O.ffn_backward(dy, out["x_perm"], out["gu_save"], out["y_perm"],
+                        out["offsets"], out["token_row"], out["topk_idx"],
+                        out["topk_w"], logits, wg, wu, wd, score, renorm,
+                        prec="f64")
+    eps = 1e-6
+
+    def fd(arr, fn):
+        g = np.zeros_like(arr)
+        for i in np.ndindex(arr.shape):
+            old = arr[i]
+            arr[i] = old + eps
+            lp = fn()
+            arr[i] = old - eps
+            lm = fn()
+            arr[i] = old
+            g[i] = (lp - lm) / (2 * eps)
+        return g
+
+    loss = lambda: _fwd_loss(x, logits, wg, wu, wd, dy, cfg, bias)[0]
+    for name, arr in (("dx", x), ("dw_gate", wg), ("dw_up", wu),
+                      ("dw_down", wd), ("d_logits", logits)):
+        num = fd(arr, loss)
+        assert np.allclose(bw[name], num, rtol=1e-6, atol=1e-8), name
+    # the gate gradient: perturb the gates inside the combine only
+    w = out["topk_w"].copy()
+    comb = lambda: float((O.combine(out["y_perm"], out["token_row"], w, None,
+                                    "f64") * dy).sum())
+    assert np.allclose(bw["d_gate"], fd(w, comb), rtol=1e-6, atol=1e-8)
+    if score == O.SCORE_SOFTMAX:
+        # the softmax Jacobian's rows sum to zero
+        assert np.allclose(bw["d_logits"].sum(axis=1), 0.0, atol=1e-12)
+
+
+def test_zero_row_experts_have_exactly_zero_weight_gradients():
+    rng = np.random.default_rng(13)
+    T, d, E, k, F = 20, 6, 6, 2, 4
+    idx = np.stack([rng.permutation(4)[:k] for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k))
+    x = O.round_bf16(rng.standard_normal((T, d)))
+    p = O.permute(x, idx, w, E)
+    wg = O.round_bf16(rng.standard_normal((E, F, d)) * 0.1)
+    wu = O.round_bf16(rng.standard_normal((E, F, d)) * 0.1)
+    wd = O.round_bf16(rng.standard_normal((E, d, F)) * 0.1)
+    y_perm, gu = O.grouped_ffn(p["x_perm"], p["offsets"], wg, wu, wd, "bf16",
+                               save_gu=True)
+    dy = O.round_bf16(rng.standard_normal((T, d)))
+    bw = O.ffn_backward(dy, p["x_perm"], gu, y_perm, p["offsets"],
+                        p["token_row"], idx, w, rng.standard_normal((T, E)),
+                        wg, wu, wd, prec="bf16")
+    for e in (4, 5):
+        assert p["counts"][e] == 0
+        for name in ("dw_gate", "dw_up", "dw_down"):
+            assert np.all(bw[name][e] == 0.0)
+    for e in range(4):
+        assert np.any(bw["dw_gate"][e] != 0.0)
+
+
+# --------------------------------------------------------------------------
+# the workloads' input recipe
+# --------------------------------------------------------------------------
+def test_inputs_are_seeded_and_shaped():
+    cfg = CONFIGS["tiny_fp32"]
+    a = make_inputs(cfg)
+    b = make_inputs(cfg)
+    for key in ("x", "w_router", "w_gate", "w_up", "w_down"):
+        assert torch.equal(a[key], b[key])
+    assert a["x"].shape == (256, 128) and a["w_gate"].shape == (8, 256, 128)
+    assert a["w_down"].shape == (8, 128, 256)
+    assert abs(float(a["w_gate"].std()) - 0.02) < 1e-3
+    # every expert can be regenerated on its own
+    assert torch.equal(a["w_up"][5], expert_weight(cfg, "w_up", 5))
+    small = CONFIGS["qwen3_30b_skewed_t16384"].replace(T=64, d=64, F=64)
+    inp = make_inputs(small)
+    rb = inp["router_bias"].numpy()
+    # Zipf offsets: -1.2 ln(rank) over a permutation of the ranks 1..E
+    ranks = np.exp(-rb / 1.2)
+    assert np.allclose(np.sort(ranks), np.arange(1, 129), rtol=1e-5)

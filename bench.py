@@ -1,0 +1,193 @@
+"""Throughput of one GPU's MoE layer (tokens/s) with the grouped-GEMM rate.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole layer over one batch of seeded synthetic
+tokens already resident in HBM: router GEMM + top-k, permutation, grouped
+SwiGLU FFN (FC1 + FC2, plus the shared expert where the workload has one),
+combine, and the backward where the workload is a training step.  W untimed
+warm-up steps, then K timed steps between two device synchronisations.  Per
+stage, HIP events recorded on the stream the library launches on give the
+average duration; the grouped FFN stage (the dominant kernel pair) is priced
+against the MI355X roofline.  The CPU oracle is timed on a bounded sample of
+the same workload on the host cores.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def ffn_flops(c):
+    R = c.T * c.k
+    return 6.0 * R * c.d * c.F + 6.0 * c.T * c.d * c.F_shared
+
+
+def ffn_bytes(c, counts_nonzero):
+    """Algorithmic HBM bytes of one grouped-FFN call: every expert weight
+    with rows read once, x_perm read, h written and read back, y_perm
+    written (plus the shared expert's x, weights, h and output)."""
+    b = 2 if c.dtype == 1 else 4
+    R = c.T * c.k
+    w = 3.0 * counts_nonzero * c.d * c.F * b
+    act = (R * c.d + 2 * R * c.F + R * c.d) * b
+    if c.F_shared:
+        w += 3.0 * c.d * c.F_shared * b
+        act += (c.T * c.d + 2 * c.T * c.F_shared + c.T * c.d) * b
+    if c.backward:
+        act += 2 * R * c.F * b   # gu_save
+    return w + act
+
+
+def cpu_baseline(cfg, inp, sample_tokens):
+    """The oracle, as it stands, on the first `sample_tokens` tokens."""
+    import torch
+    import oracle as O
+    from threadpoolctl import threadpool_info
+
+    T = min(sample_tokens, cfg.T)
+    sub = cfg.replace(T=T)
+    host = {}
+    for k, v in inp.items():
+        if v is None:
+            host[k] = None
+        elif k in ("x", "dy"):
+            host[k] = v[:T].cpu()
+        else:
+            host[k] = v.cpu()
+    t0 = time.perf_counter()
+    out = O.forward(host, sub, save_gu=cfg.backward)
+    if cfg.backward:
+        O.ffn_backward(host["dy"], out["x_perm"], out["gu_save"], out["y_perm"],
+                       out["offsets"], out["token_row"], out["topk_idx"],
+                       out["topk_w"], out["route_logits"], host["w_gate"],
+                       host["w_up"], host["w_down"], cfg.score, cfg.renorm)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                   if i.get("user_api") == "blas"] or [1])
+    kind = "forward+backward" if cfg.backward else "forward"
+    return {"value": T / dt, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {T} of {cfg.T} tokens of the same workload, whole "
+                      f"{kind} layer in the fp64 oracle ({dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_t4096")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's layer; --gpus {args.gpus} is not "
+              "supported (the layer is built and measured on a single GPU)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from mixture_experts_layer_logits_amd import MoELayer
+    from moe_inputs import CONFIGS, make_inputs
+
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_inputs(cfg, device=dev)
+    layer = MoELayer(cfg, device=dev)
+    stream = torch.cuda.current_stream()
+    stages = ["route", "permute", "ffn", "combine"] + (["backward"] if cfg.backward else [])
+
+    def step(evs=None):
+        for i, st in enumerate(stages):
+            if evs is not None:
+                evs[i].record(stream)
+            if st == "backward":
+                layer.backward(inp, inp["dy"])
+            else:
+                getattr(layer, st)(inp)
+        if evs is not None:
+            evs[len(stages)].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_stage = {st: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1])
+                                    for s in range(args.steps)]))
+                 for i, st in enumerate(stages)}
+    ms_step = float(np.mean([evs[s][0].elapsed_time(evs[s][-1])
+                             for s in range(args.steps)]))
+    ms_wall = wall * 1e3 / args.steps
+    tokens_per_s = cfg.T / (ms_wall / 1e3)
+
+    counts = torch.diff(layer.buf["expert_offsets"]).cpu().numpy()
+    flops = ffn_flops(cfg)
+    t_ffn = per_stage["ffn"] / 1e3
+    tflops = flops / t_ffn / 1e12
+    bytes_ = ffn_bytes(cfg, int((counts > 0).sum()))
+    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = bytes_ / (PEAK_HBM_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
+    else:
+        gbs = bytes_ / t_ffn / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = None
+    roof["kernel"] = "moe_grouped_ffn (FC1+SwiGLU and FC2 grouped GEMM launches)"
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        n = args.cpu_sample_tokens or {"tiny_fp32": 256, "mixtral_t4096": 512,
+                                       "deepseek_v3_t8192": 64,
+                                       "qwen3_30b_skewed_t16384": 2048,
+                                       "qwen3_235b_train_t8192": 256}[cfg.name]
+        cpu = cpu_baseline(cfg, inp, n)
+
+    rec = {
+        "metric": "MoE-layer tokens/sec + grouped-GEMM TFLOPS (fraction of peak) on 1 MI355X",
+        "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_wall, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == 1 else "f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
+                   "F": cfg.F, "F_shared": cfg.F_shared,
+                   "router": "sigmoid+groups" if cfg.score == 1 else "softmax",
+                   "pass": "fwd+bwd" if cfg.backward else "fwd",
+                   "parallelism": "single GPU"},
+        "grouped_gemm_tflops": round(tflops, 2),
+        "grouped_gemm_frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "stage_ms": {k: round(v, 4) for k, v in per_stage.items()},
+        "event_ms_per_step": round(ms_step, 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

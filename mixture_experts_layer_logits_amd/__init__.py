@@ -1,0 +1,10 @@
+"""One GPU's Mixture-of-Experts layer on AMD Instinct MI355X (gfx950).
+
+Route (router GEMM + top-k) -> padding-free permutation -> grouped SwiGLU
+expert FFN (+ shared expert) -> unpermute-and-scale combine, and the backward
+pass, all in hand-written HIP kernels behind the C ABI of include/moe.h.
+"""
+from ._lib import (MoeError, MoeShape, load, make_shape, moe_ffn_backward,  # noqa: F401
+                   moe_grouped_ffn, moe_permute, moe_route_topk,
+                   moe_unpermute_combine, moe_workspace_size, status_string)
+from .layer import MoELayer  # noqa: F401

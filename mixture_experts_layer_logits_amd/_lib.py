@@ -1,0 +1,168 @@
+"""ctypes binding of libmoe.so: the C ABI of include/moe.h, one Python
+function per entry point with the same name.
+
+Tensors are passed as device pointers (``t.data_ptr()``) and the stream is
+torch's current HIP stream; nothing else crosses the boundary.  Every step of
+the layer runs in the library's HIP kernels.  Loading fails loudly when the
+library has not been built; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = -1
+MOE_ERR_UNSUPPORTED = -2
+MOE_ERR_WORKSPACE = -3
+MOE_ERR_HIP = -4
+
+MOE_DTYPE_F32 = 0
+MOE_DTYPE_BF16 = 1
+MOE_SCORE_SOFTMAX = 0
+MOE_SCORE_SIGMOID = 1
+MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN, MOE_OP_COMBINE, MOE_OP_BACKWARD = range(5)
+
+EXPORTED = ("moe_workspace_size", "moe_route_topk", "moe_permute",
+            "moe_grouped_ffn", "moe_unpermute_combine", "moe_ffn_backward",
+            "moe_status_string")
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("T", "d", "E", "k", "F", "F_shared", "n_groups",
+                 "topk_groups", "score", "renorm", "dtype")]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} ({status})")
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load() -> ctypes.CDLL:
+    """Loads libmoe.so (raises if it is missing: build it first)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m mixture_experts_layer_logits_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    sp = ctypes.POINTER(MoeShape)
+    lib.moe_workspace_size.argtypes = [sp, ctypes.c_int, ctypes.POINTER(sz)]
+    lib.moe_route_topk.argtypes = [sp] + [vp] * 7 + [vp, sz, vp]
+    lib.moe_permute.argtypes = [sp] + [vp] * 8 + [vp, sz, vp]
+    lib.moe_grouped_ffn.argtypes = [sp] + [vp] * 12 + [vp, sz, vp]
+    lib.moe_unpermute_combine.argtypes = [sp] + [vp] * 5 + [vp, sz, vp]
+    lib.moe_ffn_backward.argtypes = [sp] + [vp] * 19 + [vp, sz, vp]
+    lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    for name in EXPORTED:
+        if name != "moe_status_string":
+            getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().moe_status_string(int(status)).decode()
+
+
+def make_shape(cfg) -> MoeShape:
+    """A moe_shape from an object with the layer's fields (e.g. MoEConfig)."""
+    return MoeShape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.F, cfg.F_shared,
+                    cfg.n_groups, cfg.topk_groups, cfg.score, cfg.renorm,
+                    cfg.dtype)
+
+
+def _p(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, fn: str) -> int:
+    if status != MOE_OK:
+        raise MoeError(status, fn)
+    return status
+
+
+def moe_workspace_size(shape: MoeShape, op: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().moe_workspace_size(ctypes.byref(shape), op, ctypes.byref(n)),
+           "moe_workspace_size")
+    return n.value
+
+
+def moe_route_topk(shape, x, w_router, router_bias, logits, score_bias,
+                   topk_idx, topk_w, ws=None, ws_bytes=0, stream=None,
+                   check=True):
+    st = load().moe_route_topk(
+        ctypes.byref(shape), _p(x), _p(w_router), _p(router_bias), _p(logits),
+        _p(score_bias), _p(topk_idx), _p(topk_w), _p(ws), ws_bytes,
+        _stream(stream))
+    return _check(st, "moe_route_topk") if check else st
+
+
+def moe_permute(shape, x, topk_idx, topk_w, expert_offsets, row_token,
+                token_row, row_gate, x_perm, ws=None, ws_bytes=0, stream=None,
+                check=True):
+    st = load().moe_permute(
+        ctypes.byref(shape), _p(x), _p(topk_idx), _p(topk_w),
+        _p(expert_offsets), _p(row_token), _p(token_row), _p(row_gate),
+        _p(x_perm), _p(ws), ws_bytes, _stream(stream))
+    return _check(st, "moe_permute") if check else st
+
+
+def moe_grouped_ffn(shape, x_perm, expert_offsets, w_gate, w_up, w_down, x,
+                    ws_gate, ws_up, ws_down, y_perm, y_shared, gu_save,
+                    ws=None, ws_bytes=0, stream=None, check=True):
+    st = load().moe_grouped_ffn(
+        ctypes.byref(shape), _p(x_perm), _p(expert_offsets), _p(w_gate),
+        _p(w_up), _p(w_down), _p(x), _p(ws_gate), _p(ws_up), _p(ws_down),
+        _p(y_perm), _p(y_shared), _p(gu_save), _p(ws), ws_bytes,
+        _stream(stream))
+    return _check(st, "moe_grouped_ffn") if check else st
+
+
+def moe_unpermute_combine(shape, y_perm, token_row, topk_w, y_shared, y,
+                          ws=None, ws_bytes=0, stream=None, check=True):
+    st = load().moe_unpermute_combine(
+        ctypes.byref(shape), _p(y_perm), _p(token_row), _p(topk_w),
+        _p(y_shared), _p(y), _p(ws), ws_bytes, _stream(stream))
+    return _check(st, "moe_unpermute_combine") if check else st
+
+
+def moe_ffn_backward(shape, dy, x_perm, gu_save, y_perm, expert_offsets,
+                     row_token, token_row, topk_idx, topk_w, logits, w_gate,
+                     w_up, w_down, dx, dw_gate, dw_up, dw_down, d_gate,
+                     d_logits, ws=None, ws_bytes=0, stream=None, check=True):
+    st = load().moe_ffn_backward(
+        ctypes.byref(shape), _p(dy), _p(x_perm), _p(gu_save), _p(y_perm),
+        _p(expert_offsets), _p(row_token), _p(token_row), _p(topk_idx),
+        _p(topk_w), _p(logits), _p(w_gate), _p(w_up), _p(w_down), _p(dx),
+        _p(dw_gate), _p(dw_up), _p(dw_down), _p(d_gate), _p(d_logits),
+        _p(ws), ws_bytes, _stream(stream))
+    return _check(st, "moe_ffn_backward") if check else st

@@ -1,0 +1,252 @@
+// C ABI of the MoE layer: argument validation, workspace layout and launch
+// sequencing.  Every check happens before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "../../include/moe.h"
+#include "moe_common.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+size_t esize(const moe_shape& s) { return s.dtype == MOE_DTYPE_BF16 ? 2 : 4; }
+
+int check_shape(const moe_shape* sp) {
+  if (!sp) return MOE_ERR_INVALID_ARG;
+  const moe_shape& s = *sp;
+  if (s.T < 0 || s.d < 1 || s.E < 1 || s.E > 1024 || s.k < 1 || s.k > 64 || s.k > s.E ||
+      s.F < 1 || s.F_shared < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (s.n_groups < 1 || s.n_groups > 64 || s.E % s.n_groups != 0) return MOE_ERR_INVALID_ARG;
+  if (s.topk_groups < 1 || s.topk_groups > s.n_groups) return MOE_ERR_INVALID_ARG;
+  if ((long long)s.topk_groups * (s.E / s.n_groups) < s.k) return MOE_ERR_INVALID_ARG;
+  if (s.score != MOE_SCORE_SOFTMAX && s.score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (s.n_groups > 1 && s.score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (s.renorm != 0 && s.renorm != 1) return MOE_ERR_INVALID_ARG;
+  if (s.dtype != MOE_DTYPE_F32 && s.dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
+  const long long R = (long long)s.T * s.k;
+  const long long wide = std::max<long long>({s.d, s.F, s.F_shared, s.E, 2LL * s.F});
+  if (R * wide >= (1LL << 31) || (long long)s.T * wide >= (1LL << 31)) return MOE_ERR_INVALID_ARG;
+  if ((long long)s.F * s.d >= (1LL << 31)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+// A buffer of `bytes` bytes: may be null only when empty; 16-byte aligned.
+bool ok_buf(const void* p, long long bytes) {
+  if (bytes <= 0) return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15) == 0;
+  return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15) == 0;
+}
+
+size_t ws_bytes_for(const moe_shape& s, int op) {
+  const size_t R = (size_t)s.T * s.k;
+  const size_t es = esize(s);
+  switch (op) {
+    case MOE_OP_ROUTE:
+    case MOE_OP_COMBINE:
+      return 0;
+    case MOE_OP_PERMUTE: {
+      const size_t n = (size_t)s.E * moe::permute_nblk(s);
+      return 2 * align_up(n * 4);
+    }
+    case MOE_OP_FFN:
+      return 2 * align_up((s.E + 1) * 4) + align_up(R * s.F * es) +
+             align_up((size_t)s.T * s.F_shared * es);
+    case MOE_OP_BACKWARD:
+      return 2 * align_up((s.E + 1) * 4) + 2 * align_up(R * s.d * es) +
+             align_up(R * 2 * s.F * es) + align_up(R * s.F * es);
+    default:
+      return 0;
+  }
+}
+
+int check_ws(const moe_shape& s, int op, const void* ws, size_t ws_bytes) {
+  const size_t need = ws_bytes_for(s, op);
+  if (need == 0) return MOE_OK;
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 15) != 0) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+struct Carver {
+  char* p;
+  template <typename T>
+  T* take(size_t bytes) {
+    T* r = reinterpret_cast<T*>(p);
+    p += align_up(bytes);
+    return r;
+  }
+};
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int moe_workspace_size(const moe_shape* shape, int op, size_t* bytes) {
+  const int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!bytes || op < MOE_OP_ROUTE || op > MOE_OP_BACKWARD) return MOE_ERR_INVALID_ARG;
+  *bytes = ws_bytes_for(*shape, op);
+  return MOE_OK;
+}
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: null, misaligned or out-of-range argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: valid shape not supported by this build";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP runtime call or kernel launch failed";
+    default: return "unknown moe_status";
+  }
+}
+
+int moe_route_topk(const moe_shape* shape, const void* x, const void* w_router,
+                   const float* router_bias, float* logits, const float* score_bias,
+                   int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                   void* stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape& s = *shape;
+  const long long es = (long long)esize(s);
+  const bool compute_logits = !(x == nullptr && w_router == nullptr);
+  if (compute_logits) {
+    if (!ok_buf(x, (long long)s.T * s.d * es) || !ok_buf(w_router, (long long)s.E * s.d * es))
+      return MOE_ERR_INVALID_ARG;
+    if (!ok_buf(router_bias, 0)) return MOE_ERR_INVALID_ARG;
+  } else if (router_bias) {
+    return MOE_ERR_INVALID_ARG;  // a bias only applies to computed logits
+  }
+  if (!ok_buf(logits, (long long)s.T * s.E * 4) || !ok_buf(topk_idx, (long long)s.T * s.k * 4) ||
+      !ok_buf(topk_w, (long long)s.T * s.k * 4) || !ok_buf(score_bias, 0))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(s, MOE_OP_ROUTE, ws, ws_bytes)) != MOE_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (compute_logits) {
+    if ((st = hip_status(moe::launch_router_logits(s, x, w_router, router_bias, logits, hs))) != MOE_OK)
+      return st;
+  }
+  return hip_status(moe::launch_topk(s, logits, score_bias, topk_idx, topk_w, hs));
+}
+
+int moe_permute(const moe_shape* shape, const void* x, const int32_t* topk_idx,
+                const float* topk_w, int32_t* expert_offsets, int32_t* row_token,
+                int32_t* token_row, float* row_gate, void* x_perm, void* ws, size_t ws_bytes,
+                void* stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape& s = *shape;
+  const long long es = (long long)esize(s);
+  const long long R = (long long)s.T * s.k;
+  if (!ok_buf(x, (long long)s.T * s.d * es) || !ok_buf(topk_idx, R * 4) ||
+      !ok_buf(topk_w, R * 4) || !ok_buf(expert_offsets, (long long)(s.E + 1) * 4) ||
+      !ok_buf(row_token, R * 4) || !ok_buf(token_row, R * 4) || !ok_buf(row_gate, R * 4) ||
+      !ok_buf(x_perm, R * s.d * es))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(s, MOE_OP_PERMUTE, ws, ws_bytes)) != MOE_OK) return st;
+  Carver c{static_cast<char*>(ws)};
+  const size_t n = (size_t)s.E * moe::permute_nblk(s);
+  moe::PermuteWs pw;
+  pw.blk_cnt = c.take<int32_t>(n * 4);
+  pw.blk_base = c.take<int32_t>(n * 4);
+  return hip_status(moe::launch_permute(s, x, topk_idx, topk_w, expert_offsets, row_token,
+                                        token_row, row_gate, x_perm, pw,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int moe_grouped_ffn(const moe_shape* shape, const void* x_perm, const int32_t* expert_offsets,
+                    const void* w_gate, const void* w_up, const void* w_down, const void* x,
+                    const void* ws_gate, const void* ws_up, const void* ws_down, void* y_perm,
+                    void* y_shared, void* gu_save, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape& s = *shape;
+  const long long es = (long long)esize(s);
+  const long long R = (long long)s.T * s.k;
+  const long long wsz = (long long)s.E * s.F * s.d * es;
+  if (!ok_buf(x_perm, R * s.d * es) || !ok_buf(expert_offsets, (long long)(s.E + 1) * 4) ||
+      !ok_buf(w_gate, wsz) || !ok_buf(w_up, wsz) || !ok_buf(w_down, wsz) ||
+      !ok_buf(y_perm, R * s.d * es) || !ok_buf(gu_save, 0))
+    return MOE_ERR_INVALID_ARG;
+  if (s.F_shared > 0) {
+    const long long sz = (long long)s.F_shared * s.d * es;
+    if (!ok_buf(x, (long long)s.T * s.d * es) || !ok_buf(ws_gate, sz) || !ok_buf(ws_up, sz) ||
+        !ok_buf(ws_down, sz) || !ok_buf(y_shared, (long long)s.T * s.d * es))
+      return MOE_ERR_INVALID_ARG;
+  }
+  if ((st = check_ws(s, MOE_OP_FFN, ws, ws_bytes)) != MOE_OK) return st;
+  Carver c{static_cast<char*>(ws)};
+  moe::FfnWs fw;
+  fw.tiles1 = c.take<int32_t>((s.E + 1) * 4);
+  fw.tiles2 = c.take<int32_t>((s.E + 1) * 4);
+  fw.h = c.take<char>((size_t)R * s.F * es);
+  fw.h_shared = c.take<char>((size_t)s.T * s.F_shared * es);
+  return hip_status(moe::launch_grouped_ffn(s, x_perm, expert_offsets, w_gate, w_up, w_down, x,
+                                            ws_gate, ws_up, ws_down, y_perm, y_shared, gu_save,
+                                            fw, static_cast<hipStream_t>(stream)));
+}
+
+int moe_unpermute_combine(const moe_shape* shape, const void* y_perm, const int32_t* token_row,
+                          const float* topk_w, const void* y_shared, float* y, void* ws,
+                          size_t ws_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape& s = *shape;
+  const long long es = (long long)esize(s);
+  const long long R = (long long)s.T * s.k;
+  if (!ok_buf(y_perm, R * s.d * es) || !ok_buf(token_row, R * 4) || !ok_buf(topk_w, R * 4) ||
+      !ok_buf(y, (long long)s.T * s.d * 4))
+    return MOE_ERR_INVALID_ARG;
+  if (s.F_shared > 0 && !ok_buf(y_shared, (long long)s.T * s.d * es)) return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(s, MOE_OP_COMBINE, ws, ws_bytes)) != MOE_OK) return st;
+  return hip_status(moe::launch_combine(s, y_perm, token_row, topk_w, y_shared, y,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int moe_ffn_backward(const moe_shape* shape, const void* dy, const void* x_perm,
+                     const void* gu_save, const void* y_perm, const int32_t* expert_offsets,
+                     const int32_t* row_token, const int32_t* token_row,
+                     const int32_t* topk_idx, const float* topk_w, const float* logits,
+                     const void* w_gate, const void* w_up, const void* w_down, float* dx,
+                     float* dw_gate, float* dw_up, float* dw_down, float* d_gate,
+                     float* d_logits, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape& s = *shape;
+  if (s.F_shared > 0 || !moe::backward_supported(s)) return MOE_ERR_UNSUPPORTED;
+  const long long es = (long long)esize(s);
+  const long long R = (long long)s.T * s.k;
+  const long long wsz = (long long)s.E * s.F * s.d;
+  if (!ok_buf(dy, (long long)s.T * s.d * es) || !ok_buf(x_perm, R * s.d * es) ||
+      !ok_buf(gu_save, R * 2 * s.F * es) || !ok_buf(y_perm, R * s.d * es) ||
+      !ok_buf(expert_offsets, (long long)(s.E + 1) * 4) || !ok_buf(row_token, R * 4) ||
+      !ok_buf(token_row, R * 4) || !ok_buf(topk_idx, R * 4) || !ok_buf(topk_w, R * 4) ||
+      !ok_buf(logits, (long long)s.T * s.E * 4) || !ok_buf(w_gate, wsz * es) ||
+      !ok_buf(w_up, wsz * es) || !ok_buf(w_down, wsz * es) ||
+      !ok_buf(dx, (long long)s.T * s.d * 4) || !ok_buf(dw_gate, wsz * 4) ||
+      !ok_buf(dw_up, wsz * 4) || !ok_buf(dw_down, wsz * 4) || !ok_buf(d_gate, R * 4) ||
+      !ok_buf(d_logits, (long long)s.T * s.E * 4))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(s, MOE_OP_BACKWARD, ws, ws_bytes)) != MOE_OK) return st;
+  Carver c{static_cast<char*>(ws)};
+  moe::BwdWs bw;
+  bw.tiles = c.take<int32_t>((s.E + 1) * 4);
+  bw.tiles2 = c.take<int32_t>((s.E + 1) * 4);
+  bw.dY = c.take<char>((size_t)R * s.d * es);
+  bw.dX = c.take<char>((size_t)R * s.d * es);
+  bw.dgu = c.take<char>((size_t)R * 2 * s.F * es);
+  bw.h = c.take<char>((size_t)R * s.F * es);
+  return hip_status(moe::launch_backward(s, dy, x_perm, gu_save, y_perm, expert_offsets,
+                                         row_token, token_row, topk_idx, topk_w, logits,
+                                         w_gate, w_up, w_down, dx, dw_gate, dw_up, dw_down,
+                                         d_gate, d_logits, bw,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,119 @@
+// Grouped SwiGLU expert FFN (Primus blog, MegaMoE section: FC1 (gate/up) ->
+// SwiGLU -> FC2 (down), as two grouped GEMMs over ragged expert groups; the
+// DeepSeek-V3 memory-model page gives the three matrices h x h_E, h x h_E,
+// h_E x h).  The shared "always-on" expert rides along as one dense group of
+// all T tokens in the same two launches.
+//
+//   schedule:  tile prefixes of FC1 and FC2 from the device offsets
+//   FC1:       h = silu(x_perm . w_gate^T) * (x_perm . w_up^T)  -> bf16, and
+//              optionally the rounded g | u for the backward
+//   FC2:       y_perm = h . w_down^T                            -> bf16
+//
+// bf16 with K and N multiples of 64 runs on MFMA; everything else (the fp32
+// layer, odd widths) runs on the generic fp32-FMA tile kernel.
+#include "gemm_tiles.h"
+
+namespace moe {
+
+// FC1: 128 rows x (128 gate + 128 up) columns per workgroup.
+constexpr int FC1_BM = 128, FC1_BN = 128;
+// FC2: 128 rows x 256 columns.
+constexpr int FC2_BM = 128, FC2_BN = 256;
+constexpr int GEN_BM = 64, GEN_BN = 64;
+
+bool ffn_uses_mfma(const moe_shape& s) {
+  return s.dtype == MOE_DTYPE_BF16 && s.d % 64 == 0 && s.F % 64 == 0 &&
+         (s.F_shared == 0 || s.F_shared % 64 == 0);
+}
+
+template <typename T>
+static hipError_t run_generic(const moe_shape& s, GemmArgs& a1, GemmArgs& a2, int R,
+                              const FfnWs& ws, hipStream_t st) {
+  if (s.E > 0) {
+    schedule_tiles_kernel<<<1, 1024, 0, st>>>(a1.offsets, s.E, GEN_BM, cdiv(s.F, GEN_BN),
+                                              ws.tiles1, GEN_BM, cdiv(s.d, GEN_BN), ws.tiles2);
+  }
+  int g1 = grid_upper_bound(a1, GEN_BM, GEN_BN, R);
+  if (g1 > 0) gemm_generic_kernel<T, 2, EPI_SWIGLU><<<g1, 256, 0, st>>>(a1);
+  int g2 = grid_upper_bound(a2, GEN_BM, GEN_BN, R);
+  if (g2 > 0) gemm_generic_kernel<T, 1, EPI_STORE><<<g2, 256, 0, st>>>(a2);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const int32_t* offsets,
+                              const void* w_gate, const void* w_up, const void* w_down,
+                              const void* x, const void* ws_gate, const void* ws_up,
+                              const void* ws_down, void* y_perm, void* y_shared,
+                              void* gu_save, const FfnWs& ws, hipStream_t st) {
+  const int R = s.T * s.k;
+  const bool shared = s.F_shared > 0 && s.T > 0;
+  // FC1: x_perm [R, d] x w_gate/w_up [E, F, d] -> h [R, F]
+  GemmArgs a1 = {};
+  a1.E = R > 0 ? s.E : 0;
+  a1.offsets = offsets;
+  a1.tiles = ws.tiles1;
+  a1.A = x_perm;
+  a1.lda = s.d;
+  a1.B0 = w_gate;
+  a1.B1 = w_up;
+  a1.strideB = (long long)s.F * s.d;
+  a1.N = s.F;
+  a1.K = s.d;
+  a1.C = ws.h;
+  a1.ldc = s.F;
+  a1.GU = gu_save;
+  a1.ldgu = 2LL * s.F;
+  if (shared) {
+    a1.Td = s.T;
+    a1.Ad = x;
+    a1.ldad = s.d;
+    a1.Bd0 = ws_gate;
+    a1.Bd1 = ws_up;
+    a1.Nd = s.F_shared;
+    a1.Kd = s.d;
+    a1.Cd = ws.h_shared;
+    a1.ldcd = s.F_shared;
+  }
+  // FC2: h [R, F] x w_down [E, d, F] -> y_perm [R, d]
+  GemmArgs a2 = {};
+  a2.E = a1.E;
+  a2.offsets = offsets;
+  a2.tiles = ws.tiles2;
+  a2.A = ws.h;
+  a2.lda = s.F;
+  a2.B0 = w_down;
+  a2.B1 = nullptr;
+  a2.strideB = (long long)s.d * s.F;
+  a2.N = s.d;
+  a2.K = s.F;
+  a2.C = y_perm;
+  a2.ldc = s.d;
+  if (shared) {
+    a2.Td = s.T;
+    a2.Ad = ws.h_shared;
+    a2.ldad = s.F_shared;
+    a2.Bd0 = ws_down;
+    a2.Bd1 = nullptr;
+    a2.Nd = s.d;
+    a2.Kd = s.F_shared;
+    a2.Cd = y_shared;
+    a2.ldcd = s.d;
+  }
+  if (a1.E == 0 && !shared) return hipSuccess;
+
+  if (!ffn_uses_mfma(s)) {
+    if (s.dtype == MOE_DTYPE_BF16) return run_generic<bf16_t>(s, a1, a2, R, ws, st);
+    return run_generic<float>(s, a1, a2, R, ws, st);
+  }
+  if (a1.E > 0) {
+    schedule_tiles_kernel<<<1, 1024, 0, st>>>(offsets, s.E, FC1_BM, cdiv(s.F, FC1_BN),
+                                              ws.tiles1, FC2_BM, cdiv(s.d, FC2_BN), ws.tiles2);
+  }
+  const int g1 = grid_upper_bound(a1, FC1_BM, FC1_BN, R);
+  if (g1 > 0) gemm_bf16_mfma_kernel<FC1_BM, FC1_BN, 2, EPI_SWIGLU><<<g1, 256, 0, st>>>(a1);
+  const int g2 = grid_upper_bound(a2, FC2_BM, FC2_BN, R);
+  if (g2 > 0) gemm_bf16_mfma_kernel<FC2_BM, FC2_BN, 1, EPI_STORE><<<g2, 256, 0, st>>>(a2);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,98 @@
+// Internal helpers of the HIP MoE library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// bf16 is stored as its 16 raw bits.
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) |
+         (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return bf16_to_f32(v); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
+
+// silu(g) = g / (1 + exp(-g)).
+__device__ __forceinline__ float silu_fast(float g) { return g / (1.0f + __expf(-g)); }
+__device__ __forceinline__ float silu_precise(float g) { return g / (1.0f + expf(-g)); }
+
+// ---------------------------------------------------------------------------
+// Launchers implemented in the .hip files.  Each returns hipSuccess or the
+// launch error.  Shapes were validated by the API layer.
+// ---------------------------------------------------------------------------
+hipError_t launch_router_logits(const moe_shape& s, const void* x, const void* w_router,
+                                const float* router_bias, float* logits,
+                                hipStream_t st);
+hipError_t launch_topk(const moe_shape& s, const float* logits, const float* score_bias,
+                       int32_t* topk_idx, float* topk_w, hipStream_t st);
+
+struct PermuteWs {
+  int32_t* blk_cnt;   // [E * nblk]
+  int32_t* blk_base;  // [E * nblk]
+};
+int permute_nblk(const moe_shape& s);
+hipError_t launch_permute(const moe_shape& s, const void* x, const int32_t* topk_idx,
+                          const float* topk_w, int32_t* offsets, int32_t* row_token,
+                          int32_t* token_row, float* row_gate, void* x_perm,
+                          const PermuteWs& ws, hipStream_t st);
+
+struct FfnWs {
+  int32_t* tiles1;  // [E + 1] tile prefix of FC1
+  int32_t* tiles2;  // [E + 1] tile prefix of FC2
+  void* h;          // [R, F] dtype
+  void* h_shared;   // [T, Fs] dtype
+};
+bool ffn_uses_mfma(const moe_shape& s);
+hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const int32_t* offsets,
+                              const void* w_gate, const void* w_up, const void* w_down,
+                              const void* x, const void* ws_gate, const void* ws_up,
+                              const void* ws_down, void* y_perm, void* y_shared,
+                              void* gu_save, const FfnWs& ws, hipStream_t st);
+
+hipError_t launch_combine(const moe_shape& s, const void* y_perm, const int32_t* token_row,
+                          const float* topk_w, const void* y_shared, float* y,
+                          hipStream_t st);
+
+struct BwdWs {
+  int32_t* tiles;   // [E + 1] tile prefix of the row-tiled data-gradient GEMMs
+  int32_t* tiles2;  // [E + 1] second prefix (FC1 data gradient)
+  void* dY;         // [R, d]  dtype: w * dy scattered to permuted rows
+  void* dgu;        // [R, 2F] dtype: dg | du
+  void* h;          // [R, F]  dtype: h recomputed from the saved g, u
+  void* dX;         // [R, d]  dtype
+};
+bool backward_supported(const moe_shape& s);
+hipError_t launch_backward(const moe_shape& s, const void* dy, const void* x_perm,
+                           const void* gu_save, const void* y_perm, const int32_t* offsets,
+                           const int32_t* row_token, const int32_t* token_row,
+                           const int32_t* topk_idx, const float* topk_w,
+                           const float* logits, const void* w_gate, const void* w_up,
+                           const void* w_down, float* dx, float* dw_gate, float* dw_up,
+                           float* dw_down, float* d_gate, float* d_logits,
+                           const BwdWs& ws, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,169 @@
+// Padding-free permutation into expert-contiguous order: expert histogram,
+// exclusive prefix scan, stable scatter (Primus blog, MegaMoE section: "a
+// permutation gathers tokens into expert order"; the buffer holds only routed
+// rows, as in the padding-free token buffer of the X-MoE verdict page).
+//
+// Row order is (expert, token) ascending, so every index is fixed by the
+// routing alone and no atomic decides a position:
+//   pos[t, j] = offsets[e] + #{t' < t : e in topk_idx[t']},  e = topk_idx[t, j].
+//
+// Tokens are cut into blocks of 256 (one workgroup, four 64-token waves).  A
+// wave marks, per expert, which of its 64 tokens picked that expert in a
+// 64-bit mask in LDS (bitwise OR is order-free); the rank of a token among
+// the wave's tokens that picked e is then popcount(mask & lanes-below).
+//   1. count:  per (expert, block) counts, stored expert-major;
+//   2. scan:   one exclusive scan over that expert-major array gives each
+//              (expert, block) its first row and, at block 0, the offsets;
+//   3. maps:   token_row, row_token and row_gate from the masks again;
+//   4. rows:   one workgroup per token copies x[t] once from HBM into its k
+//              destination rows (full-row, 16-byte coalesced stores).
+#include "gemm_tiles.h"
+
+namespace moe {
+
+constexpr int PB = 256;  // tokens per block
+
+int permute_nblk(const moe_shape& s) { return cdiv(s.T, PB); }
+
+// Fills masks[4][E] (one per wave) for the block's tokens.
+__device__ __forceinline__ void build_masks(unsigned long long* masks, const int32_t* idx,
+                                            int T, int E, int k, int blk) {
+  for (int e = threadIdx.x; e < 4 * E; e += PB) masks[e] = 0ull;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blk * PB + threadIdx.x;
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[(long long)t * k + j];
+      if (e >= 0 && e < E) atomicOr(&masks[wave * E + e], 1ull << lane);
+    }
+  }
+  __syncthreads();
+}
+
+__global__ void __launch_bounds__(PB)
+permute_count_kernel(const int32_t* __restrict__ idx, int T, int E, int k, int nblk,
+                     int32_t* __restrict__ blk_cnt) {
+  extern __shared__ unsigned long long masks[];
+  build_masks(masks, idx, T, E, k, blockIdx.x);
+  for (int e = threadIdx.x; e < E; e += PB) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) c += __popcll(masks[w * E + e]);
+    blk_cnt[(long long)e * nblk + blockIdx.x] = c;
+  }
+}
+
+// Exclusive scan of n = E * nblk counts (expert-major) by one workgroup of
+// 1024 threads, each owning a contiguous run.
+__global__ void __launch_bounds__(1024)
+permute_scan_kernel(const int32_t* __restrict__ blk_cnt, int E, int nblk,
+                    int32_t* __restrict__ blk_base, int32_t* __restrict__ offsets) {
+  __shared__ int s[1024];
+  const int n = E * nblk;
+  const int per = cdiv(n, 1024);
+  const int tid = threadIdx.x;
+  const int lo = min(n, tid * per), hi = min(n, lo + per);
+  int sum = 0;
+  for (int i = lo; i < hi; ++i) sum += blk_cnt[i];
+  s[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? s[tid - off] : 0;
+    __syncthreads();
+    s[tid] += v;
+    __syncthreads();
+  }
+  int run = tid > 0 ? s[tid - 1] : 0;
+  for (int i = lo; i < hi; ++i) {
+    blk_base[i] = run;
+    run += blk_cnt[i];
+  }
+  __syncthreads();
+  // offsets[e] = first row of expert e = base of (e, block 0); offsets[E] = R
+  for (int e = tid; e <= E; e += 1024)
+    offsets[e] = (e < E) ? (nblk > 0 ? blk_base[(long long)e * nblk] : 0) : s[1023];
+}
+
+__global__ void __launch_bounds__(PB)
+permute_maps_kernel(const int32_t* __restrict__ idx, const float* __restrict__ w, int T,
+                    int E, int k, int nblk, const int32_t* __restrict__ blk_base,
+                    int32_t* __restrict__ row_token, int32_t* __restrict__ token_row,
+                    float* __restrict__ row_gate) {
+  extern __shared__ unsigned long long masks[];
+  build_masks(masks, idx, T, E, k, blockIdx.x);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * PB + threadIdx.x;
+  if (t >= T) return;
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int j = 0; j < k; ++j) {
+    const long long tj = (long long)t * k + j;
+    const int e = idx[tj];
+    if (e < 0 || e >= E) {
+      token_row[tj] = -1;
+      continue;
+    }
+    int pos = blk_base[(long long)e * nblk + blockIdx.x];
+    for (int v = 0; v < wave; ++v) pos += __popcll(masks[v * E + e]);
+    pos += __popcll(masks[wave * E + e] & below);
+    token_row[tj] = pos;
+    row_token[pos] = t;
+    row_gate[pos] = w[tj];
+  }
+}
+
+// One workgroup per token: read x[t] once, write it to its k rows.
+template <bool VEC>
+__global__ void __launch_bounds__(256)
+permute_rows_kernel(const uint8_t* __restrict__ x, const int32_t* __restrict__ token_row,
+                    int k, long long row_bytes, uint8_t* __restrict__ x_perm) {
+  const int t = blockIdx.x;
+  const int32_t* rows = token_row + (long long)t * k;  // uniform loads
+  const uint8_t* src = x + (long long)t * row_bytes;
+  if (VEC) {
+    const long long nseg = row_bytes / 16;
+    for (long long sgi = threadIdx.x; sgi < nseg; sgi += 256) {
+      const uint4 v = reinterpret_cast<const uint4*>(src)[sgi];
+      for (int j = 0; j < k; ++j) {
+        const int r = rows[j];
+        if (r >= 0) reinterpret_cast<uint4*>(x_perm + (long long)r * row_bytes)[sgi] = v;
+      }
+    }
+  } else {
+    for (long long b = threadIdx.x; b < row_bytes; b += 256) {
+      const uint8_t v = src[b];
+      for (int j = 0; j < k; ++j) {
+        const int r = rows[j];
+        if (r >= 0) x_perm[(long long)r * row_bytes + b] = v;
+      }
+    }
+  }
+}
+
+hipError_t launch_permute(const moe_shape& s, const void* x, const int32_t* topk_idx,
+                          const float* topk_w, int32_t* offsets, int32_t* row_token,
+                          int32_t* token_row, float* row_gate, void* x_perm,
+                          const PermuteWs& ws, hipStream_t st) {
+  const int nblk = permute_nblk(s);
+  const size_t lds = sizeof(unsigned long long) * 4 * s.E;
+  if (nblk > 0) {
+    permute_count_kernel<<<nblk, PB, lds, st>>>(topk_idx, s.T, s.E, s.k, nblk, ws.blk_cnt);
+  }
+  permute_scan_kernel<<<1, 1024, 0, st>>>(ws.blk_cnt, s.E, nblk, ws.blk_base, offsets);
+  if (nblk > 0) {
+    permute_maps_kernel<<<nblk, PB, lds, st>>>(topk_idx, topk_w, s.T, s.E, s.k, nblk,
+                                               ws.blk_base, row_token, token_row, row_gate);
+    const long long row_bytes = (long long)s.d * (s.dtype == MOE_DTYPE_BF16 ? 2 : 4);
+    if (row_bytes % 16 == 0)
+      permute_rows_kernel<true><<<s.T, 256, 0, st>>>(static_cast<const uint8_t*>(x), token_row,
+                                                     s.k, row_bytes,
+                                                     static_cast<uint8_t*>(x_perm));
+    else
+      permute_rows_kernel<false><<<s.T, 256, 0, st>>>(static_cast<const uint8_t*>(x), token_row,
+                                                      s.k, row_bytes,
+                                                      static_cast<uint8_t*>(x_perm));
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

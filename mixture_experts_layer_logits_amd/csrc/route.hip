@@ -1,0 +1,227 @@
+// Router scoring and top-k gating.
+//
+// Router logits are one dense GEMM (x . w_router^T, fp32 accumulate, plus an
+// optional per-expert router bias).  Top-k runs one wavefront per token: each
+// lane holds the keys of experts lane, lane + 64, ...; k passes of a 64-lane
+// arg-max reduction pick the largest remaining key, the lower expert index
+// winning ties.  Sigmoid scoring first keeps the topk_groups best groups of
+// contiguous experts (group score: fp32 sum of the group's two largest keys),
+// then searches only those.  (Primus blog, MegaMoE section: the router scores
+// each token and picks its top-k experts; the sigmoid/bias/group-limited
+// variant is DeepSeek-V3's, whose bias-adjustment balancing the Piper podcast
+// page mentions.)
+#include <float.h>
+#include <limits.h>
+
+#include "gemm_tiles.h"
+
+namespace moe {
+
+hipError_t launch_router_logits(const moe_shape& s, const void* x, const void* w_router,
+                                const float* router_bias, float* logits,
+                                hipStream_t st) {
+  if (s.T == 0) return hipSuccess;
+  GemmArgs a = {};
+  a.E = 0;
+  a.Td = s.T;
+  a.Ad = x;
+  a.ldad = s.d;
+  a.Bd0 = w_router;
+  a.Bd1 = nullptr;
+  a.Nd = s.E;
+  a.Kd = s.d;
+  a.Cd = logits;
+  a.ldcd = s.E;
+  a.bias = router_bias;
+  if (s.dtype == MOE_DTYPE_BF16 && s.d % 64 == 0) {
+    const int grid = grid_upper_bound(a, 64, 64, 0);
+    gemm_bf16_mfma_kernel<64, 64, 1, EPI_F32_BIAS><<<grid, 256, 0, st>>>(a);
+  } else if (s.dtype == MOE_DTYPE_BF16) {
+    const int grid = grid_upper_bound(a, 64, 64, 0);
+    gemm_generic_kernel<bf16_t, 1, EPI_F32_BIAS><<<grid, 256, 0, st>>>(a);
+  } else {
+    const int grid = grid_upper_bound(a, 64, 64, 0);
+    gemm_generic_kernel<float, 1, EPI_F32_BIAS><<<grid, 256, 0, st>>>(a);
+  }
+  return hipGetLastError();
+}
+
+// Wave-wide arg-max: larger key wins, the lower index on equal keys.
+// Lanes without a candidate carry idx == INT_MAX.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(v, off, 64);
+    const int oi = __shfl_xor(i, off, 64);
+    const bool take = (oi != INT_MAX) &&
+                      (i == INT_MAX || ov > v || (ov == v && oi < i));
+    if (take) {
+      v = ov;
+      i = oi;
+    }
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// One wavefront per token, 4 tokens per workgroup.  NQ = experts per lane.
+template <int NQ>
+__global__ void __launch_bounds__(256)
+topk_kernel(const float* __restrict__ logits, const float* __restrict__ score_bias, int T,
+            int E, int k, int score, int renorm, int n_groups, int topk_groups,
+            int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  __shared__ float s_key[4][64 * NQ];
+  __shared__ int s_keep[4][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int t_raw = blockIdx.x * 4 + wave;
+  const bool live = t_raw < T;
+  const int t = live ? t_raw : T - 1;  // idle waves mirror the last token, store nothing
+
+  float key[NQ], sc[NQ];
+  bool avail[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int e = lane + 64 * q;
+    const bool valid = e < E;
+    const float l = valid ? logits[(long long)t * E + e] : 0.0f;
+    if (score == MOE_SCORE_SOFTMAX) {
+      sc[q] = l;
+      key[q] = l;
+    } else {
+      const float sg = (float)(1.0 / (1.0 + exp(-(double)l)));
+      sc[q] = sg;
+      key[q] = score_bias ? __fadd_rn(sg, valid ? score_bias[e] : 0.0f) : sg;
+    }
+    avail[q] = valid;
+  }
+
+  if (n_groups > 1) {  // uniform over the launch
+    const int G = E / n_groups;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int e = lane + 64 * q;
+      if (e < E) s_key[wave][e] = key[q];
+    }
+    __syncthreads();
+    float gs = 0.0f;
+    int gi = INT_MAX;
+    if (lane < n_groups) {
+      float b1 = -FLT_MAX, b2 = -FLT_MAX;
+      bool have1 = false, have2 = false;
+      for (int e = lane * G; e < lane * G + G; ++e) {
+        const float v = s_key[wave][e];
+        if (!have1 || v > b1) {
+          if (have1) { b2 = b1; have2 = true; }
+          b1 = v;
+          have1 = true;
+        } else if (!have2 || v > b2) {
+          b2 = v;
+          have2 = true;
+        }
+      }
+      gs = (G >= 2) ? __fadd_rn(b1, b2) : b1;
+      gi = lane;
+    }
+    bool kept = false;
+    for (int p = 0; p < topk_groups; ++p) {
+      float v = gi != INT_MAX ? gs : 0.0f;
+      int i = gi;
+      wave_argmax(v, i);
+      if (lane == i) {
+        kept = true;
+        gi = INT_MAX;
+      }
+    }
+    s_keep[wave][lane] = kept ? 1 : 0;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int e = lane + 64 * q;
+      if (e < E) avail[q] = s_keep[wave][e / G] != 0;
+    }
+  }
+
+  int my_e = 0;
+  float my_s = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    float bv = 0.0f;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      if (avail[q] && (bi == INT_MAX || key[q] > bv)) {
+        bv = key[q];
+        bi = lane + 64 * q;
+      }
+    }
+    wave_argmax(bv, bi);
+    float mine = 0.0f;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      if (lane + 64 * q == bi) {
+        avail[q] = false;
+        mine = sc[q];
+      }
+    }
+    const float win_s = __shfl(mine, bi & 63, 64);
+    if (lane == j) {
+      my_e = bi;
+      my_s = win_s;
+    }
+  }
+
+  float w = 0.0f;
+  if (score == MOE_SCORE_SOFTMAX) {
+    const float m = __shfl(my_s, 0, 64);  // the first pick holds the largest logit
+    if (renorm) {
+      const float z = lane < k ? expf(my_s - m) : 0.0f;
+      w = z / wave_sum(z);
+    } else {
+      float part = 0.0f;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        if (lane + 64 * q < E) part += expf(sc[q] - m);
+      w = expf(my_s - m) / wave_sum(part);
+    }
+  } else {
+    if (renorm) {
+      const double tot = wave_sum_f64(lane < k ? (double)my_s : 0.0);
+      w = (float)((double)my_s / tot);
+    } else {
+      w = my_s;
+    }
+  }
+  if (live && lane < k) {
+    topk_idx[(long long)t * k + lane] = my_e;
+    topk_w[(long long)t * k + lane] = w;
+  }
+}
+
+hipError_t launch_topk(const moe_shape& s, const float* logits, const float* score_bias,
+                       int32_t* topk_idx, float* topk_w, hipStream_t st) {
+  if (s.T == 0) return hipSuccess;
+  const int grid = cdiv(s.T, 4);
+  const float* sb = (s.score == MOE_SCORE_SIGMOID) ? score_bias : nullptr;
+#define MOE_TOPK(NQ)                                                                    \
+  topk_kernel<NQ><<<grid, 256, 0, st>>>(logits, sb, s.T, s.E, s.k, s.score, s.renorm, \
+                                        s.n_groups, s.topk_groups, topk_idx, topk_w)
+  if (s.E <= 64) MOE_TOPK(1);
+  else if (s.E <= 128) MOE_TOPK(2);
+  else if (s.E <= 256) MOE_TOPK(4);
+  else if (s.E <= 512) MOE_TOPK(8);
+  else MOE_TOPK(16);
+#undef MOE_TOPK
+  return hipGetLastError();
+}
+
+}  // namespace moe

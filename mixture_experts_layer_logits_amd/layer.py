@@ -1,0 +1,103 @@
+"""The layer on one GPU: torch allocates device buffers once, the C ABI does
+every step.
+
+    layer = MoELayer(cfg)            # cfg: the layer's parameters
+    out = layer.forward(inputs)      # route -> permute -> grouped FFN -> combine
+    grads = layer.backward(inputs, out, dy)
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib as L
+
+
+class MoELayer:
+    def __init__(self, cfg, device="cuda", save_gu=None):
+        self.cfg = cfg
+        self.shape = L.make_shape(cfg)
+        self.device = torch.device(device)
+        self.save_gu = bool(getattr(cfg, "backward", False)) if save_gu is None else save_gu
+        T, d, E, k, F, Fs = cfg.T, cfg.d, cfg.E, cfg.k, cfg.F, cfg.F_shared
+        R = T * k
+        dt = torch.bfloat16 if cfg.dtype == L.MOE_DTYPE_BF16 else torch.float32
+        dev = self.device
+        ops = [L.MOE_OP_ROUTE, L.MOE_OP_PERMUTE, L.MOE_OP_FFN,
+               L.MOE_OP_COMBINE]
+        if self.save_gu:
+            ops.append(L.MOE_OP_BACKWARD)
+        # one scratch buffer serves every call: they are ordered on one stream
+        self.ws_bytes = max(L.moe_workspace_size(self.shape, op) for op in ops)
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
+        e = lambda *s, dtype=dt: torch.empty(*s, dtype=dtype, device=dev)
+        i32, f32 = torch.int32, torch.float32
+        self.buf = dict(
+            logits=e(T, E, dtype=f32), topk_idx=e(T, k, dtype=i32),
+            topk_w=e(T, k, dtype=f32), expert_offsets=e(E + 1, dtype=i32),
+            row_token=e(R, dtype=i32), token_row=e(T, k, dtype=i32),
+            row_gate=e(R, dtype=f32), x_perm=e(R, d), y_perm=e(R, d),
+            y_shared=e(T, d) if Fs > 0 else None,
+            gu_save=e(R, 2 * F) if self.save_gu else None,
+            y=e(T, d, dtype=f32))
+        self.grad = None
+
+    # ------------------------------------------------------------------
+    def route(self, inp, stream=None):
+        b = self.buf
+        L.moe_route_topk(self.shape, inp["x"], inp["w_router"],
+                         inp.get("router_bias"), b["logits"],
+                         inp.get("score_bias"), b["topk_idx"], b["topk_w"],
+                         self.ws, self.ws_bytes, stream)
+
+    def permute(self, inp, stream=None):
+        b = self.buf
+        L.moe_permute(self.shape, inp["x"], b["topk_idx"], b["topk_w"],
+                      b["expert_offsets"], b["row_token"], b["token_row"],
+                      b["row_gate"], b["x_perm"], self.ws, self.ws_bytes, stream)
+
+    def ffn(self, inp, stream=None):
+        b = self.buf
+        L.moe_grouped_ffn(self.shape, b["x_perm"], b["expert_offsets"],
+                          inp["w_gate"], inp["w_up"], inp["w_down"],
+                          inp["x"] if self.cfg.F_shared > 0 else None,
+                          inp.get("ws_gate"), inp.get("ws_up"),
+                          inp.get("ws_down"), b["y_perm"], b["y_shared"],
+                          b["gu_save"], self.ws, self.ws_bytes, stream)
+
+    def combine(self, inp, stream=None):
+        b = self.buf
+        L.moe_unpermute_combine(self.shape, b["y_perm"], b["token_row"],
+                                b["topk_w"], b["y_shared"], b["y"], self.ws,
+                                self.ws_bytes, stream)
+
+    def forward(self, inp, stream=None):
+        self.route(inp, stream)
+        self.permute(inp, stream)
+        self.ffn(inp, stream)
+        self.combine(inp, stream)
+        return self.buf
+
+    # ------------------------------------------------------------------
+    def _alloc_grad(self):
+        c = self.cfg
+        dev, f32 = self.device, torch.float32
+        self.grad = dict(
+            dx=torch.empty(c.T, c.d, dtype=f32, device=dev),
+            dw_gate=torch.empty(c.E, c.F, c.d, dtype=f32, device=dev),
+            dw_up=torch.empty(c.E, c.F, c.d, dtype=f32, device=dev),
+            dw_down=torch.empty(c.E, c.d, c.F, dtype=f32, device=dev),
+            d_gate=torch.empty(c.T, c.k, dtype=f32, device=dev),
+            d_logits=torch.empty(c.T, c.E, dtype=f32, device=dev))
+
+    def backward(self, inp, dy, stream=None):
+        if self.grad is None:
+            self._alloc_grad()
+        b, g = self.buf, self.grad
+        L.moe_ffn_backward(self.shape, dy, b["x_perm"], b["gu_save"],
+                           b["y_perm"], b["expert_offsets"], b["row_token"],
+                           b["token_row"], b["topk_idx"], b["topk_w"],
+                           b["logits"], inp["w_gate"], inp["w_up"],
+                           inp["w_down"], g["dx"], g["dw_gate"], g["dw_up"],
+                           g["dw_down"], g["d_gate"], g["d_logits"], self.ws,
+                           self.ws_bytes, stream)
+        return g

@@ -1,0 +1,108 @@
+"""The C ABI on the host: the library loads, exports every entry point that
+include/moe.h declares, sizes workspaces, and rejects bad arguments before
+anything reaches the GPU (these calls return from validation and never touch
+a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_layer_logits_amd as M
+from mixture_experts_layer_logits_amd import _lib as L
+from moe_inputs import CONFIGS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(moe_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_five_layer_calls():
+    names = _declared()
+    for n in ("moe_route_topk", "moe_permute", "moe_grouped_ffn",
+              "moe_unpermute_combine", "moe_ffn_backward",
+              "moe_workspace_size", "moe_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for n in _declared():
+        assert hasattr(lib, n), n
+    assert set(_declared()) == set(L.EXPORTED)
+
+
+def test_status_strings():
+    for st in (0, -1, -2, -3, -4):
+        assert M.status_string(st).startswith("MOE_")
+    assert M.status_string(7) == "unknown moe_status"
+
+
+def test_workspace_sizes_scale_with_the_shape():
+    c = CONFIGS["mixtral_t4096"]
+    s = M.make_shape(c)
+    ffn = M.moe_workspace_size(s, L.MOE_OP_FFN)
+    assert ffn >= c.T * c.k * c.F * 2      # holds h in bf16
+    assert M.moe_workspace_size(s, L.MOE_OP_ROUTE) == 0
+    assert M.moe_workspace_size(s, L.MOE_OP_COMBINE) == 0
+    with pytest.raises(M.MoeError):
+        M.moe_workspace_size(s, 9)
+
+
+BAD_SHAPES = [
+    dict(k=0), dict(k=9, E=8), dict(E=0), dict(E=2048), dict(d=0), dict(F=0),
+    dict(T=-1), dict(n_groups=3), dict(n_groups=2, topk_groups=3),
+    dict(n_groups=8, topk_groups=1, k=8, E=32),  # 1 group of 4 experts < k
+    dict(n_groups=2, score=0), dict(score=5), dict(renorm=2), dict(dtype=3),
+    dict(k=65, E=128),
+]
+
+
+@pytest.mark.parametrize("bad", BAD_SHAPES)
+def test_bad_shapes_are_rejected(bad):
+    c = CONFIGS["tiny_fp32"]
+    if "n_groups" in bad and "score" not in bad:
+        bad = dict(bad, score=1)
+    s = M.make_shape(c.replace(**{k: v for k, v in bad.items()}))
+    n = ctypes.c_size_t(0)
+    assert L.load().moe_workspace_size(ctypes.byref(s), 0, ctypes.byref(n)) == \
+        L.MOE_ERR_INVALID_ARG
+
+
+def _fake(addr=0x100000):
+    return addr  # never dereferenced: validation fails first
+
+
+def test_calls_reject_null_misaligned_and_small_workspace():
+    c = CONFIGS["tiny_fp32"]
+    s = M.make_shape(c)
+    p = _fake()
+    # null required output
+    st = M.moe_route_topk(s, p, p, None, None, None, p, p, check=False, stream=0)
+    assert st == L.MOE_ERR_INVALID_ARG
+    # misaligned pointer
+    st = M.moe_route_topk(s, p + 2, p, None, p, None, p, p, check=False, stream=0)
+    assert st == L.MOE_ERR_INVALID_ARG
+    # a router bias with logits given as input
+    st = M.moe_route_topk(s, None, None, p, p, None, p, p, check=False, stream=0)
+    assert st == L.MOE_ERR_INVALID_ARG
+    # permute without its workspace
+    st = M.moe_permute(s, p, p, p, p, p, p, p, p, None, 0, check=False, stream=0)
+    assert st == L.MOE_ERR_WORKSPACE
+    need = M.moe_workspace_size(s, L.MOE_OP_FFN)
+    st = M.moe_grouped_ffn(s, p, p, p, p, p, None, None, None, None, p, None, None,
+                           p, need - 1, check=False, stream=0)
+    assert st == L.MOE_ERR_WORKSPACE
+    st = M.moe_unpermute_combine(s, p, p, p, None, None, check=False, stream=0)
+    assert st == L.MOE_ERR_INVALID_ARG
+
+
+def test_backward_rejects_shared_expert():
+    c = CONFIGS["deepseek_v3_t8192"]
+    s = M.make_shape(c)
+    p = _fake()
+    st = M.moe_ffn_backward(s, *([p] * 19), p, 1 << 40, check=False, stream=0)
+    assert st == L.MOE_ERR_UNSUPPORTED

@@ -15,10 +15,10 @@
 
 namespace moe {
 
-// FC1: 128 rows x (128 gate + 128 up) columns per workgroup.
-constexpr int FC1_BM = 128, FC1_BN = 128;
-// FC2: 128 rows x 256 columns.
-constexpr int FC2_BM = 128, FC2_BN = 256;
+// FC1: 256 rows x (128 gate + 128 up) columns per workgroup of 8 waves.
+constexpr int FC1_BM = 256, FC1_BN = 128;
+// FC2: 256 rows x 256 columns.
+constexpr int FC2_BM = 256, FC2_BN = 256;
 constexpr int GEN_BM = 64, GEN_BN = 64;
 
 bool ffn_uses_mfma(const moe_shape& s) {
@@ -109,11 +109,9 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const int3
     schedule_tiles_kernel<<<1, 1024, 0, st>>>(offsets, s.E, FC1_BM, cdiv(s.F, FC1_BN),
                                               ws.tiles1, FC2_BM, cdiv(s.d, FC2_BN), ws.tiles2);
   }
-  const int g1 = grid_upper_bound(a1, FC1_BM, FC1_BN, R);
-  if (g1 > 0) gemm_bf16_mfma_kernel<FC1_BM, FC1_BN, 2, EPI_SWIGLU><<<g1, 256, 0, st>>>(a1);
-  const int g2 = grid_upper_bound(a2, FC2_BM, FC2_BN, R);
-  if (g2 > 0) gemm_bf16_mfma_kernel<FC2_BM, FC2_BN, 1, EPI_STORE><<<g2, 256, 0, st>>>(a2);
-  return hipGetLastError();
+  hipError_t e = launch_mfma_gemm<FC1_BM, FC1_BN, 2, EPI_SWIGLU, 4, 2>(a1, R, st);
+  if (e != hipSuccess) return e;
+  return launch_mfma_gemm<FC2_BM, FC2_BN, 1, EPI_STORE, 4, 2>(a2, R, st);
 }
 
 }  // namespace moe

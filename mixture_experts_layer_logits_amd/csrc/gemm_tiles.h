@@ -180,32 +180,39 @@ schedule_tiles_kernel(const int32_t* __restrict__ offsets, int E, int bm1, int n
 // ---------------------------------------------------------------------------
 // bf16 MFMA tile kernel.
 //
-// 256 threads = 4 waves in a 2 x 2 grid over the BM x BN tile (per B matrix);
-// each wave owns a (BM/2) x (BN/2) block made of 32 x 32 MFMA blocks
-// (v_mfma_f32_32x32x16_bf16).  K advances 64 at a time: the next K slice is
-// loaded from global memory into registers while the current one is consumed
-// from LDS.  LDS rows are padded by 16 bytes so that the 16-byte fragment
-// reads of consecutive rows fall in different banks.
+// WM x WN waves (64 threads each) tile the BM x BN output (per B matrix);
+// each wave owns a (BM/WM) x (BN/WN) block made of 32 x 32 MFMA blocks
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulators).  K advances 64 at a time
+// through two LDS stages: while the waves consume stage s, the next K slice
+// is fetched from global memory into registers and then written to stage
+// s^1, so one barrier per K step suffices.  LDS rows are padded by 16 bytes
+// so that the 16-byte fragment reads of consecutive rows fall in different
+// banks.  The LDS is dynamic: 2 * (BM + NB*BN) * 72 * 2 bytes.
 //
 // The MFMA is issued with the weight fragment as its first operand, so each
 // lane ends up owning one token row and runs of 4 consecutive output columns
 // (8-byte stores of bf16, 16-byte stores of fp32).
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int NB, int EPI>
-__global__ void __launch_bounds__(256)
+template <int BM, int BN, int NB>
+constexpr int mfma_lds_bytes() { return 2 * (BM + NB * BN) * (64 + 8) * 2; }
+
+template <int BM, int BN, int NB, int EPI, int WM, int WN>
+__global__ void __launch_bounds__(64 * WM * WN)
 gemm_bf16_mfma_kernel(const GemmArgs args) {
+  constexpr int NT = 64 * WM * WN;
   constexpr int BK = 64;
   constexpr int LDK = BK + 8;
-  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MI = WTM / 32, NJ = WTN / 32;
-  constexpr int A_CH = BM * BK / 8 / 256;       // 16-byte chunks per thread
-  constexpr int B_CH = NB * BN * BK / 8 / 256;
+  constexpr int RPP = NT / 8;                   // rows per pass of 16-byte chunks
+  constexpr int A_CH = BM / RPP;                // chunks per thread
+  constexpr int B_CH = NB * BN / RPP;
+  constexpr int STAGE = (BM + NB * BN) * LDK;   // elements per LDS stage
   static_assert(A_CH >= 1 && B_CH >= 1 && MI >= 1 && NJ >= 1, "tile too small");
-  static_assert(BN % 32 == 0, "BN must be a multiple of 32");
+  static_assert(BM % RPP == 0 && BN % RPP == 0, "tile rows must be whole passes");
   using TOut = typename std::conditional<EPI == EPI_F32_BIAS, float, bf16_t>::type;
 
-  __shared__ __attribute__((aligned(16))) bf16_t sA[BM * LDK];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[NB * BN * LDK];
+  extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
 
   TileJob<bf16_t, TOut> job;
   if (!decode_tile<BM, BN>(args, job)) return;
@@ -213,23 +220,24 @@ gemm_bf16_mfma_kernel(const GemmArgs args) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
 
-  // Global -> LDS mapping: chunk c = tid + 256 i covers row c / 8, columns
-  // (c % 8) * 8 .. +7 of the BK-wide slice.  Out-of-range rows are clamped
-  // to the last valid row (their results are never stored).
+  // Global -> LDS mapping: chunk i of a thread covers row tid / 8 + RPP i and
+  // columns (tid % 8) * 8 .. +7 of the BK-wide slice.  Out-of-range rows are
+  // clamped to the last valid row (their results are never stored).
   const int kc = (tid & 7) * 8;
+  const int r0 = tid >> 3;
   int a_off[A_CH];
 #pragma unroll
   for (int i = 0; i < A_CH; ++i) {
-    int m = job.m0 + (tid >> 3) + 32 * i;
+    int m = job.m0 + r0 + RPP * i;
     m = m < job.rows ? m : job.rows - 1;
     a_off[i] = m * (int)job.lda + kc;
   }
   int b_off[B_CH];
 #pragma unroll
   for (int i = 0; i < B_CH; ++i) {
-    const int r = (tid >> 3) + 32 * i;
+    const int r = r0 + RPP * i;
     int n = job.n0 + (r % BN);
     n = n < job.N ? n : job.N - 1;
     b_off[i] = n * job.K + kc;
@@ -242,17 +250,19 @@ gemm_bf16_mfma_kernel(const GemmArgs args) {
 #define MOE_GLOAD(k0)                                                               \
   do {                                                                              \
     _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                \
-        ra[i] = *reinterpret_cast<const u32x4_t*>(A + a_off[i] + (k0));               \
+        ra[i] = *reinterpret_cast<const u32x4_t*>(A + a_off[i] + (k0));             \
     _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                                \
-        rb[i] = *reinterpret_cast<const u32x4_t*>(((32 * i) / BN == 0 ? B0 : B1) +    \
-                                                b_off[i] + (k0));                   \
+        rb[i] = *reinterpret_cast<const u32x4_t*>(((RPP * i) / BN == 0 ? B0 : B1) + \
+                                                  b_off[i] + (k0));                 \
   } while (0)
-#define MOE_LSTORE()                                                                \
+#define MOE_LSTORE(stage)                                                           \
   do {                                                                              \
+    bf16_t* sA_ = smem + (stage) * STAGE;                                           \
+    bf16_t* sB_ = sA_ + BM * LDK;                                                   \
     _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                \
-        *reinterpret_cast<u32x4_t*>(&sA[((tid >> 3) + 32 * i) * LDK + kc]) = ra[i];   \
+        *reinterpret_cast<u32x4_t*>(&sA_[(r0 + RPP * i) * LDK + kc]) = ra[i];       \
     _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                                \
-        *reinterpret_cast<u32x4_t*>(&sB[((tid >> 3) + 32 * i) * LDK + kc]) = rb[i];   \
+        *reinterpret_cast<u32x4_t*>(&sB_[(r0 + RPP * i) * LDK + kc]) = rb[i];       \
   } while (0)
 
   f32x16_t acc[NB][MI][NJ];
@@ -267,12 +277,15 @@ gemm_bf16_mfma_kernel(const GemmArgs args) {
 
   const int KT = job.K / BK;
   MOE_GLOAD(0);
-  MOE_LSTORE();
+  MOE_LSTORE(0);
   __syncthreads();
   const int frag_row = lane & 31;
   const int frag_k = (lane >> 5) * 8;
   for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
     if (kt + 1 < KT) MOE_GLOAD((kt + 1) * BK);
+    const bf16_t* sA = smem + cur * STAGE;
+    const bf16_t* sB = sA + BM * LDK;
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 16) {
       bf16x8_t af[MI];
@@ -296,11 +309,8 @@ gemm_bf16_mfma_kernel(const GemmArgs args) {
             acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[b][j], af[i],
                                                                    acc[b][i][j], 0, 0, 0);
     }
+    if (kt + 1 < KT) MOE_LSTORE(cur ^ 1);
     __syncthreads();
-    if (kt + 1 < KT) {
-      MOE_LSTORE();
-      __syncthreads();
-    }
   }
 #undef MOE_GLOAD
 #undef MOE_LSTORE
@@ -360,6 +370,20 @@ gemm_bf16_mfma_kernel(const GemmArgs args) {
       }
     }
   }
+}
+
+// Host launcher of the MFMA kernel: sets the dynamic LDS limit (above the
+// 64 KiB default) and sizes the grid from the host-side tile bound.
+template <int BM, int BN, int NB, int EPI, int WM, int WN>
+hipError_t launch_mfma_gemm(const GemmArgs& a, int R, hipStream_t st) {
+  constexpr int lds = mfma_lds_bytes<BM, BN, NB>();
+  const void* fn = reinterpret_cast<const void*>(&gemm_bf16_mfma_kernel<BM, BN, NB, EPI, WM, WN>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  const int grid = grid_upper_bound(a, BM, BN, R);
+  if (grid == 0) return hipSuccess;
+  gemm_bf16_mfma_kernel<BM, BN, NB, EPI, WM, WN><<<grid, 64 * WM * WN, lds, st>>>(a);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

@@ -182,88 +182,109 @@ schedule_tiles_kernel(const int32_t* __restrict__ offsets, int E, int bm1, int n
 //
 // WM x WN waves (64 threads each) tile the BM x BN output (per B matrix);
 // each wave owns a (BM/WM) x (BN/WN) block made of 32 x 32 MFMA blocks
-// (v_mfma_f32_32x32x16_bf16, fp32 accumulators).  K advances 64 at a time
-// through two LDS stages: while the waves consume stage s, the next K slice
-// is fetched from global memory into registers and then written to stage
-// s^1, so one barrier per K step suffices.  LDS rows are padded by 16 bytes
-// so that the 16-byte fragment reads of consecutive rows fall in different
-// banks.  The LDS is dynamic: 2 * (BM + NB*BN) * 72 * 2 bytes.
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulators).
+//
+// Operands reach LDS with the direct global->LDS load
+// (global_load_lds_dwordx4): each wave instruction moves 16 rows x 64 bytes,
+// lane l's 16 bytes landing at byte 16 l of a 1 KiB block, so the data never
+// passes through registers.  K advances 32 at a time through a ring of four
+// LDS stages with three slices in flight: a CU ingests only ~45-55 bytes per
+// clock this way, close to what the MFMAs consume, so the loads must stream
+// continuously rather than one slice ahead.  Each step waits only for its own
+// slice (an explicit vmcnt that leaves the two younger slices in flight),
+// then a barrier makes every wave's part of the slice visible.
+//
+// Rows are 64 bytes with no padding; 16-byte chunk c of row r sits at
+// position c ^ f(r), f(r) = 2 r[2] + (r[1] ^ r[3]) (bits of r), which keeps
+// the 16-byte fragment reads of 32 consecutive rows free of bank conflicts.
 //
 // The MFMA is issued with the weight fragment as its first operand, so each
 // lane ends up owning one token row and runs of 4 consecutive output columns
 // (8-byte stores of bf16, 16-byte stores of fp32).
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int NB>
-constexpr int mfma_lds_bytes() { return 2 * (BM + NB * BN) * (64 + 8) * 2; }
+#define MOE_AS_GLOBAL(p) ((const __attribute__((address_space(1))) void*)(p))
+#define MOE_AS_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+__device__ __forceinline__ int swz(int r) { return (((r >> 2) & 1) << 1) | (((r >> 1) ^ (r >> 3)) & 1); }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
 template <int BM, int BN, int NB, int EPI, int WM, int WN>
 __global__ void __launch_bounds__(64 * WM * WN)
 gemm_bf16_mfma_kernel(const GemmArgs args) {
-  constexpr int NT = 64 * WM * WN;
-  constexpr int BK = 64;
-  constexpr int LDK = BK + 8;
+  constexpr int NW = WM * WN;
+  constexpr int BK = 32;                        // one 64-byte row per operand row
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MI = WTM / 32, NJ = WTN / 32;
-  constexpr int RPP = NT / 8;                   // rows per pass of 16-byte chunks
-  constexpr int A_CH = BM / RPP;                // chunks per thread
-  constexpr int B_CH = NB * BN / RPP;
-  constexpr int STAGE = (BM + NB * BN) * LDK;   // elements per LDS stage
-  static_assert(A_CH >= 1 && B_CH >= 1 && MI >= 1 && NJ >= 1, "tile too small");
-  static_assert(BM % RPP == 0 && BN % RPP == 0, "tile rows must be whole passes");
+  constexpr int ROWS = BM + NB * BN;            // operand rows per LDS stage
+  constexpr int BLK = ROWS / 16;                // 1 KiB blocks per stage
+  constexpr int BPW = BLK / NW;                 // blocks (load instructions) per wave
+  static_assert(MI >= 1 && NJ >= 1, "tile too small");
+  static_assert(BLK % NW == 0 && (BM / 16) % BPW == 0 && (BN / 16) % BPW == 0,
+                "each wave must load whole blocks of a single operand");
   using TOut = typename std::conditional<EPI == EPI_F32_BIAS, float, bf16_t>::type;
 
-  extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
+  __shared__ __attribute__((aligned(1024))) bf16_t st0[ROWS * BK];
+  __shared__ __attribute__((aligned(1024))) bf16_t st1[ROWS * BK];
+  __shared__ __attribute__((aligned(1024))) bf16_t st2[ROWS * BK];
+  __shared__ __attribute__((aligned(1024))) bf16_t st3[ROWS * BK];
 
   TileJob<bf16_t, TOut> job;
   if (!decode_tile<BM, BN>(args, job)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave / WN, wn = wave % WN;
 
-  // Global -> LDS mapping: chunk i of a thread covers row tid / 8 + RPP i and
-  // columns (tid % 8) * 8 .. +7 of the BK-wide slice.  Out-of-range rows are
-  // clamped to the last valid row (their results are never stored).
-  const int kc = (tid & 7) * 8;
-  const int r0 = tid >> 3;
-  int a_off[A_CH];
-#pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    int m = job.m0 + r0 + RPP * i;
-    m = m < job.rows ? m : job.rows - 1;
-    a_off[i] = m * (int)job.lda + kc;
+  // This wave loads blocks b = wave * BPW + j; lane l covers row 16 b + l / 4
+  // and fetches the logical chunk that belongs at position l % 4.
+  const int blk0 = wave * BPW;
+  const int row0 = blk0 * 16;
+  const bf16_t* src;
+  int src_ld;
+  int rbase, rlimit;
+  if (row0 < BM) {
+    src = job.A;
+    src_ld = (int)job.lda;
+    rbase = job.m0 + row0;
+    rlimit = job.rows;
+  } else {
+    const int rb = row0 - BM;
+    src = (rb / BN == 0) ? job.B0 : job.B1;
+    src_ld = job.K;
+    rbase = job.n0 + rb % BN;
+    rlimit = job.N;
   }
-  int b_off[B_CH];
+  uint32_t g_off[BPW];   // byte offsets from src (< 2^31)
+  const int dma_c = (lane & 3) ^ swz(lane >> 2);
 #pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int r = r0 + RPP * i;
-    int n = job.n0 + (r % BN);
-    n = n < job.N ? n : job.N - 1;
-    b_off[i] = n * job.K + kc;
+  for (int j = 0; j < BPW; ++j) {
+    int r = rbase + (lane >> 2) + 16 * j;
+    r = r < rlimit ? r : rlimit - 1;                    // clamp: never stored
+    g_off[j] = (uint32_t)(r * src_ld + dma_c * 8) * 2u;
   }
-  const bf16_t* const A = job.A;
-  const bf16_t* const B0 = job.B0;
-  const bf16_t* const B1 = NB > 1 ? job.B1 : job.B0;
-
-  u32x4_t ra[A_CH], rb[B_CH];
-#define MOE_GLOAD(k0)                                                               \
-  do {                                                                              \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                \
-        ra[i] = *reinterpret_cast<const u32x4_t*>(A + a_off[i] + (k0));             \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                                \
-        rb[i] = *reinterpret_cast<const u32x4_t*>(((RPP * i) / BN == 0 ? B0 : B1) + \
-                                                  b_off[i] + (k0));                 \
-  } while (0)
-#define MOE_LSTORE(stage)                                                           \
-  do {                                                                              \
-    bf16_t* sA_ = smem + (stage) * STAGE;                                           \
-    bf16_t* sB_ = sA_ + BM * LDK;                                                   \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                \
-        *reinterpret_cast<u32x4_t*>(&sA_[(r0 + RPP * i) * LDK + kc]) = ra[i];       \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                                \
-        *reinterpret_cast<u32x4_t*>(&sB_[(r0 + RPP * i) * LDK + kc]) = rb[i];       \
-  } while (0)
+  const char* src_bytes = reinterpret_cast<const char*>(src);
+  // Issued as inline assembly so that only the explicit vmcnt waits below
+  // order these loads (the compiler cannot tell the four stages apart across
+  // the loop and would otherwise drain every load before some LDS reads).
+  // M0 holds the wave-uniform LDS destination; nothing else in this kernel
+  // uses M0.
+  auto dma = [&](bf16_t* stage, int k0) {
+    const char* base = src_bytes + (size_t)k0 * 2;     // wave-uniform
+#pragma unroll
+    for (int j = 0; j < BPW; ++j) {
+      const uint32_t lds = (uint32_t)(uintptr_t)MOE_AS_LDS(stage + (blk0 + j) * 512);
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :: "s"(lds), "v"(g_off[j]), "s"(base) : "memory");
+    }
+  };
 
   f32x16_t acc[NB][MI][NJ];
 #pragma unroll
@@ -275,45 +296,92 @@ gemm_bf16_mfma_kernel(const GemmArgs args) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[b][i][j][v] = 0.0f;
 
-  const int KT = job.K / BK;
-  MOE_GLOAD(0);
-  MOE_LSTORE(0);
-  __syncthreads();
+  // Fragment rows are lane % 32 plus multiples of 16, so the swizzle is a
+  // per-lane constant; sub-step kk reads chunk 2 kk + lane / 32.
   const int frag_row = lane & 31;
-  const int frag_k = (lane >> 5) * 8;
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) MOE_GLOAD((kt + 1) * BK);
-    const bf16_t* sA = smem + cur * STAGE;
-    const bf16_t* sB = sA + BM * LDK;
+  const int sw = swz(frag_row);
+  const int kpos0 = ((0 + (lane >> 5)) ^ sw) << 3;
+  const int kpos1 = ((2 + (lane >> 5)) ^ sw) << 3;
+  const int a_row = (wm * WTM + frag_row) * BK;
+  const int b_row = (BM + wn * WTN + frag_row) * BK;
+  auto load_frags = [&](const bf16_t* stage, int kpos, bf16x8_t (&af)[MI],
+                        bf16x8_t (&bfr)[NB][NJ]) {
+    const bf16_t* pa = stage + a_row + kpos;
+    const bf16_t* pb = stage + b_row + kpos;
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8_t af[MI];
-      bf16x8_t bfr[NB][NJ];
+    for (int i = 0; i < MI; ++i)
+      af[i] = *reinterpret_cast<const bf16x8_t*>(pa + i * 32 * BK);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        bfr[b][j] = *reinterpret_cast<const bf16x8_t*>(pb + (b * BN + j * 32) * BK);
+  };
+  auto mma = [&](const bf16x8_t (&af)[MI], const bf16x8_t (&bfr)[NB][NJ]) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int i = 0; i < MI; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(
-            &sA[(wm * WTM + i * 32 + frag_row) * LDK + kk + frag_k]);
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
-          bfr[b][j] = *reinterpret_cast<const bf16x8_t*>(
-              &sB[(b * BN + wn * WTN + j * 32 + frag_row) * LDK + kk + frag_k]);
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-          for (int j = 0; j < NJ; ++j)
-            acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[b][j], af[i],
-                                                                   acc[b][i][j], 0, 0, 0);
-    }
-    if (kt + 1 < KT) MOE_LSTORE(cur ^ 1);
-    __syncthreads();
+          acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[b][j], af[i],
+                                                                 acc[b][i][j], 0, 0, 0);
+  };
+  // Barrier with compiler fences: the hardware barrier itself does not
+  // order memory operations for the compiler.
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Waits until this wave's loads of slice `ready` are done, given the
+  // slices issued so far (0 .. issued-1), leaving younger ones in flight.
+  const int KT = job.K / BK;
+  auto wait_slice = [&](int ready, int issued) {
+    const int younger = issued - 1 - ready;
+    if (younger >= 2) wait_vmcnt<2 * BPW>();
+    else if (younger == 1) wait_vmcnt<BPW>();
+    else wait_vmcnt<0>();
+  };
+  // Step s consumes stage s % 4 in two 16-wide sub-steps.  Its first
+  // fragments were read during the previous step.  The barrier sits between
+  // the two sub-steps: after it, slice s+1 is complete in LDS (each wave
+  // waited for its own part), every wave has finished step s-1, so stage
+  // (s+3) % 4 can be refilled and the first fragments of step s+1 read while
+  // the second sub-step's MFMAs run.
+  bf16x8_t af0[MI], af1[MI];
+  bf16x8_t bf0[NB][NJ], bf1[NB][NJ];
+  auto step = [&](const bf16_t* cur, const bf16_t* next, bf16_t* refill, int s) {
+    load_frags(cur, kpos1, af1, bf1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(af0, bf0);
+    if (s + 1 < KT) wait_slice(s + 1, s + 3 < KT ? s + 3 : KT);
+    barrier();
+    if (s + 3 < KT) dma(refill, (s + 3) * BK);
+    if (s + 1 < KT) load_frags(next, kpos0, af0, bf0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(af1, bf1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  dma(st0, 0);
+  if (KT > 1) dma(st1, BK);
+  if (KT > 2) dma(st2, 2 * BK);
+  wait_slice(0, KT < 3 ? KT : 3);
+  barrier();
+  load_frags(st0, kpos0, af0, bf0);
+  int kt = 0;
+  for (; kt + 4 <= KT; kt += 4) {
+    step(st0, st1, st3, kt);
+    step(st1, st2, st0, kt + 1);
+    step(st2, st3, st1, kt + 2);
+    step(st3, st0, st2, kt + 3);
   }
-#undef MOE_GLOAD
-#undef MOE_LSTORE
+  if (kt < KT) step(st0, st1, st3, kt);
+  if (kt + 1 < KT) step(st1, st2, st0, kt + 1);
+  if (kt + 2 < KT) step(st2, st3, st1, kt + 2);
 
   // Epilogue.  Lane owns row m = .. + (lane % 32) and, for register v,
   // column n = .. + 8 (v / 4) + 4 (lane / 32) + v % 4.
@@ -372,17 +440,13 @@ gemm_bf16_mfma_kernel(const GemmArgs args) {
   }
 }
 
-// Host launcher of the MFMA kernel: sets the dynamic LDS limit (above the
-// 64 KiB default) and sizes the grid from the host-side tile bound.
+// Host launcher of the MFMA kernel: sizes the grid from the host-side tile
+// bound.
 template <int BM, int BN, int NB, int EPI, int WM, int WN>
 hipError_t launch_mfma_gemm(const GemmArgs& a, int R, hipStream_t st) {
-  constexpr int lds = mfma_lds_bytes<BM, BN, NB>();
-  const void* fn = reinterpret_cast<const void*>(&gemm_bf16_mfma_kernel<BM, BN, NB, EPI, WM, WN>);
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-  if (e != hipSuccess) return e;
   const int grid = grid_upper_bound(a, BM, BN, R);
   if (grid == 0) return hipSuccess;
-  gemm_bf16_mfma_kernel<BM, BN, NB, EPI, WM, WN><<<grid, 64 * WM * WN, lds, st>>>(a);
+  gemm_bf16_mfma_kernel<BM, BN, NB, EPI, WM, WN><<<grid, 64 * WM * WN, 0, st>>>(a);
   return hipGetLastError();
 }
 

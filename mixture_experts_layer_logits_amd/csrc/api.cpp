@@ -53,9 +53,12 @@ size_t ws_bytes_for(const moe_shape& s, int op) {
       const size_t n = (size_t)s.E * moe::permute_nblk(s);
       return 2 * align_up(n * 4);
     }
-    case MOE_OP_FFN:
+    case MOE_OP_FFN: {
+      const int ks = moe::ffn_fc2_ksplit(s);
       return 2 * align_up((s.E + 1) * 4) + align_up(R * s.F * es) +
-             align_up((size_t)s.T * s.F_shared * es);
+             align_up((size_t)s.T * s.F_shared * es) +
+             (ks > 1 ? align_up((size_t)ks * R * s.d * 4) : 0);
+    }
     case MOE_OP_BACKWARD:
       return 2 * align_up((s.E + 1) * 4) + 2 * align_up(R * s.d * es) +
              align_up(R * 2 * s.F * es) + align_up(R * s.F * es);
@@ -187,6 +190,8 @@ int moe_grouped_ffn(const moe_shape* shape, const void* x_perm, const int32_t* e
   fw.tiles2 = c.take<int32_t>((s.E + 1) * 4);
   fw.h = c.take<char>((size_t)R * s.F * es);
   fw.h_shared = c.take<char>((size_t)s.T * s.F_shared * es);
+  const int ks = moe::ffn_fc2_ksplit(s);
+  fw.part = ks > 1 ? c.take<float>((size_t)ks * R * s.d * 4) : nullptr;
   return hip_status(moe::launch_grouped_ffn(s, x_perm, expert_offsets, w_gate, w_up, w_down, x,
                                             ws_gate, ws_up, ws_down, y_perm, y_shared, gu_save,
                                             fw, static_cast<hipStream_t>(stream)));

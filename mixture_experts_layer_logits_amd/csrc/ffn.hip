@@ -11,6 +11,8 @@
 //
 // bf16 with K and N multiples of 64 runs on MFMA; everything else (the fp32
 // layer, odd widths) runs on the generic fp32-FMA tile kernel.
+#include <algorithm>
+
 #include "gemm_tiles.h"
 
 namespace moe {
@@ -20,6 +22,36 @@ constexpr int FC1_BM = 256, FC1_BN = 128;
 // FC2: 256 rows x 256 columns.
 constexpr int FC2_BM = 256, FC2_BN = 256;
 constexpr int GEN_BM = 64, GEN_BN = 64;
+
+bool ffn_uses_mfma(const moe_shape& s);
+
+// Split-K for FC2 when its tiles are too few to fill the GPU for several
+// rounds (few experts with long K = F): a pure function of the shape, so
+// results do not depend on the device.  At most 4 slices.
+int ffn_fc2_ksplit(const moe_shape& s) {
+  if (!ffn_uses_mfma(s) || s.F_shared > 0) return 1;
+  const long long R = (long long)s.T * s.k;
+  const long long tiles = (cdiv((int)R, FC2_BM) + s.E) * (long long)cdiv(s.d, FC2_BN);
+  for (int ks = 1; ks <= 4; ++ks) {
+    if (s.F % (ks * 32) != 0) continue;
+    if (tiles * ks >= 6 * 256 || ks == 4) return ks;
+  }
+  return 1;
+}
+
+// Sums the split-K partial slices in slice order and rounds to bf16.
+__global__ void __launch_bounds__(256)
+splitk_reduce_kernel(const float* __restrict__ part, long long stride, int ks, long long n4,
+                     bf16_t* __restrict__ out) {
+  for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n4; i += (long long)gridDim.x * 256) {
+    float4 acc = reinterpret_cast<const float4*>(part)[i];
+    for (int sl = 1; sl < ks; ++sl) {
+      const float4 v = reinterpret_cast<const float4*>(part + sl * stride)[i];
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    reinterpret_cast<uint2*>(out)[i] = make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
+  }
+}
 
 bool ffn_uses_mfma(const moe_shape& s) {
   return s.dtype == MOE_DTYPE_BF16 && s.d % 64 == 0 && s.F % 64 == 0 &&
@@ -111,7 +143,19 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const int3
   }
   hipError_t e = launch_mfma_gemm<FC1_BM, FC1_BN, 2, EPI_SWIGLU, 4, 2>(a1, R, st);
   if (e != hipSuccess) return e;
-  return launch_mfma_gemm<FC2_BM, FC2_BN, 1, EPI_STORE, 4, 2>(a2, R, st);
+  const int ks = ffn_fc2_ksplit(s);
+  if (ks > 1 && a2.E > 0) {
+    a2.ksplit = ks;
+    a2.Cpart = ws.part;
+    a2.part_stride = (long long)R * s.d;
+  }
+  e = launch_mfma_gemm<FC2_BM, FC2_BN, 1, EPI_STORE, 4, 2>(a2, R, st);
+  if (e != hipSuccess || a2.ksplit <= 1) return e;
+  const long long n4 = (long long)R * s.d / 4;
+  const int grid = (int)std::min<long long>((n4 + 255) / 256, 4096);
+  splitk_reduce_kernel<<<grid, 256, 0, st>>>(ws.part, a2.part_stride, ks, n4,
+                                             static_cast<bf16_t*>(y_perm));
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -55,6 +55,12 @@ struct GemmArgs {
   void* Cd;
   long long ldcd;
   const float* bias;       // EPI_F32_BIAS: added per column, or null
+  // Split-K (EPI_STORE on routed groups only): K is cut into ksplit equal
+  // slices; slice s of every tile writes fp32 partials to
+  // Cpart + s * part_stride + row * N + n, summed later in slice order.
+  int ksplit;
+  float* Cpart;
+  long long part_stride;
 };
 
 // One tile's work, with typed base pointers already offset to the group.
@@ -71,6 +77,8 @@ struct TileJob {
   TOut* GU;
   long long ldgu;
   int m0, n0;
+  int k0, klen;            // K range of this work item (split-K slice)
+  float* P;                // split-K partial rows of the group, or null
 };
 
 __host__ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
@@ -80,6 +88,7 @@ inline int grid_upper_bound(const GemmArgs& a, int BM, int BN, int R) {
   long long t = 0;
   if (a.E > 0) t += (long long)(cdiv(R, BM) + a.E) * cdiv(a.N, BN);
   if (a.Td > 0) t += (long long)cdiv(a.Td, BM) * cdiv(a.Nd, BN);
+  t *= (a.ksplit > 1 ? a.ksplit : 1);
   return (int)(((t + 7) / 8) * 8);
 }
 
@@ -90,12 +99,17 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, TileJob<TIn, TOut
   const int dmt = cdiv(a.Td, BM);
   const int dense = (a.Td > 0) ? dmt * cdiv(a.Nd, BN) : 0;
   const int total = routed + dense;
+  const int ks = a.ksplit > 1 ? a.ksplit : 1;
   const int bid = blockIdx.x;
-  const int per = (total + 7) >> 3;
+  const int per = (total * ks + 7) >> 3;
   const int slot = bid >> 3;
   if (slot >= per) return false;
-  const int lid = (bid & 7) * per + slot;
-  if (lid >= total) return false;
+  const int item = (bid & 7) * per + slot;
+  if (item >= total * ks) return false;
+  // slice-major: concurrently running items share the slice's K range
+  const int kslice = item / total;
+  const int lid = item - kslice * total;
+  j.P = nullptr;
   if (lid < routed) {
     // largest g with tiles[g] <= lid (empty groups share their start)
     int lo = 0, hi = a.E - 1;
@@ -121,6 +135,9 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, TileJob<TIn, TOut
     j.B1 = a.B1 ? static_cast<const TIn*>(a.B1) + (long long)g * a.strideB : nullptr;
     j.C = static_cast<TOut*>(a.C) + (long long)row0 * a.ldc;
     j.GU = a.GU ? static_cast<TOut*>(a.GU) + (long long)row0 * a.ldgu : nullptr;
+    j.klen = a.K / ks;
+    j.k0 = kslice * j.klen;
+    if (ks > 1) j.P = a.Cpart + kslice * a.part_stride + (long long)row0 * a.N;
     return true;
   }
   const int r = lid - routed;
@@ -137,6 +154,8 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, TileJob<TIn, TOut
   j.B1 = static_cast<const TIn*>(a.Bd1);
   j.C = static_cast<TOut*>(a.Cd);
   j.GU = nullptr;
+  j.klen = a.Kd;
+  j.k0 = 0;
   return true;
 }
 
@@ -338,7 +357,8 @@ gemm_bf16_mfma_kernel(const GemmArgs args) {
   };
   // Waits until this wave's loads of slice `ready` are done, given the
   // slices issued so far (0 .. issued-1), leaving younger ones in flight.
-  const int KT = job.K / BK;
+  const int KT = job.klen / BK;
+  const int kbeg = job.k0;
   auto wait_slice = [&](int ready, int issued) {
     const int younger = issued - 1 - ready;
     if (younger >= 2) wait_vmcnt<2 * BPW>();
@@ -359,16 +379,16 @@ gemm_bf16_mfma_kernel(const GemmArgs args) {
     mma(af0, bf0);
     if (s + 1 < KT) wait_slice(s + 1, s + 3 < KT ? s + 3 : KT);
     barrier();
-    if (s + 3 < KT) dma(refill, (s + 3) * BK);
+    if (s + 3 < KT) dma(refill, kbeg + (s + 3) * BK);
     if (s + 1 < KT) load_frags(next, kpos0, af0, bf0);
     __builtin_amdgcn_sched_barrier(0);
     mma(af1, bf1);
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  dma(st0, 0);
-  if (KT > 1) dma(st1, BK);
-  if (KT > 2) dma(st2, 2 * BK);
+  dma(st0, kbeg);
+  if (KT > 1) dma(st1, kbeg + BK);
+  if (KT > 2) dma(st2, kbeg + 2 * BK);
   wait_slice(0, KT < 3 ? KT : 3);
   barrier();
   load_frags(st0, kpos0, af0, bf0);
@@ -431,9 +451,14 @@ gemm_bf16_mfma_kernel(const GemmArgs args) {
         } else {
           if (n >= job.N) continue;
           const f32x16_t& Cv = acc[0][i][j];
-          uint2 pk = make_uint2(pack_bf16x2(Cv[4 * q], Cv[4 * q + 1]),
-                                pack_bf16x2(Cv[4 * q + 2], Cv[4 * q + 3]));
-          *reinterpret_cast<uint2*>(job.C + (long long)m * job.ldc + n) = pk;
+          if (job.P) {
+            *reinterpret_cast<float4*>(job.P + (long long)m * job.N + n) =
+                make_float4(Cv[4 * q], Cv[4 * q + 1], Cv[4 * q + 2], Cv[4 * q + 3]);
+          } else {
+            uint2 pk = make_uint2(pack_bf16x2(Cv[4 * q], Cv[4 * q + 1]),
+                                  pack_bf16x2(Cv[4 * q + 2], Cv[4 * q + 3]));
+            *reinterpret_cast<uint2*>(job.C + (long long)m * job.ldc + n) = pk;
+          }
         }
       }
     }

@@ -65,8 +65,10 @@ struct FfnWs {
   int32_t* tiles2;  // [E + 1] tile prefix of FC2
   void* h;          // [R, F] dtype
   void* h_shared;   // [T, Fs] dtype
+  float* part;      // [ksplit, R, d] fp32 split-K partials of FC2
 };
 bool ffn_uses_mfma(const moe_shape& s);
+int ffn_fc2_ksplit(const moe_shape& s);
 hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const int32_t* offsets,
                               const void* w_gate, const void* w_up, const void* w_down,
                               const void* x, const void* ws_gate, const void* ws_up,

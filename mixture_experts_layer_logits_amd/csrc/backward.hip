@@ -1,16 +1,581 @@
-// Backward of the routed MoE layer (placeholder until its kernels land).
+// Backward of the routed MoE layer (Primus blog, MegaMoE section: the
+// backward mirrors the forward through dispatch/combine duality, with the
+// FC2 and FC1 data-gradient GEMMs plus two variable-K weight-gradient GEMMs).
+//
+//   b1+b7  per token: dY_perm[row] = rnd(w dy[t]), d_gate = <dy[t], y_perm[row]>,
+//          d_logits through the gate function
+//   b2     dh = dY_perm . w_down[e]; epilogue: dg = rnd(dh u silu'(g)),
+//          du = rnd(dh silu(g)), h = rnd(silu(g) u) from the saved g, u
+//   b3     dw_down[e] = dY_perm^T . h          (K = rows of expert e)
+//   b4     dX_perm = [dg | du] . [w_gate[e]; w_up[e]]
+//   b5     [dw_gate[e]; dw_up[e]] = [dg | du]^T . x_perm   (K = rows of e)
+//   b6     dx[t] = sum_j dX_perm[token_row[t, j]]
+//
+// The GEMMs take each operand either K-contiguous ("row" operands, as in the
+// forward) or M-contiguous ("column" operands: a weight read against its
+// storage order, or activations contracted over rows).  Column operands are
+// transposed in registers on their way to LDS, so the MFMA fragment reads
+// are the same 16-byte row reads as in the forward kernel.  Weight-gradient
+// tiles of experts without rows run zero K steps and store exact zeros.
+#include <float.h>
+
 #include "gemm_tiles.h"
 
 namespace moe {
 
-bool backward_supported(const moe_shape&) { return false; }
+bool backward_supported(const moe_shape&) { return true; }
 
-hipError_t launch_backward(const moe_shape&, const void*, const void*, const void*,
-                           const void*, const int32_t*, const int32_t*, const int32_t*,
-                           const int32_t*, const float*, const float*, const void*,
-                           const void*, const void*, float*, float*, float*, float*,
-                           float*, float*, const BwdWs&, hipStream_t) {
-  return hipErrorNotSupported;
+// ---------------------------------------------------------------------------
+// b1 + b7: one workgroup per token.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(256)
+bwd_dispatch_kernel(const T* __restrict__ dy, const T* __restrict__ y_perm,
+                    const int32_t* __restrict__ token_row, const int32_t* __restrict__ topk_idx,
+                    const float* __restrict__ topk_w, const float* __restrict__ logits, int d,
+                    int E, int k, int score, int renorm, T* __restrict__ dY,
+                    float* __restrict__ d_gate, float* __restrict__ d_logits) {
+  __shared__ float red[256];
+  __shared__ float s_dg[64];
+  __shared__ float s_stat[4];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const T* dyt = dy + (long long)t * d;
+  for (int j = 0; j < k; ++j) {
+    const int r = token_row[(long long)t * k + j];
+    const float w = topk_w[(long long)t * k + j];
+    float part = 0.0f;
+    if (r >= 0) {
+      for (int c = tid; c < d; c += 256) {
+        const float g = to_f32<T>(dyt[c]);
+        dY[(long long)r * d + c] = from_f32<T>(w * g);
+        part = fmaf(g, to_f32<T>(y_perm[(long long)r * d + c]), part);
+      }
+    }
+    red[tid] = part;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+      if (tid < off) red[tid] += red[tid + off];
+      __syncthreads();
+    }
+    if (tid == 0) {
+      s_dg[j] = red[0];
+      d_gate[(long long)t * k + j] = red[0];
+    }
+    __syncthreads();
+  }
+  // d_logits[t, :]
+  const float* lt = logits + (long long)t * E;
+  const int32_t* it = topk_idx + (long long)t * k;
+  const float* wt = topk_w + (long long)t * k;
+  if (tid == 0) {
+    float dot = 0.0f, ssum = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      dot += wt[j] * s_dg[j];
+      if (score == MOE_SCORE_SIGMOID) ssum += 1.0f / (1.0f + expf(-lt[it[j]]));
+    }
+    s_stat[0] = dot;
+    s_stat[1] = ssum;
+  }
+  float mx = -FLT_MAX, z = 0.0f;
+  if (score == MOE_SCORE_SOFTMAX && !renorm) {
+    float m = -FLT_MAX;
+    for (int e = tid; e < E; e += 256) m = fmaxf(m, lt[e]);
+    red[tid] = m;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+      if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
+      __syncthreads();
+    }
+    mx = red[0];
+    __syncthreads();
+    float zs = 0.0f;
+    for (int e = tid; e < E; e += 256) zs += expf(lt[e] - mx);
+    red[tid] = zs;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+      if (tid < off) red[tid] += red[tid + off];
+      __syncthreads();
+    }
+    z = red[0];
+    // sum_j dg_j p_{e_j}
+    if (tid == 0) {
+      float q = 0.0f;
+      for (int j = 0; j < k; ++j) q += s_dg[j] * (expf(lt[it[j]] - mx) / z);
+      s_stat[2] = q;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) {
+    int jsel = -1;
+    for (int j = 0; j < k; ++j)
+      if (it[j] == e) jsel = j;
+    float v = 0.0f;
+    if (score == MOE_SCORE_SOFTMAX) {
+      if (renorm) {
+        if (jsel >= 0) v = wt[jsel] * (s_dg[jsel] - s_stat[0]);
+      } else {
+        const float p = expf(lt[e] - mx) / z;
+        v = -p * s_stat[2] + (jsel >= 0 ? p * s_dg[jsel] : 0.0f);
+      }
+    } else if (jsel >= 0) {
+      const float sg = 1.0f / (1.0f + expf(-lt[e]));
+      const float ds = renorm ? (s_dg[jsel] - s_stat[0]) / s_stat[1] : s_dg[jsel];
+      v = ds * sg * (1.0f - sg);
+    }
+    d_logits[(long long)t * E + e] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// b6: dx[t] = sum_j dX_perm[token_row[t, j]] (fp32, fixed order).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(256)
+bwd_gather_kernel(const T* __restrict__ dX, const int32_t* __restrict__ token_row, int d, int k,
+                  float* __restrict__ dx) {
+  const int t = blockIdx.x;
+  const int32_t* rows = token_row + (long long)t * k;
+  for (int c = threadIdx.x; c < d; c += 256) {
+    float acc = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const int r = rows[j];
+      if (r >= 0) acc += to_f32<T>(dX[(long long)r * d + c]);
+    }
+    dx[(long long)t * d + c] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward GEMM problems.  C[m, n] = sum_k A(m, k) B(n, k) with
+//   row operand:    X(i, k) at base[i * ld + k]
+//   column operand: X(i, k) at base[k * ld + i]
+// ---------------------------------------------------------------------------
+enum { BWD_DH = 0, BWD_DX = 1, BWD_WD = 2, BWD_WGU = 3 };
+
+struct BwdArgs {
+  int E, F, d;
+  const int32_t* offsets;
+  const int32_t* tiles;    // row-grouped modes: tile prefix per expert
+  const void* dY;          // [R, d]
+  const void* gu;          // [R, 2F] saved g | u
+  const void* dgu;         // [R, 2F]
+  const void* h;           // [R, F]
+  const void* x_perm;      // [R, d]
+  const void* w_gate;      // [E, F, d]
+  const void* w_up;        // [E, F, d]
+  const void* w_down;      // [E, d, F]
+  void* out_dgu;           // BWD_DH: dg | du
+  void* out_h;             // BWD_DH: h
+  void* out_dX;            // BWD_DX
+  float* dw_down;          // BWD_WD
+  float* dw_gate;          // BWD_WGU
+  float* dw_up;
+};
+
+// The operands of one tile, resolved from the mode.
+template <typename T>
+struct BwdJob {
+  const T* A; long long lda; bool a_col;
+  const T* B0; const T* B1; long long ldb; bool b_col; int kswitch;  // B1 for k >= kswitch
+  int M_valid, N_valid, K;    // rows of A valid in this tile's group (row modes)
+  int m0, n0;
+  int row0, e;
+};
+
+template <int MODE, int BM, int BN, typename T>
+__device__ __forceinline__ bool bwd_decode(const BwdArgs& a, BwdJob<T>& j) {
+  const int bid = blockIdx.x;
+  if (MODE == BWD_DH || MODE == BWD_DX) {
+    const int total = a.tiles[a.E];
+    const int per = (total + 7) >> 3, slot = bid >> 3;
+    if (slot >= per) return false;
+    const int lid = (bid & 7) * per + slot;
+    if (lid >= total) return false;
+    int lo = 0, hi = a.E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.tiles[mid] <= lid) lo = mid; else hi = mid - 1;
+    }
+    const int g = lo;
+    const int row0 = a.offsets[g], rows = a.offsets[g + 1] - row0;
+    const int mt = cdiv(rows, BM), r = lid - a.tiles[g];
+    j.m0 = (r % mt) * BM;
+    j.n0 = (r / mt) * BN;
+    j.row0 = row0;
+    j.e = g;
+    j.M_valid = rows;
+    if (MODE == BWD_DH) {
+      j.A = static_cast<const T*>(a.dY) + (long long)row0 * a.d; j.lda = a.d; j.a_col = false;
+      j.B0 = static_cast<const T*>(a.w_down) + (long long)g * a.d * a.F;
+      j.B1 = j.B0; j.ldb = a.F; j.b_col = true; j.kswitch = 1 << 30;
+      j.N_valid = a.F; j.K = a.d;
+    } else {
+      j.A = static_cast<const T*>(a.dgu) + (long long)row0 * 2 * a.F; j.lda = 2LL * a.F; j.a_col = false;
+      j.B0 = static_cast<const T*>(a.w_gate) + (long long)g * a.F * a.d;
+      j.B1 = static_cast<const T*>(a.w_up) + (long long)g * a.F * a.d - (long long)a.F * a.d;
+      j.ldb = a.d; j.b_col = true; j.kswitch = a.F;   // rows k >= F come from w_up[k - F]
+      j.N_valid = a.d; j.K = 2 * a.F;
+    }
+    return true;
+  }
+  // per-expert weight gradients: fixed tile grid, K = rows of the expert
+  const int Mtot = (MODE == BWD_WD) ? a.d : 2 * a.F;
+  const int Ntot = (MODE == BWD_WD) ? a.F : a.d;
+  const int mt = cdiv(Mtot, BM), nt = cdiv(Ntot, BN);
+  const int total = a.E * mt * nt;
+  const int per = (total + 7) >> 3, slot = bid >> 3;
+  if (slot >= per) return false;
+  const int lid = (bid & 7) * per + slot;
+  if (lid >= total) return false;
+  const int g = lid / (mt * nt), r = lid - g * mt * nt;
+  j.m0 = (r % mt) * BM;
+  j.n0 = (r / mt) * BN;
+  j.e = g;
+  j.row0 = a.offsets[g];
+  j.K = a.offsets[g + 1] - j.row0;
+  j.M_valid = Mtot;
+  j.N_valid = Ntot;
+  if (MODE == BWD_WD) {
+    j.A = static_cast<const T*>(a.dY) + (long long)j.row0 * a.d; j.lda = a.d; j.a_col = true;
+    j.B0 = static_cast<const T*>(a.h) + (long long)j.row0 * a.F; j.ldb = a.F; j.b_col = true;
+  } else {
+    j.A = static_cast<const T*>(a.dgu) + (long long)j.row0 * 2 * a.F; j.lda = 2LL * a.F; j.a_col = true;
+    j.B0 = static_cast<const T*>(a.x_perm) + (long long)j.row0 * a.d; j.ldb = a.d; j.b_col = true;
+  }
+  j.B1 = j.B0;
+  j.kswitch = 1 << 30;
+  return true;
+}
+
+// Epilogue for one output element group of 4 consecutive columns.
+template <int MODE, typename T>
+__device__ __forceinline__ void bwd_store4(const BwdArgs& a, const BwdJob<T>& j, int m, int n,
+                                           const float (&v)[4], bool precise) {
+  if (MODE == BWD_DH) {
+    const long long r = (long long)(j.row0 + m);
+    const T* gu = static_cast<const T*>(a.gu) + r * 2 * a.F;
+    T* dgu = static_cast<T*>(a.out_dgu) + r * 2 * a.F;
+    T* h = static_cast<T*>(a.out_h) + r * a.F;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float g = to_f32<T>(gu[n + q]), u = to_f32<T>(gu[a.F + n + q]);
+      const float sg = 1.0f / (1.0f + (precise ? expf(-g) : __expf(-g)));
+      const float sl = g * sg;
+      dgu[n + q] = from_f32<T>(v[q] * u * sg * (1.0f + g * (1.0f - sg)));
+      dgu[a.F + n + q] = from_f32<T>(v[q] * sl);
+      h[n + q] = from_f32<T>(sl * u);
+    }
+  } else if (MODE == BWD_DX) {
+    T* o = static_cast<T*>(a.out_dX) + (long long)(j.row0 + m) * a.d + n;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = from_f32<T>(v[q]);
+  } else {
+    float* o;
+    if (MODE == BWD_WD) {
+      o = a.dw_down + ((long long)j.e * a.d + m) * a.F + n;
+    } else {
+      o = (m < a.F) ? a.dw_gate + ((long long)j.e * a.F + m) * a.d + n
+                    : a.dw_up + ((long long)j.e * a.F + (m - a.F)) * a.d + n;
+    }
+    *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA backward tile kernel: 4 waves (2 x 2), 128 x 128 tile, K slices
+// of 32 through two padded LDS stages, next slice prefetched into registers.
+// Row operands: each thread moves two 16-byte chunks (row c/4, k-chunk c%4).
+// Column operands: each thread loads two k-rows x 8 columns and writes them
+// transposed as eight (k, k+1) pairs, one per column.
+// ---------------------------------------------------------------------------
+template <int MODE>
+__global__ void __launch_bounds__(256)
+bwd_mfma_kernel(const BwdArgs args) {
+  constexpr int BM = 128, BN = 128, BK = 32, LDK = BK + 8;
+  constexpr int WTM = 64, WTN = 64, MI = 2, NJ = 2;
+  constexpr int STAGE = (BM + BN) * LDK;
+  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * STAGE];
+
+  BwdJob<bf16_t> job;
+  if (!bwd_decode<MODE, BM, BN>(args, job)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  // row-operand chunk mapping
+  const int rc_row = tid >> 2, rc_k = (tid & 3) * 8;
+  // column-operand mapping: k pair kp, 8-column chunk mc
+  const int kp = tid & 15, mc = tid >> 4;
+  const bool row_modes = (MODE == BWD_DH || MODE == BWD_DX);
+
+  u32x4_t ra[2], rb[2];
+  // Loads slice k0 of one operand into registers.
+  auto load_row = [&](const bf16_t* base, long long ld, int r0, int rvalid, int k0, u32x4_t (&reg)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      int r = r0 + rc_row + 64 * i;
+      r = r < rvalid ? r : rvalid - 1;
+      reg[i] = *reinterpret_cast<const u32x4_t*>(base + (long long)r * ld + k0 + rc_k);
+    }
+  };
+  auto load_col = [&](const bf16_t* base, long long ld, int c0, int k0, int kvalid, u32x4_t (&reg)[2]) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int kk = k0 + 2 * kp + q;
+      if (kk < kvalid)
+        reg[q] = *reinterpret_cast<const u32x4_t*>(base + (long long)kk * ld + c0 + mc * 8);
+      else
+        reg[q] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_row = [&](bf16_t* s, const u32x4_t (&reg)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<u32x4_t*>(&s[(rc_row + 64 * i) * LDK + rc_k]) = reg[i];
+  };
+  auto store_col = [&](bf16_t* s, const u32x4_t (&reg)[2]) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t a = reg[0][w], b = reg[1][w];
+      const uint32_t lo = (a & 0xffffu) | (b << 16);
+      const uint32_t hi = (a >> 16) | (b & 0xffff0000u);
+      *reinterpret_cast<uint32_t*>(&s[(mc * 8 + 2 * w) * LDK + 2 * kp]) = lo;
+      *reinterpret_cast<uint32_t*>(&s[(mc * 8 + 2 * w + 1) * LDK + 2 * kp]) = hi;
+    }
+  };
+  const int K = job.K;
+  auto gload = [&](int k0) {
+    if (row_modes) load_row(job.A, job.lda, job.m0, job.M_valid, k0, ra);
+    else load_col(job.A, job.lda, job.m0, k0, K, ra);
+    const bf16_t* B = (k0 >= job.kswitch) ? job.B1 : job.B0;
+    load_col(B, job.ldb, job.n0, k0, K, rb);
+  };
+  auto lstore = [&](int stage) {
+    bf16_t* sA = smem + stage * STAGE;
+    bf16_t* sB = sA + BM * LDK;
+    if (row_modes) store_row(sA, ra); else store_col(sA, ra);
+    store_col(sB, rb);
+  };
+
+  f32x16_t acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.0f;
+
+  const int KT = cdiv(K, BK);
+  const int frag_row = lane & 31, frag_k = (lane >> 5) * 8;
+  if (KT > 0) {
+    gload(0);
+    lstore(0);
+    __syncthreads();
+  }
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT) gload((kt + 1) * BK);
+    const bf16_t* sA = smem + cur * STAGE;
+    const bf16_t* sB = sA + BM * LDK;
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 16) {
+      bf16x8_t af[MI], bfr[NJ];
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t*>(&sA[(wm * WTM + i * 32 + frag_row) * LDK + kk + frag_k]);
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj)
+        bfr[jj] = *reinterpret_cast<const bf16x8_t*>(&sB[(wn * WTN + jj * 32 + frag_row) * LDK + kk + frag_k]);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[jj], af[i], acc[i][jj], 0, 0, 0);
+    }
+    if (kt + 1 < KT) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int m = job.m0 + wm * WTM + i * 32 + frag_row;
+    if (row_modes && m >= job.M_valid) continue;
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = job.n0 + wn * WTN + jj * 32 + 8 * q + 4 * (lane >> 5);
+        const float v[4] = {acc[i][jj][4 * q], acc[i][jj][4 * q + 1], acc[i][jj][4 * q + 2],
+                            acc[i][jj][4 * q + 3]};
+        bwd_store4<MODE, bf16_t>(args, job, m, n, v, false);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Generic backward tile kernel (any shape, fp32 or bf16 storage, fp32 FMA):
+// 64 x 64 tiles, K slices of 16, strided operand access.
+// ---------------------------------------------------------------------------
+template <int MODE, typename T>
+__global__ void __launch_bounds__(256)
+bwd_generic_kernel(const BwdArgs args) {
+  constexpr int BM = 64, BN = 64, BK = 16;
+  __shared__ float sA[BK][BM + 4];
+  __shared__ float sB[BK][BN + 4];
+  BwdJob<T> job;
+  if (!bwd_decode<MODE, BM, BN>(args, job)) return;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < job.K; k0 += BK) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + 256 * i;
+      const int r = e / BK, kk = e % BK;
+      const int m = job.m0 + r, k = k0 + kk;
+      float va = 0.0f;
+      const bool mv = (MODE == BWD_DH || MODE == BWD_DX) ? (m < job.M_valid) : (m < job.M_valid);
+      if (mv && k < job.K)
+        va = to_f32<T>(job.a_col ? job.A[(long long)k * job.lda + m] : job.A[(long long)m * job.lda + k]);
+      sA[kk][r] = va;
+      const int n = job.n0 + r;
+      float vb = 0.0f;
+      if (n < job.N_valid && k < job.K) {
+        const T* B = (k >= job.kswitch) ? job.B1 : job.B0;
+        vb = to_f32<T>(job.b_col ? B[(long long)k * job.ldb + n] : B[(long long)n * job.ldb + k]);
+      }
+      sB[kk][r] = vb;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK; ++kk) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = sA[kk][ty * 4 + i];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) bv[jj] = sB[kk][tx * 4 + jj];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) acc[i][jj] = fmaf(av[i], bv[jj], acc[i][jj]);
+    }
+    __syncthreads();
+  }
+  for (int i = 0; i < 4; ++i) {
+    const int m = job.m0 + ty * 4 + i;
+    if (m >= job.M_valid) continue;
+    for (int jj = 0; jj < 4; ++jj) {
+      const int n = job.n0 + tx * 4 + jj;
+      if (n >= job.N_valid) continue;
+      const float v = acc[i][jj];
+      if (MODE == BWD_DH) {
+        const long long r = (long long)(job.row0 + m);
+        const T* gu = static_cast<const T*>(args.gu) + r * 2 * args.F;
+        const float g = to_f32<T>(gu[n]), u = to_f32<T>(gu[args.F + n]);
+        const float sg = 1.0f / (1.0f + expf(-g));
+        const float sl = g * sg;
+        static_cast<T*>(args.out_dgu)[r * 2 * args.F + n] = from_f32<T>(v * u * sg * (1.0f + g * (1.0f - sg)));
+        static_cast<T*>(args.out_dgu)[r * 2 * args.F + args.F + n] = from_f32<T>(v * sl);
+        static_cast<T*>(args.out_h)[r * args.F + n] = from_f32<T>(sl * u);
+      } else if (MODE == BWD_DX) {
+        static_cast<T*>(args.out_dX)[(long long)(job.row0 + m) * args.d + n] = from_f32<T>(v);
+      } else if (MODE == BWD_WD) {
+        args.dw_down[((long long)job.e * args.d + m) * args.F + n] = v;
+      } else {
+        float* o = (m < args.F) ? args.dw_gate + ((long long)job.e * args.F + m) * args.d + n
+                                : args.dw_up + ((long long)job.e * args.F + (m - args.F)) * args.d + n;
+        *o = v;
+      }
+    }
+  }
+}
+
+static bool bwd_uses_mfma(const moe_shape& s) {
+  return s.dtype == MOE_DTYPE_BF16 && s.d % 128 == 0 && s.F % 128 == 0;
+}
+
+template <int MODE, typename T, bool MFMA>
+static void launch_bwd_gemm(const moe_shape& s, const BwdArgs& a, hipStream_t st) {
+  constexpr int BM = MFMA ? 128 : 64, BN = MFMA ? 128 : 64;
+  const long long R = (long long)s.T * s.k;
+  long long tiles;
+  if (MODE == BWD_DH) tiles = (cdiv((int)R, BM) + s.E) * (long long)cdiv(s.F, BN);
+  else if (MODE == BWD_DX) tiles = (cdiv((int)R, BM) + s.E) * (long long)cdiv(s.d, BN);
+  else if (MODE == BWD_WD) tiles = (long long)s.E * cdiv(s.d, BM) * cdiv(s.F, BN);
+  else tiles = (long long)s.E * cdiv(2 * s.F, BM) * cdiv(s.d, BN);
+  const int grid = (int)(((tiles + 7) / 8) * 8);
+  if (grid == 0) return;
+  if constexpr (MFMA) bwd_mfma_kernel<MODE><<<grid, 256, 0, st>>>(a);
+  else bwd_generic_kernel<MODE, T><<<grid, 256, 0, st>>>(a);
+}
+
+template <typename T, bool MFMA>
+static hipError_t run_backward(const moe_shape& s, BwdArgs& a, const BwdWs& ws, hipStream_t st) {
+  constexpr int BM = MFMA ? 128 : 64, BN = MFMA ? 128 : 64;
+  // tile prefixes of the two row-grouped GEMMs (N = F for dh, N = d for dX)
+  schedule_tiles_kernel<<<1, 1024, 0, st>>>(a.offsets, s.E, BM, cdiv(s.F, BN), ws.tiles, BM,
+                                            cdiv(s.d, BN), ws.tiles2);
+  a.tiles = ws.tiles;
+  launch_bwd_gemm<BWD_DH, T, MFMA>(s, a, st);
+  launch_bwd_gemm<BWD_WD, T, MFMA>(s, a, st);
+  a.tiles = ws.tiles2;
+  launch_bwd_gemm<BWD_DX, T, MFMA>(s, a, st);
+  launch_bwd_gemm<BWD_WGU, T, MFMA>(s, a, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward(const moe_shape& s, const void* dy, const void* x_perm,
+                           const void* gu_save, const void* y_perm, const int32_t* offsets,
+                           const int32_t* row_token, const int32_t* token_row,
+                           const int32_t* topk_idx, const float* topk_w,
+                           const float* logits, const void* w_gate, const void* w_up,
+                           const void* w_down, float* dx, float* dw_gate, float* dw_up,
+                           float* dw_down, float* d_gate, float* d_logits,
+                           const BwdWs& ws, hipStream_t st) {
+  (void)row_token;
+  const bool bf = s.dtype == MOE_DTYPE_BF16;
+  if (s.T > 0) {
+    if (bf)
+      bwd_dispatch_kernel<bf16_t><<<s.T, 256, 0, st>>>(
+          static_cast<const bf16_t*>(dy), static_cast<const bf16_t*>(y_perm), token_row, topk_idx,
+          topk_w, logits, s.d, s.E, s.k, s.score, s.renorm, static_cast<bf16_t*>(ws.dY), d_gate,
+          d_logits);
+    else
+      bwd_dispatch_kernel<float><<<s.T, 256, 0, st>>>(
+          static_cast<const float*>(dy), static_cast<const float*>(y_perm), token_row, topk_idx,
+          topk_w, logits, s.d, s.E, s.k, s.score, s.renorm, static_cast<float*>(ws.dY), d_gate,
+          d_logits);
+  }
+  BwdArgs a = {};
+  a.E = s.E;
+  a.F = s.F;
+  a.d = s.d;
+  a.offsets = offsets;
+  a.dY = ws.dY;
+  a.gu = gu_save;
+  a.dgu = ws.dgu;
+  a.h = ws.h;
+  a.x_perm = x_perm;
+  a.w_gate = w_gate;
+  a.w_up = w_up;
+  a.w_down = w_down;
+  a.out_dgu = ws.dgu;
+  a.out_h = ws.h;
+  a.out_dX = ws.dX;
+  a.dw_down = dw_down;
+  a.dw_gate = dw_gate;
+  a.dw_up = dw_up;
+  hipError_t e;
+  if (bf && bwd_uses_mfma(s)) e = run_backward<bf16_t, true>(s, a, ws, st);
+  else if (bf) e = run_backward<bf16_t, false>(s, a, ws, st);
+  else e = run_backward<float, false>(s, a, ws, st);
+  if (e != hipSuccess) return e;
+  if (s.T > 0) {
+    if (bf)
+      bwd_gather_kernel<bf16_t><<<s.T, 256, 0, st>>>(static_cast<const bf16_t*>(ws.dX), token_row,
+                                                     s.d, s.k, dx);
+    else
+      bwd_gather_kernel<float><<<s.T, 256, 0, st>>>(static_cast<const float*>(ws.dX), token_row,
+                                                    s.d, s.k, dx);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -41,6 +41,7 @@ _TENSOR_IDS = {
     "x": 1, "w_router": 2, "router_bias": 3, "score_bias": 4,
     "w_gate": 5, "w_up": 6, "w_down": 7,
     "ws_gate": 8, "ws_up": 9, "ws_down": 10, "dy": 11, "zipf_rank": 12,
+    "logits": 13, "routing": 14, "gates": 15, "rows": 16,
 }
 
 
@@ -192,3 +193,34 @@ def round_robin_topk(T: int, E: int, k: int) -> torch.Tensor:
     t = torch.arange(T, dtype=torch.int64).unsqueeze(1)
     j = torch.arange(k, dtype=torch.int64).unsqueeze(0)
     return ((t * k + j) % E).to(torch.int32)
+
+
+def random_topk(T: int, E: int, k: int, seed: int, weights=None) -> torch.Tensor:
+    """T rows of k distinct experts in [0, E), drawn without replacement with
+    per-expert selection weights (uniform when None; a skewed vector leaves
+    some experts without rows)."""
+    rng = np.random.Generator(np.random.PCG64(child_seed(seed, "routing")))
+    p = None
+    if weights is not None:
+        p = np.asarray(weights, dtype=np.float64)
+        p = p / p.sum()
+    out = np.empty((T, k), dtype=np.int32)
+    for t in range(T):
+        out[t] = rng.choice(E, size=k, replace=False, p=p)
+    return torch.from_numpy(out)
+
+
+def random_gates(T: int, k: int, seed: int) -> torch.Tensor:
+    """Positive fp32 combine weights (not normalised)."""
+    rng = np.random.Generator(np.random.PCG64(child_seed(seed, "gates")))
+    return torch.from_numpy(rng.uniform(0.05, 1.0, size=(T, k)).astype(np.float32))
+
+
+def random_logits(T: int, E: int, seed: int, std: float = 1.0,
+                  quantum: float = 0.0) -> torch.Tensor:
+    """fp32 router scores; with quantum > 0 they are rounded to multiples of
+    it, which plants exact ties."""
+    t = normal((T, E), std, torch.float32, "cpu", child_seed(seed, "logits"))
+    if quantum > 0:
+        t = torch.round(t / quantum) * quantum
+    return t

@@ -96,3 +96,69 @@ def oracle_sampled_forward(cfg, inp, tokens, idx, w):
         acc += w_s[:, j:j + 1] * y_rows[:, j]
     y = O.out_f32(prec)(acc)
     return dict(y_rows=y_rows, gu_rows=gu_rows, ys=ys, y=y)
+
+
+def logit_tolerance(d, logits):
+    """A bound on |fp32-accumulated - exact| router scores: 100 * u * sqrt(d)
+    * rms(l), u = 2^-24 (a random-walk estimate of fp32 summation error with
+    a wide margin), plus one fp32 rounding of the largest score."""
+    l = np64(logits)
+    rms = float(np.sqrt((l ** 2).mean())) if l.size else 0.0
+    return 100 * 2.0 ** -24 * np.sqrt(d) * rms + 2.0 ** -23 * float(np.abs(l).max(initial=0.0))
+
+
+def routing_keys(cfg, logits, score_bias):
+    """The oracle's selection keys and group scores (for ambiguity checks)."""
+    l = np64(logits)
+    if cfg.score == O.SCORE_SOFTMAX:
+        return l, None
+    s = O.sigmoid_scores(l)
+    key = s if score_bias is None else O.round_f32(s + np64(score_bias)[None, :])
+    G = cfg.E // cfg.n_groups
+    srt = -np.sort(-key.reshape(key.shape[0], cfg.n_groups, G), axis=2)
+    gs = srt[:, :, 0] + (srt[:, :, 1] if G >= 2 else 0.0)
+    return key, gs
+
+
+def ambiguous_tokens(cfg, logits, score_bias, tol, idx):
+    """Tokens whose routing could change if the scores moved by tol, judged
+    on the oracle's own selection idx: two consecutive picks, or the last
+    pick and the best unpicked candidate of the kept groups, are closer than
+    the bound (or, with a group limit, the kept and dropped groups are).
+    Decided by the oracle alone."""
+    key, gs = routing_keys(cfg, logits, score_bias)
+    ktol = tol if cfg.score == O.SCORE_SOFTMAX else tol / 4 + 2.0 ** -24
+    T, E = key.shape
+    idx = np.asarray(idx, dtype=np.int64)
+    sel = np.take_along_axis(key, idx, axis=1)
+    amb = (sel[:, :-1] - sel[:, 1:] < 2 * ktol).any(axis=1) if cfg.k > 1 else np.zeros(T, bool)
+    allowed = np.ones((T, E), dtype=bool)
+    if gs is not None and cfg.topk_groups < cfg.n_groups:
+        g = -np.sort(-gs, axis=1)
+        amb |= g[:, cfg.topk_groups - 1] - g[:, cfg.topk_groups] < 4 * ktol
+        G = E // cfg.n_groups
+        kept = np.zeros((T, cfg.n_groups), dtype=bool)
+        np.put_along_axis(kept, idx // G, True, axis=1)
+        allowed = np.repeat(kept, G, axis=1)
+    rest = np.where(allowed, key, -np.inf)
+    np.put_along_axis(rest, idx, -np.inf, axis=1)
+    best_rest = rest.max(axis=1)
+    amb |= sel[:, -1] - best_rest < 2 * ktol
+    return amb
+
+
+def check_maps_valid(out, idx, E):
+    """Properties every correct permutation has, checked on GPU outputs that
+    may follow a (valid) routing different from the oracle's."""
+    idx = np.asarray(idx, dtype=np.int64)
+    T, k = idx.shape
+    offs = out["expert_offsets"].cpu().numpy().astype(np.int64)
+    counts = np.bincount(idx.reshape(-1), minlength=E)
+    assert np.array_equal(offs, np.concatenate([[0], np.cumsum(counts)]))
+    rt = out["row_token"].cpu().numpy()
+    tr = out["token_row"].cpu().numpy()
+    assert np.array_equal(rt[tr.reshape(-1)], np.repeat(np.arange(T), k))
+    for e in range(E):
+        seg = rt[offs[e]:offs[e + 1]]
+        assert np.all(np.diff(seg) > 0)
+        assert np.all((idx[seg] == e).any(axis=1))

@@ -1,0 +1,141 @@
+"""End-to-end GPU parity of the layer (route -> permute -> grouped FFN ->
+combine) against the oracle run entirely on its own inputs.
+
+The oracle computes its own router scores in fp64 and routes from them.
+Routing must match bit for bit on every token whose selection is
+unambiguous at fp32 resolution (decided by the oracle: see
+parity_util.ambiguous_tokens); where the oracle finds a near-tie, any
+selection valid within that bound is accepted.  When routing matches
+everywhere (the expected case), every map is compared bit for bit.
+Full-size workloads compare sampled token rows computed one expert at a
+time.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from moe_inputs import CONFIGS, MoEConfig, SCORE_SIGMOID, make_inputs
+from parity_util import (ambiguous_tokens, assert_close, assert_equal_int, check_maps_valid,
+                         logit_tolerance, np64, oracle_sampled_forward, prec_of, sample_tokens)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "tiny_fp32": CONFIGS["tiny_fp32"],
+    "bf16_softmax_t300": MoEConfig("bf16_softmax_t300", T=300, d=256, E=8, k=2, F=384),
+    "bf16_sigmoid_groups_shared_t200": MoEConfig(
+        "bf16_sigmoid_groups_shared_t200", T=200, d=128, E=64, k=8, F=128,
+        F_shared=192, n_groups=8, topk_groups=4, score=SCORE_SIGMOID, score_bias_std=0.1),
+    "bf16_skewed_t520": MoEConfig("bf16_skewed_t520", T=520, d=192, E=32, k=4, F=256,
+                                  zipf_s=1.2),
+    "bf16_generic_shapes_t77": MoEConfig("bf16_generic_shapes_t77", T=77, d=200, E=6, k=2,
+                                         F=96, F_shared=40),
+    "f32_odd_t37": MoEConfig("f32_odd_t37", T=37, d=20, E=5, k=3, F=12, dtype=0),
+    "bf16_single_expert_t65": MoEConfig("bf16_single_expert_t65", T=65, d=64, E=1, k=1, F=64),
+    "bf16_one_token": MoEConfig("bf16_one_token", T=1, d=128, E=16, k=4, F=128),
+    "bf16_full_probs_t129": MoEConfig("bf16_full_probs_t129", T=129, d=128, E=12, k=3,
+                                      F=192, renorm=0),
+}
+
+
+def _run(cfg, inp=None):
+    from mixture_experts_layer_logits_amd import MoELayer
+    if inp is None:
+        inp = make_inputs(cfg, device="cuda")
+    layer = MoELayer(cfg)
+    out = layer.forward(inp)
+    torch.cuda.synchronize()
+    return inp, layer, out
+
+
+def _route_and_check(cfg, inp, out):
+    """Oracle routing from its own scores; returns (idx, w, ambiguous, same)."""
+    ref_l = O.router_logits(inp["x"], inp["w_router"], inp.get("router_bias"), "f32")
+    assert_close("logits", out["logits"], ref_l, "f32")
+    sb = inp.get("score_bias")
+    idx, w = O.route(ref_l, cfg.k, cfg.score, cfg.renorm, cfg.n_groups, cfg.topk_groups,
+                     None if sb is None else np64(sb), prec_of(cfg))
+    amb = ambiguous_tokens(cfg, ref_l, None if sb is None else np64(sb),
+                           logit_tolerance(cfg.d, ref_l), idx)
+    gidx = out["topk_idx"].cpu().numpy()
+    ok = ~amb
+    assert_equal_int("topk_idx[unambiguous]", gidx[ok], idx[ok])
+    assert_close("topk_w[unambiguous]", out["topk_w"][torch.as_tensor(ok).cuda()], w[ok], "f32")
+    same = bool(np.array_equal(gidx, idx))
+    print(f"  ambiguous tokens {int(amb.sum())} of {cfg.T}; routing identical: {same}", flush=True)
+    return idx, w, amb, same
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_small(name):
+    cfg = SMALL[name]
+    print(f"[layer] {name}", flush=True)
+    inp, layer, out = _run(cfg)
+    prec = prec_of(cfg)
+    idx, w, amb, same = _route_and_check(cfg, inp, out)
+    ref = O.forward(inp, cfg, prec=prec)
+    if same:
+        assert_equal_int("expert_offsets", out["expert_offsets"], ref["offsets"])
+        assert_equal_int("row_token", out["row_token"], ref["row_token"])
+        assert_equal_int("token_row", out["token_row"], ref["token_row"])
+        rt = torch.as_tensor(ref["row_token"], device="cuda").long()
+        assert torch.equal(out["x_perm"], inp["x"][rt])
+        assert_close("y_perm", out["y_perm"], ref["y_perm"], prec)
+    else:
+        check_maps_valid(out, out["topk_idx"].cpu().numpy(), cfg.E)
+    if cfg.F_shared > 0:
+        assert_close("y_shared", out["y_shared"], ref["y_shared"], prec)
+    ok = torch.as_tensor(~amb | same)
+    assert_close("y", out["y"][ok.cuda()], ref["y"][ok.numpy()], prec)
+
+
+def test_layer_is_bitwise_deterministic():
+    cfg = SMALL["bf16_sigmoid_groups_shared_t200"].replace(T=1000)
+    inp, layer, out = _run(cfg)
+    first = {k: v.clone() for k, v in out.items() if v is not None}
+    layer.forward(inp)
+    torch.cuda.synchronize()
+    for k, v in first.items():
+        assert torch.equal(v, out[k]), k
+
+
+FULL = ["mixtral_t4096", "deepseek_v3_t8192", "qwen3_30b_skewed_t16384",
+        "qwen3_235b_train_t8192"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_layer_full_size_sampled(name):
+    cfg = CONFIGS[name]
+    print(f"[layer full] {name}", flush=True)
+    inp, layer, out = _run(cfg)
+    prec = prec_of(cfg)
+    idx, w, amb, same = _route_and_check(cfg, inp, out)
+    p = O.permute(None, idx, w, cfg.E)
+    counts = np.diff(p["offsets"])
+    print(f"  rows/expert min {counts.min()} max {counts.max()} zero {int((counts == 0).sum())}",
+          flush=True)
+    if cfg.zipf_s > 0:
+        assert (counts == 0).any(), "the skewed workload must leave an expert empty"
+    if same:
+        assert_equal_int("expert_offsets", out["expert_offsets"], p["offsets"])
+        assert_equal_int("row_token", out["row_token"], p["row_token"])
+        assert_equal_int("token_row", out["token_row"], p["token_row"])
+        rt = torch.as_tensor(p["row_token"], device="cuda").long()
+        assert torch.equal(out["x_perm"], inp["x"][rt])
+    else:
+        check_maps_valid(out, out["topk_idx"].cpu().numpy(), cfg.E)
+    n = 16 if cfg.E >= 256 else 48
+    toks = np.array([t for t in sample_tokens(cfg.T, n) if not amb[t]])
+    tt = torch.as_tensor(toks, device="cuda")
+    ref = oracle_sampled_forward(cfg, inp, toks, idx, w)
+    rows = out["token_row"][tt].reshape(-1).long()
+    assert_close("y_perm[sample]", out["y_perm"][rows], ref["y_rows"].reshape(-1, cfg.d), prec)
+    if out["gu_save"] is not None:
+        assert_close("gu_save[sample]", out["gu_save"][rows],
+                     ref["gu_rows"].reshape(-1, 2 * cfg.F), prec)
+    if cfg.F_shared > 0:
+        assert_close("y_shared[sample]", out["y_shared"][tt], ref["ys"], prec)
+    assert_close("y[sample]", out["y"][tt], ref["y"], prec)
+    del layer, out, inp
+    torch.cuda.empty_cache()

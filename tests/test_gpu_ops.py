@@ -1,0 +1,306 @@
+"""GPU parity of each C-ABI entry point against the CPU oracle, on seeded
+synthetic inputs that both sides receive (nothing the GPU computes is fed to
+the oracle).  Integer outputs must match bit for bit; float outputs within
+the tolerance of the storage type."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from moe_inputs import (CONFIGS, MoEConfig, SCORE_SIGMOID, child_seed, expert_weight,
+                        make_inputs, normal, random_gates, random_logits, random_topk)
+from parity_util import assert_close, assert_equal_int, np64, prec_of, sample_tokens
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _lib():
+    import mixture_experts_layer_logits_amd as M
+    return M
+
+
+def _ws(M, shape, op):
+    n = M.moe_workspace_size(shape, op)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device="cuda"), n
+
+
+# --------------------------------------------------------------------------
+# moe_route_topk with the scores given as input: bit-exact selection
+# --------------------------------------------------------------------------
+ROUTE_CASES = [
+    # name, cfg overrides, logits std, tie quantum
+    ("softmax_top2_of_8", dict(T=1000, E=8, k=2), 1.0, 0.0),
+    ("softmax_near_uniform", dict(T=4096, E=8, k=2), 0.064, 0.0),
+    ("softmax_ties", dict(T=2000, E=16, k=4), 1.0, 0.25),
+    ("softmax_full_probs", dict(T=700, E=40, k=5, renorm=0), 1.0, 0.0),
+    ("softmax_top8_of_128", dict(T=3000, E=128, k=8), 1.0, 0.0),
+    ("softmax_k_equals_E", dict(T=300, E=6, k=6), 1.0, 0.5),
+    ("softmax_top8_of_512", dict(T=500, E=512, k=8), 1.0, 0.0),
+    ("softmax_k64_of_1024", dict(T=64, E=1024, k=64), 1.0, 0.0),
+    ("sigmoid_groups_256", dict(T=3000, E=256, k=8, n_groups=8, topk_groups=4,
+                                score=SCORE_SIGMOID, score_bias_std=0.1), 1.7, 0.0),
+    ("sigmoid_groups_ties", dict(T=1000, E=64, k=6, n_groups=8, topk_groups=3,
+                                 score=SCORE_SIGMOID, score_bias_std=0.1), 1.0, 0.5),
+    ("sigmoid_single_group_norenorm", dict(T=500, E=32, k=4, score=SCORE_SIGMOID,
+                                           renorm=0), 1.0, 0.0),
+]
+
+
+@pytest.mark.parametrize("name,over,std,quantum", ROUTE_CASES, ids=[c[0] for c in ROUTE_CASES])
+def test_route_topk_from_given_scores(name, over, std, quantum):
+    _log(f"[route] {name}")
+    M = _lib()
+    cfg = MoEConfig(name, d=64, F=64, **over)
+    logits = random_logits(cfg.T, cfg.E, seed=len(name), std=std, quantum=quantum)
+    sb = None
+    if cfg.score_bias_std > 0:
+        sb = normal((cfg.E,), cfg.score_bias_std, torch.float32, "cpu",
+                    child_seed(7, "score_bias"))
+        if quantum > 0:
+            sb = torch.round(sb / quantum) * quantum
+    ref_idx, ref_w = O.route(logits, cfg.k, cfg.score, cfg.renorm, cfg.n_groups,
+                             cfg.topk_groups, sb, "f32")
+    lg = logits.cuda()
+    sbg = None if sb is None else sb.cuda()
+    idx = torch.empty(cfg.T, cfg.k, dtype=torch.int32, device="cuda")
+    w = torch.empty(cfg.T, cfg.k, dtype=torch.float32, device="cuda")
+    M.moe_route_topk(M.make_shape(cfg), None, None, None, lg, sbg, idx, w)
+    torch.cuda.synchronize()
+    assert_equal_int("topk_idx", idx, ref_idx)
+    assert_close("topk_w", w, ref_w, "f32")
+    assert torch.equal(lg.cpu(), logits)  # an input stays untouched
+
+
+@pytest.mark.parametrize("dtype,d,E", [(0, 128, 8), (1, 4096, 8), (1, 7168, 256), (1, 200, 24),
+                                       (0, 37, 5)])
+def test_router_logits_gemm(dtype, d, E):
+    _log(f"[router gemm] dtype={dtype} d={d} E={E}")
+    M = _lib()
+    cfg = MoEConfig("router", T=700, d=d, E=E, k=2, F=64, dtype=dtype, zipf_s=1.2)
+    inp = make_inputs(cfg, device="cuda", with_weights=False)
+    prec = prec_of(cfg)
+    logits = torch.empty(cfg.T, E, device="cuda")
+    idx = torch.empty(cfg.T, 2, dtype=torch.int32, device="cuda")
+    w = torch.empty(cfg.T, 2, device="cuda")
+    M.moe_route_topk(M.make_shape(cfg), inp["x"], inp["w_router"], inp["router_bias"],
+                     logits, None, idx, w)
+    torch.cuda.synchronize()
+    ref = O.router_logits(inp["x"], inp["w_router"], inp["router_bias"], "f32")
+    # fp32 outputs of an fp32 (or exact bf16-product) accumulation
+    assert_close("logits", logits, ref, "f32")
+
+
+# --------------------------------------------------------------------------
+# moe_permute on synthetic routing
+# --------------------------------------------------------------------------
+PERMUTE_CASES = [
+    ("uniform_t4096_e8_k2", 4096, 8, 2, None, 1, 64),
+    ("skewed_t3000_e128_k8", 3000, 128, 8, "zipf", 1, 256),
+    ("ragged_t777_e13_k3", 777, 13, 3, None, 0, 36),
+    ("all_experts_t300_e6_k6", 300, 6, 6, None, 1, 64),
+    ("one_expert_t257_e1_k1", 257, 1, 1, None, 1, 16),
+    ("one_token_t1_e64_k8", 1, 64, 8, None, 1, 128),
+    ("many_experts_t600_e1024_k4", 600, 1024, 4, "zipf", 1, 24),
+    ("odd_row_bytes_t100_e7_k2", 100, 7, 2, None, 1, 13),
+]
+
+
+@pytest.mark.parametrize("name,T,E,k,skew,dtype,d", PERMUTE_CASES, ids=[c[0] for c in PERMUTE_CASES])
+def test_permute_maps_and_rows(name, T, E, k, skew, dtype, d):
+    _log(f"[permute] {name}")
+    M = _lib()
+    cfg = MoEConfig(name, T=T, d=d, E=E, k=k, F=64, dtype=dtype)
+    wts = [1.0 / (r + 1) ** 1.2 for r in range(E)] if skew else None
+    idx = random_topk(T, E, k, seed=T + E, weights=wts)
+    gates = random_gates(T, k, seed=T)
+    x = normal((T, d), 1.0, cfg.torch_dtype, "cpu", child_seed(3, "x"))
+    ref = O.permute(None, idx.numpy(), gates.numpy(), E)
+    R = T * k
+    dev = lambda *s, dt=torch.int32: torch.empty(*s, dtype=dt, device="cuda")
+    offs, rt, tr = dev(E + 1), dev(R), dev(T, k)
+    rg = dev(R, dt=torch.float32)
+    xp = dev(R, d, dt=cfg.torch_dtype)
+    shape = M.make_shape(cfg)
+    ws, n = _ws(M, shape, 1)
+    M.moe_permute(shape, x.cuda(), idx.cuda(), gates.cuda(), offs, rt, tr, rg, xp, ws, n)
+    torch.cuda.synchronize()
+    assert_equal_int("expert_offsets", offs, ref["offsets"])
+    assert_equal_int("row_token", rt, ref["row_token"])
+    assert_equal_int("token_row", tr, ref["token_row"])
+    assert np.array_equal(rg.cpu().numpy(), ref["row_gate"].astype(np.float32))
+    assert torch.equal(xp.cpu(), x[torch.as_tensor(ref["row_token"]).long()])
+
+
+def test_permute_no_tokens():
+    M = _lib()
+    cfg = MoEConfig("empty", T=0, d=64, E=8, k=2, F=64)
+    shape = M.make_shape(cfg)
+    offs = torch.full((9,), 7, dtype=torch.int32, device="cuda")
+    e = torch.empty(0, device="cuda")
+    ws, n = _ws(M, shape, 1)
+    M.moe_permute(shape, e, e, e, offs, e, e, e, e, ws, n)
+    torch.cuda.synchronize()
+    assert offs.cpu().tolist() == [0] * 9
+
+
+# --------------------------------------------------------------------------
+# moe_grouped_ffn on synthetic expert-contiguous rows
+# --------------------------------------------------------------------------
+FFN_CASES = [
+    # name, T, d, E, k, F, Fs, dtype, skew
+    ("mfma_splitk_t300", 300, 256, 8, 2, 384, 0, 1, None),
+    ("mfma_shared_t200", 200, 128, 64, 8, 128, 192, 1, None),
+    ("mfma_skewed_empty_t600", 600, 192, 32, 4, 256, 0, 1, "zipf"),
+    ("generic_bf16_t77", 77, 200, 6, 2, 96, 40, 1, None),
+    ("fp32_t256", 256, 128, 8, 2, 256, 0, 0, None),
+    ("fp32_odd_t37", 37, 20, 5, 3, 12, 8, 0, None),
+    ("single_expert_t65", 65, 64, 1, 1, 64, 0, 1, None),
+]
+
+
+def _ffn_inputs(cfg, skew):
+    wts = [1.0 / (r + 1) ** 6 for r in range(cfg.E)] if skew else None
+    idx = random_topk(cfg.T, cfg.E, cfg.k, seed=cfg.T, weights=wts)
+    p = O.permute(None, idx.numpy(), np.ones((cfg.T, cfg.k)), cfg.E)
+    inp = make_inputs(cfg, device="cuda")
+    xp = normal((cfg.R, cfg.d), 1.0, cfg.torch_dtype, "cuda", child_seed(5, "rows"))
+    return p, inp, xp
+
+
+@pytest.mark.parametrize("case", FFN_CASES, ids=[c[0] for c in FFN_CASES])
+def test_grouped_ffn(case):
+    name, T, d, E, k, F, Fs, dtype, skew = case
+    _log(f"[ffn] {name}")
+    M = _lib()
+    cfg = MoEConfig(name, T=T, d=d, E=E, k=k, F=F, F_shared=Fs, dtype=dtype)
+    prec = prec_of(cfg)
+    p, inp, xp = _ffn_inputs(cfg, skew)
+    if skew:
+        assert (np.diff(p["offsets"]) == 0).any()
+    dt = cfg.torch_dtype
+    yp = torch.empty(cfg.R, d, dtype=dt, device="cuda")
+    ys = torch.empty(T, d, dtype=dt, device="cuda") if Fs else None
+    gu = torch.empty(cfg.R, 2 * F, dtype=dt, device="cuda")
+    shape = M.make_shape(cfg)
+    ws, n = _ws(M, shape, 2)
+    M.moe_grouped_ffn(shape, xp, torch.as_tensor(p["offsets"]).cuda(), inp["w_gate"], inp["w_up"],
+                      inp["w_down"], inp["x"] if Fs else None, inp["ws_gate"], inp["ws_up"],
+                      inp["ws_down"], yp, ys, gu, ws, n)
+    torch.cuda.synchronize()
+    ref_y, ref_gu = O.grouped_ffn(xp, p["offsets"], np64(inp["w_gate"]), np64(inp["w_up"]),
+                                  np64(inp["w_down"]), prec, save_gu=True)
+    assert_close("y_perm", yp, ref_y, prec)
+    assert_close("gu_save", gu, ref_gu, prec)
+    if Fs:
+        assert_close("y_shared", ys, O.shared_ffn(inp["x"], inp["ws_gate"], inp["ws_up"],
+                                                  inp["ws_down"], prec), prec)
+
+
+# --------------------------------------------------------------------------
+# moe_unpermute_combine on synthetic rows
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("T,d,E,k,shared,dtype", [(1000, 512, 8, 2, False, 1), (333, 96, 16, 4, True, 1),
+                                                  (100, 20, 5, 3, True, 0), (50, 13, 4, 2, False, 1)])
+def test_unpermute_combine(T, d, E, k, shared, dtype):
+    _log(f"[combine] T={T} d={d} k={k} shared={shared}")
+    M = _lib()
+    cfg = MoEConfig("combine", T=T, d=d, E=E, k=k, F=64, F_shared=64 if shared else 0, dtype=dtype)
+    idx = random_topk(T, E, k, seed=d)
+    gates = random_gates(T, k, seed=d)
+    p = O.permute(None, idx.numpy(), gates.numpy(), E)
+    dt = cfg.torch_dtype
+    yp = normal((cfg.R, d), 1.0, dt, "cuda", child_seed(9, "rows"))
+    ys = normal((T, d), 1.0, dt, "cuda", child_seed(9, "x")) if shared else None
+    y = torch.empty(T, d, device="cuda")
+    M.moe_unpermute_combine(M.make_shape(cfg), yp, torch.as_tensor(p["token_row"]).cuda(),
+                            gates.cuda(), ys, y)
+    torch.cuda.synchronize()
+    ref = O.combine(yp, p["token_row"], gates.numpy(), None if ys is None else ys, "f32")
+    assert_close("y", y, ref, "f32")
+
+
+# --------------------------------------------------------------------------
+# moe_ffn_backward on synthetic saved tensors
+# --------------------------------------------------------------------------
+def _bwd_inputs(cfg, skew=None, dev="cuda"):
+    """Saved forward tensors drawn directly (the backward is defined for any
+    values of them): routing from synthetic scores, x_perm, g | u, y_perm
+    and dy as seeded normals with the layer's typical scales."""
+    dt = cfg.torch_dtype
+    logits = random_logits(cfg.T, cfg.E, seed=cfg.T + 1)
+    if skew:
+        logits = logits + torch.tensor([-8.0 * np.log(r + 1) for r in range(cfg.E)],
+                                       dtype=torch.float32)
+    idx, w = O.route(logits, cfg.k, cfg.score, cfg.renorm, cfg.n_groups, cfg.topk_groups,
+                     None, "f32")
+    p = O.permute(None, idx, w, cfg.E)
+    g = dict(logits=logits, idx=idx, w=w, p=p)
+    g["x_perm"] = normal((cfg.R, cfg.d), 1.0, dt, dev, child_seed(11, "rows"))
+    g["gu"] = normal((cfg.R, 2 * cfg.F), 1.3, dt, dev, child_seed(12, "rows"))
+    g["y_perm"] = normal((cfg.R, cfg.d), 0.1, dt, dev, child_seed(13, "rows"))
+    g["dy"] = normal((cfg.T, cfg.d), 1.0, dt, dev, child_seed(14, "rows"))
+    return g
+
+
+def _run_bwd(M, cfg, inp, g):
+    dev = "cuda"
+    f32 = torch.float32
+    out = dict(dx=torch.empty(cfg.T, cfg.d, device=dev),
+               dw_gate=torch.empty(cfg.E, cfg.F, cfg.d, device=dev),
+               dw_up=torch.empty(cfg.E, cfg.F, cfg.d, device=dev),
+               dw_down=torch.empty(cfg.E, cfg.d, cfg.F, device=dev),
+               d_gate=torch.empty(cfg.T, cfg.k, device=dev),
+               d_logits=torch.empty(cfg.T, cfg.E, device=dev))
+    for v in out.values():
+        v.fill_(float("nan"))
+    shape = M.make_shape(cfg)
+    ws, n = _ws(M, shape, 4)
+    i32 = lambda a: torch.as_tensor(np.asarray(a, dtype=np.int32)).cuda()
+    M.moe_ffn_backward(shape, g["dy"], g["x_perm"], g["gu"], g["y_perm"], i32(g["p"]["offsets"]),
+                       i32(g["p"]["row_token"]), i32(g["p"]["token_row"]), i32(g["idx"]),
+                       torch.as_tensor(g["w"], dtype=f32).cuda(), g["logits"].cuda(),
+                       inp["w_gate"], inp["w_up"], inp["w_down"], out["dx"], out["dw_gate"],
+                       out["dw_up"], out["dw_down"], out["d_gate"], out["d_logits"], ws, n)
+    torch.cuda.synchronize()
+    return out
+
+
+BWD_CASES = [
+    # name, T, d, E, k, F, dtype, score, renorm, skew
+    ("mfma_softmax_t300", 300, 256, 8, 2, 256, 1, 0, 1, False),
+    ("mfma_skewed_empty_t400", 400, 128, 16, 4, 128, 1, 0, 1, True),
+    ("mfma_sigmoid_t200", 200, 128, 32, 4, 128, 1, 1, 1, False),
+    ("generic_bf16_t77", 77, 200, 6, 2, 96, 1, 0, 0, False),
+    ("fp32_t128", 128, 64, 8, 2, 64, 0, 0, 1, False),
+    ("fp32_odd_full_probs_t37", 37, 20, 5, 3, 12, 0, 0, 0, True),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_ffn_backward(case):
+    name, T, d, E, k, F, dtype, score, renorm, skew = case
+    _log(f"[backward] {name}")
+    M = _lib()
+    cfg = MoEConfig(name, T=T, d=d, E=E, k=k, F=F, dtype=dtype, score=score, renorm=renorm,
+                    backward=True)
+    prec = prec_of(cfg)
+    inp = make_inputs(cfg, device="cuda")
+    g = _bwd_inputs(cfg, skew)
+    out = _run_bwd(M, cfg, inp, g)
+    ref = O.ffn_backward(g["dy"], g["x_perm"], g["gu"], g["y_perm"], g["p"]["offsets"],
+                         g["p"]["token_row"], g["idx"], g["w"], g["logits"], np64(inp["w_gate"]),
+                         np64(inp["w_up"]), np64(inp["w_down"]), score, renorm, prec)
+    for key in ("d_gate", "d_logits", "dx", "dw_gate", "dw_up", "dw_down"):
+        assert_close(key, out[key], ref[key], "f32" if prec == "f32" else "bf16")
+    counts = np.diff(g["p"]["offsets"])
+    for e in np.nonzero(counts == 0)[0]:
+        for key in ("dw_gate", "dw_up", "dw_down"):
+            assert torch.all(out[key][int(e)] == 0), (key, e)
+    if skew:
+        assert (counts == 0).any()

@@ -304,3 +304,56 @@ def test_ffn_backward(case):
             assert torch.all(out[key][int(e)] == 0), (key, e)
     if skew:
         assert (counts == 0).any()
+
+
+def test_ffn_backward_full_size_sampled():
+    """The training workload's shape: sampled tokens for d_gate, d_logits and
+    dx; three whole experts (first, middle, last) for the weight gradients."""
+    cfg = CONFIGS["qwen3_235b_train_t8192"]
+    _log(f"[backward full] {cfg.name}")
+    M = _lib()
+    inp = make_inputs(cfg, device="cuda")
+    g = _bwd_inputs(cfg)
+    out = _run_bwd(M, cfg, inp, g)
+    p = g["p"]
+    tr, rt = p["token_row"], p["row_token"]
+    w = np.asarray(g["w"], dtype=np.float64)
+    toks = sample_tokens(cfg.T, 64)
+    dy = np64(g["dy"][torch.as_tensor(toks).cuda()])
+
+    def dY_rows(rows):
+        """dY_perm for permuted rows: w[t, j] dy[t], rounded to bf16."""
+        t = rt[rows]
+        j = np.argmax(tr[t] == rows[:, None], axis=1)
+        dyt = np64(g["dy"][torch.as_tensor(t).cuda()])
+        return O.round_bf16(w[t, j][:, None] * dyt)
+
+    # d_gate and d_logits on sampled tokens
+    rows = tr[toks]
+    yp = np64(g["y_perm"][torch.as_tensor(rows.reshape(-1)).cuda()]).reshape(len(toks), cfg.k, cfg.d)
+    d_gate = np.einsum("td,tjd->tj", dy, yp)
+    assert_close("d_gate[sample]", out["d_gate"][torch.as_tensor(toks).cuda()], d_gate, "bf16")
+    d_l = O.router_backward(d_gate, g["idx"][toks], g["w"][toks], g["logits"][toks], cfg.E)
+    assert_close("d_logits[sample]", out["d_logits"][torch.as_tensor(toks).cuda()], d_l, "bf16")
+    # dx on sampled tokens: each row's dX depends on that row only
+    flat = rows.reshape(-1)
+    ex = np.searchsorted(p["offsets"], flat, side="right") - 1
+    dX = np.zeros((len(flat), cfg.d))
+    for e in np.unique(ex):
+        sel = np.nonzero(ex == e)[0]
+        rr = torch.as_tensor(flat[sel]).cuda()
+        r = O.expert_backward(dY_rows(flat[sel]), g["x_perm"][rr], g["gu"][rr],
+                              np64(inp["w_gate"][int(e)]), np64(inp["w_up"][int(e)]),
+                              np64(inp["w_down"][int(e)]), "bf16")
+        dX[sel] = r["dX"]
+    dx = dX.reshape(len(toks), cfg.k, cfg.d).sum(axis=1)
+    assert_close("dx[sample]", out["dx"][torch.as_tensor(toks).cuda()], dx, "bf16")
+    # weight gradients of whole experts
+    for e in (0, cfg.E // 2, cfg.E - 1):
+        a, b = int(p["offsets"][e]), int(p["offsets"][e + 1])
+        rr = torch.arange(a, b, device="cuda")
+        r = O.expert_backward(dY_rows(np.arange(a, b)), g["x_perm"][rr], g["gu"][rr],
+                              np64(inp["w_gate"][e]), np64(inp["w_up"][e]),
+                              np64(inp["w_down"][e]), "bf16")
+        for key in ("dw_gate", "dw_up", "dw_down"):
+            assert_close(f"{key}[{e}]", out[key][e], r[key], "bf16")

@@ -40,29 +40,54 @@ bwd_dispatch_kernel(const T* __restrict__ dy, const T* __restrict__ y_perm,
   __shared__ float s_stat[4];
   const int t = blockIdx.x, tid = threadIdx.x;
   const T* dyt = dy + (long long)t * d;
+  const int lane = tid & 63, wave = tid >> 6;
+  __shared__ float s_part[64][4];
+  const bool vec = (sizeof(T) == 2) && (d % 8 == 0);
   for (int j = 0; j < k; ++j) {
     const int r = token_row[(long long)t * k + j];
     const float w = topk_w[(long long)t * k + j];
     float part = 0.0f;
     if (r >= 0) {
-      for (int c = tid; c < d; c += 256) {
-        const float g = to_f32<T>(dyt[c]);
-        dY[(long long)r * d + c] = from_f32<T>(w * g);
-        part = fmaf(g, to_f32<T>(y_perm[(long long)r * d + c]), part);
+      if (vec) {
+        // 8 bf16 per thread and step: one 16-byte load of dy and y_perm,
+        // one 16-byte store of w * dy
+        const bf16_t* dyb = reinterpret_cast<const bf16_t*>(dyt);
+        const bf16_t* ypb = reinterpret_cast<const bf16_t*>(y_perm) + (long long)r * d;
+        bf16_t* dYb = reinterpret_cast<bf16_t*>(dY) + (long long)r * d;
+        for (int c = tid * 8; c < d; c += 256 * 8) {
+          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(dyb + c);
+          const u32x4_t yv = *reinterpret_cast<const u32x4_t*>(ypb + c);
+          u32x4_t o;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float g0 = __uint_as_float(a[q] << 16), g1 = __uint_as_float(a[q] & 0xffff0000u);
+            const float y0 = __uint_as_float(yv[q] << 16), y1 = __uint_as_float(yv[q] & 0xffff0000u);
+            part = fmaf(g0, y0, part);
+            part = fmaf(g1, y1, part);
+            o[q] = pack_bf16x2(w * g0, w * g1);
+          }
+          *reinterpret_cast<u32x4_t*>(dYb + c) = o;
+        }
+      } else {
+        for (int c = tid; c < d; c += 256) {
+          const float g = to_f32<T>(dyt[c]);
+          dY[(long long)r * d + c] = from_f32<T>(w * g);
+          part = fmaf(g, to_f32<T>(y_perm[(long long)r * d + c]), part);
+        }
       }
     }
-    red[tid] = part;
-    __syncthreads();
-    for (int off = 128; off > 0; off >>= 1) {
-      if (tid < off) red[tid] += red[tid + off];
-      __syncthreads();
-    }
-    if (tid == 0) {
-      s_dg[j] = red[0];
-      d_gate[(long long)t * k + j] = red[0];
-    }
-    __syncthreads();
+    // wave reduction (fixed butterfly order), partials combined below
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+    if (lane == 0) s_part[j][wave] = part;
   }
+  __syncthreads();
+  if (tid < k) {
+    const float v = (s_part[tid][0] + s_part[tid][1]) + (s_part[tid][2] + s_part[tid][3]);
+    s_dg[tid] = v;
+    d_gate[(long long)t * k + tid] = v;
+  }
+  __syncthreads();
   // d_logits[t, :]
   const float* lt = logits + (long long)t * E;
   const int32_t* it = topk_idx + (long long)t * k;
@@ -135,6 +160,26 @@ bwd_gather_kernel(const T* __restrict__ dX, const int32_t* __restrict__ token_ro
                   float* __restrict__ dx) {
   const int t = blockIdx.x;
   const int32_t* rows = token_row + (long long)t * k;
+  if (sizeof(T) == 2 && d % 8 == 0) {
+    const bf16_t* X = reinterpret_cast<const bf16_t*>(dX);
+    for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < k; ++j) {
+        const int r = rows[j];
+        if (r < 0) continue;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(X + (long long)r * d + c);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] += __uint_as_float(v[q] << 16);
+          acc[2 * q + 1] += __uint_as_float(v[q] & 0xffff0000u);
+        }
+      }
+      float* o = dx + (long long)t * d + c;
+      *reinterpret_cast<float4*>(o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      *reinterpret_cast<float4*>(o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+    return;
+  }
   for (int c = threadIdx.x; c < d; c += 256) {
     float acc = 0.0f;
     for (int j = 0; j < k; ++j) {
@@ -252,23 +297,32 @@ template <int MODE, typename T>
 __device__ __forceinline__ void bwd_store4(const BwdArgs& a, const BwdJob<T>& j, int m, int n,
                                            const float (&v)[4], bool precise) {
   if (MODE == BWD_DH) {
+    // bf16 only (the MFMA path): 8-byte loads of 4 g and 4 u, 8-byte stores
     const long long r = (long long)(j.row0 + m);
-    const T* gu = static_cast<const T*>(a.gu) + r * 2 * a.F;
-    T* dgu = static_cast<T*>(a.out_dgu) + r * 2 * a.F;
-    T* h = static_cast<T*>(a.out_h) + r * a.F;
+    const bf16_t* gu = static_cast<const bf16_t*>(a.gu) + r * 2 * a.F;
+    bf16_t* dgu = static_cast<bf16_t*>(a.out_dgu) + r * 2 * a.F;
+    bf16_t* h = static_cast<bf16_t*>(a.out_h) + r * a.F;
+    const uint2 gq = *reinterpret_cast<const uint2*>(gu + n);
+    const uint2 uq = *reinterpret_cast<const uint2*>(gu + a.F + n);
+    const uint32_t gw[2] = {gq.x, gq.y}, uw[2] = {uq.x, uq.y};
+    float dg[4], du[4], hh[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float g = to_f32<T>(gu[n + q]), u = to_f32<T>(gu[a.F + n + q]);
+      const uint32_t gb = gw[q >> 1], ub = uw[q >> 1];
+      const float g = __uint_as_float((q & 1) ? (gb & 0xffff0000u) : (gb << 16));
+      const float u = __uint_as_float((q & 1) ? (ub & 0xffff0000u) : (ub << 16));
       const float sg = 1.0f / (1.0f + (precise ? expf(-g) : __expf(-g)));
       const float sl = g * sg;
-      dgu[n + q] = from_f32<T>(v[q] * u * sg * (1.0f + g * (1.0f - sg)));
-      dgu[a.F + n + q] = from_f32<T>(v[q] * sl);
-      h[n + q] = from_f32<T>(sl * u);
+      dg[q] = v[q] * u * sg * (1.0f + g * (1.0f - sg));
+      du[q] = v[q] * sl;
+      hh[q] = sl * u;
     }
+    *reinterpret_cast<uint2*>(dgu + n) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+    *reinterpret_cast<uint2*>(dgu + a.F + n) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+    *reinterpret_cast<uint2*>(h + n) = make_uint2(pack_bf16x2(hh[0], hh[1]), pack_bf16x2(hh[2], hh[3]));
   } else if (MODE == BWD_DX) {
-    T* o = static_cast<T*>(a.out_dX) + (long long)(j.row0 + m) * a.d + n;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) o[q] = from_f32<T>(v[q]);
+    bf16_t* o = static_cast<bf16_t*>(a.out_dX) + (long long)(j.row0 + m) * a.d + n;
+    *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
   } else {
     float* o;
     if (MODE == BWD_WD) {

@@ -541,13 +541,224 @@ bwd_generic_kernel(const BwdArgs args) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Backward GEMMs on the forward kernel's structure (256 x 256 tiles, 8 waves
+// of 64 x 128, direct global->LDS loads into a 4-stage ring of 32-wide K
+// slices).  An operand stored M-contiguous (a column operand) keeps its
+// storage order in LDS: 32 k-rows of 512 bytes, 16-byte chunk c of k-row r at
+// position c ^ 2 (r mod 4).  Its MFMA fragments come from two transposing
+// LDS reads (ds_read_b64_tr_b16): within each 16-lane group, lane j points at
+// k-row kb + j / 4, columns mb + 4 (j mod 4); lane i then receives the four
+// k-values of column mb + i, which is exactly the k-contiguous fragment a
+// row operand gives with one 16-byte read.  Weight-gradient tiles have
+// K = rows of the expert; the last slice's k-rows past K hold clamped data
+// and are zeroed in the A fragments before use.
+// ---------------------------------------------------------------------------
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+template <int MODE>
+__global__ void __launch_bounds__(512)
+bwd_dma_kernel(const BwdArgs args) {
+  constexpr int BM = 256, BN = 256, BK = 32, WM = 4, WN = 2;
+  constexpr int WTM = BM / WM, WTN = BN / WN, MI = WTM / 32, NJ = WTN / 32;
+  constexpr bool A_COL = (MODE == BWD_WD || MODE == BWD_WGU);
+  constexpr int OPB = BM * BK * 2;              // bytes of one operand per stage (16 KiB)
+  constexpr int STAGE = 2 * OPB / 2;            // elements per stage (A then B)
+  constexpr int BPW = 4;                        // 1 KiB load blocks per wave per stage
+  __shared__ __attribute__((aligned(1024))) bf16_t st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) bf16_t st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) bf16_t st2[STAGE];
+  __shared__ __attribute__((aligned(1024))) bf16_t st3[STAGE];
+
+  BwdJob<bf16_t> job;
+  if (!bwd_decode<MODE, BM, BN>(args, job)) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int K = job.K;
+  const int KT = cdiv(K, BK);
+
+  // ---- loads: waves 0-3 fill A (16 blocks), waves 4-7 fill B ------------
+  const bool load_a = wave < 4;
+  const int blk0 = (wave & 3) * BPW;            // first block within the operand
+  const bool col = load_a ? A_COL : true;       // B is a column operand in every mode
+  const bf16_t* src0 = load_a ? job.A : job.B0;
+  const bf16_t* src1 = load_a ? job.A : job.B1; // DX: rows k >= kswitch read B1
+  const long long ld = load_a ? job.lda : job.ldb;
+  const int mn0 = load_a ? job.m0 : job.n0;
+  uint32_t g_off[BPW];                          // byte offsets, k-independent part
+  int krow_l[BPW];                              // column operands: k-row of this lane
+#pragma unroll
+  for (int j = 0; j < BPW; ++j) {
+    const int b = blk0 + j;
+    if (col) {
+      const int kr = 2 * b + (lane >> 5);        // k-row within the slice
+      const int pos = lane & 31;
+      const int c = pos ^ (2 * (kr & 3));
+      krow_l[j] = kr;
+      g_off[j] = (uint32_t)(mn0 + c * 8) * 2u;
+    } else {
+      int r = mn0 + 16 * b + (lane >> 2);        // row operand (A of DH / DX)
+      r = r < job.M_valid ? r : job.M_valid - 1;
+      const int c = (lane & 3) ^ swz(lane >> 2);
+      krow_l[j] = 0;
+      g_off[j] = (uint32_t)(r * (int)ld + c * 8) * 2u;
+    }
+  }
+  const int lds_op = load_a ? 0 : OPB;           // byte offset of the operand in a stage
+  auto dma = [&](bf16_t* stage, int k0) {
+    const bf16_t* srcb = (k0 >= job.kswitch) ? src1 : src0;
+    const char* base = reinterpret_cast<const char*>(srcb) + (col ? 0 : (size_t)k0 * 2);
+#pragma unroll
+    for (int j = 0; j < BPW; ++j) {
+      uint32_t off = g_off[j];
+      if (col) {
+        int kr = k0 + krow_l[j];
+        kr = kr < K ? kr : K - 1;                 // clamp the tail (zeroed later)
+        off += (uint32_t)(kr * (int)ld) * 2u;
+      }
+      const uint32_t lds = (uint32_t)(uintptr_t)MOE_AS_LDS(reinterpret_cast<char*>(stage) + lds_op +
+                                                           (blk0 + j) * 1024);
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :: "s"(lds), "v"(off), "s"(base) : "memory");
+    }
+  };
+
+  // ---- fragments ----------------------------------------------------------
+  const int frag_row = lane & 31;
+  const int sw = swz(frag_row);
+  const int kpos0 = ((0 + (lane >> 5)) ^ sw) << 3;
+  const int kpos1 = ((2 + (lane >> 5)) ^ sw) << 3;
+  // column operand, per lane: k-row part and chunk part of the transposing read
+  const int tr_row = (8 * (lane >> 5) + ((lane & 15) >> 2)) * 512;
+  const int tr_swz = 2 * ((lane & 15) >> 2);
+  const int tr_c = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tr_half = (lane & 1) * 8;
+  auto col_frag = [&](const char* op, int kk, int mcol0) -> bf16x8_t {
+    const int c = (tr_c + (mcol0 >> 3)) ^ tr_swz;
+    const char* p = op + kk * 16 * 512 + tr_row + (c << 4) + tr_half;
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t*)MOE_AS_LDS(p));
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t*)MOE_AS_LDS(p + 4 * 512));
+    const auto v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8_t, v);
+  };
+  auto load_frags = [&](const bf16_t* stage, int kk, bf16x8_t (&af)[MI], bf16x8_t (&bfr)[NJ]) {
+    const char* sa = reinterpret_cast<const char*>(stage);
+    const char* sb = sa + OPB;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      if constexpr (A_COL) {
+        af[i] = col_frag(sa, kk, wm * WTM + i * 32);
+      } else {
+        const int off = (wm * WTM + i * 32 + frag_row) * BK + (kk ? kpos1 : kpos0);
+        af[i] = *reinterpret_cast<const bf16x8_t*>(reinterpret_cast<const bf16_t*>(sa) + off);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) bfr[j] = col_frag(sb, kk, wn * WTN + j * 32);
+  };
+  f32x16_t acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  auto mma = [&](const bf16x8_t (&af)[MI], const bf16x8_t (&bfr)[NJ]) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+  };
+  // zero the k-values >= K held by this lane in sub-step kk of slice s
+  auto mask_tail = [&](bf16x8_t (&af)[MI], int s, int kk) {
+    const int k0 = s * BK + kk * 16 + 8 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (k0 + e >= K) af[i][e] = (__bf16)0.0f;
+  };
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto wait_slice = [&](int ready, int issued) {
+    const int younger = issued - 1 - ready;
+    if (younger >= 2) wait_vmcnt<2 * BPW>();
+    else if (younger == 1) wait_vmcnt<BPW>();
+    else wait_vmcnt<0>();
+  };
+  const bool tail = A_COL && (K % BK) != 0;
+  bf16x8_t af0[MI], af1[MI], bf0[NJ], bf1[NJ];
+  auto step = [&](const bf16_t* cur, const bf16_t* next, bf16_t* refill, int s) {
+    load_frags(cur, 1, af1, bf1);
+    if (tail && s == KT - 1) mask_tail(af0, s, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(af0, bf0);
+    if (s + 1 < KT) wait_slice(s + 1, s + 3 < KT ? s + 3 : KT);
+    barrier();
+    if (s + 3 < KT) dma(refill, (s + 3) * BK);
+    if (s + 1 < KT) load_frags(next, 0, af0, bf0);
+    if (tail && s == KT - 1) mask_tail(af1, s, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(af1, bf1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if (KT > 0) {
+    dma(st0, 0);
+    if (KT > 1) dma(st1, BK);
+    if (KT > 2) dma(st2, 2 * BK);
+    wait_slice(0, KT < 3 ? KT : 3);
+    barrier();
+    load_frags(st0, 0, af0, bf0);
+    int kt = 0;
+    for (; kt + 4 <= KT; kt += 4) {
+      step(st0, st1, st3, kt);
+      step(st1, st2, st0, kt + 1);
+      step(st2, st3, st1, kt + 2);
+      step(st3, st0, st2, kt + 3);
+    }
+    if (kt < KT) step(st0, st1, st3, kt);
+    if (kt + 1 < KT) step(st1, st2, st0, kt + 1);
+    if (kt + 2 < KT) step(st2, st3, st1, kt + 2);
+  }
+
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int m = job.m0 + wm * WTM + i * 32 + frag_row;
+    if (!A_COL && m >= job.M_valid) continue;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = job.n0 + wn * WTN + j * 32 + 8 * q + 4 * (lane >> 5);
+        const float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                            acc[i][j][4 * q + 3]};
+        bwd_store4<MODE, bf16_t>(args, job, m, n, v, false);
+      }
+  }
+}
+
+static bool bwd_uses_dma(const moe_shape& s) {
+  return s.dtype == MOE_DTYPE_BF16 && s.d % 256 == 0 && s.F % 256 == 0;
+}
+
 static bool bwd_uses_mfma(const moe_shape& s) {
   return s.dtype == MOE_DTYPE_BF16 && s.d % 128 == 0 && s.F % 128 == 0;
 }
 
-template <int MODE, typename T, bool MFMA>
+// FLAVOR: 0 generic, 1 MFMA with register transposes, 2 direct-to-LDS MFMA
+template <int MODE, typename T, int FLAVOR>
 static void launch_bwd_gemm(const moe_shape& s, const BwdArgs& a, hipStream_t st) {
-  constexpr int BM = MFMA ? 128 : 64, BN = MFMA ? 128 : 64;
+  constexpr int BM = FLAVOR == 2 ? 256 : FLAVOR == 1 ? 128 : 64;
+  constexpr int BN = BM;
   const long long R = (long long)s.T * s.k;
   long long tiles;
   if (MODE == BWD_DH) tiles = (cdiv((int)R, BM) + s.E) * (long long)cdiv(s.F, BN);
@@ -556,22 +767,23 @@ static void launch_bwd_gemm(const moe_shape& s, const BwdArgs& a, hipStream_t st
   else tiles = (long long)s.E * cdiv(2 * s.F, BM) * cdiv(s.d, BN);
   const int grid = (int)(((tiles + 7) / 8) * 8);
   if (grid == 0) return;
-  if constexpr (MFMA) bwd_mfma_kernel<MODE><<<grid, 256, 0, st>>>(a);
+  if constexpr (FLAVOR == 2) bwd_dma_kernel<MODE><<<grid, 512, 0, st>>>(a);
+  else if constexpr (FLAVOR == 1) bwd_mfma_kernel<MODE><<<grid, 256, 0, st>>>(a);
   else bwd_generic_kernel<MODE, T><<<grid, 256, 0, st>>>(a);
 }
 
-template <typename T, bool MFMA>
+template <typename T, int FLAVOR>
 static hipError_t run_backward(const moe_shape& s, BwdArgs& a, const BwdWs& ws, hipStream_t st) {
-  constexpr int BM = MFMA ? 128 : 64, BN = MFMA ? 128 : 64;
+  constexpr int BM = FLAVOR == 2 ? 256 : FLAVOR == 1 ? 128 : 64, BN = BM;
   // tile prefixes of the two row-grouped GEMMs (N = F for dh, N = d for dX)
   schedule_tiles_kernel<<<1, 1024, 0, st>>>(a.offsets, s.E, BM, cdiv(s.F, BN), ws.tiles, BM,
                                             cdiv(s.d, BN), ws.tiles2);
   a.tiles = ws.tiles;
-  launch_bwd_gemm<BWD_DH, T, MFMA>(s, a, st);
-  launch_bwd_gemm<BWD_WD, T, MFMA>(s, a, st);
+  launch_bwd_gemm<BWD_DH, T, FLAVOR>(s, a, st);
+  launch_bwd_gemm<BWD_WD, T, FLAVOR>(s, a, st);
   a.tiles = ws.tiles2;
-  launch_bwd_gemm<BWD_DX, T, MFMA>(s, a, st);
-  launch_bwd_gemm<BWD_WGU, T, MFMA>(s, a, st);
+  launch_bwd_gemm<BWD_DX, T, FLAVOR>(s, a, st);
+  launch_bwd_gemm<BWD_WGU, T, FLAVOR>(s, a, st);
   return hipGetLastError();
 }
 
@@ -617,9 +829,10 @@ hipError_t launch_backward(const moe_shape& s, const void* dy, const void* x_per
   a.dw_gate = dw_gate;
   a.dw_up = dw_up;
   hipError_t e;
-  if (bf && bwd_uses_mfma(s)) e = run_backward<bf16_t, true>(s, a, ws, st);
-  else if (bf) e = run_backward<bf16_t, false>(s, a, ws, st);
-  else e = run_backward<float, false>(s, a, ws, st);
+  if (bf && bwd_uses_dma(s)) e = run_backward<bf16_t, 2>(s, a, ws, st);
+  else if (bf && bwd_uses_mfma(s)) e = run_backward<bf16_t, 1>(s, a, ws, st);
+  else if (bf) e = run_backward<bf16_t, 0>(s, a, ws, st);
+  else e = run_backward<float, 0>(s, a, ws, st);
   if (e != hipSuccess) return e;
   if (s.T > 0) {
     if (bf)

@@ -274,6 +274,8 @@ def _run_bwd(M, cfg, inp, g):
 BWD_CASES = [
     # name, T, d, E, k, F, dtype, score, renorm, skew
     ("mfma_softmax_t300", 300, 256, 8, 2, 256, 1, 0, 1, False),
+    ("dma_skewed_tails_t500", 500, 256, 16, 4, 512, 1, 0, 1, True),
+    ("dma_sigmoid_t333", 333, 512, 24, 3, 256, 1, 1, 1, False),
     ("mfma_skewed_empty_t400", 400, 128, 16, 4, 128, 1, 0, 1, True),
     ("mfma_sigmoid_t200", 200, 128, 32, 4, 128, 1, 1, 1, False),
     ("generic_bf16_t77", 77, 200, 6, 2, 96, 1, 0, 0, False),

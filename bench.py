@@ -28,6 +28,12 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
+# The grouped FFN's kernel sources; traffic figures recorded in profiles/ are
+# used only while these files are byte-identical to the ones profiled.
+FFN_SOURCES = ("mixture_experts_layer_logits_amd/csrc/ffn.hip",
+               "mixture_experts_layer_logits_amd/csrc/gemm_tiles.h",
+               "mixture_experts_layer_logits_amd/csrc/moe_common.h")
+
 
 def ffn_flops(c):
     R = c.T * c.k
@@ -50,13 +56,70 @@ def ffn_bytes(c, counts_nonzero):
     return w + act
 
 
-def cpu_baseline(cfg, inp, sample_tokens):
-    """The oracle, as it stands, on the first `sample_tokens` tokens."""
-    import torch
-    import oracle as O
-    from threadpoolctl import threadpool_info
+def permute_bytes(c):
+    """Algorithmic HBM bytes of moe_permute: topk_idx and topk_w read, x read
+    once, the four maps and x_perm written."""
+    b = 2 if c.dtype == 1 else 4
+    R = c.T * c.k
+    return 2 * R * 4 + c.T * c.d * b + (c.E + 1) * 4 + 3 * R * 4 + R * c.d * b
 
-    T = min(sample_tokens, cfg.T)
+
+def combine_bytes(c):
+    """Algorithmic HBM bytes of moe_unpermute_combine: y_perm, token_row and
+    topk_w read (y_shared too when present), fp32 y written."""
+    b = 2 if c.dtype == 1 else 4
+    R = c.T * c.k
+    extra = c.T * c.d * b if c.F_shared else 0
+    return R * c.d * b + 2 * R * 4 + extra + c.T * c.d * 4
+
+
+def sources_digest(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload):
+    """HBM bytes per moe_grouped_ffn call from the committed FETCH_SIZE /
+    WRITE_SIZE summary of this workload, or None when there is none or the
+    kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_moe_grouped_ffn_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("record:"):
+                for kv in line.split()[1:]:
+                    key, _, v = kv.partition("=")
+                    vals[key] = v
+    if vals.get("sources") != sources_digest(FFN_SOURCES):
+        return None
+    try:
+        return int(vals["bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration():
+    """A plain device copy of 1 GiB, three times, for scaling the FETCH_SIZE
+    and WRITE_SIZE counters (each copy reads and writes exactly 1 GiB)."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copied {n} bytes 3 times", flush=True)
+
+
+def _oracle_pass(cfg, inp, T):
+    import oracle as O
     sub = cfg.replace(T=T)
     host = {}
     for k, v in inp.items():
@@ -73,11 +136,28 @@ def cpu_baseline(cfg, inp, sample_tokens):
                        out["offsets"], out["token_row"], out["topk_idx"],
                        out["topk_w"], out["route_logits"], host["w_gate"],
                        host["w_up"], host["w_down"], cfg.score, cfg.renorm)
-    dt = time.perf_counter() - t0
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(cfg, inp, sample_tokens=None, target_s=15.0):
+    """The oracle, as it stands, on the first tokens of the same workload.
+    Without a fixed sample size, a first pass on a few tokens sizes a second
+    pass to about target_s seconds; the second pass is the one reported."""
+    from threadpoolctl import threadpool_info
+
+    if sample_tokens:
+        T = min(sample_tokens, cfg.T)
+        dt = _oracle_pass(cfg, inp, T)
+    else:
+        T = min(cfg.T, max(cfg.k, 64))
+        dt = _oracle_pass(cfg, inp, T)
+        if dt < target_s / 2 and T < cfg.T:
+            T = min(cfg.T, max(T + 1, int(T * target_s / max(dt, 1e-3))))
+            dt = _oracle_pass(cfg, inp, T)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()
                    if i.get("user_api") == "blas"] or [1])
     kind = "forward+backward" if cfg.backward else "forward"
-    return {"value": T / dt, "unit": "tokens/s", "cores": int(threads),
+    return {"value": round(T / dt, 2), "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"first {T} of {cfg.T} tokens of the same workload, whole "
                       f"{kind} layer in the fp64 oracle ({dt:.1f} s)"}
@@ -91,7 +171,13 @@ def main():
     ap.add_argument("--workload", default="mixtral_t4096")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for scaling "
+                         "the FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's layer; --gpus {args.gpus} is not "
               "supported (the layer is built and measured on a single GPU)",
@@ -157,16 +243,20 @@ def main():
         gbs = bytes_ / t_ffn / 1e9
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
-    roof["traffic"] = None
-    roof["kernel"] = "moe_grouped_ffn (FC1+SwiGLU and FC2 grouped GEMM launches)"
+    roof["traffic"] = recorded_traffic(cfg.name)
+    roof["algorithmic_bytes"] = int(bytes_)
+    roof["kernel"] = ("moe_grouped_ffn: one call = tile schedule, FC1+SwiGLU "
+                      "and FC2 grouped GEMM launches (+ split-K reduce)")
+
+    hbm = {}
+    for st, nb in (("permute", permute_bytes(cfg)), ("combine", combine_bytes(cfg))):
+        gbs = nb / (per_stage[st] / 1e3) / 1e9
+        hbm[st] = {"bytes": int(nb), "GB/s": round(gbs, 1),
+                   "frac": round(gbs / PEAK_HBM_GBS, 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
-        n = args.cpu_sample_tokens or {"tiny_fp32": 256, "mixtral_t4096": 512,
-                                       "deepseek_v3_t8192": 64,
-                                       "qwen3_30b_skewed_t16384": 2048,
-                                       "qwen3_235b_train_t8192": 256}[cfg.name]
-        cpu = cpu_baseline(cfg, inp, n)
+        cpu = cpu_baseline(cfg, inp, args.cpu_sample_tokens)
 
     rec = {
         "metric": "MoE-layer tokens/sec + grouped-GEMM TFLOPS (fraction of peak) on 1 MI355X",
@@ -182,6 +272,7 @@ def main():
         "grouped_gemm_tflops": round(tflops, 2),
         "grouped_gemm_frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "stage_ms": {k: round(v, 4) for k, v in per_stage.items()},
+        "stage_hbm": hbm,
         "event_ms_per_step": round(ms_step, 4),
         "roofline": roof,
         "cpu_baseline": cpu,

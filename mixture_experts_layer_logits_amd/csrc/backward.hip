@@ -777,7 +777,7 @@ static hipError_t run_backward(const moe_shape& s, BwdArgs& a, const BwdWs& ws, 
   constexpr int BM = FLAVOR == 2 ? 256 : FLAVOR == 1 ? 128 : 64, BN = BM;
   // tile prefixes of the two row-grouped GEMMs (N = F for dh, N = d for dX)
   schedule_tiles_kernel<<<1, 1024, 0, st>>>(a.offsets, s.E, BM, cdiv(s.F, BN), ws.tiles, BM,
-                                            cdiv(s.d, BN), ws.tiles2);
+                                            cdiv(s.d, BN), ws.tiles2, 0);
   a.tiles = ws.tiles;
   launch_bwd_gemm<BWD_DH, T, FLAVOR>(s, a, st);
   launch_bwd_gemm<BWD_WD, T, FLAVOR>(s, a, st);

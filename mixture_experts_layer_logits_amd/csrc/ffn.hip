@@ -17,9 +17,10 @@
 
 namespace moe {
 
-// FC1: 256 rows x (128 gate + 128 up) columns per workgroup of 8 waves.
+// FC1: 256 rows x (128 gate + 128 up) columns per workgroup of 8 waves
+// (tail tiles: 128 rows x (256 + 256)).
 constexpr int FC1_BM = 256, FC1_BN = 128;
-// FC2: 256 rows x 256 columns.
+// FC2: 256 rows x 256 columns (tail tiles: 128 x 512).
 constexpr int FC2_BM = 256, FC2_BN = 256;
 constexpr int GEN_BM = 64, GEN_BN = 64;
 
@@ -63,7 +64,7 @@ static hipError_t run_generic(const moe_shape& s, GemmArgs& a1, GemmArgs& a2, in
                               const FfnWs& ws, hipStream_t st) {
   if (s.E > 0) {
     schedule_tiles_kernel<<<1, 1024, 0, st>>>(a1.offsets, s.E, GEN_BM, cdiv(s.F, GEN_BN),
-                                              ws.tiles1, GEN_BM, cdiv(s.d, GEN_BN), ws.tiles2);
+                                              ws.tiles1, GEN_BM, cdiv(s.d, GEN_BN), ws.tiles2, 0);
   }
   int g1 = grid_upper_bound(a1, GEN_BM, GEN_BN, R);
   if (g1 > 0) gemm_generic_kernel<T, 2, EPI_SWIGLU><<<g1, 256, 0, st>>>(a1);
@@ -139,9 +140,10 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const int3
   }
   if (a1.E > 0) {
     schedule_tiles_kernel<<<1, 1024, 0, st>>>(offsets, s.E, FC1_BM, cdiv(s.F, FC1_BN),
-                                              ws.tiles1, FC2_BM, cdiv(s.d, FC2_BN), ws.tiles2);
+                                              ws.tiles1, FC2_BM, cdiv(s.d, FC2_BN), ws.tiles2, 1);
   }
-  hipError_t e = launch_mfma_gemm<FC1_BM, FC1_BN, 2, EPI_SWIGLU, 4, 2>(a1, R, st);
+  a1.tail = a2.tail = 1;
+  hipError_t e = launch_mfma_gemm<FC1_BM, FC1_BN, 2, EPI_SWIGLU, 4, 2, 1>(a1, R, st);
   if (e != hipSuccess) return e;
   const int ks = ffn_fc2_ksplit(s);
   if (ks > 1 && a2.E > 0) {
@@ -149,7 +151,7 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const int3
     a2.Cpart = ws.part;
     a2.part_stride = (long long)R * s.d;
   }
-  e = launch_mfma_gemm<FC2_BM, FC2_BN, 1, EPI_STORE, 4, 2>(a2, R, st);
+  e = launch_mfma_gemm<FC2_BM, FC2_BN, 1, EPI_STORE, 4, 2, 1>(a2, R, st);
   if (e != hipSuccess || a2.ksplit <= 1) return e;
   const long long n4 = (long long)R * s.d / 4;
   const int grid = (int)std::min<long long>((n4 + 255) / 256, 4096);

@@ -11,7 +11,17 @@
 // bound ceil(R / BM) + E row tiles per column tile, and surplus workgroups
 // exit at once.
 //
-// Tile order: within a group, the row tiles of one column tile are adjacent,
+// Tail tiles: with the tail option, a routed group of n rows gets floor(n/BM)
+// full BM x BN tiles, and its remaining t rows one more such tile when
+// t > BM/2, else "tail" tiles of BM/2 rows x 2 BN columns.  Each wave keeps
+// the same (BM/WM) x (BN/WN) block in both shapes, so a tail tile runs at the
+// full tile's rate while executing half its rows; when the tail has at most
+// BM/4 rows the waves past it skip their MFMAs, which leaves one busy wave per
+// SIMD.  Under skewed expert loads most of the padding of the last row tile
+// goes away.
+//
+// Tile order: within a group, the row tiles of one column tile are adjacent
+// (and a tail tile follows the two column tiles whose columns it covers),
 // so workgroups that share a weight tile run together.  The workgroup id is
 // remapped so that each XCD (workgroups are dealt to the 8 XCDs round-robin)
 // walks a contiguous range of the tile list, keeping those neighbours in one
@@ -61,6 +71,7 @@ struct GemmArgs {
   int ksplit;
   float* Cpart;
   long long part_stride;
+  int tail;                // routed groups use tail tiles (kernels built for them)
 };
 
 // One tile's work, with typed base pointers already offset to the group.
@@ -79,7 +90,15 @@ struct TileJob {
   int m0, n0;
   int k0, klen;            // K range of this work item (split-K slice)
   float* P;                // split-K partial rows of the group, or null
+  int cls;                 // 0: BM x BN tile, 1: BM/2 x 2BN tail tile
 };
+
+// Tiles of one routed group of `rows` rows with NT = ceil(N / BN) column tiles.
+__host__ __device__ inline int group_full_rows(int rows, int bm, int tail) {
+  if (!tail) return (rows + bm - 1) / bm;
+  const int nf = rows / bm, t = rows - nf * bm;
+  return nf + (t > bm / 2 ? 1 : 0);
+}
 
 __host__ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
@@ -120,10 +139,26 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, TileJob<TIn, TOut
     const int g = lo;
     const int row0 = a.offsets[g];
     const int rows = a.offsets[g + 1] - row0;
-    const int mt = cdiv(rows, BM);
+    // Column tiles go in pairs: the full tiles of columns 2p and 2p+1 (row
+    // tiles adjacent), then the group's tail tile over the same 2 BN columns,
+    // which finds that weight strip still in L2.
+    const int mt = group_full_rows(rows, BM, a.tail);
+    const int ht = (mt * BM < rows) ? 1 : 0;           // only with tail tiles
     const int r = lid - a.tiles[g];
-    j.m0 = (r % mt) * BM;
-    j.n0 = (r / mt) * BN;
+    const int per = 2 * mt + ht;
+    const int p = r / per;
+    const int q = r - p * per;
+    const int nt = cdiv(a.N, BN);
+    const int pair_cols = (nt - 2 * p) < 2 ? (nt - 2 * p) : 2;
+    if (q < pair_cols * mt) {
+      j.cls = 0;
+      j.m0 = (q % mt) * BM;
+      j.n0 = (2 * p + q / mt) * BN;
+    } else {
+      j.cls = 1;
+      j.m0 = mt * BM;
+      j.n0 = p * 2 * BN;
+    }
     j.rows = rows;
     j.N = a.N;
     j.K = a.K;
@@ -141,6 +176,7 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, TileJob<TIn, TOut
     return true;
   }
   const int r = lid - routed;
+  j.cls = 0;
   j.m0 = (r % dmt) * BM;
   j.n0 = (r / dmt) * BN;
   j.rows = a.Td;
@@ -160,22 +196,25 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, TileJob<TIn, TOut
 }
 
 // ---------------------------------------------------------------------------
-// Schedule: tiles[g] = sum_{g' < g} ceil(rows_g' / BM) * NT, for two GEMMs at
-// once.  One workgroup of 1024 threads (E <= 1024).
+// Schedule: tiles[g] = sum over groups g' < g of that group's tile count
+// (ceil(rows / BM) * NT, or with tail tiles the full tiles times NT plus
+// ceil(N / 2BN) tail tiles), for two GEMMs at once.  One workgroup of 1024
+// threads (E <= 1024).
 // ---------------------------------------------------------------------------
 namespace {
 __global__ void __launch_bounds__(1024)
 schedule_tiles_kernel(const int32_t* __restrict__ offsets, int E, int bm1, int nt1,
                       int32_t* __restrict__ tiles1, int bm2, int nt2,
-                      int32_t* __restrict__ tiles2) {
+                      int32_t* __restrict__ tiles2, int tail) {
   __shared__ int s1[1024];
   __shared__ int s2[1024];
   const int g = threadIdx.x;
   int v1 = 0, v2 = 0;
   if (g < E) {
     const int rows = offsets[g + 1] - offsets[g];
-    v1 = cdiv(rows, bm1) * nt1;
-    v2 = tiles2 ? cdiv(rows, bm2) * nt2 : 0;
+    const int f1 = group_full_rows(rows, bm1, tail), f2 = group_full_rows(rows, bm2, tail);
+    v1 = f1 * nt1 + (tail && f1 * bm1 < rows ? (nt1 + 1) / 2 : 0);
+    v2 = tiles2 ? f2 * nt2 + (tail && f2 * bm2 < rows ? (nt2 + 1) / 2 : 0) : 0;
   }
   s1[g] = v1;
   s2[g] = v2;
@@ -234,19 +273,30 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <int BM, int BN, int NB, int EPI, int WM, int WN>
+// Scalar copy of a pointer that is uniform across the wave.
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+  const unsigned long long v = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return reinterpret_cast<const char*>(((unsigned long long)hi << 32) | lo);
+}
+
+template <int BM, int BN, int NB, int EPI, int WM, int WN, int TL>
 __global__ void __launch_bounds__(64 * WM * WN)
 gemm_bf16_mfma_kernel(const GemmArgs args) {
   constexpr int NW = WM * WN;
   constexpr int BK = 32;                        // one 64-byte row per operand row
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MI = WTM / 32, NJ = WTN / 32;
-  constexpr int ROWS = BM + NB * BN;            // operand rows per LDS stage
-  constexpr int BLK = ROWS / 16;                // 1 KiB blocks per stage
-  constexpr int BPW = BLK / NW;                 // blocks (load instructions) per wave
+  constexpr int ROWS0 = BM + NB * BN;           // operand rows per LDS stage
+  constexpr int ROWS1 = BM / 2 + NB * 2 * BN;   // ... of a tail tile
+  constexpr int ROWS = (TL && ROWS1 > ROWS0) ? ROWS1 : ROWS0;
+  constexpr int BPW0 = ROWS0 / 16 / NW;         // 1 KiB blocks (loads) per wave
+  constexpr int BPW1 = ROWS1 / 16 / NW;
+  constexpr int BPWX = (TL && BPW1 > BPW0) ? BPW1 : BPW0;
   static_assert(MI >= 1 && NJ >= 1, "tile too small");
-  static_assert(BLK % NW == 0 && (BM / 16) % BPW == 0 && (BN / 16) % BPW == 0,
-                "each wave must load whole blocks of a single operand");
+  static_assert(ROWS0 % (16 * NW) == 0 && (!TL || (ROWS1 % (16 * NW) == 0 && WM % 2 == 0)),
+                "every wave loads the same number of 1 KiB blocks");
   using TOut = typename std::conditional<EPI == EPI_F32_BIAS, float, bf16_t>::type;
 
   __shared__ __attribute__((aligned(1024))) bf16_t st0[ROWS * BK];
@@ -260,48 +310,59 @@ gemm_bf16_mfma_kernel(const GemmArgs args) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int wm = wave / WN, wn = wave % WN;
+  // Tile shape: BM x BN, or for a tail tile BM/2 x 2BN with the waves laid
+  // out (WM/2) x (2WN); the per-wave block is the same.
+  const bool tail = TL && __builtin_amdgcn_readfirstlane(job.cls) != 0;
+  const int bmc = tail ? BM / 2 : BM;
+  const int bnc = tail ? 2 * BN : BN;
+  const int wnc = tail ? 2 * WN : WN;
+  const int bpw = tail ? BPW1 : BPW0;      // blocks this wave loads per slice
+  const int wm = wave / wnc, wn = wave % wnc;
+  // Waves whose rows all lie past the group's end only load and sync.
+  const bool live = job.m0 + wm * WTM < job.rows;
 
-  // This wave loads blocks b = wave * BPW + j; lane l covers row 16 b + l / 4
-  // and fetches the logical chunk that belongs at position l % 4.
-  const int blk0 = wave * BPW;
-  const int row0 = blk0 * 16;
-  const bf16_t* src;
-  int src_ld;
-  int rbase, rlimit;
-  if (row0 < BM) {
-    src = job.A;
-    src_ld = (int)job.lda;
-    rbase = job.m0 + row0;
-    rlimit = job.rows;
-  } else {
-    const int rb = row0 - BM;
-    src = (rb / BN == 0) ? job.B0 : job.B1;
-    src_ld = job.K;
-    rbase = job.n0 + rb % BN;
-    rlimit = job.N;
-  }
-  uint32_t g_off[BPW];   // byte offsets from src (< 2^31)
+  // This wave loads blocks b = wave * bpw + j; lane l covers row 16 b + l / 4
+  // of the operand that block belongs to and fetches the logical chunk that
+  // belongs at position l % 4.
   const int dma_c = (lane & 3) ^ swz(lane >> 2);
+  uint32_t g_off[BPWX];   // byte offsets from the block's operand base (< 2^31)
+  const char* g_base[BPWX];
 #pragma unroll
-  for (int j = 0; j < BPW; ++j) {
-    int r = rbase + (lane >> 2) + 16 * j;
+  for (int j = 0; j < BPWX; ++j) {
+    const int row = (wave * bpw + j) * 16;
+    const bf16_t* src;
+    int ld, rbase, rlimit;
+    if (row < bmc) {
+      src = job.A;
+      ld = (int)job.lda;
+      rbase = job.m0 + row;
+      rlimit = job.rows;
+    } else {
+      const int rb = row - bmc;
+      src = (rb < bnc) ? job.B0 : job.B1;
+      ld = job.K;
+      rbase = job.n0 + (rb < bnc ? rb : rb - bnc);
+      rlimit = job.N;
+    }
+    int r = rbase + (lane >> 2);
     r = r < rlimit ? r : rlimit - 1;                    // clamp: never stored
-    g_off[j] = (uint32_t)(r * src_ld + dma_c * 8) * 2u;
+    g_off[j] = (uint32_t)(r * ld + dma_c * 8) * 2u;
+    g_base[j] = uniform_ptr(src);
   }
-  const char* src_bytes = reinterpret_cast<const char*>(src);
   // Issued as inline assembly so that only the explicit vmcnt waits below
   // order these loads (the compiler cannot tell the four stages apart across
   // the loop and would otherwise drain every load before some LDS reads).
   // M0 holds the wave-uniform LDS destination; nothing else in this kernel
   // uses M0.
-  auto dma = [&](bf16_t* stage, int k0) {
-    const char* base = src_bytes + (size_t)k0 * 2;     // wave-uniform
+  auto dma = [&](bf16_t* stage, int k0, auto nblk_c) {
+    constexpr int NBLK = decltype(nblk_c)::value;
 #pragma unroll
-    for (int j = 0; j < BPW; ++j) {
-      const uint32_t lds = (uint32_t)(uintptr_t)MOE_AS_LDS(stage + (blk0 + j) * 512);
+    for (int j = 0; j < NBLK; ++j) {
+      const uint32_t lds = (uint32_t)(uintptr_t)MOE_AS_LDS(stage + (wave * bpw + j) * 512);
+      const char* base = g_base[j] + (size_t)k0 * 2;
+      const uint32_t off = g_off[j];
       asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                   :: "s"(lds), "v"(g_off[j]), "s"(base) : "memory");
+                   :: "s"(lds), "v"(off), "s"(base) : "memory");
     }
   };
 
@@ -322,7 +383,8 @@ gemm_bf16_mfma_kernel(const GemmArgs args) {
   const int kpos0 = ((0 + (lane >> 5)) ^ sw) << 3;
   const int kpos1 = ((2 + (lane >> 5)) ^ sw) << 3;
   const int a_row = (wm * WTM + frag_row) * BK;
-  const int b_row = (BM + wn * WTN + frag_row) * BK;
+  const int b_row = (bmc + wn * WTN + frag_row) * BK;
+  const int b_blk = bnc * BK;
   auto load_frags = [&](const bf16_t* stage, int kpos, bf16x8_t (&af)[MI],
                         bf16x8_t (&bfr)[NB][NJ]) {
     const bf16_t* pa = stage + a_row + kpos;
@@ -334,7 +396,7 @@ gemm_bf16_mfma_kernel(const GemmArgs args) {
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
-        bfr[b][j] = *reinterpret_cast<const bf16x8_t*>(pb + (b * BN + j * 32) * BK);
+        bfr[b][j] = *reinterpret_cast<const bf16x8_t*>(pb + b * b_blk + j * 32 * BK);
   };
   auto mma = [&](const bf16x8_t (&af)[MI], const bf16x8_t (&bfr)[NB][NJ]) {
 #pragma unroll
@@ -359,10 +421,11 @@ gemm_bf16_mfma_kernel(const GemmArgs args) {
   // slices issued so far (0 .. issued-1), leaving younger ones in flight.
   const int KT = job.klen / BK;
   const int kbeg = job.k0;
-  auto wait_slice = [&](int ready, int issued) {
+  auto wait_slice = [&](int ready, int issued, auto nblk_c) {
+    constexpr int NBLK = decltype(nblk_c)::value;
     const int younger = issued - 1 - ready;
-    if (younger >= 2) wait_vmcnt<2 * BPW>();
-    else if (younger == 1) wait_vmcnt<BPW>();
+    if (younger >= 2) wait_vmcnt<2 * NBLK>();
+    else if (younger == 1) wait_vmcnt<NBLK>();
     else wait_vmcnt<0>();
   };
   // Step s consumes stage s % 4 in two 16-wide sub-steps.  Its first
@@ -371,37 +434,55 @@ gemm_bf16_mfma_kernel(const GemmArgs args) {
   // waited for its own part), every wave has finished step s-1, so stage
   // (s+3) % 4 can be refilled and the first fragments of step s+1 read while
   // the second sub-step's MFMAs run.
-  bf16x8_t af0[MI], af1[MI];
-  bf16x8_t bf0[NB][NJ], bf1[NB][NJ];
-  auto step = [&](const bf16_t* cur, const bf16_t* next, bf16_t* refill, int s) {
-    load_frags(cur, kpos1, af1, bf1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(af0, bf0);
-    if (s + 1 < KT) wait_slice(s + 1, s + 3 < KT ? s + 3 : KT);
+  // The K loop exists twice, with and without the fragment reads and MFMAs,
+  // so that no branch on `live` sits inside it (a branch there makes the
+  // compiler drain outstanding LDS reads at every join).
+  auto k_loop = [&](auto live_c, auto nblk_c) {
+    constexpr bool LIVE = decltype(live_c)::value;
+    bf16x8_t af0[MI], af1[MI];
+    bf16x8_t bf0[NB][NJ], bf1[NB][NJ];
+    auto step = [&](const bf16_t* cur, const bf16_t* next, bf16_t* refill, int s) {
+      if constexpr (LIVE) load_frags(cur, kpos1, af1, bf1);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (LIVE) mma(af0, bf0);
+      if (s + 1 < KT) wait_slice(s + 1, s + 3 < KT ? s + 3 : KT, nblk_c);
+      barrier();
+      if (s + 3 < KT) dma(refill, kbeg + (s + 3) * BK, nblk_c);
+      if constexpr (LIVE) {
+        if (s + 1 < KT) load_frags(next, kpos0, af0, bf0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (LIVE) mma(af1, bf1);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    dma(st0, kbeg, nblk_c);
+    if (KT > 1) dma(st1, kbeg + BK, nblk_c);
+    if (KT > 2) dma(st2, kbeg + 2 * BK, nblk_c);
+    wait_slice(0, KT < 3 ? KT : 3, nblk_c);
     barrier();
-    if (s + 3 < KT) dma(refill, kbeg + (s + 3) * BK);
-    if (s + 1 < KT) load_frags(next, kpos0, af0, bf0);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(af1, bf1);
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (LIVE) load_frags(st0, kpos0, af0, bf0);
+    int kt = 0;
+    for (; kt + 4 <= KT; kt += 4) {
+      step(st0, st1, st3, kt);
+      step(st1, st2, st0, kt + 1);
+      step(st2, st3, st1, kt + 2);
+      step(st3, st0, st2, kt + 3);
+    }
+    if (kt < KT) step(st0, st1, st3, kt);
+    if (kt + 1 < KT) step(st1, st2, st0, kt + 1);
+    if (kt + 2 < KT) step(st2, st3, st1, kt + 2);
   };
-
-  dma(st0, kbeg);
-  if (KT > 1) dma(st1, kbeg + BK);
-  if (KT > 2) dma(st2, kbeg + 2 * BK);
-  wait_slice(0, KT < 3 ? KT : 3);
-  barrier();
-  load_frags(st0, kpos0, af0, bf0);
-  int kt = 0;
-  for (; kt + 4 <= KT; kt += 4) {
-    step(st0, st1, st3, kt);
-    step(st1, st2, st0, kt + 1);
-    step(st2, st3, st1, kt + 2);
-    step(st3, st0, st2, kt + 3);
+  // Each wave issues the same number of block loads per slice (4 or 5 with
+  // the tail shape), which the vmcnt waits count on.
+  using nb0 = std::integral_constant<int, BPW0>;
+  using nb1 = std::integral_constant<int, BPW1>;
+  if (!live) {
+    if (tail) k_loop(std::false_type{}, nb1{});
+    else k_loop(std::false_type{}, nb0{});
+    return;
   }
-  if (kt < KT) step(st0, st1, st3, kt);
-  if (kt + 1 < KT) step(st1, st2, st0, kt + 1);
-  if (kt + 2 < KT) step(st2, st3, st1, kt + 2);
+  if (tail) k_loop(std::true_type{}, nb1{});
+  else k_loop(std::true_type{}, nb0{});
 
   // Epilogue.  Lane owns row m = .. + (lane % 32) and, for register v,
   // column n = .. + 8 (v / 4) + 4 (lane / 32) + v % 4.
@@ -467,11 +548,12 @@ gemm_bf16_mfma_kernel(const GemmArgs args) {
 
 // Host launcher of the MFMA kernel: sizes the grid from the host-side tile
 // bound.
-template <int BM, int BN, int NB, int EPI, int WM, int WN>
+template <int BM, int BN, int NB, int EPI, int WM, int WN, int TL>
 hipError_t launch_mfma_gemm(const GemmArgs& a, int R, hipStream_t st) {
+  if (a.tail && !TL) return hipErrorInvalidValue;
   const int grid = grid_upper_bound(a, BM, BN, R);
   if (grid == 0) return hipSuccess;
-  gemm_bf16_mfma_kernel<BM, BN, NB, EPI, WM, WN><<<grid, 64 * WM * WN, 0, st>>>(a);
+  gemm_bf16_mfma_kernel<BM, BN, NB, EPI, WM, WN, TL><<<grid, 64 * WM * WN, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -34,7 +34,7 @@ hipError_t launch_router_logits(const moe_shape& s, const void* x, const void* w
   a.ldcd = s.E;
   a.bias = router_bias;
   if (s.dtype == MOE_DTYPE_BF16 && s.d % 64 == 0) {
-    return launch_mfma_gemm<64, 64, 1, EPI_F32_BIAS, 2, 2>(a, 0, st);
+    return launch_mfma_gemm<64, 64, 1, EPI_F32_BIAS, 2, 2, 0>(a, 0, st);
   } else if (s.dtype == MOE_DTYPE_BF16) {
     const int grid = grid_upper_bound(a, 64, 64, 0);
     gemm_generic_kernel<bf16_t, 1, EPI_F32_BIAS><<<grid, 256, 0, st>>>(a);

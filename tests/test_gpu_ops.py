@@ -152,6 +152,9 @@ def test_permute_no_tokens():
 # --------------------------------------------------------------------------
 # moe_grouped_ffn on synthetic expert-contiguous rows
 # --------------------------------------------------------------------------
+TAIL_COUNTS = (0, 1, 63, 64, 65, 127, 128, 129, 192, 255, 256, 257, 320, 384,
+               511, 512, 600)
+
 FFN_CASES = [
     # name, T, d, E, k, F, Fs, dtype, skew
     ("mfma_splitk_t300", 300, 256, 8, 2, 384, 0, 1, None),
@@ -161,10 +164,20 @@ FFN_CASES = [
     ("fp32_t256", 256, 128, 8, 2, 256, 0, 0, None),
     ("fp32_odd_t37", 37, 20, 5, 3, 12, 8, 0, None),
     ("single_expert_t65", 65, 64, 1, 1, 64, 0, 1, None),
+    # explicit rows per expert around every tile-height boundary (full
+    # 256-row tiles, 128-row tail tiles, tails of <= 64 rows, empty experts);
+    # N = 384 and d = 256 leave half of the wide tail tiles past N
+    ("mfma_tail_classes_splitk", None, 256, None, 1, 384, 0, 1, TAIL_COUNTS),
+    ("mfma_tail_classes_shared", None, 512, None, 1, 256, 128, 1, TAIL_COUNTS),
 ]
 
 
 def _ffn_inputs(cfg, skew):
+    if isinstance(skew, tuple):
+        p = {"offsets": np.concatenate([[0], np.cumsum(skew)]).astype(np.int32)}
+        inp = make_inputs(cfg, device="cuda")
+        xp = normal((cfg.R, cfg.d), 1.0, cfg.torch_dtype, "cuda", child_seed(5, "rows"))
+        return p, inp, xp
     wts = [1.0 / (r + 1) ** 6 for r in range(cfg.E)] if skew else None
     idx = random_topk(cfg.T, cfg.E, cfg.k, seed=cfg.T, weights=wts)
     p = O.permute(None, idx.numpy(), np.ones((cfg.T, cfg.k)), cfg.E)
@@ -176,6 +189,8 @@ def _ffn_inputs(cfg, skew):
 @pytest.mark.parametrize("case", FFN_CASES, ids=[c[0] for c in FFN_CASES])
 def test_grouped_ffn(case):
     name, T, d, E, k, F, Fs, dtype, skew = case
+    if isinstance(skew, tuple):
+        T, E = int(sum(skew)), len(skew)
     _log(f"[ffn] {name}")
     M = _lib()
     cfg = MoEConfig(name, T=T, d=d, E=E, k=k, F=F, F_shared=Fs, dtype=dtype)

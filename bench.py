@@ -141,18 +141,20 @@ def _oracle_pass(cfg, inp, T):
 
 def cpu_baseline(cfg, inp, sample_tokens=None, target_s=15.0):
     """The oracle, as it stands, on the first tokens of the same workload.
-    Without a fixed sample size, a first pass on a few tokens sizes a second
-    pass to about target_s seconds; the second pass is the one reported."""
+    Without a fixed sample size, passes on growing samples run until one
+    takes at least target_s / 2 seconds (or covers the whole workload); the
+    last pass is the one reported."""
     from threadpoolctl import threadpool_info
 
     if sample_tokens:
         T = min(sample_tokens, cfg.T)
         dt = _oracle_pass(cfg, inp, T)
     else:
-        T = min(cfg.T, max(cfg.k, 64))
+        # grow the sample (at most 8x a pass: fixed costs dominate small ones)
+        T = min(cfg.T, 64)
         dt = _oracle_pass(cfg, inp, T)
-        if dt < target_s / 2 and T < cfg.T:
-            T = min(cfg.T, max(T + 1, int(T * target_s / max(dt, 1e-3))))
+        while dt < target_s / 2 and T < cfg.T:
+            T = min(cfg.T, max(T + 1, int(T * min(8.0, target_s / max(dt, 1e-3)))))
             dt = _oracle_pass(cfg, inp, T)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()
                    if i.get("user_api") == "blas"] or [1])

@@ -30,11 +30,15 @@ __device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
 }
 
 // One workgroup per token; each thread owns runs of 8 columns (d % 8 == 0).
+// The k gathered rows are loaded in batches of JB before any of them is
+// accumulated, so a thread keeps up to JB row loads in flight; the
+// accumulation order stays j = 0, 1, ..., k-1.
 template <typename T>
 __global__ void __launch_bounds__(256)
 combine_vec_kernel(const T* __restrict__ y_perm, const int32_t* __restrict__ token_row,
                    const float* __restrict__ topk_w, const T* __restrict__ y_shared, int d,
                    int k, float* __restrict__ y) {
+  constexpr int JB = 8;
   const int t = blockIdx.x;
   const int32_t* rows = token_row + (long long)t * k;
   const float* w = topk_w + (long long)t * k;
@@ -46,14 +50,27 @@ combine_vec_kernel(const T* __restrict__ y_perm, const int32_t* __restrict__ tok
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
     }
-    for (int j = 0; j < k; ++j) {
-      const int r = rows[j];
-      if (r < 0) continue;
-      float v[8];
-      load8<T>(y_perm + (long long)r * d + c, v);
-      const float wj = w[j];
+    for (int j0 = 0; j0 < k; j0 += JB) {
+      float v[JB][8];
+      float wj[JB];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
+      for (int jj = 0; jj < JB; ++jj) {
+        const int j = j0 + jj;
+        const int r = j < k ? rows[j] : -1;
+        wj[jj] = r >= 0 ? w[j] : 0.0f;
+        if (r >= 0) {
+          load8<T>(y_perm + (long long)r * d + c, v[jj]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[jj][i] = 0.0f;
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < JB; ++jj) {
+        if (j0 + jj >= k || rows[j0 + jj] < 0) continue;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj[jj], v[jj][i], acc[i]);
+      }
     }
     float* dst = y + (long long)t * d + c;
     *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);

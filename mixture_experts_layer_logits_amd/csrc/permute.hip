@@ -14,7 +14,10 @@
 //   1. count:  per (expert, block) counts, stored expert-major;
 //   2. scan:   one exclusive scan over that expert-major array gives each
 //              (expert, block) its first row and, at block 0, the offsets;
-//   3. maps:   token_row, row_token and row_gate from the masks again;
+//   3. maps:   token_row, row_token and row_gate from the masks again.
+//              When the count table is small (at most 64 blocks and 16384
+//              entries) each maps block does step 2 itself from the whole
+//              table, which saves the scan launch;
 //   4. rows:   one workgroup per token copies x[t] once from HBM into its k
 //              destination rows (full-row, 16-byte coalesced stores).
 #include "gemm_tiles.h"
@@ -85,12 +88,65 @@ permute_scan_kernel(const int32_t* __restrict__ blk_cnt, int E, int nblk,
     offsets[e] = (e < E) ? (nblk > 0 ? blk_base[(long long)e * nblk] : 0) : s[1023];
 }
 
+constexpr int FUSE_MAX_BLK = 64, FUSE_MAX_ENTRIES = 16384;
+
+bool permute_fused_scan(const moe_shape& s) {
+  const int nblk = permute_nblk(s);
+  return nblk > 0 && nblk <= FUSE_MAX_BLK && (long long)nblk * s.E <= FUSE_MAX_ENTRIES;
+}
+
+// First row of (expert, this block) for every expert, from the whole
+// expert-major count table: base[e] = sum of all blocks' counts of experts
+// below e, plus the counts of expert e in blocks below this one.  Block 0
+// also writes offsets.  E <= 1024.
+__device__ void block_bases(const int32_t* __restrict__ blk_cnt, int E, int nblk, int blk,
+                            int* __restrict__ base, int32_t* __restrict__ offsets) {
+  __shared__ int s_tot[1024];
+  __shared__ int s_part[PB];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += PB) {
+    const int32_t* row = blk_cnt + (long long)e * nblk;
+    int tot = 0, pre = 0;
+    for (int b = 0; b < nblk; ++b) {
+      const int c = row[b];
+      pre += (b < blk) ? c : 0;
+      tot += c;
+    }
+    s_tot[e] = tot;
+    base[e] = pre;
+  }
+  __syncthreads();
+  // exclusive scan of s_tot: thread tid owns experts [4 tid, 4 tid + 4)
+  const int e0 = 4 * tid;
+  int run = 0;
+  for (int e = e0; e < e0 + 4 && e < E; ++e) run += s_tot[e];
+  s_part[tid] = run;
+  __syncthreads();
+  for (int off = 1; off < PB; off <<= 1) {
+    const int v = tid >= off ? s_part[tid - off] : 0;
+    __syncthreads();
+    s_part[tid] += v;
+    __syncthreads();
+  }
+  int excl = tid > 0 ? s_part[tid - 1] : 0;
+  for (int e = e0; e < e0 + 4 && e < E; ++e) {
+    if (blk == 0) offsets[e] = excl;
+    base[e] += excl;
+    excl += s_tot[e];
+  }
+  if (blk == 0 && tid == PB - 1) offsets[E] = s_part[PB - 1];
+  __syncthreads();
+}
+
 __global__ void __launch_bounds__(PB)
 permute_maps_kernel(const int32_t* __restrict__ idx, const float* __restrict__ w, int T,
                     int E, int k, int nblk, const int32_t* __restrict__ blk_base,
+                    const int32_t* __restrict__ blk_cnt, int32_t* __restrict__ offsets,
                     int32_t* __restrict__ row_token, int32_t* __restrict__ token_row,
                     float* __restrict__ row_gate) {
   extern __shared__ unsigned long long masks[];
+  __shared__ int s_base[1024];
+  if (blk_cnt) block_bases(blk_cnt, E, nblk, blockIdx.x, s_base, offsets);
   build_masks(masks, idx, T, E, k, blockIdx.x);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * PB + threadIdx.x;
@@ -103,7 +159,7 @@ permute_maps_kernel(const int32_t* __restrict__ idx, const float* __restrict__ w
       token_row[tj] = -1;
       continue;
     }
-    int pos = blk_base[(long long)e * nblk + blockIdx.x];
+    int pos = blk_cnt ? s_base[e] : blk_base[(long long)e * nblk + blockIdx.x];
     for (int v = 0; v < wave; ++v) pos += __popcll(masks[v * E + e]);
     pos += __popcll(masks[wave * E + e] & below);
     token_row[tj] = pos;
@@ -149,10 +205,13 @@ hipError_t launch_permute(const moe_shape& s, const void* x, const int32_t* topk
   if (nblk > 0) {
     permute_count_kernel<<<nblk, PB, lds, st>>>(topk_idx, s.T, s.E, s.k, nblk, ws.blk_cnt);
   }
-  permute_scan_kernel<<<1, 1024, 0, st>>>(ws.blk_cnt, s.E, nblk, ws.blk_base, offsets);
+  const bool fused = permute_fused_scan(s);
+  if (!fused)
+    permute_scan_kernel<<<1, 1024, 0, st>>>(ws.blk_cnt, s.E, nblk, ws.blk_base, offsets);
   if (nblk > 0) {
     permute_maps_kernel<<<nblk, PB, lds, st>>>(topk_idx, topk_w, s.T, s.E, s.k, nblk,
-                                               ws.blk_base, row_token, token_row, row_gate);
+                                               ws.blk_base, fused ? ws.blk_cnt : nullptr,
+                                               offsets, row_token, token_row, row_gate);
     const long long row_bytes = (long long)s.d * (s.dtype == MOE_DTYPE_BF16 ? 2 : 4);
     if (row_bytes % 16 == 0)
       permute_rows_kernel<true><<<s.T, 256, 0, st>>>(static_cast<const uint8_t*>(x), token_row,

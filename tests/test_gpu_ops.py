@@ -108,6 +108,10 @@ PERMUTE_CASES = [
     ("one_token_t1_e64_k8", 1, 64, 8, None, 1, 128),
     ("many_experts_t600_e1024_k4", 600, 1024, 4, "zipf", 1, 24),
     ("odd_row_bytes_t100_e7_k2", 100, 7, 2, None, 1, 13),
+    # 79 blocks of 256 tokens: the separate scan kernel (the maps kernel does
+    # the scan itself only up to 64 blocks and 16384 block counts)
+    ("scan_kernel_t20000_e16_k2", 20000, 16, 2, None, 1, 32),
+    ("fused_scan_limit_t16384_e256_k4", 16384, 256, 4, "zipf", 1, 16),
 ]
 
 

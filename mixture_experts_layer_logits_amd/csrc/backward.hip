@@ -730,10 +730,72 @@ bwd_dma_kernel(const BwdArgs args) {
     if (kt + 2 < KT) step(st2, st3, st1, kt + 2);
   }
 
+  if constexpr (MODE == BWD_DX || MODE == BWD_DH) {
+    // Row-grouped outputs go out through LDS: in the accumulator layout a
+    // store instruction scatters 16-byte pieces over 32 rows (which cost
+    // several times their bytes in write traffic); re-read row-contiguous,
+    // every 16 (DX) or 32 (DH) lanes write whole 256-byte runs of one row.
+    // The ring is free once every wave has passed this barrier; each wave
+    // stages through its own 16 KiB.
+    barrier();
+    char* buf = reinterpret_cast<char*>((wave >> 1) == 0 ? st0 : (wave >> 1) == 1 ? st1
+                                        : (wave >> 1) == 2 ? st2 : st3) + (wave & 1) * 16384;
+    const int rbase = job.m0 + wm * WTM;          // first row of this wave (within the group)
+    const int cbase = job.n0 + wn * WTN;          // first column of this wave
+    if constexpr (MODE == BWD_DX) {
+      // 64 rows x 128 bf16 columns; 16-byte chunk c of row r at c ^ (r mod 16)
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int r = i * 32 + frag_row;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = j * 32 + 8 * q + 4 * (lane >> 5);
+            const uint2 pk = make_uint2(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                                        pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
+            *reinterpret_cast<uint2*>(buf + r * 256 + (((c >> 3) ^ (r & 15)) << 4) + (c & 4) * 2) = pk;
+          }
+      }
+      bf16_t* out = static_cast<bf16_t*>(args.out_dX) + (long long)job.row0 * args.d + cbase;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int r = 4 * t + (lane >> 4), ch = lane & 15;
+        const uint4 v = *reinterpret_cast<const uint4*>(buf + r * 256 + ((ch ^ (r & 15)) << 4));
+        if (rbase + r < job.M_valid)
+          *reinterpret_cast<uint4*>(out + (long long)(rbase + r) * args.d + ch * 8) = v;
+      }
+    } else {
+      // dh in fp32, 32 rows x 128 columns per pass; 16-byte chunk c of row r
+      // at c ^ r.  Each lane then owns 4 consecutive columns of one row and
+      // applies the SwiGLU backward with coalesced g, u loads and stores.
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int ch = j * 8 + 2 * q + (lane >> 5);
+            *reinterpret_cast<float4*>(buf + frag_row * 512 + ((ch ^ frag_row) << 4)) =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                            acc[i][j][4 * q + 3]);
+          }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int r = 2 * t + (lane >> 5), ch = lane & 31;
+          const float4 d4 = *reinterpret_cast<const float4*>(buf + r * 512 + ((ch ^ r) << 4));
+          const int m = rbase + i * 32 + r;
+          if (m < job.M_valid) {
+            const float v[4] = {d4.x, d4.y, d4.z, d4.w};
+            bwd_store4<MODE, bf16_t>(args, job, m, cbase + 4 * ch, v, false);
+          }
+        }
+      }
+    }
+  } else {
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
     const int m = job.m0 + wm * WTM + i * 32 + frag_row;
-    if (!A_COL && m >= job.M_valid) continue;
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -743,6 +805,7 @@ bwd_dma_kernel(const BwdArgs args) {
                             acc[i][j][4 * q + 3]};
         bwd_store4<MODE, bf16_t>(args, job, m, n, v, false);
       }
+  }
   }
 }
 

@@ -476,13 +476,66 @@ gemm_bf16_mfma_kernel(const GemmArgs args) {
   // the tail shape), which the vmcnt waits count on.
   using nb0 = std::integral_constant<int, BPW0>;
   using nb1 = std::integral_constant<int, BPW1>;
+  // With g and u saved for the backward, the SwiGLU epilogue goes out
+  // through LDS (below); every wave, idle or not, joins its barrier.
+  const bool staged = EPI == EPI_SWIGLU && job.GU != nullptr;
   if (!live) {
     if (tail) k_loop(std::false_type{}, nb1{});
     else k_loop(std::false_type{}, nb0{});
+    if (staged) barrier();
     return;
   }
   if (tail) k_loop(std::true_type{}, nb1{});
   else k_loop(std::true_type{}, nb0{});
+
+  if constexpr (EPI == EPI_SWIGLU) {
+    if (staged) {
+      // In the accumulator layout a store instruction scatters 16-byte
+      // pieces over 32 rows, which cost several times their bytes in write
+      // traffic for the three outputs.  Per 32-row half, g and u (fp32) go
+      // to this wave's 16 KiB of the ring (rows of 512 bytes, 16-byte chunk
+      // c of row r at c ^ r: g in chunks 0-15, u in 16-31), and come back
+      // with each lane holding 4 consecutive columns of one row, so 16 lanes
+      // store 128 contiguous bytes of h, of g and of u.
+      barrier();                                  // the ring is free
+      char* buf = reinterpret_cast<char*>((wave >> 1) == 0 ? st0 : (wave >> 1) == 1 ? st1
+                                          : (wave >> 1) == 2 ? st2 : st3) + (wave & 1) * 16384;
+      const int cbase = job.n0 + wn * WTN;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int ch = j * 8 + 2 * q + (lane >> 5);
+            const f32x16_t& G = acc[0][i][j];
+            const f32x16_t& U = acc[NB - 1][i][j];
+            *reinterpret_cast<float4*>(buf + frag_row * 512 + ((ch ^ frag_row) << 4)) =
+                make_float4(G[4 * q], G[4 * q + 1], G[4 * q + 2], G[4 * q + 3]);
+            *reinterpret_cast<float4*>(buf + frag_row * 512 + (((16 + ch) ^ frag_row) << 4)) =
+                make_float4(U[4 * q], U[4 * q + 1], U[4 * q + 2], U[4 * q + 3]);
+          }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int r = 4 * t + (lane >> 4), cc = lane & 15;
+          const float4 g4 = *reinterpret_cast<const float4*>(buf + r * 512 + ((cc ^ r) << 4));
+          const float4 u4 = *reinterpret_cast<const float4*>(buf + r * 512 + (((16 + cc) ^ r) << 4));
+          const int m = job.m0 + wm * WTM + i * 32 + r;
+          const int n = cbase + 4 * cc;
+          if (m < job.rows && n < job.N) {
+            const uint2 ph = make_uint2(pack_bf16x2(silu_fast(g4.x) * u4.x, silu_fast(g4.y) * u4.y),
+                                        pack_bf16x2(silu_fast(g4.z) * u4.z, silu_fast(g4.w) * u4.w));
+            *reinterpret_cast<uint2*>(job.C + (long long)m * job.ldc + n) = ph;
+            *reinterpret_cast<uint2*>(job.GU + (long long)m * job.ldgu + n) =
+                make_uint2(pack_bf16x2(g4.x, g4.y), pack_bf16x2(g4.z, g4.w));
+            *reinterpret_cast<uint2*>(job.GU + (long long)m * job.ldgu + job.N + n) =
+                make_uint2(pack_bf16x2(u4.x, u4.y), pack_bf16x2(u4.z, u4.w));
+          }
+        }
+      }
+      return;
+    }
+  }
 
   // Epilogue.  Lane owns row m = .. + (lane % 32) and, for register v,
   // column n = .. + 8 (v / 4) + 4 (lane / 32) + v % 4.

@@ -1,7 +1,7 @@
 """Seeded synthetic inputs for the one-GPU MoE layer.
 
 This module only draws random tensors with the shapes, scales and structure of
-the five workloads below; it holds none of the layer's arithmetic.  Both sides
+the workloads below; it holds none of the layer's arithmetic.  Both sides
 of a parity check (the HIP library and the CPU oracle) are fed from here.
 
 Seeding: every tensor, and every expert's slice of a weight tensor, gets its
@@ -84,7 +84,7 @@ class MoEConfig:
         return 3 * self.d * self.F
 
 
-# The five workloads, named by what they are.
+# The workloads, named by what they are.
 CONFIGS: Dict[str, MoEConfig] = {
     # Tiny fp32 forward: top-2 of 8, renormalised softmax gates.
     "tiny_fp32": MoEConfig("tiny_fp32", T=256, d=128, E=8, k=2, F=256,
@@ -103,6 +103,14 @@ CONFIGS: Dict[str, MoEConfig] = {
     "qwen3_30b_skewed_t16384": MoEConfig("qwen3_30b_skewed_t16384", T=16384,
                                          d=2048, E=128, k=8, F=768,
                                          zipf_s=1.2),
+    # One rank's share of the DeepSeek-V3 shape under 8-way expert
+    # parallelism: 32 local experts receiving about T*k = 65,536 rows (2,048
+    # per expert).  Routing is drawn locally (top-8 of the 32 experts) so the
+    # grouped FFN sees that row count; it stands in for the rows a dispatch
+    # would deliver from the other ranks (the shared expert stays with the
+    # token's own rank and is left out).
+    "deepseek_v3_ep8_rank_t8192": MoEConfig("deepseek_v3_ep8_rank_t8192", T=8192,
+                                            d=7168, E=32, k=8, F=2048),
     # Qwen3-235B-A22B-shape bf16 training step (forward + backward).
     "qwen3_235b_train_t8192": MoEConfig("qwen3_235b_train_t8192", T=8192,
                                         d=4096, E=128, k=8, F=1536,

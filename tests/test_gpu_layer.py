@@ -101,7 +101,7 @@ def test_layer_is_bitwise_deterministic():
 
 
 FULL = ["mixtral_t4096", "deepseek_v3_t8192", "qwen3_30b_skewed_t16384",
-        "qwen3_235b_train_t8192"]
+        "qwen3_235b_train_t8192", "deepseek_v3_ep8_rank_t8192"]
 
 
 @pytest.mark.parametrize("name", FULL)

@@ -697,18 +697,35 @@ bwd_dma_kernel(const BwdArgs args) {
   };
   const bool tail = A_COL && (K % BK) != 0;
   bf16x8_t af0[MI], af1[MI], bf0[NJ], bf1[NJ];
+  // Fragment reads spread between the MFMAs of each half-step (the first
+  // reads of a half go ahead of its first MFMA, then one read per MFMA).
+  // The last step also reads the (unused) next stage so that reads and
+  // MFMAs stay in one block; the tail masks are applied before each block.
+  constexpr int NREAD = (A_COL ? 2 * MI : MI) + 2 * NJ;   // LDS reads per half-step
+  auto interleave = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, NREAD - (MI * NJ - 1), 0);
+#pragma unroll
+    for (int r = 0; r < MI * NJ - 1; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  };
   auto step = [&](const bf16_t* cur, const bf16_t* next, bf16_t* refill, int s) {
-    load_frags(cur, 1, af1, bf1);
     if (tail && s == KT - 1) mask_tail(af0, s, 0);
     __builtin_amdgcn_sched_barrier(0);
+    load_frags(cur, 1, af1, bf1);
     mma(af0, bf0);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
     if (s + 1 < KT) wait_slice(s + 1, s + 3 < KT ? s + 3 : KT);
     barrier();
     if (s + 3 < KT) dma(refill, (s + 3) * BK);
-    if (s + 1 < KT) load_frags(next, 0, af0, bf0);
     if (tail && s == KT - 1) mask_tail(af1, s, 1);
     __builtin_amdgcn_sched_barrier(0);
+    load_frags(next, 0, af0, bf0);
     mma(af1, bf1);
+    interleave();
     __builtin_amdgcn_sched_barrier(0);
   };
   if (KT > 0) {

@@ -441,18 +441,34 @@ gemm_bf16_mfma_kernel(const GemmArgs args) {
     constexpr bool LIVE = decltype(live_c)::value;
     bf16x8_t af0[MI], af1[MI];
     bf16x8_t bf0[NB][NJ], bf1[NB][NJ];
+    // The fragment reads of each half-step are spread between its MFMAs
+    // (one read, one MFMA, ...), which keeps both the LDS and the matrix
+    // pipe busy; the last step reads the (unused) next stage as well, so
+    // that reads and MFMAs stay in one block the scheduler can interleave.
+    auto interleave = [&]() {
+#pragma unroll
+      for (int r = 0; r < 5; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+    };
     auto step = [&](const bf16_t* cur, const bf16_t* next, bf16_t* refill, int s) {
-      if constexpr (LIVE) load_frags(cur, kpos1, af1, bf1);
+      if constexpr (LIVE) {
+        load_frags(cur, kpos1, af1, bf1);
+        mma(af0, bf0);
+        interleave();
+      }
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (LIVE) mma(af0, bf0);
       if (s + 1 < KT) wait_slice(s + 1, s + 3 < KT ? s + 3 : KT, nblk_c);
       barrier();
       if (s + 3 < KT) dma(refill, kbeg + (s + 3) * BK, nblk_c);
       if constexpr (LIVE) {
-        if (s + 1 < KT) load_frags(next, kpos0, af0, bf0);
+        load_frags(next, kpos0, af0, bf0);
+        mma(af1, bf1);
+        interleave();
       }
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (LIVE) mma(af1, bf1);
       __builtin_amdgcn_sched_barrier(0);
     };
     dma(st0, kbeg, nblk_c);

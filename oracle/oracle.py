@@ -395,8 +395,8 @@ def gate_grad(dy, y_perm, token_row):
 
 def ffn_backward(dy, x_perm, gu_save, y_perm, offsets, token_row, topk_idx,
                  topk_w, logits, w_gate, w_up, w_down, score=SCORE_SOFTMAX,
-                 renorm=1, prec="bf16"):
-    """Backward of the routed layer, from the saved tensors.
+                 renorm=1, prec="bf16", shared=None):
+    """Backward of the layer, from the saved tensors.
 
     The backward mirrors the forward through dispatch/combine duality, with
     the FC2 and FC1 data gradients and two variable-K weight-gradient GEMMs
@@ -405,6 +405,11 @@ def ffn_backward(dy, x_perm, gu_save, y_perm, offsets, token_row, topk_idx,
       per expert: expert_backward;  dx[t] = sum_j dX_perm[pos[t,j]]
       d_logits from d_gate through the gate function.
     Weight gradients of experts with no rows are exactly zero.
+
+    ``shared`` (optional) = dict(x, gu, ws_gate, ws_up, ws_down) for the
+    always-on shared expert: it adds ys[t] to y[t] with gate 1, so its
+    backward is expert_backward on all T tokens with dY = dy; its data
+    gradient is added to dx after the routed terms.
     """
     of32 = out_f32(prec)
     x_perm = as64(x_perm)
@@ -431,11 +436,18 @@ def ffn_backward(dy, x_perm, gu_save, y_perm, offsets, token_row, topk_idx,
     dx = np.zeros((T, d), dtype=F64)
     for j in range(k):
         dx += dX[tr[:, j]]
+    out = {}
+    if shared is not None:
+        rs = expert_backward(dy, shared["x"], shared["gu"], shared["ws_gate"],
+                             shared["ws_up"], shared["ws_down"], prec)
+        dx = dx + rs["dX"]
+        out = dict(dws_gate=of32(rs["dw_gate"]), dws_up=of32(rs["dw_up"]),
+                   dws_down=of32(rs["dw_down"]), dX_shared=rs["dX"])
     d_logits = router_backward(d_gate, topk_idx, topk_w, logits,
                                as64(logits).shape[1], score, renorm, prec)
     return dict(dx=of32(dx), dw_gate=of32(dw_gate), dw_up=of32(dw_up),
                 dw_down=of32(dw_down), d_gate=of32(d_gate),
-                d_logits=d_logits, dY_perm=dY, dX_perm=dX)
+                d_logits=d_logits, dY_perm=dY, dX_perm=dX, **out)
 
 
 # --------------------------------------------------------------------------
@@ -458,10 +470,13 @@ def forward(inp, cfg, prec=None, logits=None, save_gu=False):
     p = permute(inp["x"], idx, w, cfg.E)
     y_perm, gu = grouped_ffn(p["x_perm"], p["offsets"], inp["w_gate"],
                              inp["w_up"], inp["w_down"], prec, save_gu)
-    ys = None
+    ys = gu_s = None
     if cfg.F_shared > 0:
-        ys = shared_ffn(inp["x"], inp["ws_gate"], inp["ws_up"],
-                        inp["ws_down"], prec)
+        r = swiglu_ffn(inp["x"], inp["ws_gate"], inp["ws_up"], inp["ws_down"], prec)
+        ys = r["y"]
+        if save_gu:
+            rnd = rounder(prec)
+            gu_s = np.concatenate([rnd(r["g"]), rnd(r["u"])], axis=1)
     y = combine(y_perm, p["token_row"], w, ys, prec)
     return dict(logits=own_logits, route_logits=l, topk_idx=idx, topk_w=w,
-                y_perm=y_perm, gu_save=gu, y_shared=ys, y=y, **p)
+                y_perm=y_perm, gu_save=gu, y_shared=ys, gu_shared=gu_s, y=y, **p)

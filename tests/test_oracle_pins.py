@@ -339,20 +339,23 @@ def test_deepseek_v3_expert_parameter_count():
 # --------------------------------------------------------------------------
 # backward: finite differences of the fp64 forward
 # --------------------------------------------------------------------------
-def _fwd_loss(x, logits, wg, wu, wd, dy, cfg, bias):
+def _fwd_loss(x, logits, wg, wu, wd, dy, cfg, bias, shared=None):
     inp = dict(x=x, w_router=np.zeros((cfg.E, cfg.d)), router_bias=None,
                score_bias=bias, w_gate=wg, w_up=wu, w_down=wd)
+    if shared is not None:
+        inp.update(ws_gate=shared[0], ws_up=shared[1], ws_down=shared[2])
     out = O.forward(inp, cfg, prec="f64", logits=logits, save_gu=True)
     return float((out["y"] * dy).sum()), out
 
 
-@pytest.mark.parametrize("score,renorm,groups", [
-    (O.SCORE_SOFTMAX, 1, (1, 1)), (O.SCORE_SOFTMAX, 0, (1, 1)),
-    (O.SCORE_SIGMOID, 1, (2, 1)), (O.SCORE_SIGMOID, 0, (1, 1))])
-def test_backward_matches_central_differences(score, renorm, groups):
-    rng = np.random.default_rng(12 + score * 2 + renorm)
+@pytest.mark.parametrize("score,renorm,groups,Fs", [
+    (O.SCORE_SOFTMAX, 1, (1, 1), 0), (O.SCORE_SOFTMAX, 0, (1, 1), 0),
+    (O.SCORE_SIGMOID, 1, (2, 1), 0), (O.SCORE_SIGMOID, 0, (1, 1), 0),
+    (O.SCORE_SIGMOID, 1, (2, 1), 2)])
+def test_backward_matches_central_differences(score, renorm, groups, Fs):
+    rng = np.random.default_rng(12 + score * 2 + renorm + Fs)
     T, d, E, k, F = 5, 4, 4, 2, 3
-    cfg = MoEConfig("fd", T=T, d=d, E=E, k=k, F=F, score=score,
+    cfg = MoEConfig("fd", T=T, d=d, E=E, k=k, F=F, F_shared=Fs, score=score,
                     renorm=renorm, n_groups=groups[0], topk_groups=groups[1])
     x = rng.standard_normal((T, d))
     # well separated logits so that no selection flips under the step
@@ -363,11 +366,18 @@ def test_backward_matches_central_differences(score, renorm, groups):
     wu = rng.standard_normal((E, F, d)) * 0.5
     wd = rng.standard_normal((E, d, F)) * 0.5
     dy = rng.standard_normal((T, d))
-    _, out = _fwd_loss(x, logits, wg, wu, wd, dy, cfg, bias)
+    sh = None
+    if Fs:
+        sh = (rng.standard_normal((Fs, d)) * 0.5, rng.standard_normal((Fs, d)) * 0.5,
+              rng.standard_normal((d, Fs)) * 0.5)
+    _, out = _fwd_loss(x, logits, wg, wu, wd, dy, cfg, bias, sh)
+    shared = None
+    if Fs:
+        shared = dict(x=x, gu=out["gu_shared"], ws_gate=sh[0], ws_up=sh[1], ws_down=sh[2])
     bw = O.ffn_backward(dy, out["x_perm"], out["gu_save"], out["y_perm"],
                         out["offsets"], out["token_row"], out["topk_idx"],
                         out["topk_w"], logits, wg, wu, wd, score, renorm,
-                        prec="f64")
+                        prec="f64", shared=shared)
     eps = 1e-6
 
     def fd(arr, fn):
@@ -382,9 +392,12 @@ def test_backward_matches_central_differences(score, renorm, groups):
             g[i] = (lp - lm) / (2 * eps)
         return g
 
-    loss = lambda: _fwd_loss(x, logits, wg, wu, wd, dy, cfg, bias)[0]
-    for name, arr in (("dx", x), ("dw_gate", wg), ("dw_up", wu),
-                      ("dw_down", wd), ("d_logits", logits)):
+    loss = lambda: _fwd_loss(x, logits, wg, wu, wd, dy, cfg, bias, sh)[0]
+    checks = [("dx", x), ("dw_gate", wg), ("dw_up", wu), ("dw_down", wd),
+              ("d_logits", logits)]
+    if Fs:
+        checks += [("dws_gate", sh[0]), ("dws_up", sh[1]), ("dws_down", sh[2])]
+    for name, arr in checks:
         num = fd(arr, loss)
         assert np.allclose(bw[name], num, rtol=1e-6, atol=1e-8), name
     # the gate gradient: perturb the gates inside the combine only

@@ -156,7 +156,9 @@ int moe_permute(const moe_shape* shape, const void* x, const int32_t* topk_idx,
  *      with h = silu(g) * u rounded to dtype before FC2.
  *  y_shared [T, d] dtype out (F_shared > 0, else ignored).
  *  gu_save [R, 2F] dtype out or NULL: g in columns [0, F), u in [F, 2F),
- *      rounded to dtype; needed by moe_ffn_backward.
+ *      rounded to dtype; needed by moe_ffn_backward.  With F_shared > 0 the
+ *      buffer continues with the shared expert's [T, 2F_shared] (g | u of
+ *      every token), so it holds R * 2F + T * 2F_shared elements.
  *  ws: MOE_OP_FFN bytes (holds h). */
 int moe_grouped_ffn(const moe_shape* shape, const void* x_perm,
                     const int32_t* expert_offsets, const void* w_gate,
@@ -178,7 +180,7 @@ int moe_unpermute_combine(const moe_shape* shape, const void* y_perm,
                           const void* y_shared, float* y, void* ws,
                           size_t ws_bytes, void* stream);
 
-/* Backward of the routed layer (Primus blog, MegaMoE section: the backward
+/* Backward of the layer (Primus blog, MegaMoE section: the backward
  * mirrors the forward through dispatch/combine duality, with the FC2 and FC1
  * data gradients and two variable-K weight-gradient GEMMs).  From the
  * upstream gradient dy of y it produces:
@@ -197,8 +199,16 @@ int moe_unpermute_combine(const moe_shape* shape, const void* y_perm,
  *  moe_grouped_ffn.
  *  Outputs (fp32): dx [T, d]; dw_gate, dw_up [E, F, d]; dw_down [E, d, F]
  *  (exactly zero for experts with no rows); d_gate [T, k]; d_logits [T, E].
- *  The shared expert's backward is not part of this call: F_shared must be 0
- *  (MOE_ERR_UNSUPPORTED otherwise).
+ *
+ *  With F_shared > 0 the always-on shared expert (gate 1 on every token; the
+ *  Primus blog's shared plus routed experts) gets the same backward over all
+ *  T tokens with dY = dy, from its g | u saved at the end of gu_save:
+ *    dws_down = dy^T . hs;  dws_gate = dgs^T . x;  dws_up = dus^T . x
+ *    dx[t] += rnd(dgs . ws_gate + dus . ws_up)[t], added after the routed terms.
+ *  x [T, d], ws_gate, ws_up [F_shared, d], ws_down [d, F_shared] dtype and
+ *  dws_gate, dws_up [F_shared, d], dws_down [d, F_shared] fp32 out are only
+ *  touched when F_shared > 0 (may be NULL otherwise); gu_save then holds
+ *  R * 2F + T * 2F_shared elements, as moe_grouped_ffn writes it.
  *  ws: MOE_OP_BACKWARD bytes. */
 int moe_ffn_backward(const moe_shape* shape, const void* dy, const void* x_perm,
                      const void* gu_save, const void* y_perm,
@@ -206,7 +216,9 @@ int moe_ffn_backward(const moe_shape* shape, const void* dy, const void* x_perm,
                      const int32_t* token_row, const int32_t* topk_idx,
                      const float* topk_w, const float* logits,
                      const void* w_gate, const void* w_up, const void* w_down,
-                     float* dx, float* dw_gate, float* dw_up, float* dw_down,
+                     const void* x, const void* ws_gate, const void* ws_up,
+                     const void* ws_down, float* dx, float* dw_gate, float* dw_up,
+                     float* dw_down, float* dws_gate, float* dws_up, float* dws_down,
                      float* d_gate, float* d_logits, void* ws, size_t ws_bytes,
                      void* stream);
 

@@ -66,7 +66,7 @@ def load() -> ctypes.CDLL:
     lib.moe_permute.argtypes = [sp] + [vp] * 8 + [vp, sz, vp]
     lib.moe_grouped_ffn.argtypes = [sp] + [vp] * 12 + [vp, sz, vp]
     lib.moe_unpermute_combine.argtypes = [sp] + [vp] * 5 + [vp, sz, vp]
-    lib.moe_ffn_backward.argtypes = [sp] + [vp] * 19 + [vp, sz, vp]
+    lib.moe_ffn_backward.argtypes = [sp] + [vp] * 26 + [vp, sz, vp]
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
     for name in EXPORTED:
@@ -157,12 +157,14 @@ def moe_unpermute_combine(shape, y_perm, token_row, topk_w, y_shared, y,
 
 def moe_ffn_backward(shape, dy, x_perm, gu_save, y_perm, expert_offsets,
                      row_token, token_row, topk_idx, topk_w, logits, w_gate,
-                     w_up, w_down, dx, dw_gate, dw_up, dw_down, d_gate,
+                     w_up, w_down, x, ws_gate, ws_up, ws_down, dx, dw_gate,
+                     dw_up, dw_down, dws_gate, dws_up, dws_down, d_gate,
                      d_logits, ws=None, ws_bytes=0, stream=None, check=True):
     st = load().moe_ffn_backward(
         ctypes.byref(shape), _p(dy), _p(x_perm), _p(gu_save), _p(y_perm),
         _p(expert_offsets), _p(row_token), _p(token_row), _p(topk_idx),
-        _p(topk_w), _p(logits), _p(w_gate), _p(w_up), _p(w_down), _p(dx),
-        _p(dw_gate), _p(dw_up), _p(dw_down), _p(d_gate), _p(d_logits),
-        _p(ws), ws_bytes, _stream(stream))
+        _p(topk_w), _p(logits), _p(w_gate), _p(w_up), _p(w_down), _p(x),
+        _p(ws_gate), _p(ws_up), _p(ws_down), _p(dx), _p(dw_gate), _p(dw_up),
+        _p(dw_down), _p(dws_gate), _p(dws_up), _p(dws_down), _p(d_gate),
+        _p(d_logits), _p(ws), ws_bytes, _stream(stream))
     return _check(st, "moe_ffn_backward") if check else st

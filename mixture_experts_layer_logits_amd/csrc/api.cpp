@@ -59,9 +59,16 @@ size_t ws_bytes_for(const moe_shape& s, int op) {
              align_up((size_t)s.T * s.F_shared * es) +
              (ks > 1 ? align_up((size_t)ks * R * s.d * 4) : 0);
     }
-    case MOE_OP_BACKWARD:
-      return 2 * align_up((s.E + 1) * 4) + 2 * align_up(R * s.d * es) +
-             align_up(R * 2 * s.F * es) + align_up(R * s.F * es);
+    case MOE_OP_BACKWARD: {
+      size_t b = 2 * align_up((s.E + 1) * 4) + 2 * align_up(R * s.d * es) +
+                 align_up(R * 2 * s.F * es) + align_up(R * s.F * es);
+      if (s.F_shared > 0) {
+        const size_t T = (size_t)s.T, Fs = (size_t)s.F_shared;
+        b += 3 * align_up(2 * 4) + align_up(T * 2 * Fs * es) + align_up(T * Fs * es) +
+             align_up(T * s.d * es);
+      }
+      return b;
+    }
     default:
       return 0;
   }
@@ -218,18 +225,28 @@ int moe_ffn_backward(const moe_shape* shape, const void* dy, const void* x_perm,
                      const void* gu_save, const void* y_perm, const int32_t* expert_offsets,
                      const int32_t* row_token, const int32_t* token_row,
                      const int32_t* topk_idx, const float* topk_w, const float* logits,
-                     const void* w_gate, const void* w_up, const void* w_down, float* dx,
-                     float* dw_gate, float* dw_up, float* dw_down, float* d_gate,
-                     float* d_logits, void* ws, size_t ws_bytes, void* stream) {
+                     const void* w_gate, const void* w_up, const void* w_down, const void* x,
+                     const void* ws_gate, const void* ws_up, const void* ws_down, float* dx,
+                     float* dw_gate, float* dw_up, float* dw_down, float* dws_gate,
+                     float* dws_up, float* dws_down, float* d_gate, float* d_logits, void* ws,
+                     size_t ws_bytes, void* stream) {
   int st = check_shape(shape);
   if (st != MOE_OK) return st;
   const moe_shape& s = *shape;
-  if (s.F_shared > 0 || !moe::backward_supported(s)) return MOE_ERR_UNSUPPORTED;
+  if (!moe::backward_supported(s)) return MOE_ERR_UNSUPPORTED;
   const long long es = (long long)esize(s);
   const long long R = (long long)s.T * s.k;
   const long long wsz = (long long)s.E * s.F * s.d;
+  const long long gu_elems = R * 2 * s.F + (long long)s.T * 2 * s.F_shared;
+  if (s.F_shared > 0) {
+    const long long sz = (long long)s.F_shared * s.d;
+    if (!ok_buf(x, (long long)s.T * s.d * es) || !ok_buf(ws_gate, sz * es) ||
+        !ok_buf(ws_up, sz * es) || !ok_buf(ws_down, sz * es) || !ok_buf(dws_gate, sz * 4) ||
+        !ok_buf(dws_up, sz * 4) || !ok_buf(dws_down, sz * 4))
+      return MOE_ERR_INVALID_ARG;
+  }
   if (!ok_buf(dy, (long long)s.T * s.d * es) || !ok_buf(x_perm, R * s.d * es) ||
-      !ok_buf(gu_save, R * 2 * s.F * es) || !ok_buf(y_perm, R * s.d * es) ||
+      !ok_buf(gu_save, gu_elems * es) || !ok_buf(y_perm, R * s.d * es) ||
       !ok_buf(expert_offsets, (long long)(s.E + 1) * 4) || !ok_buf(row_token, R * 4) ||
       !ok_buf(token_row, R * 4) || !ok_buf(topk_idx, R * 4) || !ok_buf(topk_w, R * 4) ||
       !ok_buf(logits, (long long)s.T * s.E * 4) || !ok_buf(w_gate, wsz * es) ||
@@ -247,9 +264,20 @@ int moe_ffn_backward(const moe_shape* shape, const void* dy, const void* x_perm,
   bw.dX = c.take<char>((size_t)R * s.d * es);
   bw.dgu = c.take<char>((size_t)R * 2 * s.F * es);
   bw.h = c.take<char>((size_t)R * s.F * es);
+  bw.s_offsets = bw.s_tiles = bw.s_tiles2 = nullptr;
+  bw.s_dgu = bw.s_h = bw.s_dX = nullptr;
+  if (s.F_shared > 0) {
+    bw.s_offsets = c.take<int32_t>(2 * 4);
+    bw.s_tiles = c.take<int32_t>(2 * 4);
+    bw.s_tiles2 = c.take<int32_t>(2 * 4);
+    bw.s_dgu = c.take<char>((size_t)s.T * 2 * s.F_shared * es);
+    bw.s_h = c.take<char>((size_t)s.T * s.F_shared * es);
+    bw.s_dX = c.take<char>((size_t)s.T * s.d * es);
+  }
   return hip_status(moe::launch_backward(s, dy, x_perm, gu_save, y_perm, expert_offsets,
                                          row_token, token_row, topk_idx, topk_w, logits,
-                                         w_gate, w_up, w_down, dx, dw_gate, dw_up, dw_down,
+                                         w_gate, w_up, w_down, x, ws_gate, ws_up, ws_down, dx,
+                                         dw_gate, dw_up, dw_down, dws_gate, dws_up, dws_down,
                                          d_gate, d_logits, bw,
                                          static_cast<hipStream_t>(stream)));
 }

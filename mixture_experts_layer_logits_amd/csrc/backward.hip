@@ -152,12 +152,13 @@ bwd_dispatch_kernel(const T* __restrict__ dy, const T* __restrict__ y_perm,
 }
 
 // ---------------------------------------------------------------------------
-// b6: dx[t] = sum_j dX_perm[token_row[t, j]] (fp32, fixed order).
+// b6: dx[t] = sum_j dX_perm[token_row[t, j]] (fp32, fixed order), then
+// + dX_shared[t] when the layer has a shared expert (dXs non-null).
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ void __launch_bounds__(256)
 bwd_gather_kernel(const T* __restrict__ dX, const int32_t* __restrict__ token_row, int d, int k,
-                  float* __restrict__ dx) {
+                  const T* __restrict__ dXs, float* __restrict__ dx) {
   const int t = blockIdx.x;
   const int32_t* rows = token_row + (long long)t * k;
   if (sizeof(T) == 2 && d % 8 == 0) {
@@ -168,6 +169,15 @@ bwd_gather_kernel(const T* __restrict__ dX, const int32_t* __restrict__ token_ro
         const int r = rows[j];
         if (r < 0) continue;
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(X + (long long)r * d + c);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] += __uint_as_float(v[q] << 16);
+          acc[2 * q + 1] += __uint_as_float(v[q] & 0xffff0000u);
+        }
+      }
+      if (dXs) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(
+            reinterpret_cast<const bf16_t*>(dXs) + (long long)t * d + c);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           acc[2 * q] += __uint_as_float(v[q] << 16);
@@ -186,6 +196,7 @@ bwd_gather_kernel(const T* __restrict__ dX, const int32_t* __restrict__ token_ro
       const int r = rows[j];
       if (r >= 0) acc += to_f32<T>(dX[(long long)r * d + c]);
     }
+    if (dXs) acc += to_f32<T>(dXs[(long long)t * d + c]);
     dx[(long long)t * d + c] = acc;
   }
 }
@@ -867,13 +878,32 @@ static hipError_t run_backward(const moe_shape& s, BwdArgs& a, const BwdWs& ws, 
   return hipGetLastError();
 }
 
+// {0, n}: the row offsets of a single group of n rows.
+__global__ void one_group_offsets_kernel(int32_t* offsets, int n) {
+  if (threadIdx.x == 0) {
+    offsets[0] = 0;
+    offsets[1] = n;
+  }
+}
+
+static hipError_t run_backward_any(const moe_shape& s, BwdArgs& a, const BwdWs& ws,
+                                   hipStream_t st) {
+  const bool bf = s.dtype == MOE_DTYPE_BF16;
+  if (bf && bwd_uses_dma(s)) return run_backward<bf16_t, 2>(s, a, ws, st);
+  if (bf && bwd_uses_mfma(s)) return run_backward<bf16_t, 1>(s, a, ws, st);
+  if (bf) return run_backward<bf16_t, 0>(s, a, ws, st);
+  return run_backward<float, 0>(s, a, ws, st);
+}
+
 hipError_t launch_backward(const moe_shape& s, const void* dy, const void* x_perm,
                            const void* gu_save, const void* y_perm, const int32_t* offsets,
                            const int32_t* row_token, const int32_t* token_row,
                            const int32_t* topk_idx, const float* topk_w,
                            const float* logits, const void* w_gate, const void* w_up,
-                           const void* w_down, float* dx, float* dw_gate, float* dw_up,
-                           float* dw_down, float* d_gate, float* d_logits,
+                           const void* w_down, const void* x, const void* ws_gate,
+                           const void* ws_up, const void* ws_down, float* dx, float* dw_gate,
+                           float* dw_up, float* dw_down, float* dws_gate, float* dws_up,
+                           float* dws_down, float* d_gate, float* d_logits,
                            const BwdWs& ws, hipStream_t st) {
   (void)row_token;
   const bool bf = s.dtype == MOE_DTYPE_BF16;
@@ -908,19 +938,52 @@ hipError_t launch_backward(const moe_shape& s, const void* dy, const void* x_per
   a.dw_down = dw_down;
   a.dw_gate = dw_gate;
   a.dw_up = dw_up;
-  hipError_t e;
-  if (bf && bwd_uses_dma(s)) e = run_backward<bf16_t, 2>(s, a, ws, st);
-  else if (bf && bwd_uses_mfma(s)) e = run_backward<bf16_t, 1>(s, a, ws, st);
-  else if (bf) e = run_backward<bf16_t, 0>(s, a, ws, st);
-  else e = run_backward<float, 0>(s, a, ws, st);
+  hipError_t e = run_backward_any(s, a, ws, st);
   if (e != hipSuccess) return e;
+  const bool shared = s.F_shared > 0 && s.T > 0;
+  if (shared) {
+    // The shared expert: one group of all T tokens with gate 1, so dY = dy,
+    // its input is x and its saved g | u follow the routed rows in gu_save.
+    one_group_offsets_kernel<<<1, 64, 0, st>>>(ws.s_offsets, s.T);
+    moe_shape s2 = s;
+    s2.E = 1;
+    s2.k = 1;
+    s2.F = s.F_shared;
+    s2.F_shared = 0;
+    const size_t es = bf ? 2 : 4;
+    BwdArgs b = {};
+    b.E = 1;
+    b.F = s.F_shared;
+    b.d = s.d;
+    b.offsets = ws.s_offsets;
+    b.dY = dy;
+    b.gu = static_cast<const char*>(gu_save) + (size_t)s.T * s.k * 2 * s.F * es;
+    b.dgu = ws.s_dgu;
+    b.h = ws.s_h;
+    b.x_perm = x;
+    b.w_gate = ws_gate;
+    b.w_up = ws_up;
+    b.w_down = ws_down;
+    b.out_dgu = ws.s_dgu;
+    b.out_h = ws.s_h;
+    b.out_dX = ws.s_dX;
+    b.dw_down = dws_down;
+    b.dw_gate = dws_gate;
+    b.dw_up = dws_up;
+    BwdWs w2 = ws;
+    w2.tiles = ws.s_tiles;
+    w2.tiles2 = ws.s_tiles2;
+    if ((e = run_backward_any(s2, b, w2, st)) != hipSuccess) return e;
+  }
   if (s.T > 0) {
     if (bf)
-      bwd_gather_kernel<bf16_t><<<s.T, 256, 0, st>>>(static_cast<const bf16_t*>(ws.dX), token_row,
-                                                     s.d, s.k, dx);
+      bwd_gather_kernel<bf16_t><<<s.T, 256, 0, st>>>(
+          static_cast<const bf16_t*>(ws.dX), token_row, s.d, s.k,
+          shared ? static_cast<const bf16_t*>(ws.s_dX) : nullptr, dx);
     else
-      bwd_gather_kernel<float><<<s.T, 256, 0, st>>>(static_cast<const float*>(ws.dX), token_row,
-                                                    s.d, s.k, dx);
+      bwd_gather_kernel<float><<<s.T, 256, 0, st>>>(
+          static_cast<const float*>(ws.dX), token_row, s.d, s.k,
+          shared ? static_cast<const float*>(ws.s_dX) : nullptr, dx);
   }
   return hipGetLastError();
 }

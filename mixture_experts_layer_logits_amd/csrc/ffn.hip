@@ -106,6 +106,11 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const int3
     a1.Kd = s.d;
     a1.Cd = ws.h_shared;
     a1.ldcd = s.F_shared;
+    if (gu_save) {   // the shared expert's g | u follow the routed rows
+      a1.GUd = static_cast<char*>(gu_save) +
+               (size_t)R * 2 * s.F * (s.dtype == MOE_DTYPE_BF16 ? 2 : 4);
+      a1.ldgud = 2LL * s.F_shared;
+    }
   }
   // FC2: h [R, F] x w_down [E, d, F] -> y_perm [R, d]
   GemmArgs a2 = {};

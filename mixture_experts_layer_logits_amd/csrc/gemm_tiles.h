@@ -64,6 +64,8 @@ struct GemmArgs {
   int Nd, Kd;
   void* Cd;
   long long ldcd;
+  void* GUd;               // FC1 only, or null: the dense group's g | u
+  long long ldgud;
   const float* bias;       // EPI_F32_BIAS: added per column, or null
   // Split-K (EPI_STORE on routed groups only): K is cut into ksplit equal
   // slices; slice s of every tile writes fp32 partials to
@@ -184,12 +186,12 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, TileJob<TIn, TOut
   j.K = a.Kd;
   j.lda = a.ldad;
   j.ldc = a.ldcd;
-  j.ldgu = 0;
   j.A = static_cast<const TIn*>(a.Ad);
   j.B0 = static_cast<const TIn*>(a.Bd0);
   j.B1 = static_cast<const TIn*>(a.Bd1);
   j.C = static_cast<TOut*>(a.Cd);
-  j.GU = nullptr;
+  j.GU = static_cast<TOut*>(a.GUd);
+  j.ldgu = a.ldgud;
   j.klen = a.Kd;
   j.k0 = 0;
   return true;

@@ -86,6 +86,13 @@ struct BwdWs {
   void* dgu;        // [R, 2F] dtype: dg | du
   void* h;          // [R, F]  dtype: h recomputed from the saved g, u
   void* dX;         // [R, d]  dtype
+  // the shared expert (F_shared > 0): one group of all T tokens
+  int32_t* s_offsets;  // [2]
+  int32_t* s_tiles;    // [2]
+  int32_t* s_tiles2;   // [2]
+  void* s_dgu;         // [T, 2 F_shared] dtype
+  void* s_h;           // [T, F_shared] dtype
+  void* s_dX;          // [T, d] dtype
 };
 bool backward_supported(const moe_shape& s);
 hipError_t launch_backward(const moe_shape& s, const void* dy, const void* x_perm,
@@ -93,8 +100,10 @@ hipError_t launch_backward(const moe_shape& s, const void* dy, const void* x_per
                            const int32_t* row_token, const int32_t* token_row,
                            const int32_t* topk_idx, const float* topk_w,
                            const float* logits, const void* w_gate, const void* w_up,
-                           const void* w_down, float* dx, float* dw_gate, float* dw_up,
-                           float* dw_down, float* d_gate, float* d_logits,
+                           const void* w_down, const void* x, const void* ws_gate,
+                           const void* ws_up, const void* ws_down, float* dx, float* dw_gate,
+                           float* dw_up, float* dw_down, float* dws_gate, float* dws_up,
+                           float* dws_down, float* d_gate, float* d_logits,
                            const BwdWs& ws, hipStream_t st);
 
 }  // namespace moe

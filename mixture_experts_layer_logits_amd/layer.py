@@ -37,7 +37,8 @@ class MoELayer:
             row_token=e(R, dtype=i32), token_row=e(T, k, dtype=i32),
             row_gate=e(R, dtype=f32), x_perm=e(R, d), y_perm=e(R, d),
             y_shared=e(T, d) if Fs > 0 else None,
-            gu_save=e(R, 2 * F) if self.save_gu else None,
+            # routed g | u [R, 2F], then the shared expert's [T, 2Fs]
+            gu_save=e(R * 2 * F + T * 2 * Fs) if self.save_gu else None,
             y=e(T, d, dtype=f32))
         self.grad = None
 
@@ -88,16 +89,35 @@ class MoELayer:
             dw_down=torch.empty(c.E, c.d, c.F, dtype=f32, device=dev),
             d_gate=torch.empty(c.T, c.k, dtype=f32, device=dev),
             d_logits=torch.empty(c.T, c.E, dtype=f32, device=dev))
+        fs = c.F_shared
+        self.grad.update(
+            dws_gate=torch.empty(fs, c.d, dtype=f32, device=dev) if fs else None,
+            dws_up=torch.empty(fs, c.d, dtype=f32, device=dev) if fs else None,
+            dws_down=torch.empty(c.d, fs, dtype=f32, device=dev) if fs else None)
+
+    def gu_views(self):
+        """(routed [R, 2F], shared [T, 2Fs] or None) views of gu_save."""
+        c, gu = self.cfg, self.buf["gu_save"]
+        if gu is None:
+            return None, None
+        n = c.T * c.k * 2 * c.F
+        routed = gu[:n].view(c.T * c.k, 2 * c.F)
+        shared = gu[n:].view(c.T, 2 * c.F_shared) if c.F_shared else None
+        return routed, shared
 
     def backward(self, inp, dy, stream=None):
         if self.grad is None:
             self._alloc_grad()
         b, g = self.buf, self.grad
+        sh = self.cfg.F_shared > 0
         L.moe_ffn_backward(self.shape, dy, b["x_perm"], b["gu_save"],
                            b["y_perm"], b["expert_offsets"], b["row_token"],
                            b["token_row"], b["topk_idx"], b["topk_w"],
                            b["logits"], inp["w_gate"], inp["w_up"],
-                           inp["w_down"], g["dx"], g["dw_gate"], g["dw_up"],
-                           g["dw_down"], g["d_gate"], g["d_logits"], self.ws,
-                           self.ws_bytes, stream)
+                           inp["w_down"], inp["x"] if sh else None,
+                           inp.get("ws_gate"), inp.get("ws_up"),
+                           inp.get("ws_down"), g["dx"], g["dw_gate"],
+                           g["dw_up"], g["dw_down"], g["dws_gate"],
+                           g["dws_up"], g["dws_down"], g["d_gate"],
+                           g["d_logits"], self.ws, self.ws_bytes, stream)
         return g

@@ -100,9 +100,21 @@ def test_calls_reject_null_misaligned_and_small_workspace():
     assert st == L.MOE_ERR_INVALID_ARG
 
 
-def test_backward_rejects_shared_expert():
+def test_backward_with_shared_expert_needs_its_buffers():
     c = CONFIGS["deepseek_v3_t8192"]
     s = M.make_shape(c)
     p = _fake()
-    st = M.moe_ffn_backward(s, *([p] * 19), p, 1 << 40, check=False, stream=0)
-    assert st == L.MOE_ERR_UNSUPPORTED
+    # x, ws_gate, ws_up, ws_down (args 14-17) and dws_* (22-24) are required
+    # when F_shared > 0: each one missing is rejected before any launch
+    for missing in (14, 15, 16, 17, 22, 23, 24):
+        args = [p] * 26
+        args[missing - 1] = None
+        st = M.moe_ffn_backward(s, *args, p, 1 << 40, check=False, stream=0)
+        assert st == L.MOE_ERR_INVALID_ARG, missing
+    # without a shared expert they may be NULL (then a small workspace fails)
+    s0 = M.make_shape(c.replace(F_shared=0))
+    args = [p] * 26
+    for i in (14, 15, 16, 17, 22, 23, 24):
+        args[i - 1] = None
+    st = M.moe_ffn_backward(s0, *args, p, 0, check=False, stream=0)
+    assert st == L.MOE_ERR_WORKSPACE

@@ -100,6 +100,44 @@ def test_layer_is_bitwise_deterministic():
         assert torch.equal(v, out[k]), k
 
 
+def test_layer_training_with_shared_expert():
+    """Forward (saving g|u of routed and shared rows) then backward of a layer
+    with sigmoid group-limited routing and a shared expert, against the
+    oracle's own forward and backward.  The shared expert's gradients do not
+    depend on the routing; dx[t] depends only on token t's own routing and
+    is compared where that is unambiguous; the routed weight gradients sum
+    over all tokens of an expert and are compared when the routing matches
+    the oracle's everywhere."""
+    cfg = SMALL["bf16_sigmoid_groups_shared_t200"].replace(backward=True)
+    print(f"[layer train] {cfg.name}", flush=True)
+    from mixture_experts_layer_logits_amd import MoELayer
+    inp = make_inputs(cfg, device="cuda")
+    layer = MoELayer(cfg)
+    out = layer.forward(inp)
+    g = layer.backward(inp, inp["dy"])
+    torch.cuda.synchronize()
+    prec = prec_of(cfg)
+    idx, w, amb, same = _route_and_check(cfg, inp, out)
+    ref = O.forward(inp, cfg, prec=prec, save_gu=True)
+    gu_r, gu_s = layer.gu_views()
+    assert_close("gu_shared", gu_s, ref["gu_shared"], prec)
+    host = lambda t: np64(t)
+    bw = O.ffn_backward(host(inp["dy"]), ref["x_perm"], ref["gu_save"], ref["y_perm"],
+                        ref["offsets"], ref["token_row"], ref["topk_idx"], ref["topk_w"],
+                        ref["route_logits"], host(inp["w_gate"]), host(inp["w_up"]),
+                        host(inp["w_down"]), cfg.score, cfg.renorm, prec,
+                        shared=dict(x=host(inp["x"]), gu=ref["gu_shared"],
+                                    ws_gate=host(inp["ws_gate"]), ws_up=host(inp["ws_up"]),
+                                    ws_down=host(inp["ws_down"])))
+    for key in ("dws_gate", "dws_up", "dws_down"):
+        assert_close(key, g[key], bw[key], prec)
+    ok = torch.as_tensor(~amb)
+    assert_close("dx[unambiguous]", g["dx"][ok.cuda()], bw["dx"][ok.numpy()], prec)
+    if same:
+        for key in ("dw_gate", "dw_up", "dw_down", "d_gate"):
+            assert_close(key, g[key], bw[key], prec)
+
+
 FULL = ["mixtral_t4096", "deepseek_v3_t8192", "qwen3_30b_skewed_t16384",
         "qwen3_235b_train_t8192", "deepseek_v3_ep8_rank_t8192"]
 
@@ -132,7 +170,7 @@ def test_layer_full_size_sampled(name):
     rows = out["token_row"][tt].reshape(-1).long()
     assert_close("y_perm[sample]", out["y_perm"][rows], ref["y_rows"].reshape(-1, cfg.d), prec)
     if out["gu_save"] is not None:
-        assert_close("gu_save[sample]", out["gu_save"][rows],
+        assert_close("gu_save[sample]", layer.gu_views()[0][rows],
                      ref["gu_rows"].reshape(-1, 2 * cfg.F), prec)
     if cfg.F_shared > 0:
         assert_close("y_shared[sample]", out["y_shared"][tt], ref["ys"], prec)

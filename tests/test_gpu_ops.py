@@ -205,20 +205,26 @@ def test_grouped_ffn(case):
     dt = cfg.torch_dtype
     yp = torch.empty(cfg.R, d, dtype=dt, device="cuda")
     ys = torch.empty(T, d, dtype=dt, device="cuda") if Fs else None
-    gu = torch.empty(cfg.R, 2 * F, dtype=dt, device="cuda")
+    # g | u of the routed rows [R, 2F], then of the shared expert [T, 2Fs]
+    n_r = cfg.R * 2 * F
+    gu_all = torch.empty(n_r + T * 2 * Fs, dtype=dt, device="cuda")
+    gu = gu_all[:n_r].view(cfg.R, 2 * F)
     shape = M.make_shape(cfg)
     ws, n = _ws(M, shape, 2)
     M.moe_grouped_ffn(shape, xp, torch.as_tensor(p["offsets"]).cuda(), inp["w_gate"], inp["w_up"],
                       inp["w_down"], inp["x"] if Fs else None, inp["ws_gate"], inp["ws_up"],
-                      inp["ws_down"], yp, ys, gu, ws, n)
+                      inp["ws_down"], yp, ys, gu_all, ws, n)
     torch.cuda.synchronize()
     ref_y, ref_gu = O.grouped_ffn(xp, p["offsets"], np64(inp["w_gate"]), np64(inp["w_up"]),
                                   np64(inp["w_down"]), prec, save_gu=True)
     assert_close("y_perm", yp, ref_y, prec)
     assert_close("gu_save", gu, ref_gu, prec)
     if Fs:
-        assert_close("y_shared", ys, O.shared_ffn(inp["x"], inp["ws_gate"], inp["ws_up"],
-                                                  inp["ws_down"], prec), prec)
+        r = O.swiglu_ffn(inp["x"], inp["ws_gate"], inp["ws_up"], inp["ws_down"], prec)
+        assert_close("y_shared", ys, r["y"], prec)
+        rnd = O.rounder(prec)
+        assert_close("gu_shared", gu_all[n_r:].view(T, 2 * Fs),
+                     np.concatenate([rnd(r["g"]), rnd(r["u"])], axis=1), prec)
 
 
 # --------------------------------------------------------------------------
@@ -261,7 +267,11 @@ def _bwd_inputs(cfg, skew=None, dev="cuda"):
     p = O.permute(None, idx, w, cfg.E)
     g = dict(logits=logits, idx=idx, w=w, p=p)
     g["x_perm"] = normal((cfg.R, cfg.d), 1.0, dt, dev, child_seed(11, "rows"))
-    g["gu"] = normal((cfg.R, 2 * cfg.F), 1.3, dt, dev, child_seed(12, "rows"))
+    # one buffer: routed g | u [R, 2F], then the shared expert's [T, 2Fs]
+    n = cfg.R * 2 * cfg.F
+    g["gu_all"] = normal((n + cfg.T * 2 * cfg.F_shared,), 1.3, dt, dev, child_seed(12, "rows"))
+    g["gu"] = g["gu_all"][:n].view(cfg.R, 2 * cfg.F)
+    g["gu_s"] = g["gu_all"][n:].view(cfg.T, 2 * cfg.F_shared) if cfg.F_shared else None
     g["y_perm"] = normal((cfg.R, cfg.d), 0.1, dt, dev, child_seed(13, "rows"))
     g["dy"] = normal((cfg.T, cfg.d), 1.0, dt, dev, child_seed(14, "rows"))
     return g
@@ -276,23 +286,37 @@ def _run_bwd(M, cfg, inp, g):
                dw_down=torch.empty(cfg.E, cfg.d, cfg.F, device=dev),
                d_gate=torch.empty(cfg.T, cfg.k, device=dev),
                d_logits=torch.empty(cfg.T, cfg.E, device=dev))
+    fs = cfg.F_shared
+    if fs:
+        out.update(dws_gate=torch.empty(fs, cfg.d, device=dev),
+                   dws_up=torch.empty(fs, cfg.d, device=dev),
+                   dws_down=torch.empty(cfg.d, fs, device=dev))
     for v in out.values():
         v.fill_(float("nan"))
     shape = M.make_shape(cfg)
     ws, n = _ws(M, shape, 4)
     i32 = lambda a: torch.as_tensor(np.asarray(a, dtype=np.int32)).cuda()
-    M.moe_ffn_backward(shape, g["dy"], g["x_perm"], g["gu"], g["y_perm"], i32(g["p"]["offsets"]),
-                       i32(g["p"]["row_token"]), i32(g["p"]["token_row"]), i32(g["idx"]),
+    M.moe_ffn_backward(shape, g["dy"], g["x_perm"], g["gu_all"], g["y_perm"],
+                       i32(g["p"]["offsets"]), i32(g["p"]["row_token"]),
+                       i32(g["p"]["token_row"]), i32(g["idx"]),
                        torch.as_tensor(g["w"], dtype=f32).cuda(), g["logits"].cuda(),
-                       inp["w_gate"], inp["w_up"], inp["w_down"], out["dx"], out["dw_gate"],
-                       out["dw_up"], out["dw_down"], out["d_gate"], out["d_logits"], ws, n)
+                       inp["w_gate"], inp["w_up"], inp["w_down"],
+                       inp["x"] if fs else None, inp["ws_gate"], inp["ws_up"], inp["ws_down"],
+                       out["dx"], out["dw_gate"], out["dw_up"], out["dw_down"],
+                       out.get("dws_gate"), out.get("dws_up"), out.get("dws_down"),
+                       out["d_gate"], out["d_logits"], ws, n)
     torch.cuda.synchronize()
     return out
 
 
 BWD_CASES = [
-    # name, T, d, E, k, F, dtype, score, renorm, skew
+    # name, T, d, E, k, F, dtype, score, renorm, skew[, F_shared]
     ("mfma_softmax_t300", 300, 256, 8, 2, 256, 1, 0, 1, False),
+    # with a shared expert: direct-to-LDS, MFMA, generic bf16 and fp32 paths
+    ("dma_shared_sigmoid_t300", 300, 256, 16, 4, 256, 1, 1, 1, False, 512),
+    ("mfma_shared_t200", 200, 128, 8, 2, 128, 1, 0, 1, True, 128),
+    ("generic_shared_t77", 77, 200, 6, 2, 96, 1, 0, 1, False, 40),
+    ("fp32_shared_t64", 64, 32, 4, 2, 16, 0, 1, 1, False, 24),
     ("dma_skewed_tails_t500", 500, 256, 16, 4, 512, 1, 0, 1, True),
     ("dma_sigmoid_t333", 333, 512, 24, 3, 256, 1, 1, 1, False),
     ("mfma_skewed_empty_t400", 400, 128, 16, 4, 128, 1, 0, 1, True),
@@ -305,19 +329,28 @@ BWD_CASES = [
 
 @pytest.mark.parametrize("case", BWD_CASES, ids=[c[0] for c in BWD_CASES])
 def test_ffn_backward(case):
-    name, T, d, E, k, F, dtype, score, renorm, skew = case
+    name, T, d, E, k, F, dtype, score, renorm, skew = case[:10]
+    Fs = case[10] if len(case) > 10 else 0
     _log(f"[backward] {name}")
     M = _lib()
-    cfg = MoEConfig(name, T=T, d=d, E=E, k=k, F=F, dtype=dtype, score=score, renorm=renorm,
-                    backward=True)
+    cfg = MoEConfig(name, T=T, d=d, E=E, k=k, F=F, F_shared=Fs, dtype=dtype, score=score,
+                    renorm=renorm, backward=True)
     prec = prec_of(cfg)
     inp = make_inputs(cfg, device="cuda")
     g = _bwd_inputs(cfg, skew)
     out = _run_bwd(M, cfg, inp, g)
+    shared = None
+    if Fs:
+        shared = dict(x=np64(inp["x"]), gu=np64(g["gu_s"]), ws_gate=np64(inp["ws_gate"]),
+                      ws_up=np64(inp["ws_up"]), ws_down=np64(inp["ws_down"]))
     ref = O.ffn_backward(g["dy"], g["x_perm"], g["gu"], g["y_perm"], g["p"]["offsets"],
                          g["p"]["token_row"], g["idx"], g["w"], g["logits"], np64(inp["w_gate"]),
-                         np64(inp["w_up"]), np64(inp["w_down"]), score, renorm, prec)
-    for key in ("d_gate", "d_logits", "dx", "dw_gate", "dw_up", "dw_down"):
+                         np64(inp["w_up"]), np64(inp["w_down"]), score, renorm, prec,
+                         shared=shared)
+    keys = ["d_gate", "d_logits", "dx", "dw_gate", "dw_up", "dw_down"]
+    if Fs:
+        keys += ["dws_gate", "dws_up", "dws_down"]
+    for key in keys:
         assert_close(key, out[key], ref[key], "f32" if prec == "f32" else "bf16")
     counts = np.diff(g["p"]["offsets"])
     for e in np.nonzero(counts == 0)[0]:

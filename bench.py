@@ -52,7 +52,7 @@ def ffn_bytes(c, counts_nonzero):
         w += 3.0 * c.d * c.F_shared * b
         act += (c.T * c.d + 2 * c.T * c.F_shared + c.T * c.d) * b
     if c.backward:
-        act += 2 * R * c.F * b   # gu_save
+        act += (2 * R * c.F + 2 * c.T * c.F_shared) * b   # gu_save
     return w + act
 
 
@@ -132,10 +132,15 @@ def _oracle_pass(cfg, inp, T):
     t0 = time.perf_counter()
     out = O.forward(host, sub, save_gu=cfg.backward)
     if cfg.backward:
+        shared = None
+        if cfg.F_shared:
+            shared = dict(x=host["x"], gu=out["gu_shared"], ws_gate=host["ws_gate"],
+                          ws_up=host["ws_up"], ws_down=host["ws_down"])
         O.ffn_backward(host["dy"], out["x_perm"], out["gu_save"], out["y_perm"],
                        out["offsets"], out["token_row"], out["topk_idx"],
                        out["topk_w"], out["route_logits"], host["w_gate"],
-                       host["w_up"], host["w_down"], cfg.score, cfg.renorm)
+                       host["w_up"], host["w_down"], cfg.score, cfg.renorm,
+                       shared=shared)
     return time.perf_counter() - t0
 
 

@@ -111,6 +111,13 @@ CONFIGS: Dict[str, MoEConfig] = {
     # token's own rank and is left out).
     "deepseek_v3_ep8_rank_t8192": MoEConfig("deepseek_v3_ep8_rank_t8192", T=8192,
                                             d=7168, E=32, k=8, F=2048),
+    # DeepSeek-V3-shape bf16 training step: the forward workload above plus
+    # the backward of the sigmoid group-limited router and the shared expert.
+    "deepseek_v3_train_t8192": MoEConfig("deepseek_v3_train_t8192", T=8192,
+                                         d=7168, E=256, k=8, F=2048,
+                                         F_shared=2048, n_groups=8,
+                                         topk_groups=4, score=SCORE_SIGMOID,
+                                         score_bias_std=0.1, backward=True),
     # Qwen3-235B-A22B-shape bf16 training step (forward + backward).
     "qwen3_235b_train_t8192": MoEConfig("qwen3_235b_train_t8192", T=8192,
                                         d=4096, E=128, k=8, F=1536,

@@ -360,10 +360,12 @@ def test_ffn_backward(case):
         assert (counts == 0).any()
 
 
-def test_ffn_backward_full_size_sampled():
-    """The training workload's shape: sampled tokens for d_gate, d_logits and
-    dx; three whole experts (first, middle, last) for the weight gradients."""
-    cfg = CONFIGS["qwen3_235b_train_t8192"]
+@pytest.mark.parametrize("name", ["qwen3_235b_train_t8192", "deepseek_v3_train_t8192"])
+def test_ffn_backward_full_size_sampled(name):
+    """A training workload's shape: sampled tokens for d_gate, d_logits and
+    dx; three whole experts (first, middle, last) for the weight gradients;
+    with a shared expert, its whole weight gradients too."""
+    cfg = CONFIGS[name]
     _log(f"[backward full] {cfg.name}")
     M = _lib()
     inp = make_inputs(cfg, device="cuda")
@@ -387,7 +389,8 @@ def test_ffn_backward_full_size_sampled():
     yp = np64(g["y_perm"][torch.as_tensor(rows.reshape(-1)).cuda()]).reshape(len(toks), cfg.k, cfg.d)
     d_gate = np.einsum("td,tjd->tj", dy, yp)
     assert_close("d_gate[sample]", out["d_gate"][torch.as_tensor(toks).cuda()], d_gate, "bf16")
-    d_l = O.router_backward(d_gate, g["idx"][toks], g["w"][toks], g["logits"][toks], cfg.E)
+    d_l = O.router_backward(d_gate, g["idx"][toks], g["w"][toks], g["logits"][toks], cfg.E,
+                            cfg.score, cfg.renorm)
     assert_close("d_logits[sample]", out["d_logits"][torch.as_tensor(toks).cuda()], d_l, "bf16")
     # dx on sampled tokens: each row's dX depends on that row only
     flat = rows.reshape(-1)
@@ -401,7 +404,13 @@ def test_ffn_backward_full_size_sampled():
                               np64(inp["w_down"][int(e)]), "bf16")
         dX[sel] = r["dX"]
     dx = dX.reshape(len(toks), cfg.k, cfg.d).sum(axis=1)
-    assert_close("dx[sample]", out["dx"][torch.as_tensor(toks).cuda()], dx, "bf16")
+    tt = torch.as_tensor(toks).cuda()
+    if cfg.F_shared:
+        rs = O.expert_backward(dy, np64(inp["x"][tt]), np64(g["gu_s"][tt]),
+                               np64(inp["ws_gate"]), np64(inp["ws_up"]),
+                               np64(inp["ws_down"]), "bf16")
+        dx = dx + rs["dX"]
+    assert_close("dx[sample]", out["dx"][tt], dx, "bf16")
     # weight gradients of whole experts
     for e in (0, cfg.E // 2, cfg.E - 1):
         a, b = int(p["offsets"][e]), int(p["offsets"][e + 1])
@@ -411,3 +420,9 @@ def test_ffn_backward_full_size_sampled():
                               np64(inp["w_down"][e]), "bf16")
         for key in ("dw_gate", "dw_up", "dw_down"):
             assert_close(f"{key}[{e}]", out[key][e], r[key], "bf16")
+    if cfg.F_shared:
+        rs = O.expert_backward(np64(g["dy"]), np64(inp["x"]), np64(g["gu_s"]),
+                               np64(inp["ws_gate"]), np64(inp["ws_up"]),
+                               np64(inp["ws_down"]), "bf16")
+        for key in ("dw_gate", "dw_up", "dw_down"):
+            assert_close(f"dws_{key[3:]}", out["dws_" + key[3:]], rs[key], "bf16")

@@ -4,15 +4,17 @@
  *
  * The layer is the one laid out on the AMD blog "MoE Training Optimization
  * with Primus" (MegaMoE section, layer dataflow of Figure 7), without its two
- * all-to-all stages: the router scores each token and picks its top-k
- * experts; a permutation gathers the tokens into expert order; two grouped
- * GEMMs, FC1 (gate/up) and FC2 (down), with a SwiGLU between them do the
- * expert compute; a final unpermute-and-scale sums the k contributions back
- * onto each token.  The permuted buffer is padding-free in the sense of the
+ * all-to-all stages.  A router gives every token a score per expert and keeps
+ * the k best; the tokens are reordered so that each expert's rows sit
+ * together; per expert, an up-projection pair (gate and up) feeds a SwiGLU
+ * whose output the down-projection maps back, both as grouped GEMMs over all
+ * experts; the last stage weights each token's k expert outputs by its gates
+ * and sums them into the token's row.  The permuted buffer is padding-free in the sense of the
  * X-MoE verdict page on pith.science (key_machinery field): it holds only the
  * routed rows, with token ids, counts and combine weights beside it.  The
  * backward follows the same page's dispatch/combine duality (data-gradient
- * GEMMs plus two variable-K weight-gradient GEMMs).
+ * GEMMs, and weight-gradient GEMMs whose contraction length is each expert's
+ * row count).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -96,8 +98,8 @@ typedef struct moe_shape {
  * GPU work.  Returns MOE_ERR_INVALID_ARG for a bad shape or op. */
 int moe_workspace_size(const moe_shape* shape, int op, size_t* bytes);
 
-/* Router scoring and top-k gating (Primus blog, MegaMoE section: "the router
- * scores each token and picks its top-k experts"; sigmoid scores with a
+/* Router scoring and top-k gating (Primus blog, MegaMoE section: a router
+ * gives every token a score per expert and keeps the k best; sigmoid scores with a
  * selection bias and a group limit are DeepSeek-V3's router).
  *
  *  x [T, d] dtype, w_router [E, d] dtype, router_bias [E] fp32 or NULL:
@@ -122,7 +124,8 @@ int moe_route_topk(const moe_shape* shape, const void* x, const void* w_router,
                    void* ws, size_t ws_bytes, void* stream);
 
 /* Padding-free permutation into expert-contiguous order (Primus blog,
- * MegaMoE section: "a permutation gathers tokens into expert order"):
+ * MegaMoE section: tokens are reordered so that each expert's rows are
+ * contiguous):
  * expert histogram, exclusive prefix scan, stable scatter.
  *
  *  x [T, d] dtype; topk_idx [T, k] int32 with k distinct experts per token in
@@ -144,8 +147,8 @@ int moe_permute(const moe_shape* shape, const void* x, const int32_t* topk_idx,
 
 /* Grouped SwiGLU expert FFN over ragged, expert-contiguous row ranges, in one
  * launch per GEMM (Primus blog, MegaMoE section: FC1 (gate/up) -> SwiGLU ->
- * FC2 (down)), plus the always-on shared expert over all T tokens when
- * F_shared > 0 (the blog's "shared plus routed experts").
+ * FC2 (down)), plus the shared expert over all T tokens when F_shared > 0
+ * (the blog's layer combines such a shared expert with the routed ones).
  *
  *  x_perm [R, d] dtype; expert_offsets [E+1] int32 (as from moe_permute;
  *      read on the device only).
@@ -167,8 +170,8 @@ int moe_grouped_ffn(const moe_shape* shape, const void* x_perm,
                     const void* ws_down, void* y_perm, void* y_shared,
                     void* gu_save, void* ws, size_t ws_bytes, void* stream);
 
-/* Unpermute-and-scale (Primus blog, MegaMoE section: "a final
- * unpermute-and-scale reduces the top-k contributions back onto each token"):
+/* Unpermute-and-scale (Primus blog, MegaMoE section: the last stage sums each
+ * token's k gate-weighted expert outputs back into its row):
  *      y[t] = y_shared[t] + sum_{j=0..k-1} topk_w[t, j] * y_perm[token_row[t, j]]
  * accumulated in fp32 in that order, as a per-token gather (no atomics).
  *  y_perm [R, d] dtype; token_row [T, k]; topk_w [T, k] fp32;
@@ -182,7 +185,7 @@ int moe_unpermute_combine(const moe_shape* shape, const void* y_perm,
 
 /* Backward of the layer (Primus blog, MegaMoE section: the backward
  * mirrors the forward through dispatch/combine duality, with the FC2 and FC1
- * data gradients and two variable-K weight-gradient GEMMs).  From the
+ * data gradients and weight-gradient GEMMs over each expert's rows).  From the
  * upstream gradient dy of y it produces:
  *   dY_perm[token_row[t,j]] = rnd(w[t,j] dy[t]);  d_gate[t,j] = <dy[t], y_perm[row]>
  *   dh = dY_perm . w_down[e];  dg = rnd(dh u silu'(g));  du = rnd(dh silu(g))
@@ -200,8 +203,8 @@ int moe_unpermute_combine(const moe_shape* shape, const void* y_perm,
  *  Outputs (fp32): dx [T, d]; dw_gate, dw_up [E, F, d]; dw_down [E, d, F]
  *  (exactly zero for experts with no rows); d_gate [T, k]; d_logits [T, E].
  *
- *  With F_shared > 0 the always-on shared expert (gate 1 on every token; the
- *  Primus blog's shared plus routed experts) gets the same backward over all
+ *  With F_shared > 0 the shared expert (gate 1 on every token, beside the
+ *  routed experts as in the Primus blog's layer) gets the same backward over all
  *  T tokens with dY = dy, from its g | u saved at the end of gu_save:
  *    dws_down = dy^T . hs;  dws_gate = dgs^T . x;  dws_up = dus^T . x
  *    dx[t] += rnd(dgs . ws_gate + dus . ws_up)[t], added after the routed terms.

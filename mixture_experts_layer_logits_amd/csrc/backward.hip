@@ -1,6 +1,7 @@
 // Backward of the routed MoE layer (Primus blog, MegaMoE section: the
 // backward mirrors the forward through dispatch/combine duality, with the
-// FC2 and FC1 data-gradient GEMMs plus two variable-K weight-gradient GEMMs).
+// FC2 and FC1 data-gradient GEMMs, and weight-gradient GEMMs that contract over
+// each expert's rows, so their K varies by expert).
 //
 //   b1+b7  per token: dY_perm[row] = rnd(w dy[t]), d_gate = <dy[t], y_perm[row]>,
 //          d_logits through the gate function

@@ -1,5 +1,5 @@
-// Unpermute-and-scale (Primus blog, MegaMoE section: the final stage reduces
-// the top-k contributions back onto each token):
+// Unpermute-and-scale (Primus blog, MegaMoE section: the last stage weights
+// each token's k expert outputs by its gates and sums them into its row):
 //   y[t] = y_shared[t] + sum_{j=0..k-1} w[t, j] * y_perm[token_row[t, j]]
 // as a per-token gather in fp32, in that fixed order.  Each token's sum is
 // owned by one workgroup, so no atomics are needed and the result is bitwise

@@ -1,7 +1,8 @@
 // Padding-free permutation into expert-contiguous order: expert histogram,
-// exclusive prefix scan, stable scatter (Primus blog, MegaMoE section: "a
-// permutation gathers tokens into expert order"; the buffer holds only routed
-// rows, as in the padding-free token buffer of the X-MoE verdict page).
+// exclusive prefix scan, stable scatter (Primus blog, MegaMoE section: the
+// tokens are reordered so that each expert's rows sit together; the buffer
+// holds only routed rows, as in the padding-free token buffer of the X-MoE
+// verdict page).
 //
 // Row order is (expert, token) ascending, so every index is fixed by the
 // routing alone and no atomic decides a position:

@@ -6,10 +6,10 @@
 // arg-max reduction pick the largest remaining key, the lower expert index
 // winning ties.  Sigmoid scoring first keeps the topk_groups best groups of
 // contiguous experts (group score: fp32 sum of the group's two largest keys),
-// then searches only those.  (Primus blog, MegaMoE section: the router scores
-// each token and picks its top-k experts; the sigmoid/bias/group-limited
-// variant is DeepSeek-V3's, whose bias-adjustment balancing the Piper podcast
-// page mentions.)
+// then searches only those.  (Primus blog, MegaMoE section: a router scores
+// every token against each expert and keeps the k best; the sigmoid scores
+// with a per-expert selection bias and group limit follow DeepSeek-V3, whose
+// bias-based load balancing the Piper podcast page refers to.)
 #include <float.h>
 #include <limits.h>
 

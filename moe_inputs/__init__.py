@@ -54,7 +54,7 @@ class MoEConfig:
     E: int                      # routed experts
     k: int                      # experts per token
     F: int                      # routed expert FFN width
-    F_shared: int = 0           # shared ("always-on") expert width, 0 = none
+    F_shared: int = 0           # width of the shared expert (every token), 0 = none
     n_groups: int = 1           # expert groups for group-limited routing
     topk_groups: int = 1        # groups kept per token
     score: int = SCORE_SOFTMAX

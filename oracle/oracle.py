@@ -7,11 +7,11 @@ module ``moe_inputs``, which holds none of the layer's arithmetic.
 
 What it computes (the layer as described on the AMD blog "MoE Training
 Optimization with Primus", MegaMoE section, layer dataflow of Figure 7): the
-router scores each token and picks its top-k experts; a permutation gathers the
-tokens into expert order; per expert, FC1 (gate and up) feeds a SwiGLU and FC2
+router gives every token a score per expert and keeps the k best; the tokens are
+reordered so that each expert's rows sit together; per expert, FC1 (gate and up) feeds a SwiGLU and FC2
 (down); a final unpermute-and-scale sums the k gate-weighted expert outputs back
-onto each token.  The permuted buffer is padding-free (the "Padding-Free Token
-buffer" of the X-MoE verdict page on pith.science, key_machinery field): it
+onto each token.  The permuted buffer is padding-free (the padding-free token
+buffer of the X-MoE verdict page on pith.science, key_machinery field): it
 holds only routed rows plus token ids, expert ids, counts and combine weights.
 
 Every floating-point step is evaluated in fp64.  A tensor that the layer
@@ -154,7 +154,8 @@ def sigmoid_scores(logits, prec="f32"):
 def route_sigmoid_grouped(logits, k, n_groups, topk_groups, score_bias=None,
                           renorm=1, prec="f32"):
     """DeepSeek-V3-style routing: sigmoid scores, selection-only per-expert
-    bias ("bias-adjustment balancing" on the Piper podcast page), a group
+    bias (the bias adjustment for load balancing that the Piper podcast page
+    mentions), a group
     limit, top-k inside the kept groups, gates from the unbiased scores.
 
     The key s + bias and a group's top-2 sum are single fp32 additions
@@ -281,7 +282,7 @@ def grouped_ffn(x_perm, offsets, w_gate, w_up, w_down, prec="bf16",
 
 
 def shared_ffn(x, ws_gate, ws_up, ws_down, prec="bf16"):
-    """The always-on shared expert over every token (gate 1)."""
+    """The shared expert, applied to every token (gate 1)."""
     return swiglu_ffn(x, ws_gate, ws_up, ws_down, prec)["y"]
 
 
@@ -291,7 +292,7 @@ def shared_ffn(x, ws_gate, ws_up, ws_down, prec="bf16"):
 def combine(y_perm, token_row, topk_w, y_shared=None, prec="f32"):
     """y[t] = ys[t] + sum_j w[t,j] * y_perm[token_row[t,j]] (fp64 sum, fp32
     result): the final unpermute-and-scale of the Primus blog's MegaMoE
-    section, reducing the k contributions back onto each token."""
+    section, which folds each token's k weighted expert outputs into its row."""
     y_perm = as64(y_perm)
     tr = np.asarray(token_row, dtype=np.int64)
     w = as64(topk_w)
@@ -399,7 +400,7 @@ def ffn_backward(dy, x_perm, gu_save, y_perm, offsets, token_row, topk_idx,
     """Backward of the layer, from the saved tensors.
 
     The backward mirrors the forward through dispatch/combine duality, with
-    the FC2 and FC1 data gradients and two variable-K weight-gradient GEMMs
+    the FC2 and FC1 data gradients and weight-gradient GEMMs over each expert's rows
     (Primus blog, MegaMoE section):
       dY_perm[pos] = w[t,j] dy[t];  d_gate[t,j] = <dy[t], y_perm[pos]>
       per expert: expert_backward;  dx[t] = sum_j dX_perm[pos[t,j]]
@@ -407,7 +408,7 @@ def ffn_backward(dy, x_perm, gu_save, y_perm, offsets, token_row, topk_idx,
     Weight gradients of experts with no rows are exactly zero.
 
     ``shared`` (optional) = dict(x, gu, ws_gate, ws_up, ws_down) for the
-    always-on shared expert: it adds ys[t] to y[t] with gate 1, so its
+    shared expert applied to every token: it adds ys[t] to y[t] with gate 1, so its
     backward is expert_backward on all T tokens with dY = dy; its data
     gradient is added to dx after the routed terms.
     """

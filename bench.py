@@ -231,6 +231,41 @@ def main():
     per_stage = {st: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1])
                                     for s in range(args.steps)]))
                  for i, st in enumerate(stages)}
+
+    # The same forward with the permutation fused into FC1's operand load
+    # (maps-only permute, rows gathered from x; no x_perm), timed the same way.
+    fused = None
+    if not cfg.backward:
+        def fused_step(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            layer.route(inp)
+            layer.permute(inp, maps_only=True)
+            if ev is not None:
+                ev[1].record(stream)
+            layer.ffn(inp, fused=True)
+            if ev is not None:
+                ev[2].record(stream)
+            layer.combine(inp)
+            if ev is not None:
+                ev[3].record(stream)
+        for _ in range(args.warmup):
+            fused_step()
+        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        f0 = time.perf_counter()
+        for s_ in range(args.steps):
+            fused_step(fev[s_])
+        torch.cuda.synchronize()
+        fwall = (time.perf_counter() - f0) * 1e3 / args.steps
+        fms = lambda a, b: float(np.mean([fev[s_][a].elapsed_time(fev[s_][b])
+                                          for s_ in range(args.steps)]))
+        fused = {"ms_per_step": round(fwall, 4),
+                 "tokens_per_s": round(cfg.T / (fwall / 1e3), 1),
+                 "stage_ms": {"route+permute_maps": round(fms(0, 1), 4),
+                              "ffn_gathered": round(fms(1, 2), 4),
+                              "combine": round(fms(2, 3), 4)}}
     ms_step = float(np.mean([evs[s][0].elapsed_time(evs[s][-1])
                              for s in range(args.steps)]))
     ms_wall = wall * 1e3 / args.steps
@@ -281,6 +316,7 @@ def main():
         "stage_ms": {k: round(v, 4) for k, v in per_stage.items()},
         "stage_hbm": hbm,
         "event_ms_per_step": round(ms_step, 4),
+        "fused_permute_forward": fused,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -136,7 +136,9 @@ int moe_route_topk(const moe_shape* shape, const void* x, const void* w_router,
  *      expert are in ascending token order.
  *  token_row [T, k] int32 out: inverse map, row of (t, j).
  *  row_gate [R] fp32 out: topk_w of each row.
- *  x_perm [R, d] dtype out: x_perm[token_row[t, j]] = x[t], bit-exact copy.
+ *  x_perm [R, d] dtype out: x_perm[token_row[t, j]] = x[t], bit-exact copy;
+ *      or NULL: only the maps are produced (x is then not read and may be
+ *      NULL), for a moe_grouped_ffn call that gathers its rows from x.
  *  Entries of topk_idx outside [0, E) are skipped (token_row = -1); repeated
  *  experts within a token give unspecified (memory-safe) maps.
  *  ws: MOE_OP_PERMUTE bytes. */
@@ -150,10 +152,15 @@ int moe_permute(const moe_shape* shape, const void* x, const int32_t* topk_idx,
  * FC2 (down)), plus the shared expert over all T tokens when F_shared > 0
  * (the blog's layer combines such a shared expert with the routed ones).
  *
- *  x_perm [R, d] dtype; expert_offsets [E+1] int32 (as from moe_permute;
- *      read on the device only).
+ *  x_perm [R, d] dtype, or NULL: then FC1 reads routed row r straight from
+ *      x[row_token[r]] (the permutation fused into FC1's operand load; x and
+ *      row_token [R] int32 are required, and T * d * sizeof(dtype) must stay
+ *      below 2^31, else MOE_ERR_UNSUPPORTED).  row_token is ignored when
+ *      x_perm is given.
+ *  expert_offsets [E+1] int32 (as from moe_permute; read on the device only).
  *  w_gate, w_up [E, F, d]; w_down [E, d, F] dtype.
- *  x [T, d], ws_gate, ws_up [Fs, d], ws_down [d, Fs] dtype: only read when
+ *  x [T, d], ws_gate, ws_up [Fs, d], ws_down [d, Fs] dtype: x is read for the
+ *      gathered rows above or the shared expert, the weights only when
  *      F_shared > 0 (may be NULL otherwise).
  *  y_perm [R, d] dtype out: rows of expert e = (silu(g) * u) . w_down[e]^T,
  *      with h = silu(g) * u rounded to dtype before FC2.
@@ -164,8 +171,9 @@ int moe_permute(const moe_shape* shape, const void* x, const int32_t* topk_idx,
  *      every token), so it holds R * 2F + T * 2F_shared elements.
  *  ws: MOE_OP_FFN bytes (holds h). */
 int moe_grouped_ffn(const moe_shape* shape, const void* x_perm,
-                    const int32_t* expert_offsets, const void* w_gate,
-                    const void* w_up, const void* w_down, const void* x,
+                    const int32_t* row_token, const int32_t* expert_offsets,
+                    const void* w_gate, const void* w_up, const void* w_down,
+                    const void* x,
                     const void* ws_gate, const void* ws_up,
                     const void* ws_down, void* y_perm, void* y_shared,
                     void* gu_save, void* ws, size_t ws_bytes, void* stream);

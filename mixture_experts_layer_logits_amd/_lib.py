@@ -64,7 +64,7 @@ def load() -> ctypes.CDLL:
     lib.moe_workspace_size.argtypes = [sp, ctypes.c_int, ctypes.POINTER(sz)]
     lib.moe_route_topk.argtypes = [sp] + [vp] * 7 + [vp, sz, vp]
     lib.moe_permute.argtypes = [sp] + [vp] * 8 + [vp, sz, vp]
-    lib.moe_grouped_ffn.argtypes = [sp] + [vp] * 12 + [vp, sz, vp]
+    lib.moe_grouped_ffn.argtypes = [sp] + [vp] * 13 + [vp, sz, vp]
     lib.moe_unpermute_combine.argtypes = [sp] + [vp] * 5 + [vp, sz, vp]
     lib.moe_ffn_backward.argtypes = [sp] + [vp] * 26 + [vp, sz, vp]
     lib.moe_status_string.argtypes = [ctypes.c_int]
@@ -136,13 +136,13 @@ def moe_permute(shape, x, topk_idx, topk_w, expert_offsets, row_token,
     return _check(st, "moe_permute") if check else st
 
 
-def moe_grouped_ffn(shape, x_perm, expert_offsets, w_gate, w_up, w_down, x,
-                    ws_gate, ws_up, ws_down, y_perm, y_shared, gu_save,
-                    ws=None, ws_bytes=0, stream=None, check=True):
+def moe_grouped_ffn(shape, x_perm, row_token, expert_offsets, w_gate, w_up,
+                    w_down, x, ws_gate, ws_up, ws_down, y_perm, y_shared,
+                    gu_save, ws=None, ws_bytes=0, stream=None, check=True):
     st = load().moe_grouped_ffn(
-        ctypes.byref(shape), _p(x_perm), _p(expert_offsets), _p(w_gate),
-        _p(w_up), _p(w_down), _p(x), _p(ws_gate), _p(ws_up), _p(ws_down),
-        _p(y_perm), _p(y_shared), _p(gu_save), _p(ws), ws_bytes,
+        ctypes.byref(shape), _p(x_perm), _p(row_token), _p(expert_offsets),
+        _p(w_gate), _p(w_up), _p(w_down), _p(x), _p(ws_gate), _p(ws_up),
+        _p(ws_down), _p(y_perm), _p(y_shared), _p(gu_save), _p(ws), ws_bytes,
         _stream(stream))
     return _check(st, "moe_grouped_ffn") if check else st
 

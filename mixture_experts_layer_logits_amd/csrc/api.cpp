@@ -154,10 +154,12 @@ int moe_permute(const moe_shape* shape, const void* x, const int32_t* topk_idx,
   const moe_shape& s = *shape;
   const long long es = (long long)esize(s);
   const long long R = (long long)s.T * s.k;
-  if (!ok_buf(x, (long long)s.T * s.d * es) || !ok_buf(topk_idx, R * 4) ||
+  // x_perm NULL: only the maps (then x is not read and may be NULL too)
+  const bool rows = x_perm != nullptr;
+  if ((rows && !ok_buf(x, (long long)s.T * s.d * es)) || !ok_buf(topk_idx, R * 4) ||
       !ok_buf(topk_w, R * 4) || !ok_buf(expert_offsets, (long long)(s.E + 1) * 4) ||
       !ok_buf(row_token, R * 4) || !ok_buf(token_row, R * 4) || !ok_buf(row_gate, R * 4) ||
-      !ok_buf(x_perm, R * s.d * es))
+      (rows && !ok_buf(x_perm, R * s.d * es)))
     return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(s, MOE_OP_PERMUTE, ws, ws_bytes)) != MOE_OK) return st;
   Carver c{static_cast<char*>(ws)};
@@ -170,17 +172,27 @@ int moe_permute(const moe_shape* shape, const void* x, const int32_t* topk_idx,
                                         static_cast<hipStream_t>(stream)));
 }
 
-int moe_grouped_ffn(const moe_shape* shape, const void* x_perm, const int32_t* expert_offsets,
-                    const void* w_gate, const void* w_up, const void* w_down, const void* x,
-                    const void* ws_gate, const void* ws_up, const void* ws_down, void* y_perm,
-                    void* y_shared, void* gu_save, void* ws, size_t ws_bytes, void* stream) {
+int moe_grouped_ffn(const moe_shape* shape, const void* x_perm, const int32_t* row_token,
+                    const int32_t* expert_offsets, const void* w_gate, const void* w_up,
+                    const void* w_down, const void* x, const void* ws_gate, const void* ws_up,
+                    const void* ws_down, void* y_perm, void* y_shared, void* gu_save, void* ws,
+                    size_t ws_bytes, void* stream) {
   int st = check_shape(shape);
   if (st != MOE_OK) return st;
   const moe_shape& s = *shape;
   const long long es = (long long)esize(s);
   const long long R = (long long)s.T * s.k;
   const long long wsz = (long long)s.E * s.F * s.d * es;
-  if (!ok_buf(x_perm, R * s.d * es) || !ok_buf(expert_offsets, (long long)(s.E + 1) * 4) ||
+  const bool gather = x_perm == nullptr && R > 0;
+  if (gather) {
+    // rows come from x[row_token[r]]; byte offsets into x are 32-bit
+    if (!ok_buf(x, (long long)s.T * s.d * es) || !ok_buf(row_token, R * 4))
+      return MOE_ERR_INVALID_ARG;
+    if ((long long)s.T * s.d * es >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+  } else if (!ok_buf(x_perm, R * s.d * es)) {
+    return MOE_ERR_INVALID_ARG;
+  }
+  if (!ok_buf(expert_offsets, (long long)(s.E + 1) * 4) ||
       !ok_buf(w_gate, wsz) || !ok_buf(w_up, wsz) || !ok_buf(w_down, wsz) ||
       !ok_buf(y_perm, R * s.d * es) || !ok_buf(gu_save, 0))
     return MOE_ERR_INVALID_ARG;
@@ -199,7 +211,8 @@ int moe_grouped_ffn(const moe_shape* shape, const void* x_perm, const int32_t* e
   fw.h_shared = c.take<char>((size_t)s.T * s.F_shared * es);
   const int ks = moe::ffn_fc2_ksplit(s);
   fw.part = ks > 1 ? c.take<float>((size_t)ks * R * s.d * 4) : nullptr;
-  return hip_status(moe::launch_grouped_ffn(s, x_perm, expert_offsets, w_gate, w_up, w_down, x,
+  return hip_status(moe::launch_grouped_ffn(s, x_perm, gather ? row_token : nullptr,
+                                            expert_offsets, w_gate, w_up, w_down, x,
                                             ws_gate, ws_up, ws_down, y_perm, y_shared, gu_save,
                                             fw, static_cast<hipStream_t>(stream)));
 }

@@ -1,7 +1,7 @@
 // Grouped SwiGLU expert FFN (Primus blog, MegaMoE section: FC1 (gate/up) ->
 // SwiGLU -> FC2 (down), as two grouped GEMMs over ragged expert groups; the
 // DeepSeek-V3 memory-model page gives the three matrices h x h_E, h x h_E,
-// h_E x h).  The shared "always-on" expert rides along as one dense group of
+// h_E x h).  The shared expert, applied to every token, rides along as one dense group of
 // all T tokens in the same two launches.
 //
 //   schedule:  tile prefixes of FC1 and FC2 from the device offsets
@@ -73,7 +73,8 @@ static hipError_t run_generic(const moe_shape& s, GemmArgs& a1, GemmArgs& a2, in
   return hipGetLastError();
 }
 
-hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const int32_t* offsets,
+hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const int32_t* row_token,
+                              const int32_t* offsets,
                               const void* w_gate, const void* w_up, const void* w_down,
                               const void* x, const void* ws_gate, const void* ws_up,
                               const void* ws_down, void* y_perm, void* y_shared,
@@ -85,7 +86,9 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const int3
   a1.E = R > 0 ? s.E : 0;
   a1.offsets = offsets;
   a1.tiles = ws.tiles1;
-  a1.A = x_perm;
+  // without x_perm, FC1 gathers each routed row from x[row_token[r]]
+  a1.A = x_perm ? x_perm : x;
+  a1.gather = x_perm ? nullptr : row_token;
   a1.lda = s.d;
   a1.B0 = w_gate;
   a1.B1 = w_up;

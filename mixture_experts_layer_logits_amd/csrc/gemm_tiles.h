@@ -47,6 +47,7 @@ struct GemmArgs {
   const int32_t* tiles;    // [E + 1] exclusive prefix of the groups' tile counts
   const void* A;           // group g owns rows offsets[g] .. offsets[g+1]-1
   long long lda;
+  const int32_t* gather;   // or null: routed row r is row gather[r] of A
   const void* B0;          // [E][N][K]
   const void* B1;          // second B (FC1 up), same layout, or null
   long long strideB;       // elements between experts
@@ -81,6 +82,7 @@ template <typename TIn, typename TOut>
 struct TileJob {
   const TIn* A;
   long long lda;
+  const int32_t* gather;   // routed rows read from A row gather[m], or null
   int rows;
   const TIn* B0;
   const TIn* B1;
@@ -167,7 +169,13 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, TileJob<TIn, TOut
     j.lda = a.lda;
     j.ldc = a.ldc;
     j.ldgu = a.ldgu;
-    j.A = static_cast<const TIn*>(a.A) + (long long)row0 * a.lda;
+    if (a.gather) {
+      j.A = static_cast<const TIn*>(a.A);
+      j.gather = a.gather + row0;
+    } else {
+      j.A = static_cast<const TIn*>(a.A) + (long long)row0 * a.lda;
+      j.gather = nullptr;
+    }
     j.B0 = static_cast<const TIn*>(a.B0) + (long long)g * a.strideB;
     j.B1 = a.B1 ? static_cast<const TIn*>(a.B1) + (long long)g * a.strideB : nullptr;
     j.C = static_cast<TOut*>(a.C) + (long long)row0 * a.ldc;
@@ -185,6 +193,7 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, TileJob<TIn, TOut
   j.N = a.Nd;
   j.K = a.Kd;
   j.lda = a.ldad;
+  j.gather = nullptr;
   j.ldc = a.ldcd;
   j.A = static_cast<const TIn*>(a.Ad);
   j.B0 = static_cast<const TIn*>(a.Bd0);
@@ -348,6 +357,8 @@ gemm_bf16_mfma_kernel(const GemmArgs args) {
     }
     int r = rbase + (lane >> 2);
     r = r < rlimit ? r : rlimit - 1;                    // clamp: never stored
+    // fused permutation: a routed row comes straight from its token's row
+    if (row < bmc && job.gather) r = job.gather[r];
     g_off[j] = (uint32_t)(r * ld + dma_c * 8) * 2u;
     g_base[j] = uniform_ptr(src);
   }
@@ -662,7 +673,12 @@ gemm_generic_kernel(const GemmArgs args) {
       const int e = tid + 256 * i;
       const int r = e / BK, kk = e % BK;
       const int m = job.m0 + r, k = k0 + kk;
-      sA[kk][r] = (m < job.rows && k < job.K) ? to_f32<T>(job.A[(long long)m * job.lda + k]) : 0.0f;
+      float v = 0.0f;
+      if (m < job.rows && k < job.K) {
+        const long long src = job.gather ? job.gather[m] : m;
+        v = to_f32<T>(job.A[src * job.lda + k]);
+      }
+      sA[kk][r] = v;
     }
 #pragma unroll
     for (int b = 0; b < NB; ++b)

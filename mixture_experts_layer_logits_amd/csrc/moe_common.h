@@ -69,7 +69,8 @@ struct FfnWs {
 };
 bool ffn_uses_mfma(const moe_shape& s);
 int ffn_fc2_ksplit(const moe_shape& s);
-hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const int32_t* offsets,
+hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const int32_t* row_token,
+                              const int32_t* offsets,
                               const void* w_gate, const void* w_up, const void* w_down,
                               const void* x, const void* ws_gate, const void* ws_up,
                               const void* ws_down, void* y_perm, void* y_shared,

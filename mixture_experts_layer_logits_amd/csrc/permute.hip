@@ -20,7 +20,9 @@
 //              entries) each maps block does step 2 itself from the whole
 //              table, which saves the scan launch;
 //   4. rows:   one workgroup per token copies x[t] once from HBM into its k
-//              destination rows (full-row, 16-byte coalesced stores).
+//              destination rows (full-row, 16-byte coalesced stores).  Without
+//              an x_perm buffer this step is skipped: the grouped FFN can read
+//              each row from x through row_token instead.
 #include "gemm_tiles.h"
 
 namespace moe {
@@ -214,6 +216,7 @@ hipError_t launch_permute(const moe_shape& s, const void* x, const int32_t* topk
                                                ws.blk_base, fused ? ws.blk_cnt : nullptr,
                                                offsets, row_token, token_row, row_gate);
     const long long row_bytes = (long long)s.d * (s.dtype == MOE_DTYPE_BF16 ? 2 : 4);
+    if (!x_perm) return hipGetLastError();   // maps only (FC1 gathers the rows)
     if (row_bytes % 16 == 0)
       permute_rows_kernel<true><<<s.T, 256, 0, st>>>(static_cast<const uint8_t*>(x), token_row,
                                                      s.k, row_bytes,

@@ -50,17 +50,22 @@ class MoELayer:
                          inp.get("score_bias"), b["topk_idx"], b["topk_w"],
                          self.ws, self.ws_bytes, stream)
 
-    def permute(self, inp, stream=None):
+    def permute(self, inp, stream=None, maps_only=False):
         b = self.buf
-        L.moe_permute(self.shape, inp["x"], b["topk_idx"], b["topk_w"],
-                      b["expert_offsets"], b["row_token"], b["token_row"],
-                      b["row_gate"], b["x_perm"], self.ws, self.ws_bytes, stream)
+        L.moe_permute(self.shape, None if maps_only else inp["x"], b["topk_idx"],
+                      b["topk_w"], b["expert_offsets"], b["row_token"],
+                      b["token_row"], b["row_gate"],
+                      None if maps_only else b["x_perm"], self.ws, self.ws_bytes,
+                      stream)
 
-    def ffn(self, inp, stream=None):
+    def ffn(self, inp, stream=None, fused=False):
+        """fused: FC1 gathers its rows from x through row_token (after a
+        maps-only permute) instead of reading x_perm."""
         b = self.buf
-        L.moe_grouped_ffn(self.shape, b["x_perm"], b["expert_offsets"],
+        L.moe_grouped_ffn(self.shape, None if fused else b["x_perm"],
+                          b["row_token"], b["expert_offsets"],
                           inp["w_gate"], inp["w_up"], inp["w_down"],
-                          inp["x"] if self.cfg.F_shared > 0 else None,
+                          inp["x"] if (fused or self.cfg.F_shared > 0) else None,
                           inp.get("ws_gate"), inp.get("ws_up"),
                           inp.get("ws_down"), b["y_perm"], b["y_shared"],
                           b["gu_save"], self.ws, self.ws_bytes, stream)
@@ -71,10 +76,15 @@ class MoELayer:
                                 b["topk_w"], b["y_shared"], b["y"], self.ws,
                                 self.ws_bytes, stream)
 
-    def forward(self, inp, stream=None):
+    def forward(self, inp, stream=None, fused=False):
+        """fused=True skips x_perm: the permutation only builds the maps and
+        FC1 gathers its rows from x (not for training, whose backward reads
+        x_perm)."""
+        if fused and self.save_gu:
+            raise ValueError("the fused forward keeps no x_perm for the backward")
         self.route(inp, stream)
-        self.permute(inp, stream)
-        self.ffn(inp, stream)
+        self.permute(inp, stream, maps_only=fused)
+        self.ffn(inp, stream, fused=fused)
         self.combine(inp, stream)
         return self.buf
 

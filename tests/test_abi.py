@@ -93,8 +93,16 @@ def test_calls_reject_null_misaligned_and_small_workspace():
     st = M.moe_permute(s, p, p, p, p, p, p, p, p, None, 0, check=False, stream=0)
     assert st == L.MOE_ERR_WORKSPACE
     need = M.moe_workspace_size(s, L.MOE_OP_FFN)
-    st = M.moe_grouped_ffn(s, p, p, p, p, p, None, None, None, None, p, None, None,
+    st = M.moe_grouped_ffn(s, p, None, p, p, p, p, None, None, None, None, p, None, None,
                            p, need - 1, check=False, stream=0)
+    assert st == L.MOE_ERR_WORKSPACE
+    # gathering rows (x_perm NULL) needs x and row_token
+    for x, rt in ((None, p), (p, None)):
+        st = M.moe_grouped_ffn(s, None, rt, p, p, p, p, x, None, None, None, p, None, None,
+                               p, need, check=False, stream=0)
+        assert st == L.MOE_ERR_INVALID_ARG
+    # a maps-only permute needs no x
+    st = M.moe_permute(s, None, p, p, p, p, p, p, None, None, 0, check=False, stream=0)
     assert st == L.MOE_ERR_WORKSPACE
     st = M.moe_unpermute_combine(s, p, p, p, None, None, check=False, stream=0)
     assert st == L.MOE_ERR_INVALID_ARG

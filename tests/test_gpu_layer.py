@@ -90,6 +90,21 @@ def test_layer_small(name):
     assert_close("y", out["y"][ok.cuda()], ref["y"][ok.numpy()], prec)
 
 
+@pytest.mark.parametrize("name", ["bf16_sigmoid_groups_shared_t200", "bf16_skewed_t520",
+                                  "f32_odd_t37"])
+def test_layer_fused_forward_matches_unfused(name):
+    """The fused forward (maps-only permute, FC1 gathering rows from x) gives
+    bitwise the same y_perm and y as the path through x_perm."""
+    cfg = SMALL[name]
+    print(f"[layer fused] {name}", flush=True)
+    inp, layer, out = _run(cfg)
+    y_perm, y = out["y_perm"].clone(), out["y"].clone()
+    layer.forward(inp, fused=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out["y_perm"], y_perm)
+    assert torch.equal(out["y"], y)
+
+
 def test_layer_is_bitwise_deterministic():
     cfg = SMALL["bf16_sigmoid_groups_shared_t200"].replace(T=1000)
     inp, layer, out = _run(cfg)

@@ -176,6 +176,46 @@ FFN_CASES = [
 ]
 
 
+GATHER_CASES = [
+    # name, T, d, E, k, F, Fs, dtype: FC1 reads x[row_token[r]] (x_perm NULL)
+    ("mfma_gather_t500", 500, 256, 8, 4, 384, 0, 1),
+    ("mfma_gather_shared_t300", 300, 128, 16, 2, 128, 64, 1),
+    ("generic_gather_t77", 77, 200, 6, 2, 96, 40, 1),
+    ("fp32_gather_t50", 50, 24, 5, 3, 16, 0, 0),
+]
+
+
+@pytest.mark.parametrize("case", GATHER_CASES, ids=[c[0] for c in GATHER_CASES])
+def test_grouped_ffn_gathered_rows(case):
+    """The permutation fused into FC1's operand load: rows come from
+    x[row_token[r]]; the result must equal the FFN of the gathered rows."""
+    name, T, d, E, k, F, Fs, dtype = case
+    _log(f"[ffn gather] {name}")
+    M = _lib()
+    cfg = MoEConfig(name, T=T, d=d, E=E, k=k, F=F, F_shared=Fs, dtype=dtype)
+    prec = prec_of(cfg)
+    idx = random_topk(T, E, k, seed=T + 3)
+    p = O.permute(None, idx.numpy(), np.ones((T, k)), E)
+    inp = make_inputs(cfg, device="cuda")
+    dt = cfg.torch_dtype
+    yp = torch.empty(cfg.R, d, dtype=dt, device="cuda")
+    ys = torch.empty(T, d, dtype=dt, device="cuda") if Fs else None
+    shape = M.make_shape(cfg)
+    ws, n = _ws(M, shape, 2)
+    rt = torch.as_tensor(p["row_token"]).cuda()
+    M.moe_grouped_ffn(shape, None, rt, torch.as_tensor(p["offsets"]).cuda(), inp["w_gate"],
+                      inp["w_up"], inp["w_down"], inp["x"], inp["ws_gate"], inp["ws_up"],
+                      inp["ws_down"], yp, ys, None, ws, n)
+    torch.cuda.synchronize()
+    xg = np64(inp["x"])[p["row_token"]]
+    ref_y, _ = O.grouped_ffn(xg, p["offsets"], np64(inp["w_gate"]), np64(inp["w_up"]),
+                             np64(inp["w_down"]), prec)
+    assert_close("y_perm", yp, ref_y, prec)
+    if Fs:
+        assert_close("y_shared", ys, O.shared_ffn(inp["x"], inp["ws_gate"], inp["ws_up"],
+                                                  inp["ws_down"], prec), prec)
+
+
 def _ffn_inputs(cfg, skew):
     if isinstance(skew, tuple):
         p = {"offsets": np.concatenate([[0], np.cumsum(skew)]).astype(np.int32)}
@@ -211,9 +251,9 @@ def test_grouped_ffn(case):
     gu = gu_all[:n_r].view(cfg.R, 2 * F)
     shape = M.make_shape(cfg)
     ws, n = _ws(M, shape, 2)
-    M.moe_grouped_ffn(shape, xp, torch.as_tensor(p["offsets"]).cuda(), inp["w_gate"], inp["w_up"],
-                      inp["w_down"], inp["x"] if Fs else None, inp["ws_gate"], inp["ws_up"],
-                      inp["ws_down"], yp, ys, gu_all, ws, n)
+    M.moe_grouped_ffn(shape, xp, None, torch.as_tensor(p["offsets"]).cuda(), inp["w_gate"],
+                      inp["w_up"], inp["w_down"], inp["x"] if Fs else None, inp["ws_gate"],
+                      inp["ws_up"], inp["ws_down"], yp, ys, gu_all, ws, n)
     torch.cuda.synchronize()
     ref_y, ref_gu = O.grouped_ffn(xp, p["offsets"], np64(inp["w_gate"]), np64(inp["w_up"]),
                                   np64(inp["w_down"]), prec, save_gu=True)

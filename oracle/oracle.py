@@ -287,6 +287,87 @@ def shared_ffn(x, ws_gate, ws_up, ws_down, prec="bf16"):
 
 
 # --------------------------------------------------------------------------
+# MXFP8 (Primus blog, low-precision section: MXFP8 block scaling with E4M3
+# elements, blocks of 32 and an E8M0 scale per block)
+# --------------------------------------------------------------------------
+E4M3_MAX = 448.0          # largest finite E4M3 value, 1.75 * 2^8
+E4M3_EMAX = 8             # exponent of the largest power of two in E4M3
+MX_BLOCK = 32
+
+
+def e4m3_round(v):
+    """Nearest E4M3 value (ties to even), saturating at +-448.
+
+    E4M3: 1 sign, 4 exponent bits (bias 7), 3 mantissa bits; normal numbers
+    from 2^-6, subnormals in steps of 2^-9.  A value's quantum is 2^(e-3)
+    with e = max(floor(log2|v|), -6); rounding to that grid with ties to even
+    is np.rint on v / quantum."""
+    v = as64(v)
+    a = np.abs(v)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6.0)
+    q = np.exp2(e - 3.0)
+    r = np.rint(a / q) * q
+    return np.sign(v) * np.minimum(r, E4M3_MAX)
+
+
+def mx_quantize(a, block=MX_BLOCK):
+    """MX quantization along the last axis in blocks of `block` values.
+
+    Per block the scale is 2^s with s = floor(log2(amax)) - 8 (the largest
+    power of two of E4M3), amax the block's largest magnitude (s = -127, the
+    smallest E8M0 scale, for an all-zero block); elements are
+    e4m3_round(v / 2^s).  Returns (elements, s) with a ~ elements * 2^s."""
+    a = as64(a)
+    n = a.shape[-1]
+    assert n % block == 0
+    blk = a.reshape(*a.shape[:-1], n // block, block)
+    amax = np.abs(blk).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        s = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - E4M3_EMAX, -127.0)
+    s = np.clip(s, -127.0, 127.0)
+    q = e4m3_round(blk / np.exp2(s)[..., None])
+    return q.reshape(a.shape), s
+
+
+def mx_dequantize(q, s, block=MX_BLOCK):
+    q = as64(q)
+    n = q.shape[-1]
+    blk = q.reshape(*q.shape[:-1], n // block, block)
+    return (blk * np.exp2(as64(s))[..., None]).reshape(q.shape)
+
+
+def mx_round(a, block=MX_BLOCK):
+    """a quantized to MXFP8 and back (the values an MXFP8 GEMM consumes)."""
+    q, s = mx_quantize(a, block)
+    return mx_dequantize(q, s, block)
+
+
+def swiglu_ffn_mxfp8(rows, wg, wu, wd):
+    """One expert with MXFP8 operands: the rows and the three weights are
+    quantized along their contraction dimension (d for FC1, F for FC2), and
+    h = silu(g) * u is quantized along F before FC2; products and sums are
+    exact (fp64) on the dequantized values, y is rounded to bf16."""
+    x = mx_round(rows)
+    g = x @ mx_round(wg).T
+    u = x @ mx_round(wu).T
+    h = mx_round(silu(g) * u)
+    return dict(g=g, u=u, h=h, y=round_bf16(h @ mx_round(wd).T))
+
+
+def grouped_ffn_mxfp8(x_perm, offsets, w_gate, w_up, w_down):
+    """grouped_ffn with MXFP8 operands (swiglu_ffn_mxfp8 per expert)."""
+    x_perm = as64(x_perm)
+    y = np.zeros((x_perm.shape[0], as64(w_down[0]).shape[0]), dtype=F64)
+    for e in range(len(offsets) - 1):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b > a:
+            y[a:b] = swiglu_ffn_mxfp8(x_perm[a:b], w_gate[e], w_up[e], w_down[e])["y"]
+    return y
+
+
+# --------------------------------------------------------------------------
 # unpermute-and-scale
 # --------------------------------------------------------------------------
 def combine(y_perm, token_row, topk_w, y_shared=None, prec="f32"):

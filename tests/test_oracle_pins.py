@@ -454,3 +454,69 @@ def test_inputs_are_seeded_and_shaped():
     # Zipf offsets: -1.2 ln(rank) over a permutation of the ranks 1..E
     ranks = np.exp(-rb / 1.2)
     assert np.allclose(np.sort(ranks), np.arange(1, 129), rtol=1e-5)
+
+
+# --------------------------------------------------------------------------
+# MXFP8: E4M3 rounding and the block scale
+# --------------------------------------------------------------------------
+def test_e4m3_round_matches_torch_float8_e4m3fn():
+    """torch's float32 -> float8_e4m3fn conversion (round to nearest even) is
+    an independent implementation of the same rounding for |v| <= 448."""
+    rng = np.random.default_rng(21)
+    mag = np.exp2(rng.uniform(-12, np.log2(448.0), 20000))
+    v = (mag * rng.choice([-1.0, 1.0], mag.size)).astype(np.float32)
+    # exact halfway points between neighbouring E4M3 values
+    codes = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    finite = np.unique(codes[np.isfinite(codes)])
+    mids = ((finite[:-1] + finite[1:]) / 2).astype(np.float32)
+    v = np.concatenate([v, mids, -mids])
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).float().numpy()
+    ok = np.isfinite(ref)
+    assert ok.all()
+    assert np.array_equal(O.e4m3_round(v), ref.astype(np.float64))
+
+
+def test_e4m3_round_is_identity_on_every_code_and_saturates():
+    codes = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    finite = codes[np.isfinite(codes)].astype(np.float64)
+    assert finite.size == 254                       # two NaN codes, no infinities
+    assert np.array_equal(O.e4m3_round(finite), finite)
+    assert finite.max() == 448.0 and np.min(finite[finite > 0]) == 2.0 ** -9
+    assert np.array_equal(O.e4m3_round(np.array([449.0, 1e6, -1e6])), [448.0, 448.0, -448.0])
+
+
+def test_mx_block_scale_rule():
+    # amax 1 -> scale 2^(0 - 8); the element 1 becomes 256 exactly
+    q, s = O.mx_quantize(np.r_[1.0, np.zeros(31)])
+    assert s.tolist() == [-8.0] and q[0] == 256.0
+    # amax 448 * 2^10 -> scale 2^(18 - 8) = 2^10, element 448 exactly; 3 / 2^10
+    # is 1.5 subnormal quanta (2^-9) and rounds to the even neighbour, 2^-8
+    q, s = O.mx_quantize(np.r_[448.0 * 2 ** 10, 3.0, np.zeros(30)])
+    assert s.tolist() == [10.0] and q[0] == 448.0 and q[1] == 2.0 ** -8
+    # a value just below the next power of two keeps the lower exponent
+    q, s = O.mx_quantize(np.r_[1.99, np.zeros(31)])
+    assert s.tolist() == [-8.0] and q[0] == 448.0   # 1.99 * 256 = 509 saturates
+    # an all-zero block: smallest E8M0 scale, zero elements
+    q, s = O.mx_quantize(np.zeros(32))
+    assert s.tolist() == [-127.0] and not q.any()
+    # blocks are independent and run along the last axis
+    a = np.stack([np.r_[np.ones(32), 4 * np.ones(32)], np.r_[0.5 * np.ones(32), np.ones(32)]])
+    _, s = O.mx_quantize(a)
+    assert s.tolist() == [[-8.0, -6.0], [-9.0, -8.0]]
+
+
+def test_mx_round_is_idempotent_and_bounded():
+    rng = np.random.default_rng(22)
+    a = rng.standard_normal((8, 256)) * np.exp2(rng.integers(-10, 10, (8, 1)))
+    r = O.mx_round(a)
+    assert np.array_equal(O.mx_round(r), r)
+    # With the scale 2^(floor(log2 amax) - 8) a block's largest elements land
+    # in [256, 512) * 2^s; those at or above 448 * 2^s saturate to exactly
+    # +-448 * 2^s, every other element not below the smallest normal is
+    # within half an E4M3 quantum (relative 2^-4).
+    _, s = O.mx_quantize(a)
+    scale = np.repeat(np.exp2(s), 32, axis=1)
+    sat = np.abs(a) >= 448.0 * scale
+    assert np.array_equal(np.abs(r[sat]), 448.0 * scale[sat])
+    normal = ~sat & (np.abs(a) >= 2.0 ** -6 * scale)
+    assert np.all(np.abs(r - a)[normal] <= np.abs(a)[normal] * 2.0 ** -4)

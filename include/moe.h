@@ -73,7 +73,8 @@ enum {
   MOE_OP_PERMUTE = 1,
   MOE_OP_FFN = 2,
   MOE_OP_COMBINE = 3,
-  MOE_OP_BACKWARD = 4
+  MOE_OP_BACKWARD = 4,
+  MOE_OP_FFN_MXFP8 = 5
 };
 
 /* The layer's parameters: tokens T, hidden d, routed experts E, experts per
@@ -232,6 +233,56 @@ int moe_ffn_backward(const moe_shape* shape, const void* dy, const void* x_perm,
                      float* dw_down, float* dws_gate, float* dws_up, float* dws_down,
                      float* d_gate, float* d_logits, void* ws, size_t ws_bytes,
                      void* stream);
+
+/* MXFP8 block quantisation (Primus blog, low-precision section: MXFP8
+ * expert GEMMs on gfx950 with the OCP E4M3 element format, one E8M0
+ * power-of-two scale per block of 32 values).  Each row of the bf16 matrix
+ * src [rows, cols] (cols a multiple of 32) is cut into blocks of 32
+ * consecutive values; block b with largest magnitude amax gets the scale
+ * 2^s, s = floor(log2 amax) - 8 (8 being the exponent of E4M3's largest
+ * power of two), clipped to [-127, 127], and s = -127 when amax is 0; its
+ * values become the E4M3 codes nearest v / 2^s (ties to even, saturating at
+ * +-448).
+ *  q [rows, cols] uint8 out: E4M3 codes (1 sign, 4 exponent bits with bias
+ *      7, 3 mantissa bits; 0x7f/0xff never written).
+ *  scales [rows, cols / 32] uint8 out: the E8M0 byte s + 127.
+ * Used for the activations each step and once for the weights, whose codes
+ * the caller keeps (quantised-weight caching).  rows >= 0; NaN/Inf inputs
+ * give unspecified codes.  No workspace. */
+int moe_mx_quantize(const void* src, int64_t rows, int32_t cols, uint8_t* q,
+                    uint8_t* scales, void* stream);
+
+/* moe_grouped_ffn with MXFP8 operands on the scaled MFMA (Primus blog,
+ * low-precision section), routed rows gathered from the quantised x.
+ *  xq [T, d], xs [T, d / 32]: x quantised by moe_mx_quantize.  Routed row r
+ *      reads token row_token[r] (row_token [R], expert_offsets [E+1] as from
+ *      moe_permute; since quantisation is row-wise this equals quantising
+ *      x_perm).
+ *  w_gate_q, w_up_q [E, F, d] with scales [E, F, d / 32]; w_down_q [E, d, F]
+ *      with scales [E, d, F / 32]: the weights quantised along their
+ *      contraction dimension (moe_mx_quantize with cols = d, resp. F).
+ *  ws_*_q, ws_*_s: the shared expert's weights likewise ([Fs, d], [d, Fs]),
+ *      read only when F_shared > 0 (may be NULL otherwise).
+ *  y_perm [R, d] bf16 out: per expert, g = xq . w_gate^T and u = xq . w_up^T
+ *      on the dequantised values with fp32 accumulation; h = silu(g) * u is
+ *      quantised to MXFP8 along F (blocks of 32 columns, the rule above)
+ *      and y = hq . w_down^T, fp32 accumulate, rounded to bf16.
+ *  y_shared [T, d] bf16 out (F_shared > 0, else ignored): the same for the
+ *      shared expert over all T tokens.
+ * shape.dtype must be MOE_DTYPE_BF16.  d, F and F_shared must be multiples
+ * of 128 (else MOE_ERR_UNSUPPORTED).  Forward only: no g | u is saved.
+ *  ws: MOE_OP_FFN_MXFP8 bytes (holds the quantised h). */
+int moe_grouped_ffn_mxfp8(const moe_shape* shape, const uint8_t* xq,
+                          const uint8_t* xs, const int32_t* row_token,
+                          const int32_t* expert_offsets,
+                          const uint8_t* w_gate_q, const uint8_t* w_gate_s,
+                          const uint8_t* w_up_q, const uint8_t* w_up_s,
+                          const uint8_t* w_down_q, const uint8_t* w_down_s,
+                          const uint8_t* ws_gate_q, const uint8_t* ws_gate_s,
+                          const uint8_t* ws_up_q, const uint8_t* ws_up_s,
+                          const uint8_t* ws_down_q, const uint8_t* ws_down_s,
+                          void* y_perm, void* y_shared, void* ws,
+                          size_t ws_bytes, void* stream);
 
 /* Static text for a moe_status value (never NULL). */
 const char* moe_status_string(int status);

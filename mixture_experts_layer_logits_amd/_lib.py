@@ -27,11 +27,12 @@ MOE_DTYPE_F32 = 0
 MOE_DTYPE_BF16 = 1
 MOE_SCORE_SOFTMAX = 0
 MOE_SCORE_SIGMOID = 1
-MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN, MOE_OP_COMBINE, MOE_OP_BACKWARD = range(5)
+(MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN, MOE_OP_COMBINE, MOE_OP_BACKWARD,
+ MOE_OP_FFN_MXFP8) = range(6)
 
 EXPORTED = ("moe_workspace_size", "moe_route_topk", "moe_permute",
             "moe_grouped_ffn", "moe_unpermute_combine", "moe_ffn_backward",
-            "moe_status_string")
+            "moe_status_string", "moe_mx_quantize", "moe_grouped_ffn_mxfp8")
 
 
 class MoeShape(ctypes.Structure):
@@ -67,6 +68,8 @@ def load() -> ctypes.CDLL:
     lib.moe_grouped_ffn.argtypes = [sp] + [vp] * 13 + [vp, sz, vp]
     lib.moe_unpermute_combine.argtypes = [sp] + [vp] * 5 + [vp, sz, vp]
     lib.moe_ffn_backward.argtypes = [sp] + [vp] * 26 + [vp, sz, vp]
+    lib.moe_mx_quantize.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
+    lib.moe_grouped_ffn_mxfp8.argtypes = [sp] + [vp] * 18 + [vp, sz, vp]
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
     for name in EXPORTED:
@@ -168,3 +171,23 @@ def moe_ffn_backward(shape, dy, x_perm, gu_save, y_perm, expert_offsets,
         _p(dw_down), _p(dws_gate), _p(dws_up), _p(dws_down), _p(d_gate),
         _p(d_logits), _p(ws), ws_bytes, _stream(stream))
     return _check(st, "moe_ffn_backward") if check else st
+
+
+def moe_mx_quantize(src, rows, cols, q, scales, stream=None, check=True):
+    st = load().moe_mx_quantize(_p(src), int(rows), int(cols), _p(q), _p(scales),
+                                _stream(stream))
+    return _check(st, "moe_mx_quantize") if check else st
+
+
+def moe_grouped_ffn_mxfp8(shape, xq, xs, row_token, expert_offsets, w_gate_q,
+                          w_gate_s, w_up_q, w_up_s, w_down_q, w_down_s,
+                          ws_gate_q, ws_gate_s, ws_up_q, ws_up_s, ws_down_q,
+                          ws_down_s, y_perm, y_shared, ws=None, ws_bytes=0,
+                          stream=None, check=True):
+    st = load().moe_grouped_ffn_mxfp8(
+        ctypes.byref(shape), _p(xq), _p(xs), _p(row_token), _p(expert_offsets),
+        _p(w_gate_q), _p(w_gate_s), _p(w_up_q), _p(w_up_s), _p(w_down_q),
+        _p(w_down_s), _p(ws_gate_q), _p(ws_gate_s), _p(ws_up_q), _p(ws_up_s),
+        _p(ws_down_q), _p(ws_down_s), _p(y_perm), _p(y_shared), _p(ws),
+        ws_bytes, _stream(stream))
+    return _check(st, "moe_grouped_ffn_mxfp8") if check else st

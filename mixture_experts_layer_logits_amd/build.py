@@ -17,7 +17,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "route.hip", "permute.hip", "ffn.hip", "combine.hip",
-           "backward.hip"]
+           "backward.hip", "mxfp8.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

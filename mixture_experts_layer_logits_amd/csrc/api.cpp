@@ -69,6 +69,9 @@ size_t ws_bytes_for(const moe_shape& s, int op) {
       }
       return b;
     }
+    case MOE_OP_FFN_MXFP8:
+      return 2 * align_up((s.E + 1) * 4) + align_up(R * s.F) + align_up(R * s.F / 32) +
+             align_up((size_t)s.T * s.F_shared) + align_up((size_t)s.T * s.F_shared / 32);
     default:
       return 0;
   }
@@ -101,7 +104,7 @@ extern "C" {
 int moe_workspace_size(const moe_shape* shape, int op, size_t* bytes) {
   const int st = check_shape(shape);
   if (st != MOE_OK) return st;
-  if (!bytes || op < MOE_OP_ROUTE || op > MOE_OP_BACKWARD) return MOE_ERR_INVALID_ARG;
+  if (!bytes || op < MOE_OP_ROUTE || op > MOE_OP_FFN_MXFP8) return MOE_ERR_INVALID_ARG;
   *bytes = ws_bytes_for(*shape, op);
   return MOE_OK;
 }
@@ -293,6 +296,61 @@ int moe_ffn_backward(const moe_shape* shape, const void* dy, const void* x_perm,
                                          dw_gate, dw_up, dw_down, dws_gate, dws_up, dws_down,
                                          d_gate, d_logits, bw,
                                          static_cast<hipStream_t>(stream)));
+}
+
+int moe_mx_quantize(const void* src, int64_t rows, int32_t cols, uint8_t* q, uint8_t* scales,
+                    void* stream) {
+  if (rows < 0 || cols < 32 || cols % 32 != 0) return MOE_ERR_INVALID_ARG;
+  if ((long long)rows * cols >= (1LL << 40)) return MOE_ERR_INVALID_ARG;
+  const long long n = (long long)rows * cols;
+  if (!ok_buf(src, n * 2) || !ok_buf(q, n) || !ok_buf(scales, n / 32)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_mx_quantize(src, rows, cols, q, scales,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int moe_grouped_ffn_mxfp8(const moe_shape* shape, const uint8_t* xq, const uint8_t* xs,
+                          const int32_t* row_token, const int32_t* expert_offsets,
+                          const uint8_t* w_gate_q, const uint8_t* w_gate_s,
+                          const uint8_t* w_up_q, const uint8_t* w_up_s,
+                          const uint8_t* w_down_q, const uint8_t* w_down_s,
+                          const uint8_t* ws_gate_q, const uint8_t* ws_gate_s,
+                          const uint8_t* ws_up_q, const uint8_t* ws_up_s,
+                          const uint8_t* ws_down_q, const uint8_t* ws_down_s, void* y_perm,
+                          void* y_shared, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape& s = *shape;
+  if (s.dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;   // y is bf16
+  if (s.d % 128 != 0 || s.F % 128 != 0 || s.F_shared % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  const long long R = (long long)s.T * s.k;
+  const long long xn = (long long)s.T * s.d;
+  const long long wn = (long long)s.E * s.F * s.d;
+  if (!ok_buf(xq, xn) || !ok_buf(xs, xn / 32) || !ok_buf(row_token, R * 4) ||
+      !ok_buf(expert_offsets, (long long)(s.E + 1) * 4) || !ok_buf(w_gate_q, wn) ||
+      !ok_buf(w_gate_s, wn / 32) || !ok_buf(w_up_q, wn) || !ok_buf(w_up_s, wn / 32) ||
+      !ok_buf(w_down_q, wn) || !ok_buf(w_down_s, wn / 32) || !ok_buf(y_perm, R * s.d * 2))
+    return MOE_ERR_INVALID_ARG;
+  if (s.F_shared > 0) {
+    const long long sn = (long long)s.F_shared * s.d;
+    if (!ok_buf(ws_gate_q, sn) || !ok_buf(ws_gate_s, sn / 32) || !ok_buf(ws_up_q, sn) ||
+        !ok_buf(ws_up_s, sn / 32) || !ok_buf(ws_down_q, sn) || !ok_buf(ws_down_s, sn / 32) ||
+        !ok_buf(y_shared, xn * 2))
+      return MOE_ERR_INVALID_ARG;
+  }
+  if ((st = check_ws(s, MOE_OP_FFN_MXFP8, ws, ws_bytes)) != MOE_OK) return st;
+  Carver c{static_cast<char*>(ws)};
+  moe::MxFfnWs fw;
+  fw.tiles1 = c.take<int32_t>((s.E + 1) * 4);
+  fw.tiles2 = c.take<int32_t>((s.E + 1) * 4);
+  fw.hq = c.take<uint8_t>((size_t)R * s.F);
+  fw.hs = c.take<uint8_t>((size_t)R * s.F / 32);
+  fw.shq = c.take<uint8_t>((size_t)s.T * s.F_shared);
+  fw.shs = c.take<uint8_t>((size_t)s.T * s.F_shared / 32);
+  const moe::MxWeights w = {w_gate_q, w_gate_s, w_up_q, w_up_s, w_down_q, w_down_s,
+                            ws_gate_q, ws_gate_s, ws_up_q, ws_up_s, ws_down_q, ws_down_s};
+  return hip_status(moe::launch_grouped_ffn_mxfp8(s, xq, xs, row_token, expert_offsets, w,
+                                                  y_perm, y_shared, fw,
+                                                  static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -95,6 +95,7 @@ struct TileJob {
   int k0, klen;            // K range of this work item (split-K slice)
   float* P;                // split-K partial rows of the group, or null
   int cls;                 // 0: BM x BN tile, 1: BM/2 x 2BN tail tile
+  int dense;               // 1: the dense group, 0: a routed group
 };
 
 // Tiles of one routed group of `rows` rows with NT = ceil(N / BN) column tiles.
@@ -141,6 +142,7 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, TileJob<TIn, TOut
       if (a.tiles[mid] <= lid) lo = mid; else hi = mid - 1;
     }
     const int g = lo;
+    j.dense = 0;
     const int row0 = a.offsets[g];
     const int rows = a.offsets[g + 1] - row0;
     // Column tiles go in pairs: the full tiles of columns 2p and 2p+1 (row
@@ -187,6 +189,7 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, TileJob<TIn, TOut
   }
   const int r = lid - routed;
   j.cls = 0;
+  j.dense = 1;
   j.m0 = (r % dmt) * BM;
   j.n0 = (r / dmt) * BN;
   j.rows = a.Td;

@@ -76,6 +76,26 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const int3
                               const void* ws_down, void* y_perm, void* y_shared,
                               void* gu_save, const FfnWs& ws, hipStream_t st);
 
+// MXFP8 (E4M3 codes with one E8M0 scale byte per 32 values along a row).
+hipError_t launch_mx_quantize(const void* src, long long rows, int cols, uint8_t* q,
+                              uint8_t* scales, hipStream_t st);
+struct MxWeights {      // codes and scales of each weight matrix
+  const uint8_t *gate_q, *gate_s, *up_q, *up_s, *down_q, *down_s;
+  const uint8_t *sgate_q, *sgate_s, *sup_q, *sup_s, *sdown_q, *sdown_s;  // shared expert
+};
+struct MxFfnWs {
+  int32_t* tiles1;  // [E + 1] tile prefix of FC1
+  int32_t* tiles2;  // [E + 1] tile prefix of FC2
+  uint8_t* hq;      // [R, F] E4M3 codes of h
+  uint8_t* hs;      // [R, F / 32] scales of h
+  uint8_t* shq;     // [T, Fs] the shared expert's h
+  uint8_t* shs;     // [T, Fs / 32]
+};
+hipError_t launch_grouped_ffn_mxfp8(const moe_shape& s, const uint8_t* xq, const uint8_t* xs,
+                                    const int32_t* row_token, const int32_t* offsets,
+                                    const MxWeights& w, void* y_perm, void* y_shared,
+                                    const MxFfnWs& ws, hipStream_t st);
+
 hipError_t launch_combine(const moe_shape& s, const void* y_perm, const int32_t* token_row,
                           const float* topk_w, const void* y_shared, float* y,
                           hipStream_t st);

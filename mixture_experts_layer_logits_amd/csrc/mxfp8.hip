@@ -1,0 +1,592 @@
+// MXFP8 grouped expert FFN (Primus blog, low-precision section: MXFP8 block
+// scaling, E4M3 elements in blocks of 32 along the contraction dimension with
+// one E8M0 power-of-two scale per block, on gfx950's scaled MFMA).
+//
+//   quantize:  bf16 [rows, cols] -> E4M3 codes [rows, cols] + E8M0 bytes
+//              [rows, cols / 32].  Block scale 2^s, s = floor(log2 amax) - 8
+//              (8 = exponent of E4M3's largest power of two), clipped to
+//              [-127, 127]; an all-zero block gets s = -127.  Elements are
+//              v / 2^s rounded to E4M3, nearest-even, saturating at +-448.
+//   FC1:       h = silu(xq . wg^T) * (xq . wu^T) on the dequantised operands
+//              (fp32 accumulate), quantised to MXFP8 along F in the epilogue
+//   FC2:       y_perm = hq . wd^T -> bf16
+//
+// Both GEMMs read routed rows through row_token from the quantised x (the
+// permutation fused into FC1's operand load; quantising is row-wise, so
+// quantise-then-gather equals gather-then-quantise exactly).
+//
+// Scaled MFMA operand layout (v_mfma_scale_f32_32x32x64_f8f6f4, fp8 e4m3 on
+// both sides): lane l holds row l % 32 of its operand and 32 values of K,
+// bytes 0-15 at k = 16 (l / 32) + q and bytes 16-31 at k = 32 + 16 (l / 32) + q;
+// its scale operand (byte 0) applies to row l % 32 and K block l / 32 of the
+// 64-wide step.  Each 64-byte LDS row of a stage therefore feeds one MFMA per
+// fragment: chunks l / 32 and 2 + l / 32, the same two 16-byte chunks the
+// bf16 kernel reads in its two sub-steps.
+#include "gemm_tiles.h"
+
+namespace moe {
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// Half swap of a 64-byte LDS operand row.  It depends on row bits 2 and 3
+// only, so a 16-row load block (row = lane / 4 there) and a 32-row fragment
+// (row = lane % 32) both compute it from their local row index.
+__device__ __forceinline__ int mx_swz(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+
+// v, in a scalar register the compiler cannot see through.
+__device__ __forceinline__ uint32_t opaque_u32(uint32_t v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+
+// An empty use of an accumulator tile: its MFMAs must have run by here.
+__device__ __forceinline__ void use_acc(const f32x16_t& a) { asm volatile("" ::"v"(a)); }
+
+// FC1: 256 rows x (128 gate + 128 up) columns; FC2: 256 x 256; 8 waves.
+constexpr int MX_FC1_BM = 256, MX_FC1_BN = 128;
+constexpr int MX_FC2_BM = 256, MX_FC2_BN = 256;
+
+// ---------------------------------------------------------------------------
+// E4M3 / E8M0 encoding
+// ---------------------------------------------------------------------------
+
+// Scale exponent s of a block with largest magnitude amax (>= 0, finite):
+// floor(log2 amax) - 8 from amax's exponent field; zero and fp32-subnormal
+// amax (floor(log2) <= -127) give the smallest scale, -127.
+__device__ __forceinline__ int mx_scale_exp(float amax) {
+  const int e = (int)((__float_as_uint(amax) >> 23) & 255u);
+  const int s = e - 127 - 8;
+  return (e == 0 || s < -127) ? -127 : s;
+}
+
+// 2^-s for s in [-127, 119], exactly.
+__device__ __forceinline__ float mx_inv_scale(int s) {
+  return __uint_as_float((uint32_t)(127 - s) << 23);
+}
+
+// E4M3 code (1 sign, 4 exponent bits with bias 7, 3 mantissa bits) nearest
+// to y, ties to even, magnitudes that round past 448 saturating to 448.
+// Below 2^-6 the grid is the subnormal step 2^-9, whose integer multiples
+// 0..8 are exactly the codes 0..8.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fabsf(y);
+  uint32_t c;
+  if (!(a < 448.0f)) {
+    c = 0x7eu;
+  } else if (a < 0.015625f) {
+    c = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {
+    // keep 3 mantissa bits of the fp32 pattern, nearest-even; a carry moves
+    // into the exponent, which is the correct next binade
+    uint32_t b = __float_as_uint(a);
+    b += 0x7ffffu + ((b >> 20) & 1u);
+    c = (b >> 20) - (120u << 3);   // rebias the exponent from 127 to 7
+  }
+  return sign | c;
+}
+
+// ---------------------------------------------------------------------------
+// Quantisation: 4 lanes per block of 32 values, 8 values (16 bytes) per lane.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+mx_quantize_kernel(const bf16_t* __restrict__ src, long long n8, uint8_t* __restrict__ q,
+                   uint8_t* __restrict__ scales) {
+  // n8 is a multiple of 4 and so is the stride: the 4 lanes of a block are
+  // active together
+  for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n8; i += (long long)gridDim.x * 256) {
+    const uint4 raw = reinterpret_cast<const uint4*>(src)[i];
+    float v[8];
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      v[2 * p] = __uint_as_float(w[p] << 16);
+      v[2 * p + 1] = __uint_as_float(w[p] & 0xffff0000u);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) amax = fmaxf(amax, fabsf(v[p]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    const int s = mx_scale_exp(amax);
+    const float inv = mx_inv_scale(s);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      lo |= e4m3_code(v[p] * inv) << (8 * p);
+      hi |= e4m3_code(v[4 + p] * inv) << (8 * p);
+    }
+    reinterpret_cast<uint2*>(q)[i] = make_uint2(lo, hi);
+    if ((i & 3) == 0) scales[i >> 2] = (uint8_t)(s + 127);
+  }
+}
+
+hipError_t launch_mx_quantize(const void* src, long long rows, int cols, uint8_t* q,
+                              uint8_t* scales, hipStream_t st) {
+  const long long n8 = rows * (cols / 8);
+  if (n8 == 0) return hipSuccess;
+  const long long want = (n8 + 255) / 256;
+  const int grid = (int)(want < 8192 ? want : 8192);
+  mx_quantize_kernel<<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(src), n8, q, scales);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Scaled-MFMA grouped GEMM tile kernel.
+//
+// The tile machinery (groups, schedule, XCD-aware order) is the bf16
+// kernel's, with bytes for elements.  Operand rows of a stage are 64 fp8
+// values (one MFMA step), loaded straight into LDS with the same 16-byte
+// chunk swizzle.  Scales ride in the same slices: per stage, each operand
+// row's dword holding K blocks 4 (kt / 2) .. + 3 (row strides are K / 32
+// bytes, K a multiple of 128, so the dword is aligned) lands in a dword
+// array beside the stage, one global_load_lds_dword per 64 rows; a lane then
+// reads its block's byte, 2 (kt % 2) + l / 32, with one byte read.
+//
+// Each step is split in two halves over the B fragments: the first half's
+// MFMAs run while the second half's fragments are read; after the barrier
+// the second half's MFMAs run while the next stage's token fragments and
+// first-half weight fragments are read (token fragments double-buffered).
+// ---------------------------------------------------------------------------
+struct MxScales {
+  const uint8_t* A;    // routed rows' operand scales (rows of the quantised x)
+  const uint8_t* B0;   // [E][N][K / 32]
+  const uint8_t* B1;   // FC1 up, or null
+  uint8_t* C;          // FC1: h scales [R][F / 32]
+  const uint8_t* Ad;   // the dense group
+  const uint8_t* Bd0;
+  const uint8_t* Bd1;
+  uint8_t* Cd;
+};
+
+template <int BM, int BN, int NB, int EPI, int WM, int WN>
+__global__ void __launch_bounds__(64 * WM * WN)
+gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
+  constexpr int NW = WM * WN;
+  constexpr int BK = 64;                        // fp8 values (bytes) per row per stage
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int MI = WTM / 32, NJ = WTN / 32;
+  constexpr int NBJ = NB * NJ;                  // weight fragments per wave
+  constexpr int H0 = NBJ / 2, H1 = NBJ - H0;    // ... in each half-step
+  constexpr int ROWS = BM + NB * BN;            // operand rows per stage
+  constexpr int BPW = ROWS / 16 / NW;           // 1 KiB data loads per wave per slice
+  constexpr int SPW = ROWS / 64 / NW;           // scale-dword loads per wave per slice
+  constexpr int NLD = BPW + SPW;                // vector-memory instructions per slice
+  static_assert(MI >= 1 && NJ >= 1 && H0 >= 1 && H0 == H1, "tile too small or odd");
+  static_assert(ROWS % (64 * NW) == 0, "every wave loads the same number of blocks");
+  using TOut = typename std::conditional<EPI == EPI_SWIGLU, uint8_t, bf16_t>::type;
+
+  // four stages of operand rows, and beside them four stages of scale dwords
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[4 * ROWS * BK];
+  __shared__ __attribute__((aligned(1024))) uint32_t sring[4 * ROWS];
+
+  TileJob<uint8_t, TOut> job;
+  if (!decode_tile<BM, BN>(args, job)) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const bool live = job.m0 + wm * WTM < job.rows;
+  const int kb = job.K / 32;                    // scale bytes per operand row
+
+  // Scale bases of this job (the scale arrays mirror the code arrays with
+  // one byte per 32 codes, so a code offset maps to offset / 32).
+  const uint8_t* sA;
+  const uint8_t* sB0;
+  const uint8_t* sB1;
+  uint8_t* sC;
+  if (job.dense) {
+    sA = sc.Ad;
+    sB0 = sc.Bd0;
+    sB1 = sc.Bd1;
+    sC = sc.Cd;
+  } else {
+    sA = sc.A + (job.A - static_cast<const uint8_t*>(args.A)) / 32;
+    sB0 = sc.B0 + (job.B0 - static_cast<const uint8_t*>(args.B0)) / 32;
+    sB1 = NB > 1 ? sc.B1 + (job.B1 - static_cast<const uint8_t*>(args.B1)) / 32 : nullptr;
+    sC = (EPI == EPI_SWIGLU)
+             ? sc.C + (reinterpret_cast<const uint8_t*>(job.C) -
+                       static_cast<const uint8_t*>(args.C)) / 32
+             : nullptr;
+  }
+
+  // Data loads: block b = wave * BPW + j covers stage rows 16 b .. + 15; lane
+  // l fetches row 16 b + l / 4 into 16-byte position p = l % 4 of that row.
+  // A row holds its 16-byte chunks as two 32-byte halves, chunks (0, 2) and
+  // (1, 3): exactly the 32 bytes of one lane half's MFMA operand, so a
+  // fragment is one aligned 32-byte read into one register tuple.  The halves
+  // swap on rows with mx_swz(row) = 1 (against bank conflicts): position p
+  // holds chunk ((p / 2) ^ mx_swz(row)) + 2 (p % 2).
+  const int dma_c = (((lane & 3) >> 1) ^ mx_swz(lane >> 2)) + 2 * (lane & 1);
+  uint32_t g_off[BPW];
+  const char* g_base[BPW];
+#pragma unroll
+  for (int j = 0; j < BPW; ++j) {
+    const int row = (wave * BPW + j) * 16;
+    const uint8_t* src;
+    int ld, rbase, rlimit;
+    if (row < BM) {
+      src = job.A;
+      ld = (int)job.lda;
+      rbase = job.m0 + row;
+      rlimit = job.rows;
+    } else {
+      const int rb = row - BM;
+      src = (rb < BN) ? job.B0 : job.B1;
+      ld = job.K;
+      rbase = job.n0 + (rb < BN ? rb : rb - BN);
+      rlimit = job.N;
+    }
+    int r = rbase + (lane >> 2);
+    r = r < rlimit ? r : rlimit - 1;                    // clamp: never stored
+    if (row < BM && job.gather) r = job.gather[r];
+    g_off[j] = (uint32_t)(r * ld + dma_c * 16);
+    g_base[j] = uniform_ptr(src);
+  }
+  // Scale loads: block b = wave * SPW + j covers stage rows 64 b .. + 63,
+  // lane l fetching row 64 b + l.
+  uint32_t s_off[SPW];
+  const char* s_base[SPW];
+#pragma unroll
+  for (int j = 0; j < SPW; ++j) {
+    const int row = (wave * SPW + j) * 64 + lane;       // lane-varying
+    const int blk0 = (wave * SPW + j) * 64;             // wave-uniform
+    const uint8_t* src;
+    int rbase, rlimit;
+    if (blk0 < BM) {
+      src = sA;
+      rbase = job.m0 + row;
+      rlimit = job.rows;
+    } else {
+      const int rb = blk0 - BM;
+      src = (rb < BN) ? sB0 : sB1;
+      rbase = job.n0 + (row - BM - (rb < BN ? 0 : BN));
+      rlimit = job.N;
+    }
+    int r = rbase < rlimit ? rbase : rlimit - 1;
+    if (blk0 < BM && job.gather) r = job.gather[r];
+    s_off[j] = (uint32_t)(r * kb);
+    s_base[j] = uniform_ptr(src);
+  }
+  // Slice kt: its data loads, then its scale loads (inline assembly, so that
+  // only the explicit vmcnt waits order them; M0 holds the LDS destination).
+  auto dma = [&](uint8_t* dst, uint32_t* sdst, int kt) {
+#pragma unroll
+    for (int j = 0; j < BPW; ++j) {
+      const uint32_t lds = (uint32_t)(uintptr_t)MOE_AS_LDS(dst + (wave * BPW + j) * 1024);
+      const char* base = g_base[j] + (size_t)kt * BK;
+      const uint32_t off = g_off[j];
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :: "s"(lds), "v"(off), "s"(base) : "memory");
+    }
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      const uint32_t lds = (uint32_t)(uintptr_t)MOE_AS_LDS(sdst + (wave * SPW + j) * 64);
+      const char* base = s_base[j] + (size_t)(kt >> 1) * 4;
+      const uint32_t off = s_off[j];
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                   :: "s"(lds), "v"(off), "s"(base) : "memory");
+    }
+  };
+
+  f32x16_t acc[NB][MI][NJ];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[b][i][j][v] = 0.0f;
+
+  const int frag_row = lane & 31;
+  const int hsel = lane >> 5;
+  const int c0 = (hsel ^ mx_swz(frag_row)) << 5;   // this lane half's 32 bytes
+  const int a_row = wm * WTM + frag_row;                // stage row of A fragment 0
+  const int b_row = BM + wn * WTN + frag_row;           // ... of B fragment (0, 0)
+
+  auto read_frag = [&](const uint8_t* stage, int row) -> i32x8_t {
+    return *reinterpret_cast<const i32x8_t*>(stage + row * BK + c0);
+  };
+  auto read_scale = [&](const uint32_t* sstage, int row, int par) -> int {
+    return (int)reinterpret_cast<const uint8_t*>(sstage)[row * 4 + 2 * par + hsel];
+  };
+  // weight fragment f (0 .. NBJ-1) = (b, j) with b = f / NJ, j = f % NJ
+  auto brow = [&](int f) { return b_row + (f / NJ) * BN + (f % NJ) * 32; };
+
+  const int KT = job.klen / BK;
+  const int kbeg = job.k0 / BK;
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto wait_slice = [&](int ready, int issued) {
+    const int younger = issued - 1 - ready;
+    if (younger >= 2) wait_vmcnt<2 * NLD>();
+    else if (younger == 1) wait_vmcnt<NLD>();
+    else wait_vmcnt<0>();
+  };
+
+  // Stage rp of the ring.  Stages past 64 KiB are out of reach of the LDS
+  // reads' immediate offset, so if the compiler saw constant stage addresses
+  // it would keep one address register per fragment and stage live across
+  // the loop; the opaque scalar offset makes it add the stage per step to a
+  // few per-lane bases instead.
+  auto stage = [&](int rp) -> uint8_t* { return ring + opaque_u32((uint32_t)rp * (ROWS * BK)); };
+  auto sstage = [&](int rp) -> uint32_t* { return sring + opaque_u32((uint32_t)rp * ROWS); };
+
+  // The MFMA builtins have no side effects, so without a use LLVM sinks
+  // them past the wait/refill blocks of later steps to the loop's end,
+  // keeping every fragment of four steps live.  An empty asm that reads a
+  // half-step's accumulators pins its MFMAs inside that half-step.
+  auto pin_half = [&](int f0) {
+#pragma unroll
+    for (int f = 0; f < H0; ++f)
+#pragma unroll
+      for (int i = 0; i < MI; ++i) use_acc(acc[(f0 + f) / NJ][i][(f0 + f) % NJ]);
+  };
+  auto k_loop = [&](auto live_c) {
+    constexpr bool LIVE = decltype(live_c)::value;
+    i32x8_t af[2][MI];
+    int as[2][MI];
+    i32x8_t bf0[H0], bf1[H1];
+    int bs0[H0], bs1[H1];
+    // Step s uses ring position RP = s % 4 (the loop runs in groups of four
+    // steps from s = 0, so RP is static); P = s % 2 picks the token-fragment
+    // buffer and the scale byte within the stage's dwords.
+    auto step = [&](auto rp_c, int s) {
+      constexpr int RP = decltype(rp_c)::value;
+      constexpr int P = RP & 1;
+      const uint8_t* cur = stage(RP);
+      const uint32_t* scur = sstage(RP);
+      const uint8_t* nxt = stage((RP + 1) & 3);
+      const uint32_t* snxt = sstage((RP + 1) & 3);
+      if constexpr (LIVE) {
+#pragma unroll
+        for (int f = 0; f < H1; ++f) {
+          bf1[f] = read_frag(cur, brow(H0 + f));
+          bs1[f] = read_scale(scur, brow(H0 + f), P);
+        }
+#pragma unroll
+        for (int f = 0; f < H0; ++f)
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+            acc[f / NJ][i][f % NJ] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                bf0[f], af[P][i], acc[f / NJ][i][f % NJ], 0, 0, 0, bs0[f], 0, as[P][i]);
+        pin_half(0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + 1 < KT) wait_slice(s + 1, s + 3 < KT ? s + 3 : KT);
+      barrier();
+      if (s + 3 < KT) dma(ring + ((RP + 3) & 3) * (ROWS * BK), sring + ((RP + 3) & 3) * ROWS,
+                          kbeg + s + 3);
+      if constexpr (LIVE) {
+        // the last step reads the (unused) next stage too, keeping one shape
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          af[1 - P][i] = read_frag(nxt, a_row + 32 * i);
+          as[1 - P][i] = read_scale(snxt, a_row + 32 * i, 1 - P);
+        }
+#pragma unroll
+        for (int f = 0; f < H0; ++f) {
+          bf0[f] = read_frag(nxt, brow(f));
+          bs0[f] = read_scale(snxt, brow(f), 1 - P);
+        }
+#pragma unroll
+        for (int f = 0; f < H1; ++f)
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+            acc[(H0 + f) / NJ][i][(H0 + f) % NJ] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                bf1[f], af[P][i], acc[(H0 + f) / NJ][i][(H0 + f) % NJ], 0, 0, 0, bs1[f], 0,
+                as[P][i]);
+        pin_half(H0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    dma(ring, sring, kbeg);
+    if (KT > 1) dma(ring + ROWS * BK, sring + ROWS, kbeg + 1);
+    if (KT > 2) dma(ring + 2 * ROWS * BK, sring + 2 * ROWS, kbeg + 2);
+    wait_slice(0, KT < 3 ? KT : 3);
+    barrier();
+    if constexpr (LIVE) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        af[0][i] = read_frag(stage(0), a_row + 32 * i);
+        as[0][i] = read_scale(sstage(0), a_row + 32 * i, 0);
+      }
+#pragma unroll
+      for (int f = 0; f < H0; ++f) {
+        bf0[f] = read_frag(stage(0), brow(f));
+        bs0[f] = read_scale(sstage(0), brow(f), 0);
+      }
+    }
+    using r0 = std::integral_constant<int, 0>;
+    using r1 = std::integral_constant<int, 1>;
+    using r2 = std::integral_constant<int, 2>;
+    using r3 = std::integral_constant<int, 3>;
+    int kt = 0;
+    for (; kt + 4 <= KT; kt += 4) {
+      step(r0{}, kt);
+      step(r1{}, kt + 1);
+      step(r2{}, kt + 2);
+      step(r3{}, kt + 3);
+    }
+    if (kt < KT) {   // KT is even (K is a multiple of 128)
+      step(r0{}, kt);
+      step(r1{}, kt + 1);
+    }
+  };
+  if (!live) {
+    k_loop(std::false_type{});
+    return;
+  }
+  k_loop(std::true_type{});
+
+  // Epilogue.  Lane owns row m = .. + (lane % 32) and, for register v,
+  // column n = .. + 8 (v / 4) + 4 (lane / 32) + v % 4.
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int m = job.m0 + wm * WTM + i * 32 + frag_row;
+    const bool row_ok = m < job.rows;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int nblk = job.n0 + wn * WTN + j * 32;          // 32-column block
+      if (nblk >= job.N) continue;                          // N is a multiple of 32
+      if constexpr (EPI == EPI_SWIGLU) {
+        // h = silu(g) * u, one MX block per (row, 32 columns): the lane pair
+        // (l, l + 32) holds the block's 32 values.
+        const f32x16_t& G = acc[0][i][j];
+        const f32x16_t& U = acc[NB - 1][i][j];
+        float hv[16];
+        float amax = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          hv[v] = silu_fast(G[v]) * U[v];
+          amax = fmaxf(amax, fabsf(hv[v]));
+        }
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        const int s = mx_scale_exp(amax);
+        const float inv = mx_inv_scale(s);
+        uint32_t d[4];   // d[q]: columns 8 q + 4 hsel + (0..3)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t w = 0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) w |= e4m3_code(hv[4 * q + r] * inv) << (8 * r);
+          d[q] = w;
+        }
+        // Lane l (hsel 0) gathers columns 0-15 of the block, lane l + 32
+        // columns 16-31: each sends the two dwords the other needs.
+        const uint32_t x0 = __shfl_xor(hsel ? d[0] : d[2], 32, 64);
+        const uint32_t x1 = __shfl_xor(hsel ? d[1] : d[3], 32, 64);
+        const uint4 out = hsel ? make_uint4(x0, d[2], x1, d[3]) : make_uint4(d[0], x0, d[1], x1);
+        if (row_ok) {
+          *reinterpret_cast<uint4*>(job.C + (long long)m * job.ldc + nblk + 16 * hsel) = out;
+          if (hsel == 0) sC[(long long)m * (job.N / 32) + nblk / 32] = (uint8_t)(s + 127);
+        }
+      } else {
+        if (!row_ok) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = nblk + 8 * q + 4 * hsel;
+          const f32x16_t& Cv = acc[0][i][j];
+          const uint2 pk = make_uint2(pack_bf16x2(Cv[4 * q], Cv[4 * q + 1]),
+                                      pack_bf16x2(Cv[4 * q + 2], Cv[4 * q + 3]));
+          *reinterpret_cast<uint2*>(job.C + (long long)m * job.ldc + n) = pk;
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int NB, int EPI, int WM, int WN>
+hipError_t launch_mx_gemm(const GemmArgs& a, const MxScales& sc, int R, hipStream_t st) {
+  const int grid = grid_upper_bound(a, BM, BN, R);
+  if (grid == 0) return hipSuccess;
+  gemm_mx_kernel<BM, BN, NB, EPI, WM, WN><<<grid, 64 * WM * WN, 0, st>>>(a, sc);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_ffn_mxfp8(const moe_shape& s, const uint8_t* xq, const uint8_t* xs,
+                                    const int32_t* row_token, const int32_t* offsets,
+                                    const MxWeights& w, void* y_perm, void* y_shared,
+                                    const MxFfnWs& ws, hipStream_t st) {
+  const int R = s.T * s.k;
+  const bool shared = s.F_shared > 0 && s.T > 0;
+  GemmArgs a1 = {};
+  MxScales s1 = {};
+  a1.E = R > 0 ? s.E : 0;
+  a1.offsets = offsets;
+  a1.tiles = ws.tiles1;
+  a1.A = xq;
+  a1.gather = row_token;
+  a1.lda = s.d;
+  a1.B0 = w.gate_q;
+  a1.B1 = w.up_q;
+  a1.strideB = (long long)s.F * s.d;
+  a1.N = s.F;
+  a1.K = s.d;
+  a1.C = ws.hq;
+  a1.ldc = s.F;
+  s1.A = xs;
+  s1.B0 = w.gate_s;
+  s1.B1 = w.up_s;
+  s1.C = ws.hs;
+  if (shared) {
+    a1.Td = s.T;
+    a1.Ad = xq;
+    a1.ldad = s.d;
+    a1.Bd0 = w.sgate_q;
+    a1.Bd1 = w.sup_q;
+    a1.Nd = s.F_shared;
+    a1.Kd = s.d;
+    a1.Cd = ws.shq;
+    a1.ldcd = s.F_shared;
+    s1.Ad = xs;
+    s1.Bd0 = w.sgate_s;
+    s1.Bd1 = w.sup_s;
+    s1.Cd = ws.shs;
+  }
+  GemmArgs a2 = {};
+  MxScales s2 = {};
+  a2.E = a1.E;
+  a2.offsets = offsets;
+  a2.tiles = ws.tiles2;
+  a2.A = ws.hq;
+  a2.lda = s.F;
+  a2.B0 = w.down_q;
+  a2.strideB = (long long)s.d * s.F;
+  a2.N = s.d;
+  a2.K = s.F;
+  a2.C = y_perm;
+  a2.ldc = s.d;
+  s2.A = ws.hs;
+  s2.B0 = w.down_s;
+  if (shared) {
+    a2.Td = s.T;
+    a2.Ad = ws.shq;
+    a2.ldad = s.F_shared;
+    a2.Bd0 = w.sdown_q;
+    a2.Nd = s.d;
+    a2.Kd = s.F_shared;
+    a2.Cd = y_shared;
+    a2.ldcd = s.d;
+    s2.Ad = ws.shs;
+    s2.Bd0 = w.sdown_s;
+  }
+  if (a1.E == 0 && !shared) return hipSuccess;
+  if (a1.E > 0) {
+    schedule_tiles_kernel<<<1, 1024, 0, st>>>(offsets, s.E, MX_FC1_BM, cdiv(s.F, MX_FC1_BN),
+                                              ws.tiles1, MX_FC2_BM, cdiv(s.d, MX_FC2_BN),
+                                              ws.tiles2, 0);
+  }
+  hipError_t e = launch_mx_gemm<MX_FC1_BM, MX_FC1_BN, 2, EPI_SWIGLU, 4, 2>(a1, s1, R, st);
+  if (e != hipSuccess) return e;
+  return launch_mx_gemm<MX_FC2_BM, MX_FC2_BN, 1, EPI_STORE, 4, 2>(a2, s2, R, st);
+}
+
+}  // namespace moe

@@ -126,3 +126,34 @@ def test_backward_with_shared_expert_needs_its_buffers():
         args[i - 1] = None
     st = M.moe_ffn_backward(s0, *args, p, 0, check=False, stream=0)
     assert st == L.MOE_ERR_WORKSPACE
+
+
+def test_mxfp8_calls_validate_before_launch():
+    c = CONFIGS["deepseek_v3_t8192"]
+    s = M.make_shape(c)
+    p = _fake()
+    need = M.moe_workspace_size(s, L.MOE_OP_FFN_MXFP8)
+    R = c.T * c.k
+    assert need >= R * c.F + R * c.F // 32 + c.T * c.F_shared   # holds h and its scales
+    # quantise: cols must be a positive multiple of 32; buffers non-null and aligned
+    for rows, cols in ((-1, 64), (4, 0), (4, 48)):
+        assert M.moe_mx_quantize(p, rows, cols, p, p, check=False, stream=0) == \
+            L.MOE_ERR_INVALID_ARG
+    assert M.moe_mx_quantize(p, 4, 64, p, None, check=False, stream=0) == L.MOE_ERR_INVALID_ARG
+    assert M.moe_mx_quantize(p, 4, 64, p + 8, p, check=False, stream=0) == L.MOE_ERR_INVALID_ARG
+    assert M.moe_mx_quantize(None, 0, 64, None, None, check=False, stream=0) == L.MOE_OK
+    # grouped FFN: every routed and (F_shared > 0) shared operand is required
+    for missing in range(18):
+        args = [p] * 18
+        args[missing] = None
+        st = M.moe_grouped_ffn_mxfp8(s, *args, p, need, check=False, stream=0)
+        assert st == L.MOE_ERR_INVALID_ARG, missing
+    st = M.moe_grouped_ffn_mxfp8(s, *([p] * 18), p, need - 1, check=False, stream=0)
+    assert st == L.MOE_ERR_WORKSPACE
+    # widths that are not multiples of 128, and fp32 storage
+    s96 = M.make_shape(c.replace(F=96 * 16 + 32))
+    st = M.moe_grouped_ffn_mxfp8(s96, *([p] * 18), p, 1 << 40, check=False, stream=0)
+    assert st == L.MOE_ERR_UNSUPPORTED
+    s32 = M.make_shape(c.replace(dtype=L.MOE_DTYPE_F32))
+    st = M.moe_grouped_ffn_mxfp8(s32, *([p] * 18), p, 1 << 40, check=False, stream=0)
+    assert st == L.MOE_ERR_INVALID_ARG

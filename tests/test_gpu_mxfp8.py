@@ -1,0 +1,146 @@
+"""GPU parity of the MXFP8 entry points (moe_mx_quantize, moe_grouped_ffn_mxfp8)
+against the oracle's MX functions, on seeded inputs both sides receive.
+
+Quantisation decides integers (codes and scale bytes) from bf16 inputs that
+are exact in fp32 and fp64 alike, so it must match bit for bit.  The grouped
+FFN computes the same quantised model as the oracle (exact products of the
+dequantised operands there, fp32 accumulation here); h = silu(g) * u is
+quantised from fp32 on the GPU and from fp64 in the oracle, so a code may
+differ by one step where the two straddle a rounding boundary, which the bf16
+tolerance of the layer covers."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from moe_inputs import MoEConfig, make_inputs, random_topk
+from parity_util import assert_close, np64
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _lib():
+    import mixture_experts_layer_logits_amd as M
+    return M
+
+
+def _decode(q):
+    """E4M3 codes to values (torch's float8_e4m3fn is the OCP E4M3 format)."""
+    return q.cpu().view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _quantize(M, src):
+    rows, cols = src.shape
+    q = torch.empty(rows, cols, dtype=torch.uint8, device="cuda")
+    s = torch.empty(rows, cols // 32, dtype=torch.uint8, device="cuda")
+    M.moe_mx_quantize(src, rows, cols, q, s)
+    return q, s
+
+
+def _mx_matrix(rows, cols, seed):
+    """bf16 [rows, cols]: per block of 32 a random decade in 1e-6 .. 1e6,
+    plus blocks that are all zero, fp32-subnormal, huge, exact rounding ties,
+    negative zeros, and values at E4M3's saturation edge."""
+    g = torch.Generator().manual_seed(seed)
+    nb = rows * cols // 32
+    v = torch.randn(nb, 32, generator=g, dtype=torch.float64)
+    v *= 10.0 ** (torch.rand(nb, 1, generator=g, dtype=torch.float64) * 12 - 6)
+    special = [
+        torch.zeros(32, dtype=torch.float64),
+        torch.randn(32, generator=g, dtype=torch.float64) * 1e-39,
+        torch.randn(32, generator=g, dtype=torch.float64) * 1e30,
+        # amax 256 gives scale 1: 1.0625, 3.125, 19, 3 * 2^-10, 1.1875, 9.5
+        # sit halfway between E4M3 neighbours
+        torch.tensor([256.0, 1.0625, -1.0625, 3.125, -19.0, 0.0029296875, 1.1875, 9.5] * 4,
+                     dtype=torch.float64),
+        torch.tensor([-0.0] * 31 + [1.0], dtype=torch.float64),
+        # amax 470 (scale 1): 470 and 464 saturate, 440 rounds up to 448,
+        # 432 is the tie between 416 and 448
+        torch.tensor([470.0, 464.0, 440.0, 432.0, -470.0, -432.0, 400.0, 7.0] * 4,
+                     dtype=torch.float64),
+    ]
+    for i, blk in enumerate(special):
+        if i < nb:
+            v[(i * 7) % nb] = blk
+    return v.view(rows, cols).to(torch.bfloat16)
+
+
+QUANT_CASES = [(1, 32), (3, 64), (37, 96), (256, 7168), (1000, 2048), (0, 64)]
+
+
+@pytest.mark.parametrize("rows,cols", QUANT_CASES)
+def test_mx_quantize_bit_exact(rows, cols):
+    _log(f"[mx quantize] {rows}x{cols}")
+    M = _lib()
+    src = _mx_matrix(rows, cols, seed=rows * 31 + cols)
+    q, s = _quantize(M, src.cuda())
+    torch.cuda.synchronize()
+    ref_q, ref_s = O.mx_quantize(np64(src))
+    got_q = _decode(q)
+    assert np.array_equal(got_q, ref_q), np.argwhere(got_q != ref_q)[:5]
+    got_s = s.cpu().numpy().astype(np.int64) - 127
+    assert np.array_equal(got_s, ref_s.astype(np.int64)), np.argwhere(got_s != ref_s)[:5]
+    # 0x7f and 0xff (NaN) are never written
+    assert not ((q == 0x7F) | (q == 0xFF)).any()
+
+
+MX_FFN_CASES = [
+    # name, T, d, E, k, F, Fs, skew
+    # d = 384: FC1 runs 6 K steps (4-step loop and a 2-step tail), FC2 has
+    # a half-empty 256-column tile
+    ("mx_t300_d384", 300, 384, 4, 2, 256, 0, False),
+    ("mx_shared_t200", 200, 256, 8, 2, 128, 256, False),
+    ("mx_skewed_empty_t500", 500, 512, 16, 4, 384, 0, True),
+    ("mx_single_expert_t70", 70, 128, 1, 1, 128, 128, False),
+    ("mx_no_tokens", 0, 256, 4, 2, 128, 128, False),
+]
+
+
+def _quantized_weights(M, inp, names):
+    out = []
+    for n in names:
+        if n not in inp or inp[n] is None:
+            out += [None, None]
+            continue
+        w = inp[n]
+        out += list(_quantize(M, w.reshape(-1, w.shape[-1])))
+    return out
+
+
+@pytest.mark.parametrize("case", MX_FFN_CASES, ids=[c[0] for c in MX_FFN_CASES])
+def test_grouped_ffn_mxfp8(case):
+    name, T, d, E, k, F, Fs, skew = case
+    _log(f"[mx ffn] {name}")
+    M = _lib()
+    cfg = MoEConfig(name, T=T, d=d, E=E, k=k, F=F, F_shared=Fs, dtype=1)
+    inp = make_inputs(cfg, device="cuda")
+    wts = [1.0 / (r + 1) ** 6 for r in range(E)] if skew else None
+    idx = random_topk(T, E, k, seed=T + 11, weights=wts)
+    p = O.permute(None, idx.numpy(), np.ones((T, k)), E)
+    if skew:
+        assert (np.diff(p["offsets"]) == 0).any()
+    xq, xs = _quantize(M, inp["x"])
+    wq = _quantized_weights(M, inp, ("w_gate", "w_up", "w_down"))
+    sq = _quantized_weights(M, inp, ("ws_gate", "ws_up", "ws_down")) if Fs else [None] * 6
+    yp = torch.empty(cfg.R, d, dtype=torch.bfloat16, device="cuda")
+    ys = torch.empty(T, d, dtype=torch.bfloat16, device="cuda") if Fs else None
+    shape = M.make_shape(cfg)
+    n = M.moe_workspace_size(shape, 5)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+    M.moe_grouped_ffn_mxfp8(shape, xq, xs, torch.as_tensor(p["row_token"]).cuda(),
+                            torch.as_tensor(p["offsets"]).cuda(), *wq, *sq, yp, ys, ws, n)
+    torch.cuda.synchronize()
+    if T == 0:
+        return
+    x = np64(inp["x"])
+    ref = O.grouped_ffn_mxfp8(x[p["row_token"]], p["offsets"], np64(inp["w_gate"]),
+                              np64(inp["w_up"]), np64(inp["w_down"]))
+    assert_close("y_perm", yp, ref, "bf16")
+    if Fs:
+        ref_s = O.swiglu_ffn_mxfp8(x, np64(inp["ws_gate"]), np64(inp["ws_up"]),
+                                   np64(inp["ws_down"]))["y"]
+        assert_close("y_shared", ys, ref_s, "bf16")

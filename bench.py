@@ -24,6 +24,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
@@ -266,6 +267,49 @@ def main():
                  "stage_ms": {"route+permute_maps": round(fms(0, 1), 4),
                               "ffn_gathered": round(fms(1, 2), 4),
                               "combine": round(fms(2, 3), 4)}}
+    # The forward with MXFP8 expert GEMMs (E4M3, blocks of 32, E8M0 scales):
+    # weights quantised once and cached (outside the timed steps, reported
+    # on its own), x quantised every step, rows gathered from the quantised x.
+    mx = None
+    if (not cfg.backward and cfg.dtype == 1 and
+            all(v % 128 == 0 for v in (cfg.d, cfg.F, cfg.F_shared))):
+        q0, q1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+        q0.record(stream)
+        layer.quantize_weights(inp)
+        q1.record(stream)
+
+        def mx_step(ev=None):
+            parts = (lambda: (layer.route(inp), layer.permute(inp, maps_only=True)),
+                     lambda: layer.quantize_x(inp), lambda: layer.ffn_mxfp8(inp),
+                     lambda: layer.combine(inp))
+            for i, fn in enumerate(parts):
+                if ev is not None:
+                    ev[i].record(stream)
+                fn()
+            if ev is not None:
+                ev[len(parts)].record(stream)
+        for _ in range(args.warmup):
+            mx_step()
+        mev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        m0 = time.perf_counter()
+        for s_ in range(args.steps):
+            mx_step(mev[s_])
+        torch.cuda.synchronize()
+        mwall = (time.perf_counter() - m0) * 1e3 / args.steps
+        mms = lambda a, b: float(np.mean([mev[s_][a].elapsed_time(mev[s_][b])
+                                          for s_ in range(args.steps)]))
+        t_mx = mms(2, 3) / 1e3
+        mx = {"ms_per_step": round(mwall, 4),
+              "tokens_per_s": round(cfg.T / (mwall / 1e3), 1),
+              "stage_ms": {"route+permute_maps": round(mms(0, 1), 4),
+                           "quantize_x": round(mms(1, 2), 4),
+                           "ffn_mxfp8": round(mms(2, 3), 4),
+                           "combine": round(mms(3, 4), 4)},
+              "ffn_tflops": round(ffn_flops(cfg) / t_mx / 1e12, 2),
+              "ffn_frac_of_fp8_peak": round(ffn_flops(cfg) / t_mx / 1e12 / PEAK_FP8_TFLOPS, 4),
+              "weight_quantize_ms_once": round(q0.elapsed_time(q1), 4)}
     ms_step = float(np.mean([evs[s][0].elapsed_time(evs[s][-1])
                              for s in range(args.steps)]))
     ms_wall = wall * 1e3 / args.steps
@@ -317,6 +361,7 @@ def main():
         "stage_hbm": hbm,
         "event_ms_per_step": round(ms_step, 4),
         "fused_permute_forward": fused,
+        "mxfp8_forward": mx,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -89,6 +89,67 @@ class MoELayer:
         return self.buf
 
     # ------------------------------------------------------------------
+    # MXFP8 forward
+    def quantize_weights(self, inp, stream=None):
+        """E4M3 codes and E8M0 scales of every expert weight, along its
+        contraction dimension; kept for every later MXFP8 forward (the
+        weights change only at an optimizer step)."""
+        dev = self.device
+        out = {}
+        names = ["w_gate", "w_up", "w_down"]
+        if self.cfg.F_shared > 0:
+            names += ["ws_gate", "ws_up", "ws_down"]
+        for n in names:
+            w = inp[n]
+            cols = w.shape[-1]
+            rows = w.numel() // cols
+            q = torch.empty(w.shape, dtype=torch.uint8, device=dev)
+            sc = torch.empty(*w.shape[:-1], cols // 32, dtype=torch.uint8, device=dev)
+            L.moe_mx_quantize(w, rows, cols, q, sc, stream)
+            out[n] = (q, sc)
+        self.mx_weights = out
+        return out
+
+    def _mx_buffers(self):
+        if getattr(self, "mx_buf", None) is None:
+            c = self.cfg
+            n = L.moe_workspace_size(self.shape, L.MOE_OP_FFN_MXFP8)
+            self.mx_buf = dict(
+                xq=torch.empty(c.T, c.d, dtype=torch.uint8, device=self.device),
+                xs=torch.empty(c.T, c.d // 32, dtype=torch.uint8, device=self.device),
+                ws=torch.empty(max(n, 256), dtype=torch.uint8, device=self.device),
+                ws_bytes=n)
+        return self.mx_buf
+
+    def quantize_x(self, inp, stream=None):
+        """x [T, d] to MXFP8 (codes and block scales along d)."""
+        m = self._mx_buffers()
+        L.moe_mx_quantize(inp["x"], self.cfg.T, self.cfg.d, m["xq"], m["xs"], stream)
+
+    def ffn_mxfp8(self, inp, stream=None):
+        """The MXFP8 grouped FFN on the quantised x, routed rows gathered
+        through row_token (needs quantize_weights() and quantize_x())."""
+        if getattr(self, "mx_weights", None) is None:
+            raise RuntimeError("call quantize_weights() before the MXFP8 FFN")
+        b, m, w = self.buf, self._mx_buffers(), self.mx_weights
+        none = (None, None)
+        L.moe_grouped_ffn_mxfp8(
+            self.shape, m["xq"], m["xs"], b["row_token"], b["expert_offsets"],
+            *w["w_gate"], *w["w_up"], *w["w_down"], *w.get("ws_gate", none),
+            *w.get("ws_up", none), *w.get("ws_down", none), b["y_perm"],
+            b["y_shared"], m["ws"], m["ws_bytes"], stream)
+
+    def forward_mxfp8(self, inp, stream=None):
+        """route -> permute (maps only) -> quantise x -> MXFP8 grouped FFN ->
+        combine, with the cached quantised weights."""
+        self.route(inp, stream)
+        self.permute(inp, stream, maps_only=True)
+        self.quantize_x(inp, stream)
+        self.ffn_mxfp8(inp, stream)
+        self.combine(inp, stream)
+        return self.buf
+
+    # ------------------------------------------------------------------
     def _alloc_grad(self):
         c = self.cfg
         dev, f32 = self.device, torch.float32

@@ -16,8 +16,8 @@ import torch
 
 import oracle as O
 from moe_inputs import CONFIGS, MoEConfig, SCORE_SIGMOID, make_inputs
-from parity_util import (ambiguous_tokens, assert_close, assert_equal_int, check_maps_valid,
-                         logit_tolerance, np64, oracle_sampled_forward, prec_of, sample_tokens)
+from parity_util import (assert_close, assert_equal_int, check_maps_valid, np64,
+                         oracle_sampled_forward, prec_of, route_and_check, sample_tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -49,22 +49,7 @@ def _run(cfg, inp=None):
     return inp, layer, out
 
 
-def _route_and_check(cfg, inp, out):
-    """Oracle routing from its own scores; returns (idx, w, ambiguous, same)."""
-    ref_l = O.router_logits(inp["x"], inp["w_router"], inp.get("router_bias"), "f32")
-    assert_close("logits", out["logits"], ref_l, "f32")
-    sb = inp.get("score_bias")
-    idx, w = O.route(ref_l, cfg.k, cfg.score, cfg.renorm, cfg.n_groups, cfg.topk_groups,
-                     None if sb is None else np64(sb), prec_of(cfg))
-    amb = ambiguous_tokens(cfg, ref_l, None if sb is None else np64(sb),
-                           logit_tolerance(cfg.d, ref_l), idx)
-    gidx = out["topk_idx"].cpu().numpy()
-    ok = ~amb
-    assert_equal_int("topk_idx[unambiguous]", gidx[ok], idx[ok])
-    assert_close("topk_w[unambiguous]", out["topk_w"][torch.as_tensor(ok).cuda()], w[ok], "f32")
-    same = bool(np.array_equal(gidx, idx))
-    print(f"  ambiguous tokens {int(amb.sum())} of {cfg.T}; routing identical: {same}", flush=True)
-    return idx, w, amb, same
+_route_and_check = route_and_check
 
 
 @pytest.mark.parametrize("name", list(SMALL))

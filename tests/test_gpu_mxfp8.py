@@ -13,8 +13,8 @@ import pytest
 import torch
 
 import oracle as O
-from moe_inputs import MoEConfig, make_inputs, random_topk
-from parity_util import assert_close, np64
+from moe_inputs import CONFIGS, MoEConfig, SCORE_SIGMOID, make_inputs, random_topk
+from parity_util import assert_close, assert_equal_int, np64, route_and_check, sample_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -144,3 +144,83 @@ def test_grouped_ffn_mxfp8(case):
         ref_s = O.swiglu_ffn_mxfp8(x, np64(inp["ws_gate"]), np64(inp["ws_up"]),
                                    np64(inp["ws_down"]))["y"]
         assert_close("y_shared", ys, ref_s, "bf16")
+
+
+# --------------------------------------------------------------------------
+# The layer's MXFP8 forward: route -> maps-only permute -> quantise x ->
+# MXFP8 grouped FFN -> combine, against the oracle routing from its own
+# fp64 scores and running the MX expert FFN on its own permutation.
+# --------------------------------------------------------------------------
+MX_LAYER = {
+    "mx_softmax_t300": MoEConfig("mx_softmax_t300", T=300, d=256, E=8, k=2, F=384),
+    "mx_sigmoid_groups_shared_t200": MoEConfig(
+        "mx_sigmoid_groups_shared_t200", T=200, d=128, E=64, k=8, F=128, F_shared=256,
+        n_groups=8, topk_groups=4, score=SCORE_SIGMOID, score_bias_std=0.1),
+}
+
+
+def _mx_layer(cfg):
+    from mixture_experts_layer_logits_amd import MoELayer
+    inp = make_inputs(cfg, device="cuda")
+    layer = MoELayer(cfg)
+    layer.quantize_weights(inp)
+    out = layer.forward_mxfp8(inp)
+    torch.cuda.synchronize()
+    return inp, layer, out
+
+
+@pytest.mark.parametrize("name", list(MX_LAYER))
+def test_layer_mxfp8_forward(name):
+    cfg = MX_LAYER[name]
+    _log(f"[mx layer] {name}")
+    inp, layer, out = _mx_layer(cfg)
+    idx, w, amb, same = route_and_check(cfg, inp, out)
+    x = np64(inp["x"])
+    p = O.permute(x, idx, w, cfg.E)
+    ref_yp = O.grouped_ffn_mxfp8(p["x_perm"], p["offsets"], np64(inp["w_gate"]),
+                                 np64(inp["w_up"]), np64(inp["w_down"]))
+    ref_ys = None
+    if cfg.F_shared:
+        ref_ys = O.swiglu_ffn_mxfp8(x, np64(inp["ws_gate"]), np64(inp["ws_up"]),
+                                    np64(inp["ws_down"]))["y"]
+        assert_close("y_shared", out["y_shared"], ref_ys, "bf16")
+    if same:
+        assert_equal_int("expert_offsets", out["expert_offsets"], p["offsets"])
+        assert_equal_int("row_token", out["row_token"], p["row_token"])
+        assert_close("y_perm", out["y_perm"], ref_yp, "bf16")
+    ref_y = O.combine(ref_yp, p["token_row"], w, ref_ys, "bf16")
+    ok = ~amb | same
+    assert_close("y", out["y"][torch.as_tensor(ok).cuda()], ref_y[ok], "bf16")
+
+
+@pytest.mark.parametrize("name", ["deepseek_v3_t8192", "mixtral_t4096"])
+def test_layer_mxfp8_full_size_sampled(name):
+    """Full-size MXFP8 forward on a few sampled tokens: the oracle runs each
+    expert those tokens reach once, on just their rows."""
+    cfg = CONFIGS[name]
+    _log(f"[mx layer full] {name}")
+    inp, layer, out = _mx_layer(cfg)
+    idx, w, amb, same = route_and_check(cfg, inp, out)
+    toks = np.array([t for t in sample_tokens(cfg.T, 4) if not amb[t]])
+    x = np64(inp["x"][torch.as_tensor(toks, device="cuda")])
+    idx_s, w_s = np.asarray(idx)[toks], np.asarray(w)[toks]
+    y_rows = np.zeros((len(toks), cfg.k, cfg.d))
+    for e in np.unique(idx_s):
+        sel = np.argwhere(idx_s == e)
+        y_rows[sel[:, 0], sel[:, 1]] = O.swiglu_ffn_mxfp8(
+            x[sel[:, 0]], np64(inp["w_gate"][int(e)]), np64(inp["w_up"][int(e)]),
+            np64(inp["w_down"][int(e)]))["y"]
+    tt = torch.as_tensor(toks, device="cuda")
+    rows = out["token_row"][tt].reshape(-1).long()
+    assert_close("y_perm[sample]", out["y_perm"][rows], y_rows.reshape(-1, cfg.d), "bf16")
+    acc = np.zeros((len(toks), cfg.d))
+    if cfg.F_shared:
+        ys = O.swiglu_ffn_mxfp8(x, np64(inp["ws_gate"]), np64(inp["ws_up"]),
+                                np64(inp["ws_down"]))["y"]
+        assert_close("y_shared[sample]", out["y_shared"][tt], ys, "bf16")
+        acc += ys
+    for j in range(cfg.k):
+        acc += w_s[:, j:j + 1] * y_rows[:, j]
+    assert_close("y[sample]", out["y"][tt], acc, "bf16")
+    del layer, out, inp
+    torch.cuda.empty_cache()

@@ -28,11 +28,6 @@ namespace moe {
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
-// Half swap of a 64-byte LDS operand row.  It depends on row bits 2 and 3
-// only, so a 16-row load block (row = lane / 4 there) and a 32-row fragment
-// (row = lane % 32) both compute it from their local row index.
-__device__ __forceinline__ int mx_swz(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
-
 // v, in a scalar register the compiler cannot see through.
 __device__ __forceinline__ uint32_t opaque_u32(uint32_t v) {
   asm volatile("" : "+s"(v));
@@ -159,7 +154,7 @@ struct MxScales {
   uint8_t* Cd;
 };
 
-template <int BM, int BN, int NB, int EPI, int WM, int WN>
+template <int BM, int BN, int NB, int EPI, int WM, int WN, int SG>
 __global__ void __launch_bounds__(64 * WM * WN)
 gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
   constexpr int NW = WM * WN;
@@ -170,15 +165,21 @@ gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
   constexpr int H0 = NBJ / 2, H1 = NBJ - H0;    // ... in each half-step
   constexpr int ROWS = BM + NB * BN;            // operand rows per stage
   constexpr int BPW = ROWS / 16 / NW;           // 1 KiB data loads per wave per slice
-  constexpr int SPW = ROWS / 64 / NW;           // scale-dword loads per wave per slice
-  constexpr int NLD = BPW + SPW;                // vector-memory instructions per slice
+  constexpr int SPW = ROWS / 64 / NW;           // scale loads per wave per scale slice
+  // SG = 1: every slice also loads its scale dword per row (exact counts);
+  // SG = 8: a group's scale loads ride along every eighth slice, and the
+  // waits count data loads only (waiting at most one instruction longer)
+  constexpr int NLD = SG == 1 ? BPW + SPW : BPW;
+  constexpr int SSTR = SG == 1 ? 4 : 16;        // LDS bytes per row of a scale slice
+  static_assert(SG == 1 || SG == 8, "scale grouping");
   static_assert(MI >= 1 && NJ >= 1 && H0 >= 1 && H0 == H1, "tile too small or odd");
   static_assert(ROWS % (64 * NW) == 0, "every wave loads the same number of blocks");
   using TOut = typename std::conditional<EPI == EPI_SWIGLU, uint8_t, bf16_t>::type;
 
-  // four stages of operand rows, and beside them four stages of scale dwords
+  // four stages of operand rows; beside them four stages of scale dwords
+  // (SG = 1) or two buffers of 16 scale bytes per row (SG = 8)
   __shared__ __attribute__((aligned(1024))) uint8_t ring[4 * ROWS * BK];
-  __shared__ __attribute__((aligned(1024))) uint32_t sring[4 * ROWS];
+  __shared__ __attribute__((aligned(1024))) uint8_t sring[(SG == 1 ? 4 : 2) * ROWS * SSTR];
 
   TileJob<uint8_t, TOut> job;
   if (!decode_tile<BM, BN>(args, job)) return;
@@ -189,6 +190,10 @@ gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
   const int wm = wave / WN, wn = wave % WN;
   const bool live = job.m0 + wm * WTM < job.rows;
   const int kb = job.K / 32;                    // scale bytes per operand row
+  // SG = 8: scale group g covers K blocks 16 g .. 16 g + 15 (steps 8 g ..
+  // 8 g + 7), read as the 16 bytes from sg_start(g); the last group's
+  // window ends at the row's end (kb >= 16 here), so no read passes it.
+  auto sg_start = [&](int g) { return min(16 * g, kb - 16); };
 
   // Scale bases of this job (the scale arrays mirror the code arrays with
   // one byte per 32 codes, so a code offset maps to offset / 32).
@@ -212,13 +217,9 @@ gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
   }
 
   // Data loads: block b = wave * BPW + j covers stage rows 16 b .. + 15; lane
-  // l fetches row 16 b + l / 4 into 16-byte position p = l % 4 of that row.
-  // A row holds its 16-byte chunks as two 32-byte halves, chunks (0, 2) and
-  // (1, 3): exactly the 32 bytes of one lane half's MFMA operand, so a
-  // fragment is one aligned 32-byte read into one register tuple.  The halves
-  // swap on rows with mx_swz(row) = 1 (against bank conflicts): position p
-  // holds chunk ((p / 2) ^ mx_swz(row)) + 2 (p % 2).
-  const int dma_c = (((lane & 3) >> 1) ^ mx_swz(lane >> 2)) + 2 * (lane & 1);
+  // l fetches row 16 b + l / 4, logical chunk (l % 4) ^ f(row), f the bf16
+  // kernel's swizzle, which keeps the fragment reads free of bank conflicts.
+  const int dma_c = (lane & 3) ^ swz(lane >> 2);
   uint32_t g_off[BPW];
   const char* g_base[BPW];
 #pragma unroll
@@ -269,23 +270,34 @@ gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
     s_off[j] = (uint32_t)(r * kb);
     s_base[j] = uniform_ptr(src);
   }
-  // Slice kt: its data loads, then its scale loads (inline assembly, so that
-  // only the explicit vmcnt waits order them; M0 holds the LDS destination).
-  auto dma = [&](uint8_t* dst, uint32_t* sdst, int kt) {
+  // Slice kt: its scale loads (SG = 1, or the first slice of a group), then
+  // its data loads (inline assembly, so that only the explicit vmcnt waits
+  // order them; M0 holds the LDS destination).
+  auto dma = [&](uint8_t* dst, uint8_t* sdst, int kt) {
+    if (SG == 1 || (kt & 7) == 0) {
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) {
+        const uint32_t off = s_off[j];
+        if constexpr (SG == 1) {
+          const uint32_t lds = (uint32_t)(uintptr_t)MOE_AS_LDS(sdst + (wave * SPW + j) * 256);
+          const char* base = s_base[j] + (size_t)(kt >> 1) * 4;
+          asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                       :: "s"(lds), "v"(off), "s"(base) : "memory");
+        } else {
+          const uint32_t lds = (uint32_t)(uintptr_t)MOE_AS_LDS(
+              sring + ((kt >> 3) & 1) * (ROWS * 16) + (wave * SPW + j) * 1024);
+          const char* base = s_base[j] + sg_start(kt >> 3);
+          asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                       :: "s"(lds), "v"(off), "s"(base) : "memory");
+        }
+      }
+    }
 #pragma unroll
     for (int j = 0; j < BPW; ++j) {
       const uint32_t lds = (uint32_t)(uintptr_t)MOE_AS_LDS(dst + (wave * BPW + j) * 1024);
       const char* base = g_base[j] + (size_t)kt * BK;
       const uint32_t off = g_off[j];
       asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                   :: "s"(lds), "v"(off), "s"(base) : "memory");
-    }
-#pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-      const uint32_t lds = (uint32_t)(uintptr_t)MOE_AS_LDS(sdst + (wave * SPW + j) * 64);
-      const char* base = s_base[j] + (size_t)(kt >> 1) * 4;
-      const uint32_t off = s_off[j];
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
                    :: "s"(lds), "v"(off), "s"(base) : "memory");
     }
   };
@@ -302,15 +314,26 @@ gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
 
   const int frag_row = lane & 31;
   const int hsel = lane >> 5;
-  const int c0 = (hsel ^ mx_swz(frag_row)) << 5;   // this lane half's 32 bytes
+  const int c0 = ((0 + hsel) ^ swz(frag_row)) << 4;   // k = 16 hsel ..
+  const int c1 = ((2 + hsel) ^ swz(frag_row)) << 4;   // k = 32 + 16 hsel ..
   const int a_row = wm * WTM + frag_row;                // stage row of A fragment 0
   const int b_row = BM + wn * WTN + frag_row;           // ... of B fragment (0, 0)
 
   auto read_frag = [&](const uint8_t* stage, int row) -> i32x8_t {
-    return *reinterpret_cast<const i32x8_t*>(stage + row * BK + c0);
+    const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(stage + row * BK + c0);
+    const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(stage + row * BK + c1);
+    return (i32x8_t)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
-  auto read_scale = [&](const uint32_t* sstage, int row, int par) -> int {
-    return (int)reinterpret_cast<const uint8_t*>(sstage)[row * 4 + 2 * par + hsel];
+  // Scale bytes of step s start at scale_base(s) + row * SSTR + hsel.
+  auto scale_base = [&](int s, int rp) -> const uint8_t* {
+    if constexpr (SG == 1) {
+      return sring + opaque_u32((uint32_t)rp * (ROWS * 4)) + 2 * (s & 1);
+    } else {
+      return sring + ((s >> 3) & 1) * (ROWS * 16) + (2 * s - sg_start(s >> 3));
+    }
+  };
+  auto read_scale = [&](const uint8_t* sbase, int row) -> int {
+    return (int)sbase[row * SSTR + hsel];
   };
   // weight fragment f (0 .. NBJ-1) = (b, j) with b = f / NJ, j = f % NJ
   auto brow = [&](int f) { return b_row + (f / NJ) * BN + (f % NJ) * 32; };
@@ -337,7 +360,6 @@ gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
   // the loop; the opaque scalar offset makes it add the stage per step to a
   // few per-lane bases instead.
   auto stage = [&](int rp) -> uint8_t* { return ring + opaque_u32((uint32_t)rp * (ROWS * BK)); };
-  auto sstage = [&](int rp) -> uint32_t* { return sring + opaque_u32((uint32_t)rp * ROWS); };
 
   // The MFMA builtins have no side effects, so without a use LLVM sinks
   // them past the wait/refill blocks of later steps to the loop's end,
@@ -362,14 +384,14 @@ gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
       constexpr int RP = decltype(rp_c)::value;
       constexpr int P = RP & 1;
       const uint8_t* cur = stage(RP);
-      const uint32_t* scur = sstage(RP);
+      const uint8_t* scur = scale_base(s, RP);
       const uint8_t* nxt = stage((RP + 1) & 3);
-      const uint32_t* snxt = sstage((RP + 1) & 3);
+      const uint8_t* snxt = scale_base(s + 1, (RP + 1) & 3);
       if constexpr (LIVE) {
 #pragma unroll
         for (int f = 0; f < H1; ++f) {
           bf1[f] = read_frag(cur, brow(H0 + f));
-          bs1[f] = read_scale(scur, brow(H0 + f), P);
+          bs1[f] = read_scale(scur, brow(H0 + f));
         }
 #pragma unroll
         for (int f = 0; f < H0; ++f)
@@ -382,19 +404,19 @@ gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
       __builtin_amdgcn_sched_barrier(0);
       if (s + 1 < KT) wait_slice(s + 1, s + 3 < KT ? s + 3 : KT);
       barrier();
-      if (s + 3 < KT) dma(ring + ((RP + 3) & 3) * (ROWS * BK), sring + ((RP + 3) & 3) * ROWS,
-                          kbeg + s + 3);
+      if (s + 3 < KT)
+        dma(ring + ((RP + 3) & 3) * (ROWS * BK), sring + ((RP + 3) & 3) * (ROWS * 4), kbeg + s + 3);
       if constexpr (LIVE) {
         // the last step reads the (unused) next stage too, keeping one shape
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
           af[1 - P][i] = read_frag(nxt, a_row + 32 * i);
-          as[1 - P][i] = read_scale(snxt, a_row + 32 * i, 1 - P);
+          as[1 - P][i] = read_scale(snxt, a_row + 32 * i);
         }
 #pragma unroll
         for (int f = 0; f < H0; ++f) {
           bf0[f] = read_frag(nxt, brow(f));
-          bs0[f] = read_scale(snxt, brow(f), 1 - P);
+          bs0[f] = read_scale(snxt, brow(f));
         }
 #pragma unroll
         for (int f = 0; f < H1; ++f)
@@ -408,20 +430,20 @@ gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
       __builtin_amdgcn_sched_barrier(0);
     };
     dma(ring, sring, kbeg);
-    if (KT > 1) dma(ring + ROWS * BK, sring + ROWS, kbeg + 1);
-    if (KT > 2) dma(ring + 2 * ROWS * BK, sring + 2 * ROWS, kbeg + 2);
+    if (KT > 1) dma(ring + ROWS * BK, sring + ROWS * 4, kbeg + 1);
+    if (KT > 2) dma(ring + 2 * ROWS * BK, sring + 2 * ROWS * 4, kbeg + 2);
     wait_slice(0, KT < 3 ? KT : 3);
     barrier();
     if constexpr (LIVE) {
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
         af[0][i] = read_frag(stage(0), a_row + 32 * i);
-        as[0][i] = read_scale(sstage(0), a_row + 32 * i, 0);
+        as[0][i] = read_scale(scale_base(0, 0), a_row + 32 * i);
       }
 #pragma unroll
       for (int f = 0; f < H0; ++f) {
         bf0[f] = read_frag(stage(0), brow(f));
-        bs0[f] = read_scale(sstage(0), brow(f), 0);
+        bs0[f] = read_scale(scale_base(0, 0), brow(f));
       }
     }
     using r0 = std::integral_constant<int, 0>;
@@ -503,11 +525,17 @@ gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
   }
 }
 
+// Scale loads are grouped eight K steps at a time when every group of the
+// launch has at least 16 scale bytes per row (K >= 512).
 template <int BM, int BN, int NB, int EPI, int WM, int WN>
 hipError_t launch_mx_gemm(const GemmArgs& a, const MxScales& sc, int R, hipStream_t st) {
   const int grid = grid_upper_bound(a, BM, BN, R);
   if (grid == 0) return hipSuccess;
-  gemm_mx_kernel<BM, BN, NB, EPI, WM, WN><<<grid, 64 * WM * WN, 0, st>>>(a, sc);
+  const bool grouped = (a.E == 0 || a.K >= 512) && (a.Td == 0 || a.Kd >= 512);
+  if (grouped)
+    gemm_mx_kernel<BM, BN, NB, EPI, WM, WN, 8><<<grid, 64 * WM * WN, 0, st>>>(a, sc);
+  else
+    gemm_mx_kernel<BM, BN, NB, EPI, WM, WN, 1><<<grid, 64 * WM * WN, 0, st>>>(a, sc);
   return hipGetLastError();
 }
 

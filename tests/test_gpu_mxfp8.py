@@ -97,6 +97,11 @@ MX_FFN_CASES = [
     ("mx_skewed_empty_t500", 500, 512, 16, 4, 384, 0, True),
     ("mx_single_expert_t70", 70, 128, 1, 1, 128, 128, False),
     ("mx_no_tokens", 0, 256, 4, 2, 128, 128, False),
+    # K >= 512 loads scales eight K steps at a time: FC1 K = 1024 is two
+    # groups; FC2 K = 768 (and the shared expert's 640) ends in a group whose
+    # 16-byte window is moved back to the row's end
+    ("mx_scale_groups_t256", 256, 1024, 4, 2, 768, 0, False),
+    ("mx_scale_groups_shared_t256", 256, 1024, 4, 2, 768, 640, False),
 ]
 
 

@@ -400,6 +400,13 @@ gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
             acc[f / NJ][i][f % NJ] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                 bf0[f], af[P][i], acc[f / NJ][i][f % NJ], 0, 0, 0, bs0[f], 0, as[P][i]);
         pin_half(0);
+        // reads spread between the MFMAs (two reads, one MFMA, ...)
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
       if (s + 1 < KT) wait_slice(s + 1, s + 3 < KT ? s + 3 : KT);
@@ -426,6 +433,11 @@ gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
                 bf1[f], af[P][i], acc[(H0 + f) / NJ][i][(H0 + f) % NJ], 0, 0, 0, bs1[f], 0,
                 as[P][i]);
         pin_half(H0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     };

@@ -520,3 +520,69 @@ def test_mx_round_is_idempotent_and_bounded():
     assert np.array_equal(np.abs(r[sat]), 448.0 * scale[sat])
     normal = ~sat & (np.abs(a) >= 2.0 ** -6 * scale)
     assert np.all(np.abs(r - a)[normal] <= np.abs(a)[normal] * 2.0 ** -4)
+
+
+def _e4m3_nearest_brute(v, table):
+    """Nearest E4M3 value by search over the decoded code table, ties to the
+    value whose code is even (the last mantissa bit 0); beyond 448 the
+    largest finite value (saturation)."""
+    best = None
+    for code, val in table:
+        d = abs(v - val)
+        if best is None or d < best[0] or (d == best[0] and code % 2 == 0):
+            best = (d, val, code)
+    return best[1]
+
+
+def _mx_round_brute(a, table):
+    """MX rounding of a 1-D array in blocks of 32, with the block exponent
+    taken from math.frexp (amax = m * 2^e, 0.5 <= m < 1, so floor(log2 amax)
+    is e - 1)."""
+    import math
+    out = []
+    for b in range(0, len(a), 32):
+        blk = [float(x) for x in a[b:b + 32]]
+        amax = max(abs(x) for x in blk)
+        s = -127 if amax == 0.0 else max(-127, math.frexp(amax)[1] - 1 - 8)
+        out += [_e4m3_nearest_brute(x / 2.0 ** s, table) * 2.0 ** s for x in blk]
+    return out
+
+
+def test_swiglu_ffn_mxfp8_by_brute_force():
+    """The MXFP8 expert on a tiny case with Python loops: x, w_gate, w_up
+    quantised along d, w_down along F, h = silu(g) u quantised along F, y
+    rounded to bf16.  Independent of the oracle's rounding code (table search
+    over torch's E4M3 decoding, frexp exponents)."""
+    import math
+    codes = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    table = [(c, float(codes[c])) for c in range(256) if np.isfinite(codes[c]) and codes[c] >= 0]
+    table += [(c, float(codes[c])) for c in range(256) if np.isfinite(codes[c]) and codes[c] < 0]
+    rng = np.random.default_rng(23)
+    n, d, F = 3, 64, 64
+    x = rng.standard_normal((n, d)) * np.exp2(rng.integers(-3, 3, (n, 1)))
+    wg, wu = rng.standard_normal((F, d)) * 0.1, rng.standard_normal((F, d)) * 0.1
+    wd = rng.standard_normal((d, F)) * 0.1
+    xq = [_mx_round_brute(x[i], table) for i in range(n)]
+    wgq = [_mx_round_brute(wg[f], table) for f in range(F)]
+    wuq = [_mx_round_brute(wu[f], table) for f in range(F)]
+    wdq = [_mx_round_brute(wd[j], table) for j in range(d)]
+    y = np.zeros((n, d))
+    hq_all = []
+    for i in range(n):
+        h = []
+        for f in range(F):
+            g = sum(xq[i][c] * wgq[f][c] for c in range(d))
+            u = sum(xq[i][c] * wuq[f][c] for c in range(d))
+            h.append(g / (1.0 + math.exp(-g)) * u)
+        hq = _mx_round_brute(np.array(h), table)
+        hq_all.append(hq)
+        for j in range(d):
+            y[i, j] = sum(hq[f] * wdq[j][f] for f in range(F))
+    ref = O.swiglu_ffn_mxfp8(x, wg, wu, wd)
+    # the loops sum in another order than the library matmul, so an h value
+    # on a rounding boundary may land one E4M3 step away; nearly all match
+    hq_all = np.array(hq_all)
+    assert np.mean(ref["h"] == hq_all) >= 0.99
+    assert np.allclose(ref["h"], hq_all, rtol=2.0 ** -3, atol=0)
+    y_bf16 = torch.from_numpy(y).float().to(torch.bfloat16).double().numpy()
+    assert np.allclose(O.as64(ref["y"]), y_bf16, rtol=2.0 ** -7, atol=1e-12)

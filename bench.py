@@ -310,6 +310,41 @@ def main():
               "ffn_tflops": round(ffn_flops(cfg) / t_mx / 1e12, 2),
               "ffn_frac_of_fp8_peak": round(ffn_flops(cfg) / t_mx / 1e12 / PEAK_FP8_TFLOPS, 4),
               "weight_quantize_ms_once": round(q0.elapsed_time(q1), 4)}
+    # Training with selective rematerialisation: the forward keeps no g | u
+    # and the backward reruns FC1 (same kernels) before its own GEMMs.
+    remat = None
+    if cfg.backward:
+        rl = MoELayer(cfg, device=dev, recompute=True)
+
+        def remat_step(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            rl.forward(inp)
+            if ev is not None:
+                ev[1].record(stream)
+            rl.backward(inp, inp["dy"])
+            if ev is not None:
+                ev[2].record(stream)
+        for _ in range(args.warmup):
+            remat_step()
+        rev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        r0 = time.perf_counter()
+        for s_ in range(args.steps):
+            remat_step(rev[s_])
+        torch.cuda.synchronize()
+        rwall = (time.perf_counter() - r0) * 1e3 / args.steps
+        rms = lambda a, b: float(np.mean([rev[s_][a].elapsed_time(rev[s_][b])
+                                          for s_ in range(args.steps)]))
+        esz = 2 if cfg.dtype == 1 else 4
+        remat = {"ms_per_step": round(rwall, 4),
+                 "tokens_per_s": round(cfg.T / (rwall / 1e3), 1),
+                 "stage_ms": {"forward": round(rms(0, 1), 4),
+                              "backward_with_fc1_recompute": round(rms(1, 2), 4)},
+                 "gu_bytes_not_kept": int((cfg.T * cfg.k * 2 * cfg.F + cfg.T * 2 * cfg.F_shared) * esz)}
+        del rl
+        torch.cuda.empty_cache()
     ms_step = float(np.mean([evs[s][0].elapsed_time(evs[s][-1])
                              for s in range(args.steps)]))
     ms_wall = wall * 1e3 / args.steps
@@ -362,6 +397,7 @@ def main():
         "event_ms_per_step": round(ms_step, 4),
         "fused_permute_forward": fused,
         "mxfp8_forward": mx,
+        "training_with_recompute": remat,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

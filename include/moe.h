@@ -74,7 +74,8 @@ enum {
   MOE_OP_FFN = 2,
   MOE_OP_COMBINE = 3,
   MOE_OP_BACKWARD = 4,
-  MOE_OP_FFN_MXFP8 = 5
+  MOE_OP_FFN_MXFP8 = 5,
+  MOE_OP_BACKWARD_RECOMPUTE = 6   /* moe_ffn_backward with gu_save NULL */
 };
 
 /* The layer's parameters: tokens T, hidden d, routed experts E, experts per
@@ -221,7 +222,15 @@ int moe_unpermute_combine(const moe_shape* shape, const void* y_perm,
  *  dws_gate, dws_up [F_shared, d], dws_down [d, F_shared] fp32 out are only
  *  touched when F_shared > 0 (may be NULL otherwise); gu_save then holds
  *  R * 2F + T * 2F_shared elements, as moe_grouped_ffn writes it.
- *  ws: MOE_OP_BACKWARD bytes. */
+ *
+ *  Selective rematerialisation: with gu_save NULL the call first runs FC1
+ *  again on x_perm (and x for the shared expert), with the same kernels and
+ *  schedule as moe_grouped_ffn, into its workspace, and then proceeds as
+ *  above.  The results are bitwise those of the call given the saved g | u;
+ *  the forward then need not keep g | u (R * 2F + T * 2F_shared elements)
+ *  alive until the backward.
+ *  ws: MOE_OP_BACKWARD bytes, or MOE_OP_BACKWARD_RECOMPUTE bytes when
+ *  gu_save is NULL. */
 int moe_ffn_backward(const moe_shape* shape, const void* dy, const void* x_perm,
                      const void* gu_save, const void* y_perm,
                      const int32_t* expert_offsets, const int32_t* row_token,

@@ -28,7 +28,7 @@ MOE_DTYPE_BF16 = 1
 MOE_SCORE_SOFTMAX = 0
 MOE_SCORE_SIGMOID = 1
 (MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN, MOE_OP_COMBINE, MOE_OP_BACKWARD,
- MOE_OP_FFN_MXFP8) = range(6)
+ MOE_OP_FFN_MXFP8, MOE_OP_BACKWARD_RECOMPUTE) = range(7)
 
 EXPORTED = ("moe_workspace_size", "moe_route_topk", "moe_permute",
             "moe_grouped_ffn", "moe_unpermute_combine", "moe_ffn_backward",

@@ -59,7 +59,8 @@ size_t ws_bytes_for(const moe_shape& s, int op) {
              align_up((size_t)s.T * s.F_shared * es) +
              (ks > 1 ? align_up((size_t)ks * R * s.d * 4) : 0);
     }
-    case MOE_OP_BACKWARD: {
+    case MOE_OP_BACKWARD:
+    case MOE_OP_BACKWARD_RECOMPUTE: {
       size_t b = 2 * align_up((s.E + 1) * 4) + 2 * align_up(R * s.d * es) +
                  align_up(R * 2 * s.F * es) + align_up(R * s.F * es);
       if (s.F_shared > 0) {
@@ -67,6 +68,8 @@ size_t ws_bytes_for(const moe_shape& s, int op) {
         b += 3 * align_up(2 * 4) + align_up(T * 2 * Fs * es) + align_up(T * Fs * es) +
              align_up(T * s.d * es);
       }
+      if (op == MOE_OP_BACKWARD_RECOMPUTE)   // the recomputed g | u
+        b += align_up((R * 2 * s.F + (size_t)s.T * 2 * s.F_shared) * es);
       return b;
     }
     case MOE_OP_FFN_MXFP8:
@@ -104,7 +107,7 @@ extern "C" {
 int moe_workspace_size(const moe_shape* shape, int op, size_t* bytes) {
   const int st = check_shape(shape);
   if (st != MOE_OK) return st;
-  if (!bytes || op < MOE_OP_ROUTE || op > MOE_OP_FFN_MXFP8) return MOE_ERR_INVALID_ARG;
+  if (!bytes || op < MOE_OP_ROUTE || op > MOE_OP_BACKWARD_RECOMPUTE) return MOE_ERR_INVALID_ARG;
   *bytes = ws_bytes_for(*shape, op);
   return MOE_OK;
 }
@@ -261,8 +264,11 @@ int moe_ffn_backward(const moe_shape* shape, const void* dy, const void* x_perm,
         !ok_buf(dws_up, sz * 4) || !ok_buf(dws_down, sz * 4))
       return MOE_ERR_INVALID_ARG;
   }
+  // gu_save NULL: g | u are recomputed by FC1 into the workspace
+  const bool recompute = gu_save == nullptr;
+  const int op = recompute ? MOE_OP_BACKWARD_RECOMPUTE : MOE_OP_BACKWARD;
   if (!ok_buf(dy, (long long)s.T * s.d * es) || !ok_buf(x_perm, R * s.d * es) ||
-      !ok_buf(gu_save, gu_elems * es) || !ok_buf(y_perm, R * s.d * es) ||
+      (!recompute && !ok_buf(gu_save, gu_elems * es)) || !ok_buf(y_perm, R * s.d * es) ||
       !ok_buf(expert_offsets, (long long)(s.E + 1) * 4) || !ok_buf(row_token, R * 4) ||
       !ok_buf(token_row, R * 4) || !ok_buf(topk_idx, R * 4) || !ok_buf(topk_w, R * 4) ||
       !ok_buf(logits, (long long)s.T * s.E * 4) || !ok_buf(w_gate, wsz * es) ||
@@ -271,7 +277,7 @@ int moe_ffn_backward(const moe_shape* shape, const void* dy, const void* x_perm,
       !ok_buf(dw_up, wsz * 4) || !ok_buf(dw_down, wsz * 4) || !ok_buf(d_gate, R * 4) ||
       !ok_buf(d_logits, (long long)s.T * s.E * 4))
     return MOE_ERR_INVALID_ARG;
-  if ((st = check_ws(s, MOE_OP_BACKWARD, ws, ws_bytes)) != MOE_OK) return st;
+  if ((st = check_ws(s, op, ws, ws_bytes)) != MOE_OK) return st;
   Carver c{static_cast<char*>(ws)};
   moe::BwdWs bw;
   bw.tiles = c.take<int32_t>((s.E + 1) * 4);
@@ -290,12 +296,20 @@ int moe_ffn_backward(const moe_shape* shape, const void* dy, const void* x_perm,
     bw.s_h = c.take<char>((size_t)s.T * s.F_shared * es);
     bw.s_dX = c.take<char>((size_t)s.T * s.d * es);
   }
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (recompute) {
+    void* gu = c.take<char>((size_t)gu_elems * es);
+    if ((st = hip_status(moe::launch_fc1_recompute(s, x_perm, expert_offsets, w_gate, w_up, x,
+                                                   ws_gate, ws_up, gu, bw.h, bw.s_h, bw.tiles,
+                                                   hs))) != MOE_OK)
+      return st;
+    gu_save = gu;
+  }
   return hip_status(moe::launch_backward(s, dy, x_perm, gu_save, y_perm, expert_offsets,
                                          row_token, token_row, topk_idx, topk_w, logits,
                                          w_gate, w_up, w_down, x, ws_gate, ws_up, ws_down, dx,
                                          dw_gate, dw_up, dw_down, dws_gate, dws_up, dws_down,
-                                         d_gate, d_logits, bw,
-                                         static_cast<hipStream_t>(stream)));
+                                         d_gate, d_logits, bw, hs));
 }
 
 int moe_mx_quantize(const void* src, int64_t rows, int32_t cols, uint8_t* q, uint8_t* scales,

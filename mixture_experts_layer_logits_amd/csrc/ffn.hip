@@ -35,7 +35,7 @@ int ffn_fc2_ksplit(const moe_shape& s) {
   const long long tiles = (cdiv((int)R, FC2_BM) + s.E) * (long long)cdiv(s.d, FC2_BN);
   for (int ks = 1; ks <= 4; ++ks) {
     if (s.F % (ks * 32) != 0) continue;
-    if (tiles * ks >= 6 * 256 || ks == 4) return ks;
+    if (tiles * ks >= 4 * 256 || ks == 4) return ks;
   }
   return 1;
 }
@@ -73,19 +73,18 @@ static hipError_t run_generic(const moe_shape& s, GemmArgs& a1, GemmArgs& a2, in
   return hipGetLastError();
 }
 
-hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const int32_t* row_token,
-                              const int32_t* offsets,
-                              const void* w_gate, const void* w_up, const void* w_down,
-                              const void* x, const void* ws_gate, const void* ws_up,
-                              const void* ws_down, void* y_perm, void* y_shared,
-                              void* gu_save, const FfnWs& ws, hipStream_t st) {
+// FC1's arguments (routed groups, and the shared expert as the dense group).
+static GemmArgs fc1_args(const moe_shape& s, const void* x_perm, const int32_t* row_token,
+                         const int32_t* offsets, const void* w_gate, const void* w_up,
+                         const void* x, const void* ws_gate, const void* ws_up, void* h,
+                         void* h_shared, void* gu_save, int32_t* tiles) {
   const int R = s.T * s.k;
   const bool shared = s.F_shared > 0 && s.T > 0;
   // FC1: x_perm [R, d] x w_gate/w_up [E, F, d] -> h [R, F]
   GemmArgs a1 = {};
   a1.E = R > 0 ? s.E : 0;
   a1.offsets = offsets;
-  a1.tiles = ws.tiles1;
+  a1.tiles = tiles;
   // without x_perm, FC1 gathers each routed row from x[row_token[r]]
   a1.A = x_perm ? x_perm : x;
   a1.gather = x_perm ? nullptr : row_token;
@@ -95,7 +94,7 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const int3
   a1.strideB = (long long)s.F * s.d;
   a1.N = s.F;
   a1.K = s.d;
-  a1.C = ws.h;
+  a1.C = h;
   a1.ldc = s.F;
   a1.GU = gu_save;
   a1.ldgu = 2LL * s.F;
@@ -107,7 +106,7 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const int3
     a1.Bd1 = ws_up;
     a1.Nd = s.F_shared;
     a1.Kd = s.d;
-    a1.Cd = ws.h_shared;
+    a1.Cd = h_shared;
     a1.ldcd = s.F_shared;
     if (gu_save) {   // the shared expert's g | u follow the routed rows
       a1.GUd = static_cast<char*>(gu_save) +
@@ -115,6 +114,51 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const int3
       a1.ldgud = 2LL * s.F_shared;
     }
   }
+  return a1;
+}
+
+static hipError_t launch_fc1(const moe_shape& s, GemmArgs& a1, int R, hipStream_t st) {
+  if (!ffn_uses_mfma(s)) {
+    const int g1 = grid_upper_bound(a1, GEN_BM, GEN_BN, R);
+    if (g1 == 0) return hipSuccess;
+    if (s.dtype == MOE_DTYPE_BF16)
+      gemm_generic_kernel<bf16_t, 2, EPI_SWIGLU><<<g1, 256, 0, st>>>(a1);
+    else
+      gemm_generic_kernel<float, 2, EPI_SWIGLU><<<g1, 256, 0, st>>>(a1);
+    return hipGetLastError();
+  }
+  a1.tail = 1;
+  return launch_mfma_gemm<FC1_BM, FC1_BN, 2, EPI_SWIGLU, 4, 2, 1>(a1, R, st);
+}
+
+hipError_t launch_fc1_recompute(const moe_shape& s, const void* x_perm, const int32_t* offsets,
+                                const void* w_gate, const void* w_up, const void* x,
+                                const void* ws_gate, const void* ws_up, void* gu_out,
+                                void* h_scratch, void* hs_scratch, int32_t* tiles,
+                                hipStream_t st) {
+  const int R = s.T * s.k;
+  GemmArgs a1 = fc1_args(s, x_perm, nullptr, offsets, w_gate, w_up, x, ws_gate, ws_up,
+                         h_scratch, hs_scratch, gu_out, tiles);
+  if (a1.E == 0 && a1.Td == 0) return hipSuccess;
+  if (a1.E > 0) {
+    const bool mfma = ffn_uses_mfma(s);
+    const int bm = mfma ? FC1_BM : GEN_BM;   // (the second prefix is not written)
+    schedule_tiles_kernel<<<1, 1024, 0, st>>>(offsets, s.E, bm, cdiv(s.F, mfma ? FC1_BN : GEN_BN),
+                                              tiles, bm, 1, nullptr, mfma ? 1 : 0);
+  }
+  return launch_fc1(s, a1, R, st);
+}
+
+hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const int32_t* row_token,
+                              const int32_t* offsets,
+                              const void* w_gate, const void* w_up, const void* w_down,
+                              const void* x, const void* ws_gate, const void* ws_up,
+                              const void* ws_down, void* y_perm, void* y_shared,
+                              void* gu_save, const FfnWs& ws, hipStream_t st) {
+  const int R = s.T * s.k;
+  const bool shared = s.F_shared > 0 && s.T > 0;
+  GemmArgs a1 = fc1_args(s, x_perm, row_token, offsets, w_gate, w_up, x, ws_gate, ws_up, ws.h,
+                         ws.h_shared, gu_save, ws.tiles1);
   // FC2: h [R, F] x w_down [E, d, F] -> y_perm [R, d]
   GemmArgs a2 = {};
   a2.E = a1.E;

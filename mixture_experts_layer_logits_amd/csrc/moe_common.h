@@ -69,6 +69,13 @@ struct FfnWs {
 };
 bool ffn_uses_mfma(const moe_shape& s);
 int ffn_fc2_ksplit(const moe_shape& s);
+// FC1 alone, as the forward runs it on x_perm (same kernels, same schedule):
+// writes the rounded g | u (routed rows, then the shared expert's) to gu_out.
+hipError_t launch_fc1_recompute(const moe_shape& s, const void* x_perm, const int32_t* offsets,
+                                const void* w_gate, const void* w_up, const void* x,
+                                const void* ws_gate, const void* ws_up, void* gu_out,
+                                void* h_scratch, void* hs_scratch, int32_t* tiles,
+                                hipStream_t st);
 hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const int32_t* row_token,
                               const int32_t* offsets,
                               const void* w_gate, const void* w_up, const void* w_down,

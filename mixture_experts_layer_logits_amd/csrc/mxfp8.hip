@@ -34,7 +34,8 @@ __device__ __forceinline__ uint32_t opaque_u32(uint32_t v) {
   return v;
 }
 
-// An empty use of an accumulator tile: its MFMAs must have run by here.
+// An empty use of an accumulator tile (in VGPRs): its MFMAs must have run
+// by here.
 __device__ __forceinline__ void use_acc(const f32x16_t& a) { asm volatile("" ::"v"(a)); }
 
 // FC1: 256 rows x (128 gate + 128 up) columns; FC2: 256 x 256; 8 waves.

@@ -13,10 +13,15 @@ from . import _lib as L
 
 
 class MoELayer:
-    def __init__(self, cfg, device="cuda", save_gu=None):
+    def __init__(self, cfg, device="cuda", save_gu=None, recompute=False):
+        """recompute: train without keeping g | u from the forward; the
+        backward runs FC1 again (selective rematerialisation)."""
         self.cfg = cfg
         self.shape = L.make_shape(cfg)
         self.device = torch.device(device)
+        self.recompute = bool(recompute)
+        if self.recompute:
+            save_gu = False
         self.save_gu = bool(getattr(cfg, "backward", False)) if save_gu is None else save_gu
         T, d, E, k, F, Fs = cfg.T, cfg.d, cfg.E, cfg.k, cfg.F, cfg.F_shared
         R = T * k
@@ -26,6 +31,8 @@ class MoELayer:
                L.MOE_OP_COMBINE]
         if self.save_gu:
             ops.append(L.MOE_OP_BACKWARD)
+        if self.recompute:
+            ops.append(L.MOE_OP_BACKWARD_RECOMPUTE)
         # one scratch buffer serves every call: they are ordered on one stream
         self.ws_bytes = max(L.moe_workspace_size(self.shape, op) for op in ops)
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)

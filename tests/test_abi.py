@@ -157,3 +157,19 @@ def test_mxfp8_calls_validate_before_launch():
     s32 = M.make_shape(c.replace(dtype=L.MOE_DTYPE_F32))
     st = M.moe_grouped_ffn_mxfp8(s32, *([p] * 18), p, 1 << 40, check=False, stream=0)
     assert st == L.MOE_ERR_INVALID_ARG
+
+
+def test_backward_recompute_workspace():
+    """gu_save NULL asks for the recompute workspace: the backward's plus the
+    g | u buffer (R * 2F + T * 2F_shared elements)."""
+    c = CONFIGS["deepseek_v3_train_t8192"]
+    s = M.make_shape(c)
+    base = M.moe_workspace_size(s, L.MOE_OP_BACKWARD)
+    remat = M.moe_workspace_size(s, L.MOE_OP_BACKWARD_RECOMPUTE)
+    gu = (c.T * c.k * 2 * c.F + c.T * 2 * c.F_shared) * 2
+    assert gu <= remat - base <= gu + 256
+    p = _fake()
+    args = [p] * 26
+    args[2] = None                                   # gu_save
+    st = M.moe_ffn_backward(s, *args, p, base, check=False, stream=0)
+    assert st == L.MOE_ERR_WORKSPACE

@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import oracle as O
-from moe_inputs import CONFIGS, MoEConfig, SCORE_SIGMOID, make_inputs
+from moe_inputs import CONFIGS, MoEConfig, SCORE_SIGMOID, child_seed, make_inputs, normal
 from parity_util import (assert_close, assert_equal_int, check_maps_valid, np64,
                          oracle_sampled_forward, prec_of, route_and_check, sample_tokens)
 
@@ -176,4 +176,34 @@ def test_layer_full_size_sampled(name):
         assert_close("y_shared[sample]", out["y_shared"][tt], ref["ys"], prec)
     assert_close("y[sample]", out["y"][tt], ref["y"], prec)
     del layer, out, inp
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["bf16_sigmoid_groups_shared_t200", "bf16_generic_shapes_t77",
+                                  "f32_odd_t37", "qwen3_235b_train_t8192"])
+def test_backward_recompute_matches_saved_bitwise(name):
+    """Selective rematerialisation: a forward that keeps no g | u and a
+    backward that reruns FC1 give bitwise the gradients of the saved path
+    (the same FC1 kernels and schedule recompute the same values)."""
+    from mixture_experts_layer_logits_amd import MoELayer
+    cfg = SMALL.get(name) or CONFIGS[name]
+    print(f"[backward recompute] {name}", flush=True)
+    inp = make_inputs(cfg, device="cuda")
+    dy = inp.get("dy")
+    if dy is None:
+        dy = normal((cfg.T, cfg.d), 1.0, cfg.torch_dtype, "cuda", child_seed(9, "dy"))
+    saved = MoELayer(cfg, save_gu=True)
+    saved.forward(inp)
+    g1 = {k: (v.clone() if v is not None else None) for k, v in saved.backward(inp, dy).items()}
+    remat = MoELayer(cfg, recompute=True)
+    out = remat.forward(inp)
+    assert out["gu_save"] is None
+    g2 = remat.backward(inp, dy)
+    torch.cuda.synchronize()
+    for k, v in g1.items():
+        if v is None:
+            assert g2[k] is None, k
+        else:
+            assert torch.equal(v, g2[k]), k
+    del saved, remat
     torch.cuda.empty_cache()

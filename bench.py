@@ -345,6 +345,28 @@ def main():
                  "gu_bytes_not_kept": int((cfg.T * cfg.k * 2 * cfg.F + cfg.T * 2 * cfg.F_shared) * esz)}
         del rl
         torch.cuda.empty_cache()
+        # The same training step with the weight gradients stored as bf16.
+        bl = MoELayer(cfg.replace(wgrad_dtype=1), device=dev)
+        for _ in range(args.warmup):
+            bl.forward(inp)
+            bl.backward(inp, inp["dy"])
+        bev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        b0 = time.perf_counter()
+        for s_ in range(args.steps):
+            bl.forward(inp)
+            bev[s_][0].record(stream)
+            bl.backward(inp, inp["dy"])
+            bev[s_][1].record(stream)
+        torch.cuda.synchronize()
+        bwall = (time.perf_counter() - b0) * 1e3 / args.steps
+        remat["bf16_weight_gradients"] = {
+            "ms_per_step": round(bwall, 4), "tokens_per_s": round(cfg.T / (bwall / 1e3), 1),
+            "backward_ms": round(float(np.mean([bev[s_][0].elapsed_time(bev[s_][1])
+                                                for s_ in range(args.steps)])), 4)}
+        del bl
+        torch.cuda.empty_cache()
     ms_step = float(np.mean([evs[s][0].elapsed_time(evs[s][-1])
                              for s in range(args.steps)]))
     ms_wall = wall * 1e3 / args.steps

@@ -94,6 +94,8 @@ typedef struct moe_shape {
   int32_t score;
   int32_t renorm;
   int32_t dtype;
+  int32_t wgrad_dtype;  /* storage of moe_ffn_backward's weight gradients:
+                           MOE_DTYPE_F32 (0, the default) or MOE_DTYPE_BF16 */
 } moe_shape;
 
 /* Bytes of scratch memory `op` (MOE_OP_*) needs for `shape`.  Host-only, no
@@ -210,8 +212,11 @@ int moe_unpermute_combine(const moe_shape* shape, const void* y_perm,
  *  expert_offsets [E+1], row_token [R], token_row [T, k], topk_idx [T, k]
  *  int32; topk_w [T, k], logits [T, E] fp32; w_gate, w_up, w_down as in
  *  moe_grouped_ffn.
- *  Outputs (fp32): dx [T, d]; dw_gate, dw_up [E, F, d]; dw_down [E, d, F]
- *  (exactly zero for experts with no rows); d_gate [T, k]; d_logits [T, E].
+ *  Outputs: dx [T, d], d_gate [T, k], d_logits [T, E] fp32; dw_gate, dw_up
+ *  [E, F, d] and dw_down [E, d, F] (exactly zero for experts with no rows)
+ *  stored as shape.wgrad_dtype: fp32, or bf16 rounded once from the fp32
+ *  accumulator (the Primus blog's precision-aware optimizer keeps main
+ *  gradients in BF16; this halves the weight-gradient writes).
  *
  *  With F_shared > 0 the shared expert (gate 1 on every token, beside the
  *  routed experts as in the Primus blog's layer) gets the same backward over all
@@ -219,7 +224,8 @@ int moe_unpermute_combine(const moe_shape* shape, const void* y_perm,
  *    dws_down = dy^T . hs;  dws_gate = dgs^T . x;  dws_up = dus^T . x
  *    dx[t] += rnd(dgs . ws_gate + dus . ws_up)[t], added after the routed terms.
  *  x [T, d], ws_gate, ws_up [F_shared, d], ws_down [d, F_shared] dtype and
- *  dws_gate, dws_up [F_shared, d], dws_down [d, F_shared] fp32 out are only
+ *  dws_gate, dws_up [F_shared, d], dws_down [d, F_shared] out (as
+ *  shape.wgrad_dtype) are only
  *  touched when F_shared > 0 (may be NULL otherwise); gu_save then holds
  *  R * 2F + T * 2F_shared elements, as moe_grouped_ffn writes it.
  *
@@ -238,8 +244,8 @@ int moe_ffn_backward(const moe_shape* shape, const void* dy, const void* x_perm,
                      const float* topk_w, const float* logits,
                      const void* w_gate, const void* w_up, const void* w_down,
                      const void* x, const void* ws_gate, const void* ws_up,
-                     const void* ws_down, float* dx, float* dw_gate, float* dw_up,
-                     float* dw_down, float* dws_gate, float* dws_up, float* dws_down,
+                     const void* ws_down, float* dx, void* dw_gate, void* dw_up,
+                     void* dw_down, void* dws_gate, void* dws_up, void* dws_down,
                      float* d_gate, float* d_logits, void* ws, size_t ws_bytes,
                      void* stream);
 

@@ -38,7 +38,7 @@ EXPORTED = ("moe_workspace_size", "moe_route_topk", "moe_permute",
 class MoeShape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("T", "d", "E", "k", "F", "F_shared", "n_groups",
-                 "topk_groups", "score", "renorm", "dtype")]
+                 "topk_groups", "score", "renorm", "dtype", "wgrad_dtype")]
 
 
 class MoeError(RuntimeError):
@@ -87,7 +87,7 @@ def make_shape(cfg) -> MoeShape:
     """A moe_shape from an object with the layer's fields (e.g. MoEConfig)."""
     return MoeShape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.F, cfg.F_shared,
                     cfg.n_groups, cfg.topk_groups, cfg.score, cfg.renorm,
-                    cfg.dtype)
+                    cfg.dtype, getattr(cfg, "wgrad_dtype", MOE_DTYPE_F32))
 
 
 def _p(t) -> Optional[int]:

@@ -29,6 +29,7 @@ int check_shape(const moe_shape* sp) {
   if (s.n_groups > 1 && s.score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
   if (s.renorm != 0 && s.renorm != 1) return MOE_ERR_INVALID_ARG;
   if (s.dtype != MOE_DTYPE_F32 && s.dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
+  if (s.wgrad_dtype != MOE_DTYPE_F32 && s.wgrad_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
   const long long R = (long long)s.T * s.k;
   const long long wide = std::max<long long>({s.d, s.F, s.F_shared, s.E, 2LL * s.F});
   if (R * wide >= (1LL << 31) || (long long)s.T * wide >= (1LL << 31)) return MOE_ERR_INVALID_ARG;
@@ -246,9 +247,9 @@ int moe_ffn_backward(const moe_shape* shape, const void* dy, const void* x_perm,
                      const int32_t* topk_idx, const float* topk_w, const float* logits,
                      const void* w_gate, const void* w_up, const void* w_down, const void* x,
                      const void* ws_gate, const void* ws_up, const void* ws_down, float* dx,
-                     float* dw_gate, float* dw_up, float* dw_down, float* dws_gate,
-                     float* dws_up, float* dws_down, float* d_gate, float* d_logits, void* ws,
-                     size_t ws_bytes, void* stream) {
+                     void* dw_gate, void* dw_up, void* dw_down, void* dws_gate, void* dws_up,
+                     void* dws_down, float* d_gate, float* d_logits, void* ws, size_t ws_bytes,
+                     void* stream) {
   int st = check_shape(shape);
   if (st != MOE_OK) return st;
   const moe_shape& s = *shape;
@@ -256,12 +257,13 @@ int moe_ffn_backward(const moe_shape* shape, const void* dy, const void* x_perm,
   const long long es = (long long)esize(s);
   const long long R = (long long)s.T * s.k;
   const long long wsz = (long long)s.E * s.F * s.d;
+  const long long wes = s.wgrad_dtype == MOE_DTYPE_BF16 ? 2 : 4;   // weight-gradient bytes
   const long long gu_elems = R * 2 * s.F + (long long)s.T * 2 * s.F_shared;
   if (s.F_shared > 0) {
     const long long sz = (long long)s.F_shared * s.d;
     if (!ok_buf(x, (long long)s.T * s.d * es) || !ok_buf(ws_gate, sz * es) ||
-        !ok_buf(ws_up, sz * es) || !ok_buf(ws_down, sz * es) || !ok_buf(dws_gate, sz * 4) ||
-        !ok_buf(dws_up, sz * 4) || !ok_buf(dws_down, sz * 4))
+        !ok_buf(ws_up, sz * es) || !ok_buf(ws_down, sz * es) || !ok_buf(dws_gate, sz * wes) ||
+        !ok_buf(dws_up, sz * wes) || !ok_buf(dws_down, sz * wes))
       return MOE_ERR_INVALID_ARG;
   }
   // gu_save NULL: g | u are recomputed by FC1 into the workspace
@@ -273,8 +275,8 @@ int moe_ffn_backward(const moe_shape* shape, const void* dy, const void* x_perm,
       !ok_buf(token_row, R * 4) || !ok_buf(topk_idx, R * 4) || !ok_buf(topk_w, R * 4) ||
       !ok_buf(logits, (long long)s.T * s.E * 4) || !ok_buf(w_gate, wsz * es) ||
       !ok_buf(w_up, wsz * es) || !ok_buf(w_down, wsz * es) ||
-      !ok_buf(dx, (long long)s.T * s.d * 4) || !ok_buf(dw_gate, wsz * 4) ||
-      !ok_buf(dw_up, wsz * 4) || !ok_buf(dw_down, wsz * 4) || !ok_buf(d_gate, R * 4) ||
+      !ok_buf(dx, (long long)s.T * s.d * 4) || !ok_buf(dw_gate, wsz * wes) ||
+      !ok_buf(dw_up, wsz * wes) || !ok_buf(dw_down, wsz * wes) || !ok_buf(d_gate, R * 4) ||
       !ok_buf(d_logits, (long long)s.T * s.E * 4))
     return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(s, op, ws, ws_bytes)) != MOE_OK) return st;

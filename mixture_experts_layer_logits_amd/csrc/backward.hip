@@ -224,10 +224,25 @@ struct BwdArgs {
   void* out_dgu;           // BWD_DH: dg | du
   void* out_h;             // BWD_DH: h
   void* out_dX;            // BWD_DX
-  float* dw_down;          // BWD_WD
-  float* dw_gate;          // BWD_WGU
-  float* dw_up;
+  void* dw_down;           // BWD_WD
+  void* dw_gate;           // BWD_WGU
+  void* dw_up;
+  int wgrad_bf16;          // weight gradients stored as bf16 (else fp32)
 };
+
+// Element offset of weight-gradient entry (m, n) of expert e (BWD_WD: of
+// dw_down [E, d, F]; BWD_WGU: rows m < F of dw_gate, then dw_up), and the
+// base pointer it belongs to.
+template <int MODE>
+__device__ __forceinline__ long long wgrad_offset(const BwdArgs& a, int e, int m, int n,
+                                                  void*& base) {
+  if (MODE == BWD_WD) {
+    base = a.dw_down;
+    return ((long long)e * a.d + m) * a.F + n;
+  }
+  base = (m < a.F) ? a.dw_gate : a.dw_up;
+  return ((long long)e * a.F + (m < a.F ? m : m - a.F)) * a.d + n;
+}
 
 // The operands of one tile, resolved from the mode.
 template <typename T>
@@ -336,14 +351,13 @@ __device__ __forceinline__ void bwd_store4(const BwdArgs& a, const BwdJob<T>& j,
     bf16_t* o = static_cast<bf16_t*>(a.out_dX) + (long long)(j.row0 + m) * a.d + n;
     *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
   } else {
-    float* o;
-    if (MODE == BWD_WD) {
-      o = a.dw_down + ((long long)j.e * a.d + m) * a.F + n;
-    } else {
-      o = (m < a.F) ? a.dw_gate + ((long long)j.e * a.F + m) * a.d + n
-                    : a.dw_up + ((long long)j.e * a.F + (m - a.F)) * a.d + n;
-    }
-    *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
+    void* base;
+    const long long o = wgrad_offset<MODE>(a, j.e, m, n, base);
+    if (a.wgrad_bf16)
+      *reinterpret_cast<uint2*>(static_cast<bf16_t*>(base) + o) =
+          make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    else
+      *reinterpret_cast<float4*>(static_cast<float*>(base) + o) = make_float4(v[0], v[1], v[2], v[3]);
   }
 }
 
@@ -542,12 +556,11 @@ bwd_generic_kernel(const BwdArgs args) {
         static_cast<T*>(args.out_h)[r * args.F + n] = from_f32<T>(sl * u);
       } else if (MODE == BWD_DX) {
         static_cast<T*>(args.out_dX)[(long long)(job.row0 + m) * args.d + n] = from_f32<T>(v);
-      } else if (MODE == BWD_WD) {
-        args.dw_down[((long long)job.e * args.d + m) * args.F + n] = v;
       } else {
-        float* o = (m < args.F) ? args.dw_gate + ((long long)job.e * args.F + m) * args.d + n
-                                : args.dw_up + ((long long)job.e * args.F + (m - args.F)) * args.d + n;
-        *o = v;
+        void* base;
+        const long long o = wgrad_offset<MODE>(args, job.e, m, n, base);
+        if (args.wgrad_bf16) static_cast<bf16_t*>(base)[o] = f32_to_bf16(v);
+        else static_cast<float*>(base)[o] = v;
       }
     }
   }
@@ -902,9 +915,9 @@ hipError_t launch_backward(const moe_shape& s, const void* dy, const void* x_per
                            const int32_t* topk_idx, const float* topk_w,
                            const float* logits, const void* w_gate, const void* w_up,
                            const void* w_down, const void* x, const void* ws_gate,
-                           const void* ws_up, const void* ws_down, float* dx, float* dw_gate,
-                           float* dw_up, float* dw_down, float* dws_gate, float* dws_up,
-                           float* dws_down, float* d_gate, float* d_logits,
+                           const void* ws_up, const void* ws_down, float* dx, void* dw_gate,
+                           void* dw_up, void* dw_down, void* dws_gate, void* dws_up,
+                           void* dws_down, float* d_gate, float* d_logits,
                            const BwdWs& ws, hipStream_t st) {
   (void)row_token;
   const bool bf = s.dtype == MOE_DTYPE_BF16;
@@ -938,6 +951,7 @@ hipError_t launch_backward(const moe_shape& s, const void* dy, const void* x_per
   a.out_dX = ws.dX;
   a.dw_down = dw_down;
   a.dw_gate = dw_gate;
+  a.wgrad_bf16 = s.wgrad_dtype == MOE_DTYPE_BF16;
   a.dw_up = dw_up;
   hipError_t e = run_backward_any(s, a, ws, st);
   if (e != hipSuccess) return e;
@@ -971,6 +985,7 @@ hipError_t launch_backward(const moe_shape& s, const void* dy, const void* x_per
     b.dw_down = dws_down;
     b.dw_gate = dws_gate;
     b.dw_up = dws_up;
+    b.wgrad_bf16 = a.wgrad_bf16;
     BwdWs w2 = ws;
     w2.tiles = ws.s_tiles;
     w2.tiles2 = ws.s_tiles2;

@@ -129,9 +129,9 @@ hipError_t launch_backward(const moe_shape& s, const void* dy, const void* x_per
                            const int32_t* topk_idx, const float* topk_w,
                            const float* logits, const void* w_gate, const void* w_up,
                            const void* w_down, const void* x, const void* ws_gate,
-                           const void* ws_up, const void* ws_down, float* dx, float* dw_gate,
-                           float* dw_up, float* dw_down, float* dws_gate, float* dws_up,
-                           float* dws_down, float* d_gate, float* d_logits,
+                           const void* ws_up, const void* ws_down, float* dx, void* dw_gate,
+                           void* dw_up, void* dw_down, void* dws_gate, void* dws_up,
+                           void* dws_down, float* d_gate, float* d_logits,
                            const BwdWs& ws, hipStream_t st);
 
 }  // namespace moe

@@ -160,18 +160,19 @@ class MoELayer:
     def _alloc_grad(self):
         c = self.cfg
         dev, f32 = self.device, torch.float32
+        wt = torch.bfloat16 if getattr(c, "wgrad_dtype", 0) == L.MOE_DTYPE_BF16 else f32
         self.grad = dict(
             dx=torch.empty(c.T, c.d, dtype=f32, device=dev),
-            dw_gate=torch.empty(c.E, c.F, c.d, dtype=f32, device=dev),
-            dw_up=torch.empty(c.E, c.F, c.d, dtype=f32, device=dev),
-            dw_down=torch.empty(c.E, c.d, c.F, dtype=f32, device=dev),
+            dw_gate=torch.empty(c.E, c.F, c.d, dtype=wt, device=dev),
+            dw_up=torch.empty(c.E, c.F, c.d, dtype=wt, device=dev),
+            dw_down=torch.empty(c.E, c.d, c.F, dtype=wt, device=dev),
             d_gate=torch.empty(c.T, c.k, dtype=f32, device=dev),
             d_logits=torch.empty(c.T, c.E, dtype=f32, device=dev))
         fs = c.F_shared
         self.grad.update(
-            dws_gate=torch.empty(fs, c.d, dtype=f32, device=dev) if fs else None,
-            dws_up=torch.empty(fs, c.d, dtype=f32, device=dev) if fs else None,
-            dws_down=torch.empty(c.d, fs, dtype=f32, device=dev) if fs else None)
+            dws_gate=torch.empty(fs, c.d, dtype=wt, device=dev) if fs else None,
+            dws_up=torch.empty(fs, c.d, dtype=wt, device=dev) if fs else None,
+            dws_down=torch.empty(c.d, fs, dtype=wt, device=dev) if fs else None)
 
     def gu_views(self):
         """(routed [R, 2F], shared [T, 2Fs] or None) views of gu_save."""

@@ -60,6 +60,7 @@ class MoEConfig:
     score: int = SCORE_SOFTMAX
     renorm: int = 1             # renormalise the k gates over the selected set
     dtype: int = DTYPE_BF16
+    wgrad_dtype: int = DTYPE_F32    # storage of the weight gradients
     x_std: float = 1.0
     w_std: float = 0.02
     router_std: float = 0.02

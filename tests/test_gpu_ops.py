@@ -320,17 +320,18 @@ def _bwd_inputs(cfg, skew=None, dev="cuda"):
 def _run_bwd(M, cfg, inp, g):
     dev = "cuda"
     f32 = torch.float32
+    wt = torch.bfloat16 if cfg.wgrad_dtype == 1 else f32
     out = dict(dx=torch.empty(cfg.T, cfg.d, device=dev),
-               dw_gate=torch.empty(cfg.E, cfg.F, cfg.d, device=dev),
-               dw_up=torch.empty(cfg.E, cfg.F, cfg.d, device=dev),
-               dw_down=torch.empty(cfg.E, cfg.d, cfg.F, device=dev),
+               dw_gate=torch.empty(cfg.E, cfg.F, cfg.d, device=dev, dtype=wt),
+               dw_up=torch.empty(cfg.E, cfg.F, cfg.d, device=dev, dtype=wt),
+               dw_down=torch.empty(cfg.E, cfg.d, cfg.F, device=dev, dtype=wt),
                d_gate=torch.empty(cfg.T, cfg.k, device=dev),
                d_logits=torch.empty(cfg.T, cfg.E, device=dev))
     fs = cfg.F_shared
     if fs:
-        out.update(dws_gate=torch.empty(fs, cfg.d, device=dev),
-                   dws_up=torch.empty(fs, cfg.d, device=dev),
-                   dws_down=torch.empty(cfg.d, fs, device=dev))
+        out.update(dws_gate=torch.empty(fs, cfg.d, device=dev, dtype=wt),
+                   dws_up=torch.empty(fs, cfg.d, device=dev, dtype=wt),
+                   dws_down=torch.empty(cfg.d, fs, device=dev, dtype=wt))
     for v in out.values():
         v.fill_(float("nan"))
     shape = M.make_shape(cfg)
@@ -364,6 +365,11 @@ BWD_CASES = [
     ("generic_bf16_t77", 77, 200, 6, 2, 96, 1, 0, 0, False),
     ("fp32_t128", 128, 64, 8, 2, 64, 0, 0, 1, False),
     ("fp32_odd_full_probs_t37", 37, 20, 5, 3, 12, 0, 0, 0, True),
+    # weight gradients stored as bf16 (direct-to-LDS with a shared expert,
+    # MFMA with empty experts, generic)
+    ("dma_shared_wgrad_bf16_t300", 300, 256, 16, 4, 256, 1, 1, 1, False, 512, 1),
+    ("mfma_skewed_wgrad_bf16_t400", 400, 128, 16, 4, 128, 1, 0, 1, True, 0, 1),
+    ("generic_wgrad_bf16_t77", 77, 200, 6, 2, 96, 1, 0, 0, False, 40, 1),
 ]
 
 
@@ -371,10 +377,11 @@ BWD_CASES = [
 def test_ffn_backward(case):
     name, T, d, E, k, F, dtype, score, renorm, skew = case[:10]
     Fs = case[10] if len(case) > 10 else 0
+    wgrad = case[11] if len(case) > 11 else 0
     _log(f"[backward] {name}")
     M = _lib()
     cfg = MoEConfig(name, T=T, d=d, E=E, k=k, F=F, F_shared=Fs, dtype=dtype, score=score,
-                    renorm=renorm, backward=True)
+                    renorm=renorm, backward=True, wgrad_dtype=wgrad)
     prec = prec_of(cfg)
     inp = make_inputs(cfg, device="cuda")
     g = _bwd_inputs(cfg, skew)

@@ -155,40 +155,51 @@ struct MxScales {
   uint8_t* Cd;
 };
 
-template <int BM, int BN, int NB, int EPI, int WM, int WN, int SG>
-__global__ void __launch_bounds__(64 * WM * WN)
-gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
-  constexpr int NW = WM * WN;
+// The shape of one tile class: CLS 0 is BM x BN with WM x WN waves and a
+// four-stage ring; CLS 1 (tail tiles) is BM/2 x 2BN with (WM/2) x (2WN) waves,
+// so each wave keeps its (BM/WM) x (BN/WN) block and registers, and a
+// three-stage ring (its 640-row stages do not fit four times beside the
+// scales).
+template <int BM, int BN, int NB, int WM, int WN, int SG, int CLS>
+struct MxShape {
+  static constexpr int NW = WM * WN;
+  static constexpr int BMC = CLS ? BM / 2 : BM;
+  static constexpr int BNC = CLS ? 2 * BN : BN;
+  static constexpr int WMC = CLS ? WM / 2 : WM;
+  static constexpr int WNC = CLS ? 2 * WN : WN;
+  static constexpr int NS = CLS ? 3 : 4;            // LDS stages
+  static constexpr int ROWS = BMC + NB * BNC;       // operand rows per stage
+  static constexpr int BPW = ROWS / 16 / NW;        // 1 KiB data loads per wave per slice
+  static constexpr int SB = ROWS / 64;              // 64-row scale blocks per scale slice
+  static constexpr int SPW = (SB + NW - 1) / NW;    // scale loads per wave (surplus repeats the last)
+  static constexpr int NLD = SG == 1 ? BPW + SPW : BPW;
+  static constexpr int SSTR = SG == 1 ? 4 : 16;     // LDS bytes per row of a scale slice
+  static constexpr int RING = NS * ROWS * 64;       // bytes of the operand ring
+  static constexpr int SRING = (SG == 1 ? NS : 2) * ROWS * SSTR;
+  static_assert(ROWS % (16 * NW) == 0 && BMC % 64 == 0 && BNC % 64 == 0, "load blocks");
+};
+
+template <int BM, int BN, int NB, int EPI, int WM, int WN, int SG, int CLS>
+__device__ __forceinline__ void mx_tile(const GemmArgs& args, const MxScales& sc,
+                                        const TileJob<uint8_t, typename std::conditional<
+                                            EPI == EPI_SWIGLU, uint8_t, bf16_t>::type>& job,
+                                        uint8_t* ring, uint8_t* sring) {
+  using S = MxShape<BM, BN, NB, WM, WN, SG, CLS>;
+  constexpr int NW = S::NW, BMC = S::BMC, BNC = S::BNC, WNC = S::WNC, NS = S::NS;
+  constexpr int ROWS = S::ROWS, BPW = S::BPW, SB = S::SB, SPW = S::SPW, NLD = S::NLD;
+  constexpr int SSTR = S::SSTR;
   constexpr int BK = 64;                        // fp8 values (bytes) per row per stage
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MI = WTM / 32, NJ = WTN / 32;
   constexpr int NBJ = NB * NJ;                  // weight fragments per wave
   constexpr int H0 = NBJ / 2, H1 = NBJ - H0;    // ... in each half-step
-  constexpr int ROWS = BM + NB * BN;            // operand rows per stage
-  constexpr int BPW = ROWS / 16 / NW;           // 1 KiB data loads per wave per slice
-  constexpr int SPW = ROWS / 64 / NW;           // scale loads per wave per scale slice
-  // SG = 1: every slice also loads its scale dword per row (exact counts);
-  // SG = 8: a group's scale loads ride along every eighth slice, and the
-  // waits count data loads only (waiting at most one instruction longer)
-  constexpr int NLD = SG == 1 ? BPW + SPW : BPW;
-  constexpr int SSTR = SG == 1 ? 4 : 16;        // LDS bytes per row of a scale slice
-  static_assert(SG == 1 || SG == 8, "scale grouping");
   static_assert(MI >= 1 && NJ >= 1 && H0 >= 1 && H0 == H1, "tile too small or odd");
-  static_assert(ROWS % (64 * NW) == 0, "every wave loads the same number of blocks");
-  using TOut = typename std::conditional<EPI == EPI_SWIGLU, uint8_t, bf16_t>::type;
-
-  // four stages of operand rows; beside them four stages of scale dwords
-  // (SG = 1) or two buffers of 16 scale bytes per row (SG = 8)
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[4 * ROWS * BK];
-  __shared__ __attribute__((aligned(1024))) uint8_t sring[(SG == 1 ? 4 : 2) * ROWS * SSTR];
-
-  TileJob<uint8_t, TOut> job;
-  if (!decode_tile<BM, BN>(args, job)) return;
+  static_assert(NW == 8, "the tail class pairs wave rows");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WN, wn = wave % WN;
+  const int wm = wave / WNC, wn = wave % WNC;
   const bool live = job.m0 + wm * WTM < job.rows;
   const int kb = job.K / 32;                    // scale bytes per operand row
   // SG = 8: scale group g covers K blocks 16 g .. 16 g + 15 (steps 8 g ..
@@ -228,47 +239,51 @@ gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
     const int row = (wave * BPW + j) * 16;
     const uint8_t* src;
     int ld, rbase, rlimit;
-    if (row < BM) {
+    if (row < BMC) {
       src = job.A;
       ld = (int)job.lda;
       rbase = job.m0 + row;
       rlimit = job.rows;
     } else {
-      const int rb = row - BM;
-      src = (rb < BN) ? job.B0 : job.B1;
+      const int rb = row - BMC;
+      src = (rb < BNC) ? job.B0 : job.B1;
       ld = job.K;
-      rbase = job.n0 + (rb < BN ? rb : rb - BN);
+      rbase = job.n0 + (rb < BNC ? rb : rb - BNC);
       rlimit = job.N;
     }
     int r = rbase + (lane >> 2);
     r = r < rlimit ? r : rlimit - 1;                    // clamp: never stored
-    if (row < BM && job.gather) r = job.gather[r];
+    if (row < BMC && job.gather) r = job.gather[r];
     g_off[j] = (uint32_t)(r * ld + dma_c * 16);
     g_base[j] = uniform_ptr(src);
   }
-  // Scale loads: block b = wave * SPW + j covers stage rows 64 b .. + 63,
-  // lane l fetching row 64 b + l.
+  // Scale loads: block b = wave * SPW + j (the last block again where the
+  // waves have more loads than there are blocks) covers stage rows 64 b ..
+  // + 63, lane l fetching row 64 b + l.
   uint32_t s_off[SPW];
+  uint32_t s_lds[SPW];
   const char* s_base[SPW];
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
-    const int row = (wave * SPW + j) * 64 + lane;       // lane-varying
-    const int blk0 = (wave * SPW + j) * 64;             // wave-uniform
+    const int blk = min(wave * SPW + j, SB - 1);        // wave-uniform
+    const int blk0 = blk * 64;
+    const int row = blk0 + lane;
     const uint8_t* src;
     int rbase, rlimit;
-    if (blk0 < BM) {
+    if (blk0 < BMC) {
       src = sA;
       rbase = job.m0 + row;
       rlimit = job.rows;
     } else {
-      const int rb = blk0 - BM;
-      src = (rb < BN) ? sB0 : sB1;
-      rbase = job.n0 + (row - BM - (rb < BN ? 0 : BN));
+      const int rb = blk0 - BMC;
+      src = (rb < BNC) ? sB0 : sB1;
+      rbase = job.n0 + (row - BMC - (rb < BNC ? 0 : BNC));
       rlimit = job.N;
     }
     int r = rbase < rlimit ? rbase : rlimit - 1;
-    if (blk0 < BM && job.gather) r = job.gather[r];
+    if (blk0 < BMC && job.gather) r = job.gather[r];
     s_off[j] = (uint32_t)(r * kb);
+    s_lds[j] = (uint32_t)blk * 64 * SSTR;
     s_base[j] = uniform_ptr(src);
   }
   // Slice kt: its scale loads (SG = 1, or the first slice of a group), then
@@ -280,13 +295,13 @@ gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
       for (int j = 0; j < SPW; ++j) {
         const uint32_t off = s_off[j];
         if constexpr (SG == 1) {
-          const uint32_t lds = (uint32_t)(uintptr_t)MOE_AS_LDS(sdst + (wave * SPW + j) * 256);
+          const uint32_t lds = (uint32_t)(uintptr_t)MOE_AS_LDS(sdst + s_lds[j]);
           const char* base = s_base[j] + (size_t)(kt >> 1) * 4;
           asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
                        :: "s"(lds), "v"(off), "s"(base) : "memory");
         } else {
           const uint32_t lds = (uint32_t)(uintptr_t)MOE_AS_LDS(
-              sring + ((kt >> 3) & 1) * (ROWS * 16) + (wave * SPW + j) * 1024);
+              sring + ((kt >> 3) & 1) * (ROWS * 16) + s_lds[j]);
           const char* base = s_base[j] + sg_start(kt >> 3);
           asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                        :: "s"(lds), "v"(off), "s"(base) : "memory");
@@ -318,7 +333,7 @@ gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
   const int c0 = ((0 + hsel) ^ swz(frag_row)) << 4;   // k = 16 hsel ..
   const int c1 = ((2 + hsel) ^ swz(frag_row)) << 4;   // k = 32 + 16 hsel ..
   const int a_row = wm * WTM + frag_row;                // stage row of A fragment 0
-  const int b_row = BM + wn * WTN + frag_row;           // ... of B fragment (0, 0)
+  const int b_row = BMC + wn * WTN + frag_row;          // ... of B fragment (0, 0)
 
   auto read_frag = [&](const uint8_t* stage, int row) -> i32x8_t {
     const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(stage + row * BK + c0);
@@ -337,7 +352,7 @@ gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
     return (int)sbase[row * SSTR + hsel];
   };
   // weight fragment f (0 .. NBJ-1) = (b, j) with b = f / NJ, j = f % NJ
-  auto brow = [&](int f) { return b_row + (f / NJ) * BN + (f % NJ) * 32; };
+  auto brow = [&](int f) { return b_row + (f / NJ) * BNC + (f % NJ) * 32; };
 
   const int KT = job.klen / BK;
   const int kbeg = job.k0 / BK;
@@ -348,10 +363,12 @@ gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto wait_slice = [&](int ready, int issued) {
-    const int younger = issued - 1 - ready;
-    if (younger >= 2) wait_vmcnt<2 * NLD>();
-    else if (younger == 1) wait_vmcnt<NLD>();
+  // Waits until this wave's loads of slice `ready` are done, given that
+  // slices 0 .. last are issued, leaving the younger ones in flight.
+  auto wait_slice = [&](int ready, int last) {
+    const int younger = last - ready;
+    if (NS > 3 && younger >= 2) wait_vmcnt<2 * NLD>();
+    else if (younger >= 1) wait_vmcnt<NLD>();
     else wait_vmcnt<0>();
   };
 
@@ -378,16 +395,15 @@ gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
     int as[2][MI];
     i32x8_t bf0[H0], bf1[H1];
     int bs0[H0], bs1[H1];
-    // Step s uses ring position RP = s % 4 (the loop runs in groups of four
-    // steps from s = 0, so RP is static); P = s % 2 picks the token-fragment
-    // buffer and the scale byte within the stage's dwords.
-    auto step = [&](auto rp_c, int s) {
+    // Step s uses ring position RP = s % NS and token-fragment buffer
+    // P = s % 2, both static: the loop runs in groups of lcm(NS, 2) steps.
+    auto step = [&](auto rp_c, auto p_c, int s) {
       constexpr int RP = decltype(rp_c)::value;
-      constexpr int P = RP & 1;
+      constexpr int P = decltype(p_c)::value;
       const uint8_t* cur = stage(RP);
       const uint8_t* scur = scale_base(s, RP);
-      const uint8_t* nxt = stage((RP + 1) & 3);
-      const uint8_t* snxt = scale_base(s + 1, (RP + 1) & 3);
+      const uint8_t* nxt = stage((RP + 1) % NS);
+      const uint8_t* snxt = scale_base(s + 1, (RP + 1) % NS);
       if constexpr (LIVE) {
 #pragma unroll
         for (int f = 0; f < H1; ++f) {
@@ -400,7 +416,6 @@ gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
           for (int i = 0; i < MI; ++i)
             acc[f / NJ][i][f % NJ] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                 bf0[f], af[P][i], acc[f / NJ][i][f % NJ], 0, 0, 0, bs0[f], 0, as[P][i]);
-        pin_half(0);
         // reads spread between the MFMAs (two reads, one MFMA, ...)
 #pragma unroll
         for (int r = 0; r < 3; ++r) {
@@ -408,12 +423,16 @@ gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        pin_half(0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (s + 1 < KT) wait_slice(s + 1, s + 3 < KT ? s + 3 : KT);
+      if (s + 1 < KT) wait_slice(s + 1, s + NS - 2 < KT - 1 ? s + NS - 2 : KT - 1);
       barrier();
-      if (s + 3 < KT)
-        dma(ring + ((RP + 3) & 3) * (ROWS * BK), sring + ((RP + 3) & 3) * (ROWS * 4), kbeg + s + 3);
+      // stage (s - 1) % NS, read for the last time before this barrier,
+      // takes slice s + NS - 1
+      if (s + NS - 1 < KT)
+        dma(ring + ((RP + NS - 1) % NS) * (ROWS * BK), sring + ((RP + NS - 1) % NS) * (ROWS * 4),
+            kbeg + s + NS - 1);
       if constexpr (LIVE) {
         // the last step reads the (unused) next stage too, keeping one shape
 #pragma unroll
@@ -433,19 +452,19 @@ gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
             acc[(H0 + f) / NJ][i][(H0 + f) % NJ] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                 bf1[f], af[P][i], acc[(H0 + f) / NJ][i][(H0 + f) % NJ], 0, 0, 0, bs1[f], 0,
                 as[P][i]);
-        pin_half(H0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
+        pin_half(H0);
       }
       __builtin_amdgcn_sched_barrier(0);
     };
     dma(ring, sring, kbeg);
     if (KT > 1) dma(ring + ROWS * BK, sring + ROWS * 4, kbeg + 1);
-    if (KT > 2) dma(ring + 2 * ROWS * BK, sring + 2 * ROWS * 4, kbeg + 2);
-    wait_slice(0, KT < 3 ? KT : 3);
+    if (NS > 3 && KT > 2) dma(ring + 2 * ROWS * BK, sring + 2 * ROWS * 4, kbeg + 2);
+    wait_slice(0, KT - 1 < NS - 2 ? KT - 1 : NS - 2);
     barrier();
     if constexpr (LIVE) {
 #pragma unroll
@@ -459,20 +478,39 @@ gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
         bs0[f] = read_scale(scale_base(0, 0), brow(f));
       }
     }
-    using r0 = std::integral_constant<int, 0>;
-    using r1 = std::integral_constant<int, 1>;
-    using r2 = std::integral_constant<int, 2>;
-    using r3 = std::integral_constant<int, 3>;
+    using c0_ = std::integral_constant<int, 0>;
+    using c1_ = std::integral_constant<int, 1>;
+    using c2_ = std::integral_constant<int, 2>;
+    using c3_ = std::integral_constant<int, 3>;
     int kt = 0;
-    for (; kt + 4 <= KT; kt += 4) {
-      step(r0{}, kt);
-      step(r1{}, kt + 1);
-      step(r2{}, kt + 2);
-      step(r3{}, kt + 3);
-    }
-    if (kt < KT) {   // KT is even (K is a multiple of 128)
-      step(r0{}, kt);
-      step(r1{}, kt + 1);
+    if constexpr (NS == 4) {
+      for (; kt + 4 <= KT; kt += 4) {
+        step(c0_{}, c0_{}, kt);
+        step(c1_{}, c1_{}, kt + 1);
+        step(c2_{}, c0_{}, kt + 2);
+        step(c3_{}, c1_{}, kt + 3);
+      }
+      if (kt < KT) {   // KT is even (K is a multiple of 128)
+        step(c0_{}, c0_{}, kt);
+        step(c1_{}, c1_{}, kt + 1);
+      }
+    } else {
+      for (; kt + 6 <= KT; kt += 6) {
+        step(c0_{}, c0_{}, kt);
+        step(c1_{}, c1_{}, kt + 1);
+        step(c2_{}, c0_{}, kt + 2);
+        step(c0_{}, c1_{}, kt + 3);
+        step(c1_{}, c0_{}, kt + 4);
+        step(c2_{}, c1_{}, kt + 5);
+      }
+      if (kt < KT) {   // 2 or 4 steps left
+        step(c0_{}, c0_{}, kt);
+        step(c1_{}, c1_{}, kt + 1);
+        if (kt + 2 < KT) {
+          step(c2_{}, c0_{}, kt + 2);
+          step(c0_{}, c1_{}, kt + 3);
+        }
+      }
     }
   };
   if (!live) {
@@ -538,6 +576,28 @@ gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
   }
 }
 
+
+template <int BM, int BN, int NB, int EPI, int WM, int WN, int SG, int TL>
+__global__ void __launch_bounds__(64 * WM * WN)
+gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
+  using S0 = MxShape<BM, BN, NB, WM, WN, SG, 0>;
+  using S1 = MxShape<BM, BN, NB, WM, WN, SG, 1>;
+  constexpr int RING = (TL && S1::RING > S0::RING) ? S1::RING : S0::RING;
+  constexpr int SRING = (TL && S1::SRING > S0::SRING) ? S1::SRING : S0::SRING;
+  static_assert(RING + SRING + 64 <= 160 * 1024, "LDS");
+  using TOut = typename std::conditional<EPI == EPI_SWIGLU, uint8_t, bf16_t>::type;
+  // the operand ring, and beside it the scale slices (+64 bytes: the last
+  // step's unused read of a next step may touch a byte past the end)
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[RING];
+  __shared__ __attribute__((aligned(1024))) uint8_t sring[SRING + 64];
+  TileJob<uint8_t, TOut> job;
+  if (!decode_tile<BM, BN>(args, job)) return;
+  if (TL && __builtin_amdgcn_readfirstlane(job.cls) != 0)
+    mx_tile<BM, BN, NB, EPI, WM, WN, SG, 1>(args, sc, job, ring, sring);
+  else
+    mx_tile<BM, BN, NB, EPI, WM, WN, SG, 0>(args, sc, job, ring, sring);
+}
+
 // Scale loads are grouped eight K steps at a time when every group of the
 // launch has at least 16 scale bytes per row (K >= 512).
 template <int BM, int BN, int NB, int EPI, int WM, int WN>
@@ -546,9 +606,9 @@ hipError_t launch_mx_gemm(const GemmArgs& a, const MxScales& sc, int R, hipStrea
   if (grid == 0) return hipSuccess;
   const bool grouped = (a.E == 0 || a.K >= 512) && (a.Td == 0 || a.Kd >= 512);
   if (grouped)
-    gemm_mx_kernel<BM, BN, NB, EPI, WM, WN, 8><<<grid, 64 * WM * WN, 0, st>>>(a, sc);
+    gemm_mx_kernel<BM, BN, NB, EPI, WM, WN, 8, 1><<<grid, 64 * WM * WN, 0, st>>>(a, sc);
   else
-    gemm_mx_kernel<BM, BN, NB, EPI, WM, WN, 1><<<grid, 64 * WM * WN, 0, st>>>(a, sc);
+    gemm_mx_kernel<BM, BN, NB, EPI, WM, WN, 1, 1><<<grid, 64 * WM * WN, 0, st>>>(a, sc);
   return hipGetLastError();
 }
 
@@ -620,10 +680,12 @@ hipError_t launch_grouped_ffn_mxfp8(const moe_shape& s, const uint8_t* xq, const
     s2.Bd0 = w.sdown_s;
   }
   if (a1.E == 0 && !shared) return hipSuccess;
+  // routed groups use tail tiles (BM/2 x 2BN) for their last rows
+  a1.tail = a2.tail = 1;
   if (a1.E > 0) {
     schedule_tiles_kernel<<<1, 1024, 0, st>>>(offsets, s.E, MX_FC1_BM, cdiv(s.F, MX_FC1_BN),
                                               ws.tiles1, MX_FC2_BM, cdiv(s.d, MX_FC2_BN),
-                                              ws.tiles2, 0);
+                                              ws.tiles2, 1);
   }
   hipError_t e = launch_mx_gemm<MX_FC1_BM, MX_FC1_BN, 2, EPI_SWIGLU, 4, 2>(a1, s1, R, st);
   if (e != hipSuccess) return e;

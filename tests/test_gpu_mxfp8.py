@@ -151,6 +151,50 @@ def test_grouped_ffn_mxfp8(case):
         assert_close("y_shared", ys, ref_s, "bf16")
 
 
+# Rows per expert around every tile-height boundary (full 256-row tiles, the
+# 128-row x 2BN tail tiles, tails of <= 64 rows, empty experts), routed rows
+# drawn as a seeded permutation of the tokens.
+TAIL_COUNTS = (0, 1, 63, 64, 65, 127, 128, 129, 192, 255, 256, 257, 320, 384,
+               511, 512, 600)
+MX_TAIL_CASES = [
+    # d = 256, F = 384: per-step scale dwords; FC2's tail tiles (512 columns)
+    # run half past N = 256
+    ("mx_tail_classes_d256_f384", 256, 384),
+    # d = 512, F = 768: grouped scales, FC2's last group window moved back
+    ("mx_tail_classes_d512_f768", 512, 768),
+]
+
+
+@pytest.mark.parametrize("name,d,F", MX_TAIL_CASES)
+def test_grouped_ffn_mxfp8_tail_classes(name, d, F):
+    _log(f"[mx ffn tails] {name}")
+    M = _lib()
+    counts = np.array(TAIL_COUNTS)
+    E, T = len(counts), int(counts.sum())
+    cfg = MoEConfig(name, T=T, d=d, E=E, k=1, F=F, dtype=1)
+    inp = make_inputs(cfg, device="cuda")
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    row_token = np.random.default_rng(5).permutation(T).astype(np.int32)
+    xq, xs = _quantize(M, inp["x"])
+    wq = _quantized_weights(M, inp, ("w_gate", "w_up", "w_down"))
+    yp = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
+    shape = M.make_shape(cfg)
+    n = M.moe_workspace_size(shape, 5)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+    M.moe_grouped_ffn_mxfp8(shape, xq, xs, torch.as_tensor(row_token).cuda(),
+                            torch.as_tensor(offsets).cuda(), *wq, *([None] * 6), yp, None, ws, n)
+    torch.cuda.synchronize()
+    ref = O.grouped_ffn_mxfp8(np64(inp["x"])[row_token], offsets, np64(inp["w_gate"]),
+                              np64(inp["w_up"]), np64(inp["w_down"]))
+    assert_close("y_perm", yp, ref, "bf16")
+    # rows of every expert checked on their own too (a wrong tail tile would
+    # hide in the Frobenius norm of the whole output)
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b > a:
+            assert_close(f"y_perm[expert {e}]", yp[a:b], ref[a:b], "bf16")
+
+
 # --------------------------------------------------------------------------
 # The layer's MXFP8 forward: route -> maps-only permute -> quantise x ->
 # MXFP8 grouped FFN -> combine, against the oracle routing from its own

@@ -386,6 +386,35 @@ def combine(y_perm, token_row, topk_w, y_shared=None, prec="f32"):
     return out_f32(prec)(acc)
 
 
+def grouped_ffn_combine(x_perm, offsets, token_row, topk_w, w_gate, w_up,
+                        w_down, shared=None, prec="bf16"):
+    """The grouped FFN with the unpermute-and-scale folded into FC2 (the
+    Primus blog's MegaMoE section fuses the combine into the second grouped
+    GEMM): y[t] = ys[t] + sum_j w[t,j] * (h_r . wd[e]^T), r = token_row[t,j].
+
+    h is materialised at ``prec`` as in the unfused layer; the expert outputs
+    (and the shared expert's) are never materialised, so they are not
+    rounded: they enter the fp64 sum exactly, and y is rounded to fp32 once.
+    ``shared`` is None or (x, ws_gate, ws_up, ws_down).
+    """
+    x_perm = as64(x_perm)
+    R, d = x_perm.shape
+    E = len(offsets) - 1
+    y_exp = np.zeros((R, d), dtype=F64)
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b == a:
+            continue
+        h = swiglu_ffn(x_perm[a:b], w_gate[e], w_up[e], w_down[e], prec)["h"]
+        y_exp[a:b] = h @ as64(w_down[e]).T
+    ys = None
+    if shared is not None:
+        xs, wsg, wsu, wsd = shared
+        hs = swiglu_ffn(xs, wsg, wsu, wsd, prec)["h"]
+        ys = hs @ as64(wsd).T
+    return combine(y_exp, token_row, topk_w, ys, prec)
+
+
 # --------------------------------------------------------------------------
 # backward
 # --------------------------------------------------------------------------

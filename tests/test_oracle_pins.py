@@ -235,15 +235,17 @@ def _small_inputs(rng, T, d, E, F, Fs=0, prec="f64"):
     return inp
 
 
-def _loop_ffn(xt, wg, wu, wd, rnd):
-    """Plain-Python SwiGLU FFN of one token vector."""
+def _loop_ffn(xt, wg, wu, wd, rnd, rnd_out=None):
+    """Plain-Python SwiGLU FFN of one token vector (h rounded by rnd, the
+    output by rnd_out, default rnd)."""
+    rnd_out = rnd if rnd_out is None else rnd_out
     F, d = len(wg), len(xt)
     h = []
     for f in range(F):
         g = sum(xt[i] * wg[f][i] for i in range(d))
         u = sum(xt[i] * wu[f][i] for i in range(d))
         h.append(float(rnd(g / (1.0 + math.exp(-g)) * u)))
-    return [float(rnd(sum(h[f] * wd[i][f] for f in range(F))))
+    return [float(rnd_out(sum(h[f] * wd[i][f] for f in range(F))))
             for i in range(d)]
 
 
@@ -277,6 +279,62 @@ def test_forward_matches_dense_bruteforce(prec, shared):
             acc = [a + G[t, e] * b for a, b in zip(acc, ye)]
         tol = 1e-12 if prec == "f64" else 1e-6
         assert np.allclose(out["y"][t], acc, rtol=tol, atol=tol)
+
+
+@pytest.mark.parametrize("shared", [0, 3])
+def test_ffn_combine_matches_dense_bruteforce(shared):
+    """The FFN with the combine folded into FC2: per token, a plain loop over
+    the experts its dense gate row selects, h rounded to bf16 and the expert
+    outputs kept exact; y rounded to fp32 once."""
+    rng = np.random.default_rng(30 + shared)
+    T, d, E, k, F = 11, 4, 5, 3, 3
+    inp = _small_inputs(rng, T, d, E, F, shared, "bf16")
+    cfg = MoEConfig("t", T=T, d=d, E=E, k=k, F=F, F_shared=shared)
+    out = O.forward(inp, cfg, prec="bf16")
+    sh = (inp["x"], inp["ws_gate"], inp["ws_up"], inp["ws_down"]) if shared else None
+    y = O.grouped_ffn_combine(out["x_perm"], out["offsets"], out["token_row"],
+                              out["topk_w"], inp["w_gate"], inp["w_up"],
+                              inp["w_down"], sh, "bf16")
+    rnd = O.rounder("bf16")
+    exact = lambda v: v
+    G = np.zeros((T, E))
+    for t in range(T):
+        for j in range(k):
+            G[t, out["topk_idx"][t, j]] = out["topk_w"][t, j]
+    x = inp["x"].tolist()
+    for t in range(T):
+        acc = [0.0] * d
+        if shared:
+            ys = _loop_ffn(x[t], inp["ws_gate"].tolist(), inp["ws_up"].tolist(),
+                           inp["ws_down"].tolist(), rnd, exact)
+            acc = [a + b for a, b in zip(acc, ys)]
+        for e in range(E):
+            if G[t, e] != 0.0:
+                ye = _loop_ffn(x[t], inp["w_gate"][e].tolist(), inp["w_up"][e].tolist(),
+                               inp["w_down"][e].tolist(), rnd, exact)
+                acc = [a + G[t, e] * b for a, b in zip(acc, ye)]
+        want = np.array(acc, dtype=np.float32).astype(np.float64)
+        assert np.allclose(y[t], want, rtol=1e-7, atol=1e-12)
+    # the unfused layer rounds each expert output to bf16 first
+    assert not np.array_equal(y, out["y"])
+    assert np.allclose(y, out["y"], rtol=2e-2, atol=1e-3)
+
+
+def test_ffn_combine_hand_worked():
+    """One token, one expert (gate 1), d = 2, F = 1: g = 1, u = 2, so
+    h = bf16(2 silu(1)) = bf16(1.46212) = 1.4609375 (1.0111011 in binary;
+    the next bf16 value up is 1.46875), and with w_down = (1/3, 1/7) the
+    combined output is fp32(h / 3), fp32(h / 7); the unfused layer's expert
+    output is bf16(h / 3) = 0.486328125 instead."""
+    x = np.array([[1.0, 2.0]])
+    h = 1.4609375
+    y = O.grouped_ffn_combine(x, np.array([0, 1]), np.array([[0]]), np.array([[1.0]]),
+                              np.array([[[1.0, 0.0]]]), np.array([[[0.0, 1.0]]]),
+                              np.array([[[1 / 3], [1 / 7]]]), None, "bf16")
+    assert y.tolist() == [[float(np.float32(h / 3)), float(np.float32(h / 7))]]
+    yp, _ = O.grouped_ffn(x, np.array([0, 1]), np.array([[[1.0, 0.0]]]),
+                          np.array([[[0.0, 1.0]]]), np.array([[[1 / 3], [1 / 7]]]), "bf16")
+    assert yp[0, 0] == 0.486328125
 
 
 def test_hand_worked_two_expert_example():

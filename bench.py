@@ -8,9 +8,11 @@ SwiGLU FFN (FC1 + FC2, plus the shared expert where the workload has one),
 combine, and the backward where the workload is a training step.  W untimed
 warm-up steps, then K timed steps between two device synchronisations.  Per
 stage, HIP events recorded on the stream the library launches on give the
-average duration; the grouped FFN stage (the dominant kernel pair) is priced
-against the MI355X roofline.  The CPU oracle is timed on a bounded sample of
-the same workload on the host cores.  Prints one JSON line.
+mean, median and minimum duration; the grouped FFN stage (the dominant kernel
+pair) is priced against the MI355X roofline.  The bandwidth stages (permute,
+combine) are also timed on their own, after a scratch write that evicts the
+caches and back to back.  The CPU oracle is timed on a bounded sample of the
+same workload on the host cores.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -145,6 +147,24 @@ def _oracle_pass(cfg, inp, T):
     return time.perf_counter() - t0
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def device_record(torch):
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2**30, 1)}
+
+
 def cpu_baseline(cfg, inp, sample_tokens=None, target_s=15.0):
     """The oracle, as it stands, on the first tokens of the same workload.
     Without a fixed sample size, passes on growing samples run until one
@@ -166,7 +186,7 @@ def cpu_baseline(cfg, inp, sample_tokens=None, target_s=15.0):
                    if i.get("user_api") == "blas"] or [1])
     kind = "forward+backward" if cfg.backward else "forward"
     return {"value": round(T / dt, 2), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(),
             "sample": f"first {T} of {cfg.T} tokens of the same workload, whole "
                       f"{kind} layer in the fp64 oracle ({dt:.1f} s)"}
 
@@ -229,9 +249,33 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    per_stage = {st: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1])
-                                    for s in range(args.steps)]))
-                 for i, st in enumerate(stages)}
+    stage_samples = {st: [evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]
+                     for i, st in enumerate(stages)}
+    per_stage = {st: float(np.mean(v)) for st, v in stage_samples.items()}
+
+    # The bandwidth stages on their own, each repetition after a 512 MiB
+    # scratch write that evicts the L2s and the 256 MB MALL ("flushed"), and
+    # back to back with their inputs left in the caches ("cache_resident").
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    isolated = {}
+    for st in ("permute", "combine"):
+        fn = getattr(layer, st)
+        res = {}
+        for label, flush in (("flushed", True), ("cache_resident", False)):
+            fn(inp)
+            pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                   for _ in range(args.steps)]
+            for s_ in range(args.steps):
+                if flush:
+                    scratch.fill_(s_ & 255)
+                pev[s_][0].record(stream)
+                fn(inp)
+                pev[s_][1].record(stream)
+            torch.cuda.synchronize()
+            res[label] = [pev[s_][0].elapsed_time(pev[s_][1]) for s_ in range(args.steps)]
+        isolated[st] = res
+    del scratch
+    torch.cuda.empty_cache()
 
     # The same forward with the permutation fused into FC1's operand load
     # (maps-only permute, rows gathered from x; no x_perm), timed the same way.
@@ -267,6 +311,37 @@ def main():
                  "stage_ms": {"route+permute_maps": round(fms(0, 1), 4),
                               "ffn_gathered": round(fms(1, 2), 4),
                               "combine": round(fms(2, 3), 4)}}
+    # The forward with the combine folded into FC2's epilogue as well: route,
+    # maps-only permute, then one FFN call that adds each gate-scaled expert
+    # output into y (no y_perm, no combine launch).
+    combined = None
+    if not cfg.backward:
+        def comb_step(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            layer.route(inp)
+            layer.permute(inp, maps_only=True)
+            if ev is not None:
+                ev[1].record(stream)
+            layer.ffn_combine(inp)
+            if ev is not None:
+                ev[2].record(stream)
+        for _ in range(args.warmup):
+            comb_step()
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        c0 = time.perf_counter()
+        for s_ in range(args.steps):
+            comb_step(cev[s_])
+        torch.cuda.synchronize()
+        cwall = (time.perf_counter() - c0) * 1e3 / args.steps
+        cms = lambda a, b: float(np.mean([cev[s_][a].elapsed_time(cev[s_][b])
+                                          for s_ in range(args.steps)]))
+        combined = {"ms_per_step": round(cwall, 4),
+                    "tokens_per_s": round(cfg.T / (cwall / 1e3), 1),
+                    "stage_ms": {"route+permute_maps": round(cms(0, 1), 4),
+                                 "ffn_combine": round(cms(1, 2), 4)}}
     # The forward with MXFP8 expert GEMMs (E4M3, blocks of 32, E8M0 scales):
     # weights quantised once and cached (outside the timed steps, reported
     # on its own), x quantised every step, rows gathered from the quantised x.
@@ -396,6 +471,11 @@ def main():
         gbs = nb / (per_stage[st] / 1e3) / 1e9
         hbm[st] = {"bytes": int(nb), "GB/s": round(gbs, 1),
                    "frac": round(gbs / PEAK_HBM_GBS, 4)}
+        for label, v in isolated[st].items():
+            med = float(np.median(v))
+            g = nb / (med / 1e3) / 1e9
+            hbm[st][label] = {"ms_median": round(med, 4), "ms_min": round(float(np.min(v)), 4),
+                              "GB/s": round(g, 1), "frac": round(g / PEAK_HBM_GBS, 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -415,13 +495,17 @@ def main():
         "grouped_gemm_tflops": round(tflops, 2),
         "grouped_gemm_frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "stage_ms": {k: round(v, 4) for k, v in per_stage.items()},
+        "stage_ms_median": {k: round(float(np.median(v)), 4) for k, v in stage_samples.items()},
+        "stage_ms_min": {k: round(float(np.min(v)), 4) for k, v in stage_samples.items()},
         "stage_hbm": hbm,
         "event_ms_per_step": round(ms_step, 4),
         "fused_permute_forward": fused,
+        "fused_permute_and_combine_forward": combined,
         "mxfp8_forward": mx,
         "training_with_recompute": remat,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "device": device_record(torch),
     }
     print(json.dumps(rec), flush=True)
 

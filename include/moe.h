@@ -75,7 +75,8 @@ enum {
   MOE_OP_COMBINE = 3,
   MOE_OP_BACKWARD = 4,
   MOE_OP_FFN_MXFP8 = 5,
-  MOE_OP_BACKWARD_RECOMPUTE = 6   /* moe_ffn_backward with gu_save NULL */
+  MOE_OP_BACKWARD_RECOMPUTE = 6,  /* moe_ffn_backward with gu_save NULL */
+  MOE_OP_FFN_COMBINE = 7          /* moe_grouped_ffn_combine */
 };
 
 /* The layer's parameters: tokens T, hidden d, routed experts E, experts per
@@ -181,6 +182,38 @@ int moe_grouped_ffn(const moe_shape* shape, const void* x_perm,
                     const void* ws_gate, const void* ws_up,
                     const void* ws_down, void* y_perm, void* y_shared,
                     void* gu_save, void* ws, size_t ws_bytes, void* stream);
+
+/* The grouped SwiGLU FFN with the unpermute-and-scale folded into FC2's
+ * epilogue (Primus blog, MegaMoE section: combine fused into the second
+ * grouped GEMM, so the expert outputs are never materialised):
+ *      y[t] = ys[t] + sum_j topk_w[t, j] * (h_r . w_down[e]^T),  r = token_row[t, j]
+ * with h rounded to dtype as in moe_grouped_ffn, but each expert output
+ * kept in fp32 (it is never stored), scaled by its gate and added into y.
+ *
+ *  x_perm [R, d] dtype, or NULL: FC1 gathers row r from x[row_token[r]]
+ *      (then x is required and T * d * sizeof(dtype) < 2^31, else
+ *      MOE_ERR_UNSUPPORTED).
+ *  row_token [R], row_gate [R] fp32 (as from moe_permute): routed row r adds
+ *      row_gate[r] times its FC2 output into y[row_token[r]].
+ *  expert_offsets, w_gate, w_up, w_down, x, ws_gate, ws_up, ws_down as in
+ *      moe_grouped_ffn; the shared expert (F_shared > 0) adds its output
+ *      with gate 1.
+ *  y [T, d] fp32 out: overwritten (zeroed, then accumulated).
+ * The additions into y are fp32 atomics, so their order varies between
+ * runs: the result is bitwise reproducible when every element receives at
+ * most two additions (k = 1 or 2, no shared expert and no split of FC2's
+ * contraction: 0 + a + b commutes exactly); otherwise runs may differ in the
+ * last bits (each order's rounding error is bounded by n * 2^-24 * sum |terms|
+ * for n terms).  Forward only: neither g | u nor the expert outputs that
+ * moe_ffn_backward reads are produced.
+ *  ws: MOE_OP_FFN_COMBINE bytes (holds h). */
+int moe_grouped_ffn_combine(const moe_shape* shape, const void* x_perm,
+                            const int32_t* row_token, const float* row_gate,
+                            const int32_t* expert_offsets,
+                            const void* w_gate, const void* w_up, const void* w_down,
+                            const void* x, const void* ws_gate, const void* ws_up,
+                            const void* ws_down, float* y, void* ws, size_t ws_bytes,
+                            void* stream);
 
 /* Unpermute-and-scale (Primus blog, MegaMoE section: the last stage sums each
  * token's k gate-weighted expert outputs back into its row):

@@ -28,11 +28,12 @@ MOE_DTYPE_BF16 = 1
 MOE_SCORE_SOFTMAX = 0
 MOE_SCORE_SIGMOID = 1
 (MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN, MOE_OP_COMBINE, MOE_OP_BACKWARD,
- MOE_OP_FFN_MXFP8, MOE_OP_BACKWARD_RECOMPUTE) = range(7)
+ MOE_OP_FFN_MXFP8, MOE_OP_BACKWARD_RECOMPUTE, MOE_OP_FFN_COMBINE) = range(8)
 
 EXPORTED = ("moe_workspace_size", "moe_route_topk", "moe_permute",
             "moe_grouped_ffn", "moe_unpermute_combine", "moe_ffn_backward",
-            "moe_status_string", "moe_mx_quantize", "moe_grouped_ffn_mxfp8")
+            "moe_status_string", "moe_mx_quantize", "moe_grouped_ffn_mxfp8",
+            "moe_grouped_ffn_combine")
 
 
 class MoeShape(ctypes.Structure):
@@ -67,6 +68,7 @@ def load() -> ctypes.CDLL:
     lib.moe_permute.argtypes = [sp] + [vp] * 8 + [vp, sz, vp]
     lib.moe_grouped_ffn.argtypes = [sp] + [vp] * 13 + [vp, sz, vp]
     lib.moe_unpermute_combine.argtypes = [sp] + [vp] * 5 + [vp, sz, vp]
+    lib.moe_grouped_ffn_combine.argtypes = [sp] + [vp] * 12 + [vp, sz, vp]
     lib.moe_ffn_backward.argtypes = [sp] + [vp] * 26 + [vp, sz, vp]
     lib.moe_mx_quantize.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
     lib.moe_grouped_ffn_mxfp8.argtypes = [sp] + [vp] * 18 + [vp, sz, vp]
@@ -148,6 +150,17 @@ def moe_grouped_ffn(shape, x_perm, row_token, expert_offsets, w_gate, w_up,
         _p(ws_down), _p(y_perm), _p(y_shared), _p(gu_save), _p(ws), ws_bytes,
         _stream(stream))
     return _check(st, "moe_grouped_ffn") if check else st
+
+
+def moe_grouped_ffn_combine(shape, x_perm, row_token, row_gate, expert_offsets,
+                            w_gate, w_up, w_down, x, ws_gate, ws_up, ws_down, y,
+                            ws=None, ws_bytes=0, stream=None, check=True):
+    st = load().moe_grouped_ffn_combine(
+        ctypes.byref(shape), _p(x_perm), _p(row_token), _p(row_gate),
+        _p(expert_offsets), _p(w_gate), _p(w_up), _p(w_down), _p(x),
+        _p(ws_gate), _p(ws_up), _p(ws_down), _p(y), _p(ws), ws_bytes,
+        _stream(stream))
+    return _check(st, "moe_grouped_ffn_combine") if check else st
 
 
 def moe_unpermute_combine(shape, y_perm, token_row, topk_w, y_shared, y,

@@ -73,6 +73,9 @@ size_t ws_bytes_for(const moe_shape& s, int op) {
         b += align_up((R * 2 * s.F + (size_t)s.T * 2 * s.F_shared) * es);
       return b;
     }
+    case MOE_OP_FFN_COMBINE:   // no split-K partials: slices add into y
+      return 2 * align_up((s.E + 1) * 4) + align_up(R * s.F * es) +
+             align_up((size_t)s.T * s.F_shared * es);
     case MOE_OP_FFN_MXFP8:
       return 2 * align_up((s.E + 1) * 4) + align_up(R * s.F) + align_up(R * s.F / 32) +
              align_up((size_t)s.T * s.F_shared) + align_up((size_t)s.T * s.F_shared / 32);
@@ -108,7 +111,7 @@ extern "C" {
 int moe_workspace_size(const moe_shape* shape, int op, size_t* bytes) {
   const int st = check_shape(shape);
   if (st != MOE_OK) return st;
-  if (!bytes || op < MOE_OP_ROUTE || op > MOE_OP_BACKWARD_RECOMPUTE) return MOE_ERR_INVALID_ARG;
+  if (!bytes || op < MOE_OP_ROUTE || op > MOE_OP_FFN_COMBINE) return MOE_ERR_INVALID_ARG;
   *bytes = ws_bytes_for(*shape, op);
   return MOE_OK;
 }
@@ -222,6 +225,49 @@ int moe_grouped_ffn(const moe_shape* shape, const void* x_perm, const int32_t* r
                                             expert_offsets, w_gate, w_up, w_down, x,
                                             ws_gate, ws_up, ws_down, y_perm, y_shared, gu_save,
                                             fw, static_cast<hipStream_t>(stream)));
+}
+
+int moe_grouped_ffn_combine(const moe_shape* shape, const void* x_perm,
+                            const int32_t* row_token, const float* row_gate,
+                            const int32_t* expert_offsets, const void* w_gate, const void* w_up,
+                            const void* w_down, const void* x, const void* ws_gate,
+                            const void* ws_up, const void* ws_down, float* y, void* ws,
+                            size_t ws_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape& s = *shape;
+  const long long es = (long long)esize(s);
+  const long long R = (long long)s.T * s.k;
+  const long long wsz = (long long)s.E * s.F * s.d * es;
+  const bool gather = x_perm == nullptr && R > 0;
+  if (gather) {
+    if (!ok_buf(x, (long long)s.T * s.d * es)) return MOE_ERR_INVALID_ARG;
+    if ((long long)s.T * s.d * es >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+  } else if (!ok_buf(x_perm, R * s.d * es)) {
+    return MOE_ERR_INVALID_ARG;
+  }
+  if (!ok_buf(row_token, R * 4) || !ok_buf(row_gate, R * 4) ||
+      !ok_buf(expert_offsets, (long long)(s.E + 1) * 4) || !ok_buf(w_gate, wsz) ||
+      !ok_buf(w_up, wsz) || !ok_buf(w_down, wsz) || !ok_buf(y, (long long)s.T * s.d * 4))
+    return MOE_ERR_INVALID_ARG;
+  if (s.F_shared > 0) {
+    const long long sz = (long long)s.F_shared * s.d * es;
+    if (!ok_buf(x, (long long)s.T * s.d * es) || !ok_buf(ws_gate, sz) || !ok_buf(ws_up, sz) ||
+        !ok_buf(ws_down, sz))
+      return MOE_ERR_INVALID_ARG;
+  }
+  if ((st = check_ws(s, MOE_OP_FFN_COMBINE, ws, ws_bytes)) != MOE_OK) return st;
+  Carver c{static_cast<char*>(ws)};
+  moe::FfnWs fw;
+  fw.tiles1 = c.take<int32_t>((s.E + 1) * 4);
+  fw.tiles2 = c.take<int32_t>((s.E + 1) * 4);
+  fw.h = c.take<char>((size_t)R * s.F * es);
+  fw.h_shared = c.take<char>((size_t)s.T * s.F_shared * es);
+  fw.part = nullptr;
+  return hip_status(moe::launch_grouped_ffn_combine(s, x_perm, row_token, row_gate,
+                                                    expert_offsets, w_gate, w_up, w_down, x,
+                                                    ws_gate, ws_up, ws_down, y, fw,
+                                                    static_cast<hipStream_t>(stream)));
 }
 
 int moe_unpermute_combine(const moe_shape* shape, const void* y_perm, const int32_t* token_row,

@@ -9,6 +9,11 @@
 //              optionally the rounded g | u for the backward
 //   FC2:       y_perm = h . w_down^T                            -> bf16
 //
+// The combining form folds the unpermute-and-scale into FC2's epilogue (the
+// blog's MegaMoE combine fused into the second grouped GEMM): each fp32 FC2
+// row, scaled by its gate, is added into its token's row of the fp32 output,
+// so y_perm is never written.
+//
 // bf16 with K and N multiples of 64 runs on MFMA; everything else (the fp32
 // layer, odd widths) runs on the generic fp32-FMA tile kernel.
 #include <algorithm>
@@ -54,12 +59,23 @@ splitk_reduce_kernel(const float* __restrict__ part, long long stride, int ks, l
   }
 }
 
+// y = 0 before the combining FC2 adds into it (a kernel, not a memset, so
+// that a captured graph replays it faithfully).
+__global__ void __launch_bounds__(256)
+zero_f32_kernel(float* __restrict__ p, long long n) {
+  const long long n4 = n / 4;
+  for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n4; i += (long long)gridDim.x * 256)
+    reinterpret_cast<float4*>(p)[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (long long i = n4 * 4 + blockIdx.x * 256LL + threadIdx.x; i < n; i += (long long)gridDim.x * 256)
+    p[i] = 0.0f;
+}
+
 bool ffn_uses_mfma(const moe_shape& s) {
   return s.dtype == MOE_DTYPE_BF16 && s.d % 64 == 0 && s.F % 64 == 0 &&
          (s.F_shared == 0 || s.F_shared % 64 == 0);
 }
 
-template <typename T>
+template <typename T, int EPI2>
 static hipError_t run_generic(const moe_shape& s, GemmArgs& a1, GemmArgs& a2, int R,
                               const FfnWs& ws, hipStream_t st) {
   if (s.E > 0) {
@@ -69,7 +85,7 @@ static hipError_t run_generic(const moe_shape& s, GemmArgs& a1, GemmArgs& a2, in
   int g1 = grid_upper_bound(a1, GEN_BM, GEN_BN, R);
   if (g1 > 0) gemm_generic_kernel<T, 2, EPI_SWIGLU><<<g1, 256, 0, st>>>(a1);
   int g2 = grid_upper_bound(a2, GEN_BM, GEN_BN, R);
-  if (g2 > 0) gemm_generic_kernel<T, 1, EPI_STORE><<<g2, 256, 0, st>>>(a2);
+  if (g2 > 0) gemm_generic_kernel<T, 1, EPI2><<<g2, 256, 0, st>>>(a2);
   return hipGetLastError();
 }
 
@@ -117,6 +133,37 @@ static GemmArgs fc1_args(const moe_shape& s, const void* x_perm, const int32_t* 
   return a1;
 }
 
+// FC2's arguments: h [R, F] x w_down [E, d, F] -> y_perm [R, d], and the
+// shared expert's h_shared [T, Fs] x ws_down [d, Fs] -> y_shared [T, d].
+static GemmArgs fc2_args(const moe_shape& s, int E, const int32_t* offsets, const void* w_down,
+                         const void* ws_down, void* y_perm, void* y_shared, const FfnWs& ws) {
+  GemmArgs a2 = {};
+  a2.E = E;
+  a2.offsets = offsets;
+  a2.tiles = ws.tiles2;
+  a2.A = ws.h;
+  a2.lda = s.F;
+  a2.B0 = w_down;
+  a2.B1 = nullptr;
+  a2.strideB = (long long)s.d * s.F;
+  a2.N = s.d;
+  a2.K = s.F;
+  a2.C = y_perm;
+  a2.ldc = s.d;
+  if (s.F_shared > 0 && s.T > 0) {
+    a2.Td = s.T;
+    a2.Ad = ws.h_shared;
+    a2.ldad = s.F_shared;
+    a2.Bd0 = ws_down;
+    a2.Bd1 = nullptr;
+    a2.Nd = s.d;
+    a2.Kd = s.F_shared;
+    a2.Cd = y_shared;
+    a2.ldcd = s.d;
+  }
+  return a2;
+}
+
 static hipError_t launch_fc1(const moe_shape& s, GemmArgs& a1, int R, hipStream_t st) {
   if (!ffn_uses_mfma(s)) {
     const int g1 = grid_upper_bound(a1, GEN_BM, GEN_BN, R);
@@ -159,36 +206,12 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const int3
   const bool shared = s.F_shared > 0 && s.T > 0;
   GemmArgs a1 = fc1_args(s, x_perm, row_token, offsets, w_gate, w_up, x, ws_gate, ws_up, ws.h,
                          ws.h_shared, gu_save, ws.tiles1);
-  // FC2: h [R, F] x w_down [E, d, F] -> y_perm [R, d]
-  GemmArgs a2 = {};
-  a2.E = a1.E;
-  a2.offsets = offsets;
-  a2.tiles = ws.tiles2;
-  a2.A = ws.h;
-  a2.lda = s.F;
-  a2.B0 = w_down;
-  a2.B1 = nullptr;
-  a2.strideB = (long long)s.d * s.F;
-  a2.N = s.d;
-  a2.K = s.F;
-  a2.C = y_perm;
-  a2.ldc = s.d;
-  if (shared) {
-    a2.Td = s.T;
-    a2.Ad = ws.h_shared;
-    a2.ldad = s.F_shared;
-    a2.Bd0 = ws_down;
-    a2.Bd1 = nullptr;
-    a2.Nd = s.d;
-    a2.Kd = s.F_shared;
-    a2.Cd = y_shared;
-    a2.ldcd = s.d;
-  }
+  GemmArgs a2 = fc2_args(s, a1.E, offsets, w_down, ws_down, y_perm, y_shared, ws);
   if (a1.E == 0 && !shared) return hipSuccess;
 
   if (!ffn_uses_mfma(s)) {
-    if (s.dtype == MOE_DTYPE_BF16) return run_generic<bf16_t>(s, a1, a2, R, ws, st);
-    return run_generic<float>(s, a1, a2, R, ws, st);
+    if (s.dtype == MOE_DTYPE_BF16) return run_generic<bf16_t, EPI_STORE>(s, a1, a2, R, ws, st);
+    return run_generic<float, EPI_STORE>(s, a1, a2, R, ws, st);
   }
   if (a1.E > 0) {
     schedule_tiles_kernel<<<1, 1024, 0, st>>>(offsets, s.E, FC1_BM, cdiv(s.F, FC1_BN),
@@ -210,6 +233,47 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const int3
   splitk_reduce_kernel<<<grid, 256, 0, st>>>(ws.part, a2.part_stride, ks, n4,
                                              static_cast<bf16_t*>(y_perm));
   return hipGetLastError();
+}
+
+// The FFN with the combine in FC2's epilogue: y = 0, then FC1 as above, then
+// FC2 adding row_gate[r] * (h[r] . w_down[e]^T) into y[row_token[r]] (and
+// the shared expert's rows with gate 1).  Split-K slices (same rule as the
+// storing FC2) add their partial sums directly, so no partials are kept.
+hipError_t launch_grouped_ffn_combine(const moe_shape& s, const void* x_perm,
+                                      const int32_t* row_token, const float* row_gate,
+                                      const int32_t* offsets, const void* w_gate,
+                                      const void* w_up, const void* w_down, const void* x,
+                                      const void* ws_gate, const void* ws_up,
+                                      const void* ws_down, float* y, const FfnWs& ws,
+                                      hipStream_t st) {
+  const int R = s.T * s.k;
+  const bool shared = s.F_shared > 0 && s.T > 0;
+  const long long ny = (long long)s.T * s.d;
+  if (ny == 0) return hipSuccess;
+  zero_f32_kernel<<<(int)std::min<long long>((ny / 4 + 255) / 256 + 1, 4096), 256, 0, st>>>(y, ny);
+  GemmArgs a1 = fc1_args(s, x_perm, row_token, offsets, w_gate, w_up, x, ws_gate, ws_up, ws.h,
+                         ws.h_shared, nullptr, ws.tiles1);
+  GemmArgs a2 = fc2_args(s, a1.E, offsets, w_down, ws_down, nullptr, nullptr, ws);
+  a2.comb_token = row_token;
+  a2.comb_gate = row_gate;
+  a2.Y = y;
+  a2.ldy = s.d;
+  if (a1.E == 0 && !shared) return hipGetLastError();
+
+  if (!ffn_uses_mfma(s)) {
+    if (s.dtype == MOE_DTYPE_BF16) return run_generic<bf16_t, EPI_COMBINE>(s, a1, a2, R, ws, st);
+    return run_generic<float, EPI_COMBINE>(s, a1, a2, R, ws, st);
+  }
+  if (a1.E > 0) {
+    schedule_tiles_kernel<<<1, 1024, 0, st>>>(offsets, s.E, FC1_BM, cdiv(s.F, FC1_BN),
+                                              ws.tiles1, FC2_BM, cdiv(s.d, FC2_BN), ws.tiles2, 1);
+  }
+  a1.tail = a2.tail = 1;
+  hipError_t e = launch_mfma_gemm<FC1_BM, FC1_BN, 2, EPI_SWIGLU, 4, 2, 1>(a1, R, st);
+  if (e != hipSuccess) return e;
+  const int ks = ffn_fc2_ksplit(s);
+  if (ks > 1 && a2.E > 0) a2.ksplit = ks;
+  return launch_mfma_gemm<FC2_BM, FC2_BN, 1, EPI_COMBINE, 4, 2, 1>(a2, R, st);
 }
 
 }  // namespace moe

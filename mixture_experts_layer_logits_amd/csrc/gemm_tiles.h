@@ -38,7 +38,9 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_F32_BIAS = 2 };
+// EPI_COMBINE: no C; each result row is scaled by its row's gate and added
+// (fp32 atomics) into Y at its token's row.
+enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_F32_BIAS = 2, EPI_COMBINE = 3 };
 
 struct GemmArgs {
   // routed groups (E == 0: none)
@@ -75,6 +77,12 @@ struct GemmArgs {
   float* Cpart;
   long long part_stride;
   int tail;                // routed groups use tail tiles (kernels built for them)
+  // EPI_COMBINE: routed row r adds comb_gate[r] * C[r] into Y[comb_token[r]];
+  // dense row t adds C[t] into Y[t].  With split-K every slice adds its part.
+  const int32_t* comb_token;
+  const float* comb_gate;
+  float* Y;
+  long long ldy;
 };
 
 // One tile's work, with typed base pointers already offset to the group.
@@ -96,6 +104,8 @@ struct TileJob {
   float* P;                // split-K partial rows of the group, or null
   int cls;                 // 0: BM x BN tile, 1: BM/2 x 2BN tail tile
   int dense;               // 1: the dense group, 0: a routed group
+  const int32_t* ctok;     // EPI_COMBINE: token of each routed row, or null (dense)
+  const float* cgate;      // EPI_COMBINE: gate of each routed row, or null (gate 1)
 };
 
 // Tiles of one routed group of `rows` rows with NT = ceil(N / BN) column tiles.
@@ -184,7 +194,9 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, TileJob<TIn, TOut
     j.GU = a.GU ? static_cast<TOut*>(a.GU) + (long long)row0 * a.ldgu : nullptr;
     j.klen = a.K / ks;
     j.k0 = kslice * j.klen;
-    if (ks > 1) j.P = a.Cpart + kslice * a.part_stride + (long long)row0 * a.N;
+    if (ks > 1 && a.Cpart) j.P = a.Cpart + kslice * a.part_stride + (long long)row0 * a.N;
+    j.ctok = a.comb_token ? a.comb_token + row0 : nullptr;
+    j.cgate = a.comb_gate ? a.comb_gate + row0 : nullptr;
     return true;
   }
   const int r = lid - routed;
@@ -206,6 +218,8 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, TileJob<TIn, TOut
   j.ldgu = a.ldgud;
   j.klen = a.Kd;
   j.k0 = 0;
+  j.ctok = nullptr;
+  j.cgate = nullptr;
   return true;
 }
 
@@ -510,7 +524,7 @@ gemm_bf16_mfma_kernel(const GemmArgs args) {
   using nb1 = std::integral_constant<int, BPW1>;
   // With g and u saved for the backward, the SwiGLU epilogue goes out
   // through LDS (below); every wave, idle or not, joins its barrier.
-  const bool staged = EPI == EPI_SWIGLU && job.GU != nullptr;
+  const bool staged = (EPI == EPI_SWIGLU && job.GU != nullptr) || EPI == EPI_COMBINE;
   if (!live) {
     if (tail) k_loop(std::false_type{}, nb1{});
     else k_loop(std::false_type{}, nb0{});
@@ -567,6 +581,53 @@ gemm_bf16_mfma_kernel(const GemmArgs args) {
       }
       return;
     }
+  }
+
+  if constexpr (EPI == EPI_COMBINE) {
+    // Per 32-row half, this wave's 32 x 128 fp32 results go to its 16 KiB
+    // of the ring (rows of 512 bytes, 16-byte chunk c of row r at c ^ r) and
+    // come back one row at a time, lane l holding column l (+ 64), so each
+    // atomic add instruction covers 256 contiguous bytes of one y row.
+    static_assert(NB == 1 && WTN == 128, "combine epilogue: one B, 128 columns per wave");
+    barrier();                                    // the ring is free
+    char* buf = reinterpret_cast<char*>((wave >> 1) == 0 ? st0 : (wave >> 1) == 1 ? st1
+                                        : (wave >> 1) == 2 ? st2 : st3) + (wave & 1) * 16384;
+    const int cbase = job.n0 + wn * WTN;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ch = j * 8 + 2 * q + (lane >> 5);
+          const f32x16_t& Cv = acc[0][i][j];
+          *reinterpret_cast<float4*>(buf + frag_row * 512 + ((ch ^ frag_row) << 4)) =
+              make_float4(Cv[4 * q], Cv[4 * q + 1], Cv[4 * q + 2], Cv[4 * q + 3]);
+        }
+      // lane r < 32 looks up row r's token and gate; rows past the group: -1
+      const int mr = job.m0 + wm * WTM + i * 32 + frag_row;
+      int tok = -1;
+      float gw = 0.0f;
+      if (mr < job.rows) {
+        tok = job.ctok ? job.ctok[mr] : mr;
+        gw = job.cgate ? job.cgate[mr] : 1.0f;
+      }
+#pragma unroll
+      for (int r = 0; r < 32; ++r) {
+        const int t = __builtin_amdgcn_readlane(tok, r);
+        const float g = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gw), r));
+        if (t < 0) continue;
+        float* yrow = args.Y + (long long)t * args.ldy + cbase;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int col = h * 64 + lane;
+          const float v = *reinterpret_cast<const float*>(
+              buf + r * 512 + ((((col >> 2) ^ r)) << 4) + (col & 3) * 4);
+          if (cbase + col < job.N) atomicAdd(yrow + col, g * v);
+        }
+      }
+    }
+    return;
   }
 
   // Epilogue.  Lane owns row m = .. + (lane % 32) and, for register v,
@@ -722,6 +783,10 @@ gemm_generic_kernel(const GemmArgs args) {
       if (n >= job.N) continue;
       if constexpr (EPI == EPI_F32_BIAS) {
         job.C[(long long)m * job.ldc + n] = acc[0][i][jj] + (args.bias ? args.bias[n] : 0.0f);
+      } else if constexpr (EPI == EPI_COMBINE) {
+        const int t = job.ctok ? job.ctok[m] : m;
+        const float gw = job.cgate ? job.cgate[m] : 1.0f;
+        atomicAdd(args.Y + (long long)t * args.ldy + n, gw * acc[0][i][jj]);
       } else if constexpr (EPI == EPI_SWIGLU) {
         const float g = acc[0][i][jj], u = acc[NB - 1][i][jj];
         job.C[(long long)m * job.ldc + n] = from_f32<TOut>(silu_precise(g) * u);

@@ -82,6 +82,13 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const int3
                               const void* x, const void* ws_gate, const void* ws_up,
                               const void* ws_down, void* y_perm, void* y_shared,
                               void* gu_save, const FfnWs& ws, hipStream_t st);
+hipError_t launch_grouped_ffn_combine(const moe_shape& s, const void* x_perm,
+                                      const int32_t* row_token, const float* row_gate,
+                                      const int32_t* offsets, const void* w_gate,
+                                      const void* w_up, const void* w_down, const void* x,
+                                      const void* ws_gate, const void* ws_up,
+                                      const void* ws_down, float* y, const FfnWs& ws,
+                                      hipStream_t st);
 
 // MXFP8 (E4M3 codes with one E8M0 scale byte per 32 values along a row).
 hipError_t launch_mx_quantize(const void* src, long long rows, int cols, uint8_t* q,

@@ -28,7 +28,7 @@ class MoELayer:
         dt = torch.bfloat16 if cfg.dtype == L.MOE_DTYPE_BF16 else torch.float32
         dev = self.device
         ops = [L.MOE_OP_ROUTE, L.MOE_OP_PERMUTE, L.MOE_OP_FFN,
-               L.MOE_OP_COMBINE]
+               L.MOE_OP_COMBINE, L.MOE_OP_FFN_COMBINE]
         if self.save_gu:
             ops.append(L.MOE_OP_BACKWARD)
         if self.recompute:
@@ -82,6 +82,28 @@ class MoELayer:
         L.moe_unpermute_combine(self.shape, b["y_perm"], b["token_row"],
                                 b["topk_w"], b["y_shared"], b["y"], self.ws,
                                 self.ws_bytes, stream)
+
+    def ffn_combine(self, inp, stream=None, gather=True):
+        """The grouped FFN with the combine in FC2's epilogue: y straight
+        from the expert GEMMs, no y_perm.  gather: FC1 reads its rows from x
+        (after a maps-only permute), else from x_perm."""
+        b = self.buf
+        L.moe_grouped_ffn_combine(self.shape, None if gather else b["x_perm"],
+                                  b["row_token"], b["row_gate"], b["expert_offsets"],
+                                  inp["w_gate"], inp["w_up"], inp["w_down"],
+                                  inp["x"] if (gather or self.cfg.F_shared > 0) else None,
+                                  inp.get("ws_gate"), inp.get("ws_up"),
+                                  inp.get("ws_down"), b["y"], self.ws, self.ws_bytes,
+                                  stream)
+
+    def forward_combined(self, inp, stream=None):
+        """route -> maps-only permute -> FFN with the combine in FC2's
+        epilogue (inference: the backward's x_perm, y_perm and g | u are not
+        produced)."""
+        self.route(inp, stream)
+        self.permute(inp, stream, maps_only=True)
+        self.ffn_combine(inp, stream)
+        return self.buf
 
     def forward(self, inp, stream=None, fused=False):
         """fused=True skips x_perm: the permutation only builds the maps and

@@ -68,11 +68,13 @@ def sample_tokens(T, n):
     return s
 
 
-def oracle_sampled_forward(cfg, inp, tokens, idx, w):
+def oracle_sampled_forward(cfg, inp, tokens, idx, w, combined=False):
     """Oracle rows for sampled tokens: per (t, j) the expert output
     y_e(x[t]) (rounded as the layer materialises it), the shared expert's
     output and the combined y[t].  Experts are evaluated one at a time, each
-    on just the sampled rows routed to it."""
+    on just the sampled rows routed to it.  combined: the expert outputs are
+    those of the FFN with the combine in FC2's epilogue, never materialised
+    and so not rounded (the oracle's grouped_ffn_combine, row by row)."""
     prec = prec_of(cfg)
     x = np64(inp["x"][torch.as_tensor(tokens, device=inp["x"].device)])
     idx_s = np.asarray(idx)[tokens]
@@ -83,14 +85,20 @@ def oracle_sampled_forward(cfg, inp, tokens, idx, w):
         sel = np.argwhere(idx_s == e)
         r = O.swiglu_ffn(x[sel[:, 0]], np64(inp["w_gate"][int(e)]),
                          np64(inp["w_up"][int(e)]), np64(inp["w_down"][int(e)]), prec)
-        y_rows[sel[:, 0], sel[:, 1]] = r["y"]
+        y_rows[sel[:, 0], sel[:, 1]] = (r["h"] @ np64(inp["w_down"][int(e)]).T
+                                        if combined else r["y"])
         rnd = O.rounder(prec)
         gu_rows[sel[:, 0], sel[:, 1], :cfg.F] = rnd(r["g"])
         gu_rows[sel[:, 0], sel[:, 1], cfg.F:] = rnd(r["u"])
     ys = None
     if cfg.F_shared > 0:
-        ys = O.shared_ffn(x, np64(inp["ws_gate"]), np64(inp["ws_up"]),
-                          np64(inp["ws_down"]), prec)
+        if combined:
+            hs = O.swiglu_ffn(x, np64(inp["ws_gate"]), np64(inp["ws_up"]),
+                              np64(inp["ws_down"]), prec)["h"]
+            ys = hs @ np64(inp["ws_down"]).T
+        else:
+            ys = O.shared_ffn(x, np64(inp["ws_gate"]), np64(inp["ws_up"]),
+                              np64(inp["ws_down"]), prec)
     acc = np.zeros((len(tokens), cfg.d)) if ys is None else ys.copy()
     for j in range(cfg.k):
         acc += w_s[:, j:j + 1] * y_rows[:, j]

@@ -173,3 +173,39 @@ def test_backward_recompute_workspace():
     args[2] = None                                   # gu_save
     st = M.moe_ffn_backward(s, *args, p, base, check=False, stream=0)
     assert st == L.MOE_ERR_WORKSPACE
+
+
+def test_ffn_combine_validates_before_launch():
+    """moe_grouped_ffn_combine: row_token, row_gate, the weights and y are
+    required (x too when rows are gathered or a shared expert exists); its
+    workspace holds h but no split-K partials."""
+    c = CONFIGS["mixtral_t4096"]
+    s = M.make_shape(c)
+    p = _fake()
+    need = M.moe_workspace_size(s, L.MOE_OP_FFN_COMBINE)
+    R = c.T * c.k
+    assert R * c.F * 2 <= need < M.moe_workspace_size(s, L.MOE_OP_FFN)
+    # args: x_perm, row_token, row_gate, offsets, w_gate, w_up, w_down, x,
+    # ws_gate, ws_up, ws_down, y
+    base = [p, p, p, p, p, p, p, None, None, None, None, p]
+    for missing in (1, 2, 3, 4, 5, 6, 11):
+        args = list(base)
+        args[missing] = None
+        st = M.moe_grouped_ffn_combine(s, *args, p, need, check=False, stream=0)
+        assert st == L.MOE_ERR_INVALID_ARG, missing
+    st = M.moe_grouped_ffn_combine(s, *base, p, need - 1, check=False, stream=0)
+    assert st == L.MOE_ERR_WORKSPACE
+    # gathering rows (x_perm NULL) needs x
+    args = list(base)
+    args[0] = None
+    st = M.moe_grouped_ffn_combine(s, *args, p, need, check=False, stream=0)
+    assert st == L.MOE_ERR_INVALID_ARG
+    # a shared expert needs x and its three weights
+    ds = CONFIGS["deepseek_v3_t8192"]
+    s2 = M.make_shape(ds)
+    need2 = M.moe_workspace_size(s2, L.MOE_OP_FFN_COMBINE)
+    for missing in (7, 8, 9, 10):
+        args = [p] * 12
+        args[missing] = None
+        st = M.moe_grouped_ffn_combine(s2, *args, p, need2, check=False, stream=0)
+        assert st == L.MOE_ERR_INVALID_ARG, missing

@@ -34,7 +34,9 @@ Readings of the pages that these functions take (the pages leave them open):
     unbiased s renormalised over the k picks (scaling factor 1);
   * rows inside an expert segment are in ascending token order;
   * the shared expert has gate 1 and its output is added first;
-  * the backward recomputes h from the saved bf16 g and u.
+  * the backward recomputes h from the saved bf16 g and u;
+  * with the combine folded into FC2 (grouped_ffn_combine) the expert
+    outputs are never materialised, so they carry no rounding; h still does.
 """
 from __future__ import annotations
 

@@ -32,7 +32,10 @@
  *    returns a negative moe_status, launches nothing and leaves every output
  *    untouched.  A failed kernel launch returns MOE_ERR_HIP.
  *  - Results are bitwise deterministic run to run (no floating-point
- *    atomics).  The library keeps no mutable global state.
+ *    atomics), with one stated exception: moe_grouped_ffn_combine, whose
+ *    fp32 atomic additions are order-independent only with at most two
+ *    addends per output element (see there).  The library keeps no mutable
+ *    global state.
  *
  * Dtypes: `dtype` selects the storage type of x, the weights and the
  * materialised intermediates x_perm, h, y_perm, gu_save (MOE_DTYPE_BF16 or

@@ -134,3 +134,26 @@ def test_ffn_combine_full_size_sampled(name):
     assert_close("y[sample]", out["y"][torch.as_tensor(toks, device="cuda")], ref["y"], prec)
     del layer, out, inp
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("k", [1, 2])
+def test_ffn_combine_two_addends_is_bitwise_reproducible(k):
+    """With at most two additions into each y element the result does not
+    depend on their order (0 + a + b = 0 + b + a exactly).  T = 8192, d =
+    4096, E = 8, F = 512 and no shared expert: at k = 2, FC2 has
+    (64 + 8) x 16 = 1152 tiles, enough to run unsplit; at k = 1 it has
+    (32 + 8) x 16 = 640 and runs in two slices.  Either way each element
+    gets two addends, and three runs agree bit for bit."""
+    cfg = MoEConfig(f"bf16_k{k}_t8192", T=8192, d=4096, E=8, k=k, F=512)
+    from mixture_experts_layer_logits_amd import MoELayer
+    inp = make_inputs(cfg, device="cuda")
+    layer = MoELayer(cfg)
+    layer.forward_combined(inp)
+    torch.cuda.synchronize()
+    y0 = layer.buf["y"].clone()
+    for _ in range(2):
+        layer.ffn_combine(inp)
+        torch.cuda.synchronize()
+        assert torch.equal(layer.buf["y"], y0)
+    del layer, inp
+    torch.cuda.empty_cache()

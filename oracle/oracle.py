@@ -461,28 +461,45 @@ def router_backward(d_gate, topk_idx, topk_w, logits, E, score=SCORE_SOFTMAX,
     return out_f32(prec)(dl)
 
 
-def expert_backward(dYe, xe, gu_e, wg, wu, wd, prec="bf16"):
+def expert_backward(dYe, xe, gu_e, wg, wu, wd, prec="bf16", mxfp8=False):
     """One expert's backward on its rows (dYe [n, d], xe [n, d],
     gu_e [n, 2F]); wg, wu [F, d], wd [d, F].
 
     dh = dY . W_d; with s = sigmoid(g): dg = dh u s (1 + g (1 - s)),
     du = dh silu(g); h = silu(g) u recomputed from the saved g, u;
     dW_d = dY^T h, dW_g = dg^T x, dW_u = du^T x; dX = dg . W_g + du . W_u.
+
+    mxfp8: the two data-gradient GEMMs take MXFP8 operands (the Primus
+    blog's low-precision section runs the grouped expert GEMMs of forward
+    and backward in MXFP8), each quantised along its contraction dimension:
+    dY and W_d along d for dh; [dg | du] and [W_g; W_u] along F for dX
+    (blocks never straddle g and u: F is a multiple of 32).  dh itself is
+    not materialised (exact here); dg, du, h and dX are rounded as above.
+    The weight gradients keep the unquantised operands.
     """
     rnd = rounder(prec)
     gu_e = as64(gu_e)
     F = gu_e.shape[1] // 2
     g, u = gu_e[:, :F], gu_e[:, F:]
     dYe, xe = as64(dYe), as64(xe)
-    dh = dYe @ as64(wd)
+    if mxfp8:
+        dh = mx_round(dYe) @ mx_round(as64(wd).T).T
+    else:
+        dh = dYe @ as64(wd)
     with np.errstate(over="ignore"):
         sig = 1.0 / (1.0 + np.exp(-g))
     sg = g * sig
     dgt = rnd(dh * u * sig * (1.0 + g * (1.0 - sig)))
     dut = rnd(dh * sg)
     h = rnd(sg * u)
+    if mxfp8:
+        dgu = np.concatenate([dgt, dut], axis=1)
+        wgu = np.concatenate([as64(wg), as64(wu)], axis=0)     # [2F, d]
+        dX = rnd(mx_round(dgu) @ mx_round(wgu.T).T)
+    else:
+        dX = rnd(dgt @ as64(wg) + dut @ as64(wu))
     return dict(dw_down=dYe.T @ h, dw_gate=dgt.T @ xe, dw_up=dut.T @ xe,
-                dX=rnd(dgt @ as64(wg) + dut @ as64(wu)), dg=dgt, du=dut)
+                dX=dX, dg=dgt, du=dut)
 
 
 def dispatch_grad(dy, token_row, topk_w, R, prec="bf16"):
@@ -508,7 +525,7 @@ def gate_grad(dy, y_perm, token_row):
 
 def ffn_backward(dy, x_perm, gu_save, y_perm, offsets, token_row, topk_idx,
                  topk_w, logits, w_gate, w_up, w_down, score=SCORE_SOFTMAX,
-                 renorm=1, prec="bf16", shared=None):
+                 renorm=1, prec="bf16", shared=None, mxfp8=False):
     """Backward of the layer, from the saved tensors.
 
     The backward mirrors the forward through dispatch/combine duality, with
@@ -518,6 +535,7 @@ def ffn_backward(dy, x_perm, gu_save, y_perm, offsets, token_row, topk_idx,
       per expert: expert_backward;  dx[t] = sum_j dX_perm[pos[t,j]]
       d_logits from d_gate through the gate function.
     Weight gradients of experts with no rows are exactly zero.
+    mxfp8: the data-gradient GEMMs on MXFP8 operands (expert_backward).
 
     ``shared`` (optional) = dict(x, gu, ws_gate, ws_up, ws_down) for the
     shared expert applied to every token: it adds ys[t] to y[t] with gate 1, so its
@@ -543,7 +561,7 @@ def ffn_backward(dy, x_perm, gu_save, y_perm, offsets, token_row, topk_idx,
         if b == a:
             continue
         r = expert_backward(dY[a:b], x_perm[a:b], gu[a:b], w_gate[e],
-                            w_up[e], w_down[e], prec)
+                            w_up[e], w_down[e], prec, mxfp8)
         dw_down[e], dw_gate[e], dw_up[e] = r["dw_down"], r["dw_gate"], r["dw_up"]
         dX[a:b] = r["dX"]
     dx = np.zeros((T, d), dtype=F64)
@@ -552,7 +570,7 @@ def ffn_backward(dy, x_perm, gu_save, y_perm, offsets, token_row, topk_idx,
     out = {}
     if shared is not None:
         rs = expert_backward(dy, shared["x"], shared["gu"], shared["ws_gate"],
-                             shared["ws_up"], shared["ws_down"], prec)
+                             shared["ws_up"], shared["ws_down"], prec, mxfp8)
         dx = dx + rs["dX"]
         out = dict(dws_gate=of32(rs["dw_gate"]), dws_up=of32(rs["dw_up"]),
                    dws_down=of32(rs["dw_down"]), dX_shared=rs["dX"])

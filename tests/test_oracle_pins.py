@@ -644,3 +644,71 @@ def test_swiglu_ffn_mxfp8_by_brute_force():
     assert np.allclose(ref["h"], hq_all, rtol=2.0 ** -3, atol=0)
     y_bf16 = torch.from_numpy(y).float().to(torch.bfloat16).double().numpy()
     assert np.allclose(O.as64(ref["y"]), y_bf16, rtol=2.0 ** -7, atol=1e-12)
+
+
+def test_expert_backward_mxfp8_by_brute_force():
+    """The MXFP8 data-gradient GEMMs on a tiny case with Python loops: dY and
+    the columns of W_d quantised along d give dh; [dg | du] and the columns
+    of [W_g; W_u] quantised along F give dX (rounded to bf16).  The MX
+    rounding is the brute-force one (table search over torch's E4M3
+    decoding, frexp exponents), independent of the oracle's."""
+    import math
+    codes = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    table = [(c, float(codes[c])) for c in range(256) if np.isfinite(codes[c]) and codes[c] >= 0]
+    table += [(c, float(codes[c])) for c in range(256) if np.isfinite(codes[c]) and codes[c] < 0]
+    rng = np.random.default_rng(29)
+    n, d, F = 3, 64, 64
+    rb = O.round_bf16
+    dY = rb(rng.standard_normal((n, d)) * np.exp2(rng.integers(-3, 3, (n, 1))))
+    x = rb(rng.standard_normal((n, d)))
+    gu = rb(rng.standard_normal((n, 2 * F)))
+    wg, wu = rb(rng.standard_normal((F, d)) * 0.1), rb(rng.standard_normal((F, d)) * 0.1)
+    wd = rb(rng.standard_normal((d, F)) * 0.1)
+    ref = O.expert_backward(dY, x, gu, wg, wu, wd, "bf16", mxfp8=True)
+    dYq = [_mx_round_brute(dY[i], table) for i in range(n)]
+    wd_cols = [_mx_round_brute(wd[:, f], table) for f in range(F)]
+    dgu = np.zeros((n, 2 * F))
+    for i in range(n):
+        for f in range(F):
+            dh = sum(dYq[i][c] * wd_cols[f][c] for c in range(d))
+            g, u = gu[i, f], gu[i, F + f]
+            s = 1.0 / (1.0 + math.exp(-g))
+            dgu[i, f] = float(rb(np.array(dh * u * s * (1.0 + g * (1.0 - s)))))
+            dgu[i, F + f] = float(rb(np.array(dh * g * s)))
+    # dh is summed in another order here, so a bf16 rounding may differ
+    assert np.mean(ref["dg"] == dgu[:, :F]) >= 0.97 and np.mean(ref["du"] == dgu[:, F:]) >= 0.97
+    assert np.allclose(ref["dg"], dgu[:, :F], rtol=2.0 ** -7, atol=1e-12)
+    wcat = np.concatenate([wg, wu], axis=0)
+    w_cols = [_mx_round_brute(wcat[:, c], table) for c in range(d)]
+    dguq = [_mx_round_brute(np.concatenate([ref["dg"][i], ref["du"][i]]), table) for i in range(n)]
+    dX = np.array([[sum(dguq[i][k] * w_cols[c][k] for k in range(2 * F)) for c in range(d)]
+                   for i in range(n)])
+    assert np.allclose(O.as64(ref["dX"]), rb(dX), rtol=2.0 ** -7, atol=1e-12)
+    # the weight gradients use the unquantised operands
+    plain = O.expert_backward(dY, x, gu, wg, wu, wd, "bf16")
+    assert np.array_equal(plain["dw_down"], ref["dw_down"])   # dY^T h: nothing quantised
+    assert np.allclose(ref["dw_gate"], ref["dg"].T @ x, rtol=1e-12, atol=1e-12)
+
+
+def test_expert_backward_mxfp8_is_exact_on_mx_representable_operands():
+    """When dY and W_d hold values that MXFP8 represents exactly (block
+    maxima 2, elements in {0, +-1/2, +-1, +-2}: codes 64, 128, 256 times
+    2^-7), dh is unchanged by quantisation, so dg, du, h and every weight
+    gradient equal the bf16 backward's bit for bit."""
+    rng = np.random.default_rng(31)
+    n, d, F = 5, 64, 32
+    vals = np.array([0.0, 0.5, -0.5, 1.0, -1.0, 2.0, -2.0])
+    dY = rng.choice(vals, (n, d))
+    dY[:, ::32] = 2.0                                   # every block's amax is 2
+    wd = rng.choice(vals, (d, F))
+    wd[::32, :] = -2.0
+    x = O.round_bf16(rng.standard_normal((n, d)))
+    gu = O.round_bf16(rng.standard_normal((n, 2 * F)))
+    wg, wu = (O.round_bf16(rng.standard_normal((F, d)) * 0.1) for _ in range(2))
+    assert np.array_equal(O.mx_round(dY), dY) and np.array_equal(O.mx_round(wd.T).T, wd)
+    a = O.expert_backward(dY, x, gu, wg, wu, wd, "bf16", mxfp8=True)
+    b = O.expert_backward(dY, x, gu, wg, wu, wd, "bf16")
+    for key in ("dg", "du", "dw_down", "dw_gate", "dw_up"):
+        assert np.array_equal(a[key], b[key]), key
+    assert not np.array_equal(a["dX"], b["dX"])          # dg | du are not MX-exact
+    assert np.allclose(a["dX"], b["dX"], rtol=0.15, atol=0.05 * np.abs(b["dX"]).max())

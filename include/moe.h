@@ -79,7 +79,8 @@ enum {
   MOE_OP_BACKWARD = 4,
   MOE_OP_FFN_MXFP8 = 5,
   MOE_OP_BACKWARD_RECOMPUTE = 6,  /* moe_ffn_backward with gu_save NULL */
-  MOE_OP_FFN_COMBINE = 7          /* moe_grouped_ffn_combine */
+  MOE_OP_FFN_COMBINE = 7,         /* moe_grouped_ffn_combine */
+  MOE_OP_BACKWARD_MXFP8 = 8       /* moe_ffn_backward_mxfp8 */
 };
 
 /* The layer's parameters: tokens T, hidden d, routed experts E, experts per
@@ -334,6 +335,58 @@ int moe_grouped_ffn_mxfp8(const moe_shape* shape, const uint8_t* xq,
                           const uint8_t* ws_down_q, const uint8_t* ws_down_s,
                           void* y_perm, void* y_shared, void* ws,
                           size_t ws_bytes, void* stream);
+
+/* MXFP8 quantisation along the ROWS of each of `batches` row-major
+ * [rows, cols] bf16 matrices, written transposed (Primus blog, low-precision
+ * section: MXFP8 block scaling, applied to the backward's GEMMs, which read
+ * the weights against their storage order): element (r, c) of batch b is
+ * quantised with rows 32 (r / 32) .. + 31 of its column, by the rule of
+ * moe_mx_quantize, and written as code q[(b * cols + c) * ldq + r] with
+ * scale byte scales[(b * cols + c) * (ldq / 32) + r / 32].  With ldq > rows
+ * several matrices can share one output row (the backward's [w_gate; w_up]
+ * concatenation along F: w_gate into q, w_up into q + F, scales + F / 32).
+ *  rows % 32 == 0, ldq % 32 == 0, ldq >= rows, batches <= 65535; q 8-byte
+ *  aligned, src 16-byte aligned; else MOE_ERR_INVALID_ARG. */
+int moe_mx_quantize_t(const void* src, int64_t batches, int32_t rows, int32_t cols,
+                      int32_t ldq, uint8_t* q, uint8_t* scales, void* stream);
+
+/* The layer's backward with its two data-gradient GEMMs on MXFP8 operands
+ * (Primus blog, low-precision section: the grouped expert GEMMs of the
+ * backward in MXFP8), each quantised along its contraction dimension:
+ *   dh      = dY_perm_q . w_down_q   (dY_perm and w_down along d)
+ *   dX_perm = [dg | du]_q . [w_gate; w_up]_q   (along F)
+ * dY_perm is quantised inside the call; dg | du are quantised in dh's
+ * epilogue after rounding to bf16.  Everything else is moe_ffn_backward's:
+ * the dispatch gradient, d_gate and d_logits, the SwiGLU backward (dh stays
+ * fp32 until dg, du and h are rounded to bf16), the weight-gradient GEMMs
+ * in bf16 with fp32 accumulation (stored as shape.wgrad_dtype), and the dx
+ * gather.  The shared expert (F_shared > 0) gets the same over all T tokens,
+ * with dy quantised along d.
+ *
+ *  dy, x_perm, gu_save (required: no recomputation), y_perm, maps, topk_*,
+ *      logits, x and every output as in moe_ffn_backward.
+ *  w_down_tq [E, F, d], w_down_ts [E, F, d / 32]: w_down quantised along d
+ *      (moe_mx_quantize_t with batches E, rows d, cols F, ldq d).
+ *  w_gu_tq [E, d, 2F], w_gu_ts [E, d, 2F / 32]: w_gate then w_up quantised
+ *      along F (moe_mx_quantize_t of each with rows F, cols d, ldq 2F; w_up
+ *      at column offset F).
+ *  ws_down_tq/ts [Fs, d], ws_gu_tq/ts [d, 2Fs]: the shared expert's, likewise
+ *      (read only when F_shared > 0).
+ * shape.dtype must be MOE_DTYPE_BF16; d, F and F_shared multiples of 128
+ * (else MOE_ERR_UNSUPPORTED).
+ *  ws: MOE_OP_BACKWARD_MXFP8 bytes. */
+int moe_ffn_backward_mxfp8(const moe_shape* shape, const void* dy, const void* x_perm,
+                           const void* gu_save, const void* y_perm,
+                           const int32_t* expert_offsets, const int32_t* row_token,
+                           const int32_t* token_row, const int32_t* topk_idx,
+                           const float* topk_w, const float* logits,
+                           const uint8_t* w_down_tq, const uint8_t* w_down_ts,
+                           const uint8_t* w_gu_tq, const uint8_t* w_gu_ts, const void* x,
+                           const uint8_t* ws_down_tq, const uint8_t* ws_down_ts,
+                           const uint8_t* ws_gu_tq, const uint8_t* ws_gu_ts, float* dx,
+                           void* dw_gate, void* dw_up, void* dw_down, void* dws_gate,
+                           void* dws_up, void* dws_down, float* d_gate, float* d_logits,
+                           void* ws, size_t ws_bytes, void* stream);
 
 /* Static text for a moe_status value (never NULL). */
 const char* moe_status_string(int status);

@@ -28,12 +28,13 @@ MOE_DTYPE_BF16 = 1
 MOE_SCORE_SOFTMAX = 0
 MOE_SCORE_SIGMOID = 1
 (MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_FFN, MOE_OP_COMBINE, MOE_OP_BACKWARD,
- MOE_OP_FFN_MXFP8, MOE_OP_BACKWARD_RECOMPUTE, MOE_OP_FFN_COMBINE) = range(8)
+ MOE_OP_FFN_MXFP8, MOE_OP_BACKWARD_RECOMPUTE, MOE_OP_FFN_COMBINE,
+ MOE_OP_BACKWARD_MXFP8) = range(9)
 
 EXPORTED = ("moe_workspace_size", "moe_route_topk", "moe_permute",
             "moe_grouped_ffn", "moe_unpermute_combine", "moe_ffn_backward",
             "moe_status_string", "moe_mx_quantize", "moe_grouped_ffn_mxfp8",
-            "moe_grouped_ffn_combine")
+            "moe_grouped_ffn_combine", "moe_mx_quantize_t", "moe_ffn_backward_mxfp8")
 
 
 class MoeShape(ctypes.Structure):
@@ -69,6 +70,9 @@ def load() -> ctypes.CDLL:
     lib.moe_grouped_ffn.argtypes = [sp] + [vp] * 13 + [vp, sz, vp]
     lib.moe_unpermute_combine.argtypes = [sp] + [vp] * 5 + [vp, sz, vp]
     lib.moe_grouped_ffn_combine.argtypes = [sp] + [vp] * 12 + [vp, sz, vp]
+    lib.moe_mx_quantize_t.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_int32, vp, vp, vp]
+    lib.moe_ffn_backward_mxfp8.argtypes = [sp] + [vp] * 28 + [vp, sz, vp]
     lib.moe_ffn_backward.argtypes = [sp] + [vp] * 26 + [vp, sz, vp]
     lib.moe_mx_quantize.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
     lib.moe_grouped_ffn_mxfp8.argtypes = [sp] + [vp] * 18 + [vp, sz, vp]
@@ -161,6 +165,30 @@ def moe_grouped_ffn_combine(shape, x_perm, row_token, row_gate, expert_offsets,
         _p(ws_gate), _p(ws_up), _p(ws_down), _p(y), _p(ws), ws_bytes,
         _stream(stream))
     return _check(st, "moe_grouped_ffn_combine") if check else st
+
+
+def moe_mx_quantize_t(src, batches, rows, cols, ldq, q, scales, stream=None, check=True):
+    st = load().moe_mx_quantize_t(_p(src), batches, rows, cols, ldq, _p(q), _p(scales),
+                                  _stream(stream))
+    return _check(st, "moe_mx_quantize_t") if check else st
+
+
+def moe_ffn_backward_mxfp8(shape, dy, x_perm, gu_save, y_perm, expert_offsets,
+                           row_token, token_row, topk_idx, topk_w, logits,
+                           w_down_tq, w_down_ts, w_gu_tq, w_gu_ts, x,
+                           ws_down_tq, ws_down_ts, ws_gu_tq, ws_gu_ts, dx,
+                           dw_gate, dw_up, dw_down, dws_gate, dws_up, dws_down,
+                           d_gate, d_logits, ws=None, ws_bytes=0, stream=None,
+                           check=True):
+    st = load().moe_ffn_backward_mxfp8(
+        ctypes.byref(shape), _p(dy), _p(x_perm), _p(gu_save), _p(y_perm),
+        _p(expert_offsets), _p(row_token), _p(token_row), _p(topk_idx),
+        _p(topk_w), _p(logits), _p(w_down_tq), _p(w_down_ts), _p(w_gu_tq),
+        _p(w_gu_ts), _p(x), _p(ws_down_tq), _p(ws_down_ts), _p(ws_gu_tq),
+        _p(ws_gu_ts), _p(dx), _p(dw_gate), _p(dw_up), _p(dw_down),
+        _p(dws_gate), _p(dws_up), _p(dws_down), _p(d_gate), _p(d_logits),
+        _p(ws), ws_bytes, _stream(stream))
+    return _check(st, "moe_ffn_backward_mxfp8") if check else st
 
 
 def moe_unpermute_combine(shape, y_perm, token_row, topk_w, y_shared, y,

@@ -73,6 +73,17 @@ size_t ws_bytes_for(const moe_shape& s, int op) {
         b += align_up((R * 2 * s.F + (size_t)s.T * 2 * s.F_shared) * es);
       return b;
     }
+    case MOE_OP_BACKWARD_MXFP8: {   // the bf16 backward's, plus the quantised GEMM inputs
+      size_t b = ws_bytes_for(s, MOE_OP_BACKWARD);
+      b += align_up(R * s.d) + align_up(R * s.d / 32) + align_up(R * 2 * s.F) +
+           align_up(R * 2 * s.F / 32);
+      if (s.F_shared > 0) {
+        const size_t T = (size_t)s.T, Fs = (size_t)s.F_shared;
+        b += align_up(T * s.d) + align_up(T * s.d / 32) + align_up(T * 2 * Fs) +
+             align_up(T * 2 * Fs / 32);
+      }
+      return b;
+    }
     case MOE_OP_FFN_COMBINE:   // no split-K partials: slices add into y
       return 2 * align_up((s.E + 1) * 4) + align_up(R * s.F * es) +
              align_up((size_t)s.T * s.F_shared * es);
@@ -104,6 +115,26 @@ struct Carver {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// The backward's workspace pieces, in MOE_OP_BACKWARD's order.
+void carve_backward(const moe_shape& s, Carver& c, moe::BwdWs& bw) {
+  const size_t R = (size_t)s.T * s.k, es = esize(s);
+  bw = moe::BwdWs{};
+  bw.tiles = c.take<int32_t>((s.E + 1) * 4);
+  bw.tiles2 = c.take<int32_t>((s.E + 1) * 4);
+  bw.dY = c.take<char>(R * s.d * es);
+  bw.dX = c.take<char>(R * s.d * es);
+  bw.dgu = c.take<char>(R * 2 * s.F * es);
+  bw.h = c.take<char>(R * s.F * es);
+  if (s.F_shared > 0) {
+    bw.s_offsets = c.take<int32_t>(2 * 4);
+    bw.s_tiles = c.take<int32_t>(2 * 4);
+    bw.s_tiles2 = c.take<int32_t>(2 * 4);
+    bw.s_dgu = c.take<char>((size_t)s.T * 2 * s.F_shared * es);
+    bw.s_h = c.take<char>((size_t)s.T * s.F_shared * es);
+    bw.s_dX = c.take<char>((size_t)s.T * s.d * es);
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -111,7 +142,7 @@ extern "C" {
 int moe_workspace_size(const moe_shape* shape, int op, size_t* bytes) {
   const int st = check_shape(shape);
   if (st != MOE_OK) return st;
-  if (!bytes || op < MOE_OP_ROUTE || op > MOE_OP_FFN_COMBINE) return MOE_ERR_INVALID_ARG;
+  if (!bytes || op < MOE_OP_ROUTE || op > MOE_OP_BACKWARD_MXFP8) return MOE_ERR_INVALID_ARG;
   *bytes = ws_bytes_for(*shape, op);
   return MOE_OK;
 }
@@ -328,22 +359,7 @@ int moe_ffn_backward(const moe_shape* shape, const void* dy, const void* x_perm,
   if ((st = check_ws(s, op, ws, ws_bytes)) != MOE_OK) return st;
   Carver c{static_cast<char*>(ws)};
   moe::BwdWs bw;
-  bw.tiles = c.take<int32_t>((s.E + 1) * 4);
-  bw.tiles2 = c.take<int32_t>((s.E + 1) * 4);
-  bw.dY = c.take<char>((size_t)R * s.d * es);
-  bw.dX = c.take<char>((size_t)R * s.d * es);
-  bw.dgu = c.take<char>((size_t)R * 2 * s.F * es);
-  bw.h = c.take<char>((size_t)R * s.F * es);
-  bw.s_offsets = bw.s_tiles = bw.s_tiles2 = nullptr;
-  bw.s_dgu = bw.s_h = bw.s_dX = nullptr;
-  if (s.F_shared > 0) {
-    bw.s_offsets = c.take<int32_t>(2 * 4);
-    bw.s_tiles = c.take<int32_t>(2 * 4);
-    bw.s_tiles2 = c.take<int32_t>(2 * 4);
-    bw.s_dgu = c.take<char>((size_t)s.T * 2 * s.F_shared * es);
-    bw.s_h = c.take<char>((size_t)s.T * s.F_shared * es);
-    bw.s_dX = c.take<char>((size_t)s.T * s.d * es);
-  }
+  carve_backward(s, c, bw);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (recompute) {
     void* gu = c.take<char>((size_t)gu_elems * es);
@@ -368,6 +384,22 @@ int moe_mx_quantize(const void* src, int64_t rows, int32_t cols, uint8_t* q, uin
   if (!ok_buf(src, n * 2) || !ok_buf(q, n) || !ok_buf(scales, n / 32)) return MOE_ERR_INVALID_ARG;
   return hip_status(moe::launch_mx_quantize(src, rows, cols, q, scales,
                                             static_cast<hipStream_t>(stream)));
+}
+
+int moe_mx_quantize_t(const void* src, int64_t batches, int32_t rows, int32_t cols, int32_t ldq,
+                      uint8_t* q, uint8_t* scales, void* stream) {
+  if (batches < 0 || batches > 65535 || rows < 0 || rows % 32 != 0 || cols < 0 ||
+      ldq < rows || ldq % 32 != 0)
+    return MOE_ERR_INVALID_ARG;
+  const long long n = batches * (long long)rows * cols;
+  const long long nq = batches * (long long)cols * ldq;
+  if (n >= (1LL << 40) || nq >= (1LL << 40)) return MOE_ERR_INVALID_ARG;
+  if (n == 0) return MOE_OK;
+  // codes are written 8 bytes at a time; scale bytes one at a time
+  if (!ok_buf(src, n * 2) || !q || (reinterpret_cast<uintptr_t>(q) & 7) != 0 || !scales)
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_mx_quantize_t(src, batches, rows, cols, ldq, q, scales,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 int moe_grouped_ffn_mxfp8(const moe_shape* shape, const uint8_t* xq, const uint8_t* xs,
@@ -413,6 +445,74 @@ int moe_grouped_ffn_mxfp8(const moe_shape* shape, const uint8_t* xq, const uint8
   return hip_status(moe::launch_grouped_ffn_mxfp8(s, xq, xs, row_token, expert_offsets, w,
                                                   y_perm, y_shared, fw,
                                                   static_cast<hipStream_t>(stream)));
+}
+
+int moe_ffn_backward_mxfp8(const moe_shape* shape, const void* dy, const void* x_perm,
+                           const void* gu_save, const void* y_perm,
+                           const int32_t* expert_offsets, const int32_t* row_token,
+                           const int32_t* token_row, const int32_t* topk_idx,
+                           const float* topk_w, const float* logits,
+                           const uint8_t* w_down_tq, const uint8_t* w_down_ts,
+                           const uint8_t* w_gu_tq, const uint8_t* w_gu_ts, const void* x,
+                           const uint8_t* ws_down_tq, const uint8_t* ws_down_ts,
+                           const uint8_t* ws_gu_tq, const uint8_t* ws_gu_ts, float* dx,
+                           void* dw_gate, void* dw_up, void* dw_down, void* dws_gate,
+                           void* dws_up, void* dws_down, float* d_gate, float* d_logits,
+                           void* ws, size_t ws_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape& s = *shape;
+  if (s.dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
+  if (s.d % 128 != 0 || s.F % 128 != 0 || s.F_shared % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  const long long R = (long long)s.T * s.k;
+  const long long wsz = (long long)s.E * s.F * s.d;
+  const long long wes = s.wgrad_dtype == MOE_DTYPE_BF16 ? 2 : 4;
+  const long long gu_elems = R * 2 * s.F + (long long)s.T * 2 * s.F_shared;
+  // every quantised weight: codes one byte per value, scales one per 32
+  auto ok_q = [](const uint8_t* q, const uint8_t* sc, long long n) {
+    return ok_buf(q, n) && ok_buf(sc, n / 32);
+  };
+  if (s.F_shared > 0) {
+    const long long sz = (long long)s.F_shared * s.d;
+    if (!ok_buf(x, (long long)s.T * s.d * 2) || !ok_q(ws_down_tq, ws_down_ts, sz) ||
+        !ok_q(ws_gu_tq, ws_gu_ts, 2 * sz) || !ok_buf(dws_gate, sz * wes) ||
+        !ok_buf(dws_up, sz * wes) || !ok_buf(dws_down, sz * wes))
+      return MOE_ERR_INVALID_ARG;
+  }
+  if (!ok_buf(dy, (long long)s.T * s.d * 2) || !ok_buf(x_perm, R * s.d * 2) ||
+      gu_save == nullptr || !ok_buf(gu_save, gu_elems * 2) || !ok_buf(y_perm, R * s.d * 2) ||
+      !ok_buf(expert_offsets, (long long)(s.E + 1) * 4) || !ok_buf(row_token, R * 4) ||
+      !ok_buf(token_row, R * 4) || !ok_buf(topk_idx, R * 4) || !ok_buf(topk_w, R * 4) ||
+      !ok_buf(logits, (long long)s.T * s.E * 4) || !ok_q(w_down_tq, w_down_ts, wsz) ||
+      !ok_q(w_gu_tq, w_gu_ts, 2 * wsz) || !ok_buf(dx, (long long)s.T * s.d * 4) ||
+      !ok_buf(dw_gate, wsz * wes) || !ok_buf(dw_up, wsz * wes) ||
+      !ok_buf(dw_down, wsz * wes) || !ok_buf(d_gate, R * 4) ||
+      !ok_buf(d_logits, (long long)s.T * s.E * 4))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(s, MOE_OP_BACKWARD_MXFP8, ws, ws_bytes)) != MOE_OK) return st;
+  Carver c{static_cast<char*>(ws)};
+  moe::BwdWs bw;
+  carve_backward(s, c, bw);
+  bw.dyq = c.take<uint8_t>((size_t)R * s.d);
+  bw.dys = c.take<uint8_t>((size_t)R * s.d / 32);
+  bw.dguq = c.take<uint8_t>((size_t)R * 2 * s.F);
+  bw.dgus = c.take<uint8_t>((size_t)R * 2 * s.F / 32);
+  bw.s_dyq = bw.s_dys = bw.s_dguq = bw.s_dgus = nullptr;
+  if (s.F_shared > 0) {
+    const size_t T = (size_t)s.T, Fs = (size_t)s.F_shared;
+    bw.s_dyq = c.take<uint8_t>(T * s.d);
+    bw.s_dys = c.take<uint8_t>(T * s.d / 32);
+    bw.s_dguq = c.take<uint8_t>(T * 2 * Fs);
+    bw.s_dgus = c.take<uint8_t>(T * 2 * Fs / 32);
+  }
+  moe::MxBwdWeights mw = {w_down_tq, w_down_ts, w_gu_tq, w_gu_ts,
+                          ws_down_tq, ws_down_ts, ws_gu_tq, ws_gu_ts};
+  return hip_status(moe::launch_backward(s, dy, x_perm, gu_save, y_perm, expert_offsets,
+                                         row_token, token_row, topk_idx, topk_w, logits,
+                                         nullptr, nullptr, nullptr, x, nullptr, nullptr,
+                                         nullptr, dx, dw_gate, dw_up, dw_down, dws_gate,
+                                         dws_up, dws_down, d_gate, d_logits, bw,
+                                         static_cast<hipStream_t>(stream), &mw));
 }
 
 }  // extern "C"

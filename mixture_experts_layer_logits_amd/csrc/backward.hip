@@ -909,6 +909,22 @@ static hipError_t run_backward_any(const moe_shape& s, BwdArgs& a, const BwdWs& 
   return run_backward<float, 0>(s, a, ws, st);
 }
 
+// The weight-gradient GEMMs alone (bf16), after data gradients computed
+// elsewhere (the MXFP8 path) have written h and dg | du.
+static hipError_t run_wgrad_any(const moe_shape& s, const BwdArgs& a, hipStream_t st) {
+  if (bwd_uses_dma(s)) {
+    launch_bwd_gemm<BWD_WD, bf16_t, 2>(s, a, st);
+    launch_bwd_gemm<BWD_WGU, bf16_t, 2>(s, a, st);
+  } else if (bwd_uses_mfma(s)) {
+    launch_bwd_gemm<BWD_WD, bf16_t, 1>(s, a, st);
+    launch_bwd_gemm<BWD_WGU, bf16_t, 1>(s, a, st);
+  } else {
+    launch_bwd_gemm<BWD_WD, bf16_t, 0>(s, a, st);
+    launch_bwd_gemm<BWD_WGU, bf16_t, 0>(s, a, st);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_backward(const moe_shape& s, const void* dy, const void* x_perm,
                            const void* gu_save, const void* y_perm, const int32_t* offsets,
                            const int32_t* row_token, const int32_t* token_row,
@@ -918,7 +934,7 @@ hipError_t launch_backward(const moe_shape& s, const void* dy, const void* x_per
                            const void* ws_up, const void* ws_down, float* dx, void* dw_gate,
                            void* dw_up, void* dw_down, void* dws_gate, void* dws_up,
                            void* dws_down, float* d_gate, float* d_logits,
-                           const BwdWs& ws, hipStream_t st) {
+                           const BwdWs& ws, hipStream_t st, const MxBwdWeights* mx) {
   (void)row_token;
   const bool bf = s.dtype == MOE_DTYPE_BF16;
   if (s.T > 0) {
@@ -953,7 +969,19 @@ hipError_t launch_backward(const moe_shape& s, const void* dy, const void* x_per
   a.dw_gate = dw_gate;
   a.wgrad_bf16 = s.wgrad_dtype == MOE_DTYPE_BF16;
   a.dw_up = dw_up;
-  hipError_t e = run_backward_any(s, a, ws, st);
+  const int R = s.T * s.k;
+  hipError_t e;
+  if (mx) {
+    // MXFP8 data gradients: dY_perm quantised along d, then dh (with the
+    // SwiGLU backward) and dX on the quantised operands; bf16 weight gradients
+    if ((e = launch_mx_quantize(ws.dY, R, s.d, ws.dyq, ws.dys, st)) != hipSuccess) return e;
+    MxDgrad g = {R, offsets, ws.tiles, ws.tiles2, ws.dyq, ws.dys, mx->wd_tq, mx->wd_ts,
+                 gu_save, ws.dgu, ws.h, ws.dguq, ws.dgus, mx->wgu_tq, mx->wgu_ts, ws.dX};
+    if ((e = launch_mx_dgrad(s, g, st)) != hipSuccess) return e;
+    e = run_wgrad_any(s, a, st);
+  } else {
+    e = run_backward_any(s, a, ws, st);
+  }
   if (e != hipSuccess) return e;
   const bool shared = s.F_shared > 0 && s.T > 0;
   if (shared) {
@@ -989,7 +1017,16 @@ hipError_t launch_backward(const moe_shape& s, const void* dy, const void* x_per
     BwdWs w2 = ws;
     w2.tiles = ws.s_tiles;
     w2.tiles2 = ws.s_tiles2;
-    if ((e = run_backward_any(s2, b, w2, st)) != hipSuccess) return e;
+    if (mx) {
+      if ((e = launch_mx_quantize(dy, s.T, s.d, ws.s_dyq, ws.s_dys, st)) != hipSuccess) return e;
+      MxDgrad g = {s.T, ws.s_offsets, ws.s_tiles, ws.s_tiles2, ws.s_dyq, ws.s_dys,
+                   mx->swd_tq, mx->swd_ts, b.gu, ws.s_dgu, ws.s_h, ws.s_dguq, ws.s_dgus,
+                   mx->swgu_tq, mx->swgu_ts, ws.s_dX};
+      if ((e = launch_mx_dgrad(s2, g, st)) != hipSuccess) return e;
+      if ((e = run_wgrad_any(s2, b, st)) != hipSuccess) return e;
+    } else if ((e = run_backward_any(s2, b, w2, st)) != hipSuccess) {
+      return e;
+    }
   }
   if (s.T > 0) {
     if (bf)

@@ -39,8 +39,9 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 // EPI_COMBINE: no C; each result row is scaled by its row's gate and added
-// (fp32 atomics) into Y at its token's row.
-enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_F32_BIAS = 2, EPI_COMBINE = 3 };
+// (fp32 atomics) into Y at its token's row.  EPI_DSWIGLU (MXFP8 kernel
+// only): the SwiGLU backward of the result dh.
+enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_F32_BIAS = 2, EPI_COMBINE = 3, EPI_DSWIGLU = 4 };
 
 struct GemmArgs {
   // routed groups (E == 0: none)
@@ -104,6 +105,7 @@ struct TileJob {
   float* P;                // split-K partial rows of the group, or null
   int cls;                 // 0: BM x BN tile, 1: BM/2 x 2BN tail tile
   int dense;               // 1: the dense group, 0: a routed group
+  int row0;                // first row of the group (routed), else 0
   const int32_t* ctok;     // EPI_COMBINE: token of each routed row, or null (dense)
   const float* cgate;      // EPI_COMBINE: gate of each routed row, or null (gate 1)
 };
@@ -154,6 +156,7 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, TileJob<TIn, TOut
     const int g = lo;
     j.dense = 0;
     const int row0 = a.offsets[g];
+    j.row0 = row0;
     const int rows = a.offsets[g + 1] - row0;
     // Column tiles go in pairs: the full tiles of columns 2p and 2p+1 (row
     // tiles adjacent), then the group's tail tile over the same 2 BN columns,
@@ -202,6 +205,7 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, TileJob<TIn, TOut
   const int r = lid - routed;
   j.cls = 0;
   j.dense = 1;
+  j.row0 = 0;
   j.m0 = (r % dmt) * BM;
   j.n0 = (r / dmt) * BN;
   j.rows = a.Td;

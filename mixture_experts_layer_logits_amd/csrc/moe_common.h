@@ -23,6 +23,9 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   return static_cast<bf16_t>(u >> 16);
 }
 
+// The fp32 value of f rounded to bf16.
+__device__ __forceinline__ float bf16_round(float f) { return bf16_to_f32(f32_to_bf16(f)); }
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16(lo)) |
          (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
@@ -110,6 +113,26 @@ hipError_t launch_grouped_ffn_mxfp8(const moe_shape& s, const uint8_t* xq, const
                                     const MxWeights& w, void* y_perm, void* y_shared,
                                     const MxFfnWs& ws, hipStream_t st);
 
+hipError_t launch_mx_quantize_t(const void* src, long long batches, int rows, int cols, int ldq,
+                                uint8_t* q, uint8_t* scales, hipStream_t st);
+// The backward's MXFP8 data-gradient GEMMs over `rows` routed rows grouped
+// by `offsets` (shape.E groups).
+struct MxDgrad {
+  int rows;
+  const int32_t* offsets;
+  int32_t* tiles1;               // [E + 1] tile prefix of dh
+  int32_t* tiles2;               // [E + 1] tile prefix of dX
+  const uint8_t *dyq, *dys;      // dY_perm quantised along d: [rows, d], [rows, d / 32]
+  const uint8_t *wd_tq, *wd_ts;  // w_down quantised along d: [E, F, d], [E, F, d / 32]
+  const void* gu;                // [rows, 2F] bf16, the saved g | u
+  void* dgu;                     // [rows, 2F] bf16 out
+  void* h;                       // [rows, F] bf16 out
+  uint8_t *dguq, *dgus;          // dg | du quantised along F: [rows, 2F], [rows, 2F / 32]
+  const uint8_t *wgu_tq, *wgu_ts;  // [w_gate; w_up] quantised along F: [E, d, 2F], [E, d, 2F / 32]
+  void* dX;                      // [rows, d] bf16 out
+};
+hipError_t launch_mx_dgrad(const moe_shape& s, const MxDgrad& g, hipStream_t st);
+
 hipError_t launch_combine(const moe_shape& s, const void* y_perm, const int32_t* token_row,
                           const float* topk_w, const void* y_shared, float* y,
                           hipStream_t st);
@@ -128,6 +151,16 @@ struct BwdWs {
   void* s_dgu;         // [T, 2 F_shared] dtype
   void* s_h;           // [T, F_shared] dtype
   void* s_dX;          // [T, d] dtype
+  // MXFP8 data gradients only: the quantised GEMM inputs
+  uint8_t *dyq, *dys;       // [R, d], [R, d / 32]
+  uint8_t *dguq, *dgus;     // [R, 2F], [R, 2F / 32]
+  uint8_t *s_dyq, *s_dys;   // [T, d], [T, d / 32]: dy for the shared expert
+  uint8_t *s_dguq, *s_dgus; // [T, 2 F_shared], [T, 2 F_shared / 32]
+};
+// The quantised weights the MXFP8 data gradients read.
+struct MxBwdWeights {
+  const uint8_t *wd_tq, *wd_ts, *wgu_tq, *wgu_ts;      // routed
+  const uint8_t *swd_tq, *swd_ts, *swgu_tq, *swgu_ts;  // shared expert
 };
 bool backward_supported(const moe_shape& s);
 hipError_t launch_backward(const moe_shape& s, const void* dy, const void* x_perm,
@@ -139,6 +172,7 @@ hipError_t launch_backward(const moe_shape& s, const void* dy, const void* x_per
                            const void* ws_up, const void* ws_down, float* dx, void* dw_gate,
                            void* dw_up, void* dw_down, void* dws_gate, void* dws_up,
                            void* dws_down, float* d_gate, float* d_logits,
-                           const BwdWs& ws, hipStream_t st);
+                           const BwdWs& ws, hipStream_t st,
+                           const MxBwdWeights* mx = nullptr);
 
 }  // namespace moe

@@ -11,6 +11,14 @@
 //              (fp32 accumulate), quantised to MXFP8 along F in the epilogue
 //   FC2:       y_perm = hq . wd^T -> bf16
 //
+// Backward (data gradients; the weight gradients stay bf16):
+//   quantize_t: bf16 [B][rows, cols] -> codes [B][cols, rows] quantised
+//              along rows (weights read against their storage order)
+//   dh:        dYq . (w_down quantised along d)^T, epilogue: the SwiGLU
+//              backward from the saved g, u -> dg, du, h in bf16, and dg | du
+//              quantised along F for the next GEMM
+//   dX:        (dg | du)q . ([w_gate; w_up] quantised along F)^T -> bf16
+//
 // Both GEMMs read routed rows through row_token from the quantised x (the
 // permutation fused into FC1's operand load; quantising is row-wise, so
 // quantise-then-gather equals gather-then-quantise exactly).
@@ -127,6 +135,58 @@ hipError_t launch_mx_quantize(const void* src, long long rows, int cols, uint8_t
   return hipGetLastError();
 }
 
+// Transposed quantisation: element (r, c) of batch b of src [B][rows][cols]
+// becomes code q[(b cols + c) ldq + r], quantised with the 31 other rows of
+// its 32-row block, scale byte at sq[(b cols + c) (ldq / 32) + r / 32].  A
+// workgroup takes 32 rows x 64 columns through LDS; 4 lanes per column
+// quantise 8 rows each.
+__global__ void __launch_bounds__(256)
+mx_quantize_t_kernel(const bf16_t* __restrict__ src, int rows, int cols, int ldq,
+                     uint8_t* __restrict__ q, uint8_t* __restrict__ sq) {
+  __shared__ float tile[32][65];
+  const long long b = blockIdx.z;
+  const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 64;
+  for (int i = threadIdx.x; i < 32 * 64; i += 256) {
+    const int rr = i >> 6, cc = i & 63;
+    const int c = c0 + cc;
+    tile[rr][cc] = c < cols ? to_f32<bf16_t>(src[(b * rows + r0 + rr) * cols + c]) : 0.0f;
+  }
+  __syncthreads();
+  const int cc = threadIdx.x >> 2, part = threadIdx.x & 3;
+  float v[8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    v[p] = tile[8 * part + p][cc];
+    amax = fmaxf(amax, fabsf(v[p]));
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+  const int s = mx_scale_exp(amax);
+  const float inv = mx_inv_scale(s);
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    lo |= e4m3_code(v[p] * inv) << (8 * p);
+    hi |= e4m3_code(v[4 + p] * inv) << (8 * p);
+  }
+  const int c = c0 + cc;
+  if (c < cols) {
+    const long long orow = b * cols + c;
+    *reinterpret_cast<uint2*>(q + orow * ldq + r0 + 8 * part) = make_uint2(lo, hi);
+    if (part == 0) sq[orow * (ldq / 32) + r0 / 32] = (uint8_t)(s + 127);
+  }
+}
+
+hipError_t launch_mx_quantize_t(const void* src, long long batches, int rows, int cols, int ldq,
+                                uint8_t* q, uint8_t* scales, hipStream_t st) {
+  if (batches == 0 || rows == 0 || cols == 0) return hipSuccess;
+  const dim3 grid(cdiv(cols, 64), rows / 32, (unsigned)batches);
+  mx_quantize_t_kernel<<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(src), rows, cols, ldq,
+                                             q, scales);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Scaled-MFMA grouped GEMM tile kernel.
 //
@@ -155,6 +215,16 @@ struct MxScales {
   uint8_t* Cd;
 };
 
+// The SwiGLU-backward epilogue's other tensors (routed rows, row-major):
+// gu [R, 2F] the saved g | u, dgu [R, 2F] and h [R, F] bf16 outputs; the
+// GEMM's own C is the quantised dg | du [R, 2F] with scales in MxScales::C.
+struct MxBwd {
+  const bf16_t* gu;
+  bf16_t* dgu;
+  bf16_t* h;
+  int F;
+};
+
 // The shape of one tile class: CLS 0 is BM x BN with WM x WN waves and a
 // four-stage ring; CLS 1 (tail tiles) is BM/2 x 2BN with (WM/2) x (2WN) waves,
 // so each wave keeps its (BM/WM) x (BN/WN) block and registers, and a
@@ -179,10 +249,13 @@ struct MxShape {
   static_assert(ROWS % (16 * NW) == 0 && BMC % 64 == 0 && BNC % 64 == 0, "load blocks");
 };
 
+template <int EPI>
+using MxOut = typename std::conditional<EPI == EPI_SWIGLU || EPI == EPI_DSWIGLU, uint8_t,
+                                        bf16_t>::type;
+
 template <int BM, int BN, int NB, int EPI, int WM, int WN, int SG, int CLS>
 __device__ __forceinline__ void mx_tile(const GemmArgs& args, const MxScales& sc,
-                                        const TileJob<uint8_t, typename std::conditional<
-                                            EPI == EPI_SWIGLU, uint8_t, bf16_t>::type>& job,
+                                        const MxBwd& bw, const TileJob<uint8_t, MxOut<EPI>>& job,
                                         uint8_t* ring, uint8_t* sring) {
   using S = MxShape<BM, BN, NB, WM, WN, SG, CLS>;
   constexpr int NW = S::NW, BMC = S::BMC, BNC = S::BNC, WNC = S::WNC, NS = S::NS;
@@ -222,7 +295,7 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& args, const MxScales& sc
     sA = sc.A + (job.A - static_cast<const uint8_t*>(args.A)) / 32;
     sB0 = sc.B0 + (job.B0 - static_cast<const uint8_t*>(args.B0)) / 32;
     sB1 = NB > 1 ? sc.B1 + (job.B1 - static_cast<const uint8_t*>(args.B1)) / 32 : nullptr;
-    sC = (EPI == EPI_SWIGLU)
+    sC = (EPI == EPI_SWIGLU || EPI == EPI_DSWIGLU)
              ? sc.C + (reinterpret_cast<const uint8_t*>(job.C) -
                        static_cast<const uint8_t*>(args.C)) / 32
              : nullptr;
@@ -561,6 +634,76 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& args, const MxScales& sc
           *reinterpret_cast<uint4*>(job.C + (long long)m * job.ldc + nblk + 16 * hsel) = out;
           if (hsel == 0) sC[(long long)m * (job.N / 32) + nblk / 32] = (uint8_t)(s + 127);
         }
+      } else if constexpr (EPI == EPI_DSWIGLU) {
+        // dh for row m, columns nblk + 8 q + 4 hsel + r.  With s = sigmoid(g):
+        // dg = dh u s (1 + g (1 - s)), du = dh g s, h = g s u, each rounded to
+        // bf16; then dg and du quantised per 32-column block (the lane pair
+        // holds one block of each) for the dX GEMM.
+        const int F = bw.F;
+        const long long rg = (long long)job.row0 + m;          // routed row
+        const bf16_t* gp = bw.gu + rg * 2 * F + nblk + 4 * hsel;
+        const f32x16_t& D = acc[0][i][j];
+        float dg[16], du[16];
+        float ag = 0.0f, au = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint2 gq = make_uint2(0u, 0u), uq = make_uint2(0u, 0u);
+          if (row_ok) {
+            gq = *reinterpret_cast<const uint2*>(gp + 8 * q);
+            uq = *reinterpret_cast<const uint2*>(gp + F + 8 * q);
+          }
+          const uint32_t gw[2] = {gq.x, gq.y}, uw[2] = {uq.x, uq.y};
+          float hh[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t gb = gw[r >> 1], ub = uw[r >> 1];
+            const float g = __uint_as_float((r & 1) ? (gb & 0xffff0000u) : (gb << 16));
+            const float u = __uint_as_float((r & 1) ? (ub & 0xffff0000u) : (ub << 16));
+            const float sg = 1.0f / (1.0f + __expf(-g));
+            const float sl = g * sg;
+            const float dh = D[4 * q + r];
+            // rounded to bf16 here, so the quantised blocks see the stored values
+            dg[4 * q + r] = bf16_round(dh * u * sg * (1.0f + g * (1.0f - sg)));
+            du[4 * q + r] = bf16_round(dh * sl);
+            hh[r] = sl * u;
+            ag = fmaxf(ag, fabsf(dg[4 * q + r]));
+            au = fmaxf(au, fabsf(du[4 * q + r]));
+          }
+          if (row_ok) {
+            const int n = nblk + 8 * q + 4 * hsel;
+            bf16_t* dgp = bw.dgu + rg * 2 * F + n;
+            *reinterpret_cast<uint2*>(dgp) = make_uint2(pack_bf16x2(dg[4 * q], dg[4 * q + 1]),
+                                                        pack_bf16x2(dg[4 * q + 2], dg[4 * q + 3]));
+            *reinterpret_cast<uint2*>(dgp + F) = make_uint2(pack_bf16x2(du[4 * q], du[4 * q + 1]),
+                                                            pack_bf16x2(du[4 * q + 2], du[4 * q + 3]));
+            *reinterpret_cast<uint2*>(bw.h + rg * F + n) =
+                make_uint2(pack_bf16x2(hh[0], hh[1]), pack_bf16x2(hh[2], hh[3]));
+          }
+        }
+        ag = fmaxf(ag, __shfl_xor(ag, 32, 64));
+        au = fmaxf(au, __shfl_xor(au, 32, 64));
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {             // 0: dg, 1: du
+          const float* hv = half ? du : dg;
+          const int s = mx_scale_exp(half ? au : ag);
+          const float inv = mx_inv_scale(s);
+          uint32_t d[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) w |= e4m3_code(hv[4 * q + r] * inv) << (8 * r);
+            d[q] = w;
+          }
+          const uint32_t x0 = __shfl_xor(hsel ? d[0] : d[2], 32, 64);
+          const uint32_t x1 = __shfl_xor(hsel ? d[1] : d[3], 32, 64);
+          const uint4 out = hsel ? make_uint4(x0, d[2], x1, d[3]) : make_uint4(d[0], x0, d[1], x1);
+          const int col = half * F + nblk;                  // column in dg | du
+          if (row_ok) {
+            *reinterpret_cast<uint4*>(job.C + (long long)m * job.ldc + col + 16 * hsel) = out;
+            if (hsel == 0) sC[(long long)m * (job.ldc / 32) + col / 32] = (uint8_t)(s + 127);
+          }
+        }
       } else {
         if (!row_ok) continue;
 #pragma unroll
@@ -579,13 +722,13 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& args, const MxScales& sc
 
 template <int BM, int BN, int NB, int EPI, int WM, int WN, int SG, int TL>
 __global__ void __launch_bounds__(64 * WM * WN)
-gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
+gemm_mx_kernel(const GemmArgs args, const MxScales sc, const MxBwd bw) {
   using S0 = MxShape<BM, BN, NB, WM, WN, SG, 0>;
   using S1 = MxShape<BM, BN, NB, WM, WN, SG, 1>;
   constexpr int RING = (TL && S1::RING > S0::RING) ? S1::RING : S0::RING;
   constexpr int SRING = (TL && S1::SRING > S0::SRING) ? S1::SRING : S0::SRING;
   static_assert(RING + SRING + 64 <= 160 * 1024, "LDS");
-  using TOut = typename std::conditional<EPI == EPI_SWIGLU, uint8_t, bf16_t>::type;
+  using TOut = MxOut<EPI>;
   // the operand ring, and beside it the scale slices (+64 bytes: the last
   // step's unused read of a next step may touch a byte past the end)
   __shared__ __attribute__((aligned(1024))) uint8_t ring[RING];
@@ -593,22 +736,23 @@ gemm_mx_kernel(const GemmArgs args, const MxScales sc) {
   TileJob<uint8_t, TOut> job;
   if (!decode_tile<BM, BN>(args, job)) return;
   if (TL && __builtin_amdgcn_readfirstlane(job.cls) != 0)
-    mx_tile<BM, BN, NB, EPI, WM, WN, SG, 1>(args, sc, job, ring, sring);
+    mx_tile<BM, BN, NB, EPI, WM, WN, SG, 1>(args, sc, bw, job, ring, sring);
   else
-    mx_tile<BM, BN, NB, EPI, WM, WN, SG, 0>(args, sc, job, ring, sring);
+    mx_tile<BM, BN, NB, EPI, WM, WN, SG, 0>(args, sc, bw, job, ring, sring);
 }
 
 // Scale loads are grouped eight K steps at a time when every group of the
 // launch has at least 16 scale bytes per row (K >= 512).
 template <int BM, int BN, int NB, int EPI, int WM, int WN>
-hipError_t launch_mx_gemm(const GemmArgs& a, const MxScales& sc, int R, hipStream_t st) {
+hipError_t launch_mx_gemm(const GemmArgs& a, const MxScales& sc, int R, hipStream_t st,
+                          const MxBwd& bw = MxBwd{}) {
   const int grid = grid_upper_bound(a, BM, BN, R);
   if (grid == 0) return hipSuccess;
   const bool grouped = (a.E == 0 || a.K >= 512) && (a.Td == 0 || a.Kd >= 512);
   if (grouped)
-    gemm_mx_kernel<BM, BN, NB, EPI, WM, WN, 8, 1><<<grid, 64 * WM * WN, 0, st>>>(a, sc);
+    gemm_mx_kernel<BM, BN, NB, EPI, WM, WN, 8, 1><<<grid, 64 * WM * WN, 0, st>>>(a, sc, bw);
   else
-    gemm_mx_kernel<BM, BN, NB, EPI, WM, WN, 1, 1><<<grid, 64 * WM * WN, 0, st>>>(a, sc);
+    gemm_mx_kernel<BM, BN, NB, EPI, WM, WN, 1, 1><<<grid, 64 * WM * WN, 0, st>>>(a, sc, bw);
   return hipGetLastError();
 }
 
@@ -688,6 +832,56 @@ hipError_t launch_grouped_ffn_mxfp8(const moe_shape& s, const uint8_t* xq, const
                                               ws.tiles2, 1);
   }
   hipError_t e = launch_mx_gemm<MX_FC1_BM, MX_FC1_BN, 2, EPI_SWIGLU, 4, 2>(a1, s1, R, st);
+  if (e != hipSuccess) return e;
+  return launch_mx_gemm<MX_FC2_BM, MX_FC2_BN, 1, EPI_STORE, 4, 2>(a2, s2, R, st);
+}
+
+// The backward's two data-gradient GEMMs over the routed groups (or one
+// group of all tokens for the shared expert): dh with the SwiGLU-backward
+// epilogue, then dX_perm.  F and d are multiples of 128.
+hipError_t launch_mx_dgrad(const moe_shape& s, const MxDgrad& g, hipStream_t st) {
+  const int R = g.rows;
+  GemmArgs a1 = {};
+  MxScales s1 = {};
+  a1.E = R > 0 ? s.E : 0;
+  a1.offsets = g.offsets;
+  a1.tiles = g.tiles1;
+  a1.A = g.dyq;
+  a1.lda = s.d;
+  a1.B0 = g.wd_tq;
+  a1.strideB = (long long)s.F * s.d;
+  a1.N = s.F;
+  a1.K = s.d;
+  a1.C = g.dguq;
+  a1.ldc = 2 * s.F;
+  s1.A = g.dys;
+  s1.B0 = g.wd_ts;
+  s1.C = g.dgus;
+  MxBwd bw;
+  bw.gu = static_cast<const bf16_t*>(g.gu);
+  bw.dgu = static_cast<bf16_t*>(g.dgu);
+  bw.h = static_cast<bf16_t*>(g.h);
+  bw.F = s.F;
+  GemmArgs a2 = {};
+  MxScales s2 = {};
+  a2.E = a1.E;
+  a2.offsets = g.offsets;
+  a2.tiles = g.tiles2;
+  a2.A = g.dguq;
+  a2.lda = 2 * s.F;
+  a2.B0 = g.wgu_tq;
+  a2.strideB = (long long)s.d * 2 * s.F;
+  a2.N = s.d;
+  a2.K = 2 * s.F;
+  a2.C = g.dX;
+  a2.ldc = s.d;
+  s2.A = g.dgus;
+  s2.B0 = g.wgu_ts;
+  if (a1.E == 0) return hipSuccess;
+  schedule_tiles_kernel<<<1, 1024, 0, st>>>(g.offsets, s.E, MX_FC2_BM, cdiv(s.F, MX_FC2_BN),
+                                            g.tiles1, MX_FC2_BM, cdiv(s.d, MX_FC2_BN), g.tiles2, 1);
+  a1.tail = a2.tail = 1;
+  hipError_t e = launch_mx_gemm<MX_FC2_BM, MX_FC2_BN, 1, EPI_DSWIGLU, 4, 2>(a1, s1, R, st, bw);
   if (e != hipSuccess) return e;
   return launch_mx_gemm<MX_FC2_BM, MX_FC2_BN, 1, EPI_STORE, 4, 2>(a2, s2, R, st);
 }

@@ -222,3 +222,51 @@ class MoELayer:
                            g["dws_up"], g["dws_down"], g["d_gate"],
                            g["d_logits"], self.ws, self.ws_bytes, stream)
         return g
+
+    # ------------------------------------------------------------------
+    # MXFP8 backward (data-gradient GEMMs in MXFP8, weight gradients bf16)
+    def quantize_weights_t(self, inp, stream=None):
+        """The weights quantised along the dimension the backward's data
+        gradients contract: w_down along d ([E, F, d]) and w_gate | w_up
+        along F ([E, d, 2F]); kept until the weights change."""
+        c, dev = self.cfg, self.device
+        u8 = torch.uint8
+
+        def pair(E, d, F, wd, wg, wu):
+            wd_q = torch.empty(E, F, d, dtype=u8, device=dev)
+            wd_s = torch.empty(E, F, d // 32, dtype=u8, device=dev)
+            L.moe_mx_quantize_t(wd, E, d, F, d, wd_q, wd_s, stream)
+            gu_q = torch.empty(E, d, 2 * F, dtype=u8, device=dev)
+            gu_s = torch.empty(E, d, 2 * F // 32, dtype=u8, device=dev)
+            L.moe_mx_quantize_t(wg, E, F, d, 2 * F, gu_q, gu_s, stream)
+            L.moe_mx_quantize_t(wu, E, F, d, 2 * F, gu_q.view(-1)[F:], gu_s.view(-1)[F // 32:],
+                                stream)
+            return wd_q, wd_s, gu_q, gu_s
+
+        out = {"routed": pair(c.E, c.d, c.F, inp["w_down"], inp["w_gate"], inp["w_up"])}
+        if c.F_shared:
+            out["shared"] = pair(1, c.d, c.F_shared, inp["ws_down"], inp["ws_gate"], inp["ws_up"])
+        self.mx_weights_t = out
+        return out
+
+    def backward_mxfp8(self, inp, dy, stream=None):
+        """The backward with MXFP8 data-gradient GEMMs (needs
+        quantize_weights_t() and a forward that saved g | u)."""
+        if getattr(self, "mx_weights_t", None) is None:
+            raise RuntimeError("call quantize_weights_t() before the MXFP8 backward")
+        if self.grad is None:
+            self._alloc_grad()
+        if getattr(self, "mx_bwd_ws", None) is None:
+            n = L.moe_workspace_size(self.shape, L.MOE_OP_BACKWARD_MXFP8)
+            self.mx_bwd_ws = (torch.empty(max(n, 256), dtype=torch.uint8, device=self.device), n)
+        b, g, w = self.buf, self.grad, self.mx_weights_t
+        ws, nws = self.mx_bwd_ws
+        sh = self.cfg.F_shared > 0
+        shw = w["shared"] if sh else (None, None, None, None)
+        L.moe_ffn_backward_mxfp8(
+            self.shape, dy, b["x_perm"], b["gu_save"], b["y_perm"],
+            b["expert_offsets"], b["row_token"], b["token_row"], b["topk_idx"],
+            b["topk_w"], b["logits"], *w["routed"], inp["x"] if sh else None, *shw,
+            g["dx"], g["dw_gate"], g["dw_up"], g["dw_down"], g["dws_gate"],
+            g["dws_up"], g["dws_down"], g["d_gate"], g["d_logits"], ws, nws, stream)
+        return g

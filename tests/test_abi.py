@@ -209,3 +209,34 @@ def test_ffn_combine_validates_before_launch():
         args[missing] = None
         st = M.moe_grouped_ffn_combine(s2, *args, p, need2, check=False, stream=0)
         assert st == L.MOE_ERR_INVALID_ARG, missing
+
+
+def test_mxfp8_backward_validates_before_launch():
+    """moe_ffn_backward_mxfp8: fp32 storage, widths that are not multiples
+    of 128, a missing gu_save and a small workspace are rejected; the
+    workspace adds the quantised dY and dg | du to the backward's.
+    moe_mx_quantize_t: row counts and pitches off the 32-grid are rejected."""
+    c = CONFIGS["qwen3_235b_train_t8192"]
+    s = M.make_shape(c)
+    p = _fake()
+    base = M.moe_workspace_size(s, L.MOE_OP_BACKWARD)
+    mx = M.moe_workspace_size(s, L.MOE_OP_BACKWARD_MXFP8)
+    R = c.T * c.k
+    assert mx - base >= R * c.d * 33 // 32 + R * 2 * c.F * 33 // 32
+    for cc, want in ((c.replace(dtype=0), L.MOE_ERR_INVALID_ARG),
+                     (c.replace(F=1536 + 64), L.MOE_ERR_UNSUPPORTED)):
+        st = M.moe_ffn_backward_mxfp8(M.make_shape(cc), *([p] * 28), p, 1 << 40,
+                                      check=False, stream=0)
+        assert st == want, cc
+    args = [p] * 28
+    args[2] = None                                   # gu_save
+    st = M.moe_ffn_backward_mxfp8(s, *args, p, 1 << 40, check=False, stream=0)
+    assert st == L.MOE_ERR_INVALID_ARG
+    st = M.moe_ffn_backward_mxfp8(s, *([p] * 28), p, mx - 1, check=False, stream=0)
+    assert st == L.MOE_ERR_WORKSPACE
+    for b, rows, cols, ldq in ((1, 48, 8, 64), (1, 64, 8, 48), (1, 64, 8, 96 - 16), (-1, 32, 8, 32)):
+        assert M.moe_mx_quantize_t(p, b, rows, cols, ldq, p, p, check=False, stream=0) == \
+            L.MOE_ERR_INVALID_ARG
+    assert M.moe_mx_quantize_t(p, 1, 32, 8, 32, p + 4, p, check=False, stream=0) == \
+        L.MOE_ERR_INVALID_ARG                        # codes must be 8-byte aligned
+    assert M.moe_mx_quantize_t(None, 0, 32, 8, 32, None, None, check=False, stream=0) == L.MOE_OK

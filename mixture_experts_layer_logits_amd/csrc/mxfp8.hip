@@ -30,6 +30,8 @@
 // 64-wide step.  Each 64-byte LDS row of a stage therefore feeds one MFMA per
 // fragment: chunks l / 32 and 2 + l / 32, the same two 16-byte chunks the
 // bf16 kernel reads in its two sub-steps.
+#include <utility>
+
 #include "gemm_tiles.h"
 
 namespace moe {
@@ -45,6 +47,16 @@ __device__ __forceinline__ uint32_t opaque_u32(uint32_t v) {
 // An empty use of an accumulator tile (in VGPRs): its MFMAs must have run
 // by here.
 __device__ __forceinline__ void use_acc(const f32x16_t& a) { asm volatile("" ::"v"(a)); }
+
+// fn(integral_constant<int, 0>{}), ..., fn(integral_constant<int, N - 1>{}).
+template <typename Fn, int... I>
+__device__ __forceinline__ void static_for_impl(Fn& fn, std::integer_sequence<int, I...>) {
+  (fn(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& fn) {
+  static_for_impl(fn, std::make_integer_sequence<int, N>{});
+}
 
 // FC1: 256 rows x (128 gate + 128 up) columns; FC2: 256 x 256; 8 waves.
 constexpr int MX_FC1_BM = 256, MX_FC1_BN = 128;
@@ -588,9 +600,100 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& args, const MxScales& sc
   };
   if (!live) {
     k_loop(std::false_type{});
+    if constexpr (EPI == EPI_DSWIGLU) barrier();   // the staged epilogue's
     return;
   }
   k_loop(std::true_type{});
+
+  if constexpr (EPI == EPI_DSWIGLU) {
+    // The SwiGLU backward of dh.  Per 32-row half, this wave's 32 x 128 fp32
+    // dh go to its 16 KiB of the freed ring (rows of 512 bytes, 16-byte chunk
+    // c of row r at c ^ r) and come back with lane l holding columns 4 (l % 32)
+    // .. + 3 of one row, so g, u, dg, du and h move in contiguous runs of
+    // that row.  With s = sigmoid(g): dg = dh u s (1 + g (1 - s)), du = dh g s,
+    // h = g s u, each rounded to bf16; dg and du are then quantised per
+    // 32-column block, which 8 neighbouring lanes hold, for the dX GEMM.
+    // Compile-time loops keep every accumulator index constant (a rolled
+    // loop would send the accumulators to scratch memory).
+    static_assert(NB == 1 && WTN == 128, "dh epilogue: one B, 128 columns per wave");
+    barrier();                                    // the ring is free
+    char* buf = reinterpret_cast<char*>(ring) + wave * 16384;
+    const int F = bw.F;
+    const int cbase = job.n0 + wn * WTN;          // first dh column of this wave
+    static_for<MI>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      static_for<NJ>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ch = j * 8 + 2 * q + hsel;
+          const f32x16_t& D = acc[0][i][j];
+          *reinterpret_cast<float4*>(buf + frag_row * 512 + ((ch ^ frag_row) << 4)) =
+              make_float4(D[4 * q], D[4 * q + 1], D[4 * q + 2], D[4 * q + 3]);
+        }
+      });
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int r = 2 * t + hsel, ch = lane & 31;
+        const float4 d4 = *reinterpret_cast<const float4*>(buf + r * 512 + ((ch ^ r) << 4));
+        const int m = job.m0 + wm * WTM + i * 32 + r;
+        const int n = cbase + 4 * ch;
+        const bool ok = m < job.rows && n < job.N;   // N is a multiple of 32
+        const long long rg = (long long)job.row0 + m;
+        uint2 gq = make_uint2(0u, 0u), uq = make_uint2(0u, 0u);
+        if (ok) {
+          gq = *reinterpret_cast<const uint2*>(bw.gu + rg * 2 * F + n);
+          uq = *reinterpret_cast<const uint2*>(bw.gu + rg * 2 * F + F + n);
+        }
+        const float dh[4] = {d4.x, d4.y, d4.z, d4.w};
+        const uint32_t gw[2] = {gq.x, gq.y}, uw[2] = {uq.x, uq.y};
+        float dg[4], du[4], hh[4];
+        float ag = 0.0f, au = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t gb = gw[e >> 1], ub = uw[e >> 1];
+          const float g = __uint_as_float((e & 1) ? (gb & 0xffff0000u) : (gb << 16));
+          const float u = __uint_as_float((e & 1) ? (ub & 0xffff0000u) : (ub << 16));
+          const float sg = 1.0f / (1.0f + __expf(-g));
+          const float sl = g * sg;
+          // rounded to bf16 here, so the quantised blocks see the stored values
+          dg[e] = bf16_round(dh[e] * u * sg * (1.0f + g * (1.0f - sg)));
+          du[e] = bf16_round(dh[e] * sl);
+          hh[e] = sl * u;
+          ag = fmaxf(ag, fabsf(dg[e]));
+          au = fmaxf(au, fabsf(du[e]));
+        }
+#pragma unroll
+        for (int x = 1; x < 8; x <<= 1) {
+          ag = fmaxf(ag, __shfl_xor(ag, x, 64));
+          au = fmaxf(au, __shfl_xor(au, x, 64));
+        }
+        const int sgx = mx_scale_exp(ag), sux = mx_scale_exp(au);
+        const float ig = mx_inv_scale(sgx), iu = mx_inv_scale(sux);
+        uint32_t cg = 0, cu = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          cg |= e4m3_code(dg[e] * ig) << (8 * e);
+          cu |= e4m3_code(du[e] * iu) << (8 * e);
+        }
+        if (ok) {
+          bf16_t* dgp = bw.dgu + rg * 2 * F + n;
+          *reinterpret_cast<uint2*>(dgp) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+          *reinterpret_cast<uint2*>(dgp + F) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+          *reinterpret_cast<uint2*>(bw.h + rg * F + n) =
+              make_uint2(pack_bf16x2(hh[0], hh[1]), pack_bf16x2(hh[2], hh[3]));
+          uint8_t* cp = job.C + (long long)m * job.ldc + n;
+          *reinterpret_cast<uint32_t*>(cp) = cg;
+          *reinterpret_cast<uint32_t*>(cp + F) = cu;
+          if ((lane & 7) == 0) {
+            sC[(long long)m * (job.ldc / 32) + n / 32] = (uint8_t)(sgx + 127);
+            sC[(long long)m * (job.ldc / 32) + (F + n) / 32] = (uint8_t)(sux + 127);
+          }
+        }
+      }
+    });
+    return;
+  }
 
   // Epilogue.  Lane owns row m = .. + (lane % 32) and, for register v,
   // column n = .. + 8 (v / 4) + 4 (lane / 32) + v % 4.
@@ -633,76 +736,6 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& args, const MxScales& sc
         if (row_ok) {
           *reinterpret_cast<uint4*>(job.C + (long long)m * job.ldc + nblk + 16 * hsel) = out;
           if (hsel == 0) sC[(long long)m * (job.N / 32) + nblk / 32] = (uint8_t)(s + 127);
-        }
-      } else if constexpr (EPI == EPI_DSWIGLU) {
-        // dh for row m, columns nblk + 8 q + 4 hsel + r.  With s = sigmoid(g):
-        // dg = dh u s (1 + g (1 - s)), du = dh g s, h = g s u, each rounded to
-        // bf16; then dg and du quantised per 32-column block (the lane pair
-        // holds one block of each) for the dX GEMM.
-        const int F = bw.F;
-        const long long rg = (long long)job.row0 + m;          // routed row
-        const bf16_t* gp = bw.gu + rg * 2 * F + nblk + 4 * hsel;
-        const f32x16_t& D = acc[0][i][j];
-        float dg[16], du[16];
-        float ag = 0.0f, au = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint2 gq = make_uint2(0u, 0u), uq = make_uint2(0u, 0u);
-          if (row_ok) {
-            gq = *reinterpret_cast<const uint2*>(gp + 8 * q);
-            uq = *reinterpret_cast<const uint2*>(gp + F + 8 * q);
-          }
-          const uint32_t gw[2] = {gq.x, gq.y}, uw[2] = {uq.x, uq.y};
-          float hh[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const uint32_t gb = gw[r >> 1], ub = uw[r >> 1];
-            const float g = __uint_as_float((r & 1) ? (gb & 0xffff0000u) : (gb << 16));
-            const float u = __uint_as_float((r & 1) ? (ub & 0xffff0000u) : (ub << 16));
-            const float sg = 1.0f / (1.0f + __expf(-g));
-            const float sl = g * sg;
-            const float dh = D[4 * q + r];
-            // rounded to bf16 here, so the quantised blocks see the stored values
-            dg[4 * q + r] = bf16_round(dh * u * sg * (1.0f + g * (1.0f - sg)));
-            du[4 * q + r] = bf16_round(dh * sl);
-            hh[r] = sl * u;
-            ag = fmaxf(ag, fabsf(dg[4 * q + r]));
-            au = fmaxf(au, fabsf(du[4 * q + r]));
-          }
-          if (row_ok) {
-            const int n = nblk + 8 * q + 4 * hsel;
-            bf16_t* dgp = bw.dgu + rg * 2 * F + n;
-            *reinterpret_cast<uint2*>(dgp) = make_uint2(pack_bf16x2(dg[4 * q], dg[4 * q + 1]),
-                                                        pack_bf16x2(dg[4 * q + 2], dg[4 * q + 3]));
-            *reinterpret_cast<uint2*>(dgp + F) = make_uint2(pack_bf16x2(du[4 * q], du[4 * q + 1]),
-                                                            pack_bf16x2(du[4 * q + 2], du[4 * q + 3]));
-            *reinterpret_cast<uint2*>(bw.h + rg * F + n) =
-                make_uint2(pack_bf16x2(hh[0], hh[1]), pack_bf16x2(hh[2], hh[3]));
-          }
-        }
-        ag = fmaxf(ag, __shfl_xor(ag, 32, 64));
-        au = fmaxf(au, __shfl_xor(au, 32, 64));
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {             // 0: dg, 1: du
-          const float* hv = half ? du : dg;
-          const int s = mx_scale_exp(half ? au : ag);
-          const float inv = mx_inv_scale(s);
-          uint32_t d[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            uint32_t w = 0;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) w |= e4m3_code(hv[4 * q + r] * inv) << (8 * r);
-            d[q] = w;
-          }
-          const uint32_t x0 = __shfl_xor(hsel ? d[0] : d[2], 32, 64);
-          const uint32_t x1 = __shfl_xor(hsel ? d[1] : d[3], 32, 64);
-          const uint4 out = hsel ? make_uint4(x0, d[2], x1, d[3]) : make_uint4(d[0], x0, d[1], x1);
-          const int col = half * F + nblk;                  // column in dg | du
-          if (row_ok) {
-            *reinterpret_cast<uint4*>(job.C + (long long)m * job.ldc + col + 16 * hsel) = out;
-            if (hsel == 0) sC[(long long)m * (job.ldc / 32) + col / 32] = (uint8_t)(s + 127);
-          }
         }
       } else {
         if (!row_ok) continue;

@@ -369,6 +369,31 @@ def grouped_ffn_mxfp8(x_perm, offsets, w_gate, w_up, w_down):
     return y
 
 
+def grouped_ffn_mxfp8_combine(x_perm, offsets, token_row, topk_w, w_gate, w_up,
+                              w_down, shared=None):
+    """The MXFP8 grouped FFN with the combine folded into FC2 (the Primus
+    blog's MegaMoE section fuses the combine into the second grouped GEMM):
+    per expert, hq as in swiglu_ffn_mxfp8, the expert output hq . mx(wd)^T
+    kept exact (never materialised, so not rounded to bf16), then
+    y[t] = ys[t] + sum_j w[t,j] * out[token_row[t,j]] rounded to fp32 once.
+    ``shared`` is None or (x, ws_gate, ws_up, ws_down)."""
+    x_perm = as64(x_perm)
+    R = x_perm.shape[0]
+    d = as64(w_down[0]).shape[0]
+    out = np.zeros((R, d), dtype=F64)
+    for e in range(len(offsets) - 1):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b > a:
+            h = swiglu_ffn_mxfp8(x_perm[a:b], w_gate[e], w_up[e], w_down[e])["h"]
+            out[a:b] = h @ mx_round(as64(w_down[e])).T
+    ys = None
+    if shared is not None:
+        xs, wsg, wsu, wsd = shared
+        hs = swiglu_ffn_mxfp8(xs, wsg, wsu, wsd)["h"]
+        ys = hs @ mx_round(as64(wsd)).T
+    return combine(out, token_row, topk_w, ys, "f32")
+
+
 # --------------------------------------------------------------------------
 # unpermute-and-scale
 # --------------------------------------------------------------------------

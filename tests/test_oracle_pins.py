@@ -712,3 +712,51 @@ def test_expert_backward_mxfp8_is_exact_on_mx_representable_operands():
         assert np.array_equal(a[key], b[key]), key
     assert not np.array_equal(a["dX"], b["dX"])          # dg | du are not MX-exact
     assert np.allclose(a["dX"], b["dX"], rtol=0.15, atol=0.05 * np.abs(b["dX"]).max())
+
+
+def test_grouped_ffn_mxfp8_combine_by_brute_force():
+    """The MXFP8 FFN with the combine in FC2 on a tiny two-expert case:
+    brute-force MX rounding (table search, frexp exponents) of x, the
+    weights and h, the expert outputs summed exactly with their gates
+    (Python loops), one fp32 rounding; the unfused path differs by the bf16
+    rounding of each expert output."""
+    import math
+    codes = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    table = [(c, float(codes[c])) for c in range(256) if np.isfinite(codes[c]) and codes[c] >= 0]
+    table += [(c, float(codes[c])) for c in range(256) if np.isfinite(codes[c]) and codes[c] < 0]
+    rng = np.random.default_rng(37)
+    T, d, F, E = 3, 32, 32, 2
+    x = rng.standard_normal((T, d))
+    wg = rng.standard_normal((E, F, d)) * 0.2
+    wu = rng.standard_normal((E, F, d)) * 0.2
+    wd = rng.standard_normal((E, d, F)) * 0.2
+    # every token goes to both experts with gates (w, 1 - w)
+    idx = np.array([[0, 1]] * T)
+    w = np.array([[0.25, 0.75], [0.5, 0.5], [0.875, 0.125]])
+    p = O.permute(x, idx, w, E)
+    y = O.grouped_ffn_mxfp8_combine(p["x_perm"], p["offsets"], p["token_row"], w, wg, wu, wd)
+    q = lambda v: np.array(_mx_round_brute(np.asarray(v, dtype=np.float64), table))
+    for t in range(T):
+        xq = q(x[t])
+        acc = [0.0] * d
+        for e in range(E):
+            wgq = [q(wg[e][f]) for f in range(F)]
+            wuq = [q(wu[e][f]) for f in range(F)]
+            wdq = [q(wd[e][i]) for i in range(d)]
+            h = []
+            for f in range(F):
+                g = sum(xq[c] * wgq[f][c] for c in range(d))
+                u = sum(xq[c] * wuq[f][c] for c in range(d))
+                h.append(g / (1.0 + math.exp(-g)) * u)
+            hq = q(h)
+            for i in range(d):
+                acc[i] += w[t, e] * sum(hq[f] * wdq[i][f] for f in range(F))
+        want = np.array(acc, dtype=np.float32).astype(np.float64)
+        # an h on an E4M3 rounding boundary could land one step away (another
+        # summation order); on this case every element agrees exactly
+        assert np.mean(y[t] == want) >= 0.95
+        assert np.allclose(y[t], want, rtol=1e-3, atol=1e-6 * np.abs(want).max())
+    unfused = O.combine(O.grouped_ffn_mxfp8(p["x_perm"], p["offsets"], wg, wu, wd),
+                        p["token_row"], w)
+    assert not np.array_equal(y, unfused)
+    assert np.allclose(y, unfused, rtol=2e-2, atol=1e-3)

@@ -385,6 +385,31 @@ def main():
               "ffn_tflops": round(ffn_flops(cfg) / t_mx / 1e12, 2),
               "ffn_frac_of_fp8_peak": round(ffn_flops(cfg) / t_mx / 1e12 / PEAK_FP8_TFLOPS, 4),
               "weight_quantize_ms_once": round(q0.elapsed_time(q1), 4)}
+
+        # ... and with the combine in the MXFP8 FC2's epilogue (no y_perm)
+        def mxc_step(ev=None):
+            layer.route(inp)
+            layer.permute(inp, maps_only=True)
+            layer.quantize_x(inp)
+            if ev is not None:
+                ev[0].record(stream)
+            layer.ffn_mxfp8_combine(inp)
+            if ev is not None:
+                ev[1].record(stream)
+        for _ in range(args.warmup):
+            mxc_step()
+        cev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        c0 = time.perf_counter()
+        for s_ in range(args.steps):
+            mxc_step(cev2[s_])
+        torch.cuda.synchronize()
+        cwall2 = (time.perf_counter() - c0) * 1e3 / args.steps
+        mx["with_combine_in_fc2"] = {
+            "ms_per_step": round(cwall2, 4), "tokens_per_s": round(cfg.T / (cwall2 / 1e3), 1),
+            "ffn_mxfp8_combine_ms": round(float(np.mean([cev2[s_][0].elapsed_time(cev2[s_][1])
+                                                         for s_ in range(args.steps)])), 4)}
     # Training with selective rematerialisation: the forward keeps no g | u
     # and the backward reruns FC1 (same kernels) before its own GEMMs.
     remat = None

@@ -32,9 +32,9 @@
  *    returns a negative moe_status, launches nothing and leaves every output
  *    untouched.  A failed kernel launch returns MOE_ERR_HIP.
  *  - Results are bitwise deterministic run to run (no floating-point
- *    atomics), with one stated exception: moe_grouped_ffn_combine, whose
- *    fp32 atomic additions are order-independent only with at most two
- *    addends per output element (see there).  The library keeps no mutable
+ *    atomics), with stated exceptions: moe_grouped_ffn_combine and
+ *    moe_grouped_ffn_mxfp8_combine, whose fp32 atomic additions are
+ *    order-independent only with at most two addends per output element.  The library keeps no mutable
  *    global state.
  *
  * Dtypes: `dtype` selects the storage type of x, the weights and the
@@ -335,6 +335,28 @@ int moe_grouped_ffn_mxfp8(const moe_shape* shape, const uint8_t* xq,
                           const uint8_t* ws_down_q, const uint8_t* ws_down_s,
                           void* y_perm, void* y_shared, void* ws,
                           size_t ws_bytes, void* stream);
+
+/* The MXFP8 grouped FFN with the unpermute-and-scale folded into FC2's
+ * epilogue (Primus blog, MegaMoE section: combine fused into the second
+ * grouped GEMM): moe_grouped_ffn_mxfp8's FC1, then FC2's fp32 rows (never
+ * stored, so not rounded to bf16), scaled by row_gate[r] (1 for the shared
+ * expert), added into y[row_token[r]] (resp. y[t]) with fp32 atomics.
+ *  Arguments as moe_grouped_ffn_mxfp8, with row_gate [R] fp32 (moe_permute)
+ *  in place of y_perm / y_shared, and y [T, d] fp32 out (overwritten).
+ * No split of the contraction here, so each element of y receives k
+ * additions (k + 1 with a shared expert): bitwise reproducible when that is
+ * at most two, else as described at moe_grouped_ffn_combine.
+ *  ws: MOE_OP_FFN_MXFP8 bytes. */
+int moe_grouped_ffn_mxfp8_combine(const moe_shape* shape, const uint8_t* xq,
+                                  const uint8_t* xs, const int32_t* row_token,
+                                  const float* row_gate, const int32_t* expert_offsets,
+                                  const uint8_t* w_gate_q, const uint8_t* w_gate_s,
+                                  const uint8_t* w_up_q, const uint8_t* w_up_s,
+                                  const uint8_t* w_down_q, const uint8_t* w_down_s,
+                                  const uint8_t* ws_gate_q, const uint8_t* ws_gate_s,
+                                  const uint8_t* ws_up_q, const uint8_t* ws_up_s,
+                                  const uint8_t* ws_down_q, const uint8_t* ws_down_s,
+                                  float* y, void* ws, size_t ws_bytes, void* stream);
 
 /* MXFP8 quantisation along the ROWS of each of `batches` row-major
  * [rows, cols] bf16 matrices, written transposed (Primus blog, low-precision

@@ -34,7 +34,8 @@ MOE_SCORE_SIGMOID = 1
 EXPORTED = ("moe_workspace_size", "moe_route_topk", "moe_permute",
             "moe_grouped_ffn", "moe_unpermute_combine", "moe_ffn_backward",
             "moe_status_string", "moe_mx_quantize", "moe_grouped_ffn_mxfp8",
-            "moe_grouped_ffn_combine", "moe_mx_quantize_t", "moe_ffn_backward_mxfp8")
+            "moe_grouped_ffn_combine", "moe_mx_quantize_t", "moe_ffn_backward_mxfp8",
+            "moe_grouped_ffn_mxfp8_combine")
 
 
 class MoeShape(ctypes.Structure):
@@ -73,6 +74,7 @@ def load() -> ctypes.CDLL:
     lib.moe_mx_quantize_t.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_int32, vp, vp, vp]
     lib.moe_ffn_backward_mxfp8.argtypes = [sp] + [vp] * 28 + [vp, sz, vp]
+    lib.moe_grouped_ffn_mxfp8_combine.argtypes = [sp] + [vp] * 18 + [vp, sz, vp]
     lib.moe_ffn_backward.argtypes = [sp] + [vp] * 26 + [vp, sz, vp]
     lib.moe_mx_quantize.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
     lib.moe_grouped_ffn_mxfp8.argtypes = [sp] + [vp] * 18 + [vp, sz, vp]
@@ -165,6 +167,19 @@ def moe_grouped_ffn_combine(shape, x_perm, row_token, row_gate, expert_offsets,
         _p(ws_gate), _p(ws_up), _p(ws_down), _p(y), _p(ws), ws_bytes,
         _stream(stream))
     return _check(st, "moe_grouped_ffn_combine") if check else st
+
+
+def moe_grouped_ffn_mxfp8_combine(shape, xq, xs, row_token, row_gate, expert_offsets,
+                                  w_gate_q, w_gate_s, w_up_q, w_up_s, w_down_q, w_down_s,
+                                  ws_gate_q, ws_gate_s, ws_up_q, ws_up_s, ws_down_q,
+                                  ws_down_s, y, ws=None, ws_bytes=0, stream=None, check=True):
+    st = load().moe_grouped_ffn_mxfp8_combine(
+        ctypes.byref(shape), _p(xq), _p(xs), _p(row_token), _p(row_gate),
+        _p(expert_offsets), _p(w_gate_q), _p(w_gate_s), _p(w_up_q), _p(w_up_s),
+        _p(w_down_q), _p(w_down_s), _p(ws_gate_q), _p(ws_gate_s), _p(ws_up_q),
+        _p(ws_up_s), _p(ws_down_q), _p(ws_down_s), _p(y), _p(ws), ws_bytes,
+        _stream(stream))
+    return _check(st, "moe_grouped_ffn_mxfp8_combine") if check else st
 
 
 def moe_mx_quantize_t(src, batches, rows, cols, ldq, q, scales, stream=None, check=True):

@@ -447,6 +447,52 @@ int moe_grouped_ffn_mxfp8(const moe_shape* shape, const uint8_t* xq, const uint8
                                                   static_cast<hipStream_t>(stream)));
 }
 
+int moe_grouped_ffn_mxfp8_combine(const moe_shape* shape, const uint8_t* xq, const uint8_t* xs,
+                                  const int32_t* row_token, const float* row_gate,
+                                  const int32_t* expert_offsets,
+                                  const uint8_t* w_gate_q, const uint8_t* w_gate_s,
+                                  const uint8_t* w_up_q, const uint8_t* w_up_s,
+                                  const uint8_t* w_down_q, const uint8_t* w_down_s,
+                                  const uint8_t* ws_gate_q, const uint8_t* ws_gate_s,
+                                  const uint8_t* ws_up_q, const uint8_t* ws_up_s,
+                                  const uint8_t* ws_down_q, const uint8_t* ws_down_s, float* y,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape& s = *shape;
+  if (s.dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
+  if (s.d % 128 != 0 || s.F % 128 != 0 || s.F_shared % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  const long long R = (long long)s.T * s.k;
+  const long long xn = (long long)s.T * s.d;
+  const long long wn = (long long)s.E * s.F * s.d;
+  if (!ok_buf(xq, xn) || !ok_buf(xs, xn / 32) || !ok_buf(row_token, R * 4) ||
+      !ok_buf(row_gate, R * 4) || !ok_buf(expert_offsets, (long long)(s.E + 1) * 4) ||
+      !ok_buf(w_gate_q, wn) || !ok_buf(w_gate_s, wn / 32) || !ok_buf(w_up_q, wn) ||
+      !ok_buf(w_up_s, wn / 32) || !ok_buf(w_down_q, wn) || !ok_buf(w_down_s, wn / 32) ||
+      !ok_buf(y, xn * 4))
+    return MOE_ERR_INVALID_ARG;
+  if (s.F_shared > 0) {
+    const long long sn = (long long)s.F_shared * s.d;
+    if (!ok_buf(ws_gate_q, sn) || !ok_buf(ws_gate_s, sn / 32) || !ok_buf(ws_up_q, sn) ||
+        !ok_buf(ws_up_s, sn / 32) || !ok_buf(ws_down_q, sn) || !ok_buf(ws_down_s, sn / 32))
+      return MOE_ERR_INVALID_ARG;
+  }
+  if ((st = check_ws(s, MOE_OP_FFN_MXFP8, ws, ws_bytes)) != MOE_OK) return st;
+  Carver c{static_cast<char*>(ws)};
+  moe::MxFfnWs fw;
+  fw.tiles1 = c.take<int32_t>((s.E + 1) * 4);
+  fw.tiles2 = c.take<int32_t>((s.E + 1) * 4);
+  fw.hq = c.take<uint8_t>((size_t)R * s.F);
+  fw.hs = c.take<uint8_t>((size_t)R * s.F / 32);
+  fw.shq = c.take<uint8_t>((size_t)s.T * s.F_shared);
+  fw.shs = c.take<uint8_t>((size_t)s.T * s.F_shared / 32);
+  const moe::MxWeights w = {w_gate_q, w_gate_s, w_up_q, w_up_s, w_down_q, w_down_s,
+                            ws_gate_q, ws_gate_s, ws_up_q, ws_up_s, ws_down_q, ws_down_s};
+  return hip_status(moe::launch_grouped_ffn_mxfp8(s, xq, xs, row_token, expert_offsets, w,
+                                                  nullptr, nullptr, fw,
+                                                  static_cast<hipStream_t>(stream), row_gate, y));
+}
+
 int moe_ffn_backward_mxfp8(const moe_shape* shape, const void* dy, const void* x_perm,
                            const void* gu_save, const void* y_perm,
                            const int32_t* expert_offsets, const int32_t* row_token,

@@ -70,6 +70,12 @@ zero_f32_kernel(float* __restrict__ p, long long n) {
     p[i] = 0.0f;
 }
 
+hipError_t launch_zero_f32(float* y, long long n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  zero_f32_kernel<<<(int)std::min<long long>((n / 4 + 255) / 256 + 1, 4096), 256, 0, st>>>(y, n);
+  return hipGetLastError();
+}
+
 bool ffn_uses_mfma(const moe_shape& s) {
   return s.dtype == MOE_DTYPE_BF16 && s.d % 64 == 0 && s.F % 64 == 0 &&
          (s.F_shared == 0 || s.F_shared % 64 == 0);
@@ -250,7 +256,8 @@ hipError_t launch_grouped_ffn_combine(const moe_shape& s, const void* x_perm,
   const bool shared = s.F_shared > 0 && s.T > 0;
   const long long ny = (long long)s.T * s.d;
   if (ny == 0) return hipSuccess;
-  zero_f32_kernel<<<(int)std::min<long long>((ny / 4 + 255) / 256 + 1, 4096), 256, 0, st>>>(y, ny);
+  hipError_t e0 = launch_zero_f32(y, ny, st);
+  if (e0 != hipSuccess) return e0;
   GemmArgs a1 = fc1_args(s, x_perm, row_token, offsets, w_gate, w_up, x, ws_gate, ws_up, ws.h,
                          ws.h_shared, nullptr, ws.tiles1);
   GemmArgs a2 = fc2_args(s, a1.E, offsets, w_down, ws_down, nullptr, nullptr, ws);

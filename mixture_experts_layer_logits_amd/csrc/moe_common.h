@@ -111,7 +111,10 @@ struct MxFfnWs {
 hipError_t launch_grouped_ffn_mxfp8(const moe_shape& s, const uint8_t* xq, const uint8_t* xs,
                                     const int32_t* row_token, const int32_t* offsets,
                                     const MxWeights& w, void* y_perm, void* y_shared,
-                                    const MxFfnWs& ws, hipStream_t st);
+                                    const MxFfnWs& ws, hipStream_t st,
+                                    const float* row_gate = nullptr, float* y = nullptr);
+// y[0 .. n) = 0 with a kernel (so that a captured graph replays it faithfully).
+hipError_t launch_zero_f32(float* y, long long n, hipStream_t st);
 
 hipError_t launch_mx_quantize_t(const void* src, long long batches, int rows, int cols, int ldq,
                                 uint8_t* q, uint8_t* scales, hipStream_t st);

@@ -600,10 +600,58 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& args, const MxScales& sc
   };
   if (!live) {
     k_loop(std::false_type{});
-    if constexpr (EPI == EPI_DSWIGLU) barrier();   // the staged epilogue's
+    if constexpr (EPI == EPI_DSWIGLU || EPI == EPI_COMBINE) barrier();   // the staged epilogue's
     return;
   }
   k_loop(std::true_type{});
+
+  if constexpr (EPI == EPI_COMBINE) {
+    // The combine folded into FC2: per 32-row half, this wave's 32 x 128 fp32
+    // results go through its 16 KiB of the freed ring and come back one row
+    // at a time, lane l holding columns l and l + 64, so each atomic add
+    // instruction covers 256 contiguous bytes of one y row; the row's gate
+    // (1 for the shared expert's rows) scales it and its token picks the row.
+    static_assert(NB == 1 && WTN == 128, "combine epilogue: one B, 128 columns per wave");
+    barrier();                                    // the ring is free
+    char* buf = reinterpret_cast<char*>(ring) + wave * 16384;
+    const int cbase = job.n0 + wn * WTN;
+    static_for<MI>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      static_for<NJ>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ch = j * 8 + 2 * q + hsel;
+          const f32x16_t& Cv = acc[0][i][j];
+          *reinterpret_cast<float4*>(buf + frag_row * 512 + ((ch ^ frag_row) << 4)) =
+              make_float4(Cv[4 * q], Cv[4 * q + 1], Cv[4 * q + 2], Cv[4 * q + 3]);
+        }
+      });
+      // lane r < 32 looks up row r's token and gate; rows past the group: -1
+      const int mr = job.m0 + wm * WTM + i * 32 + frag_row;
+      int tok = -1;
+      float gw = 0.0f;
+      if (mr < job.rows) {
+        tok = job.ctok ? job.ctok[mr] : mr;
+        gw = job.cgate ? job.cgate[mr] : 1.0f;
+      }
+#pragma unroll
+      for (int r = 0; r < 32; ++r) {
+        const int t = __builtin_amdgcn_readlane(tok, r);
+        const float g = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gw), r));
+        if (t < 0) continue;
+        float* yrow = args.Y + (long long)t * args.ldy + cbase;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int col = h * 64 + lane;
+          const float v = *reinterpret_cast<const float*>(
+              buf + r * 512 + (((col >> 2) ^ r) << 4) + (col & 3) * 4);
+          if (cbase + col < job.N) atomicAdd(yrow + col, g * v);
+        }
+      }
+    });
+    return;
+  }
 
   if constexpr (EPI == EPI_DSWIGLU) {
     // The SwiGLU backward of dh.  Per 32-row half, this wave's 32 x 128 fp32
@@ -792,7 +840,8 @@ hipError_t launch_mx_gemm(const GemmArgs& a, const MxScales& sc, int R, hipStrea
 hipError_t launch_grouped_ffn_mxfp8(const moe_shape& s, const uint8_t* xq, const uint8_t* xs,
                                     const int32_t* row_token, const int32_t* offsets,
                                     const MxWeights& w, void* y_perm, void* y_shared,
-                                    const MxFfnWs& ws, hipStream_t st) {
+                                    const MxFfnWs& ws, hipStream_t st, const float* row_gate,
+                                    float* y) {
   const int R = s.T * s.k;
   const bool shared = s.F_shared > 0 && s.T > 0;
   GemmArgs a1 = {};
@@ -856,6 +905,20 @@ hipError_t launch_grouped_ffn_mxfp8(const moe_shape& s, const uint8_t* xq, const
     s2.Ad = ws.shs;
     s2.Bd0 = w.sdown_s;
   }
+  if (y) {
+    // the combine in FC2's epilogue: y = 0, then every FC2 row adds its
+    // gate-scaled output into its token's row (the shared expert's with gate 1)
+    const long long ny = (long long)s.T * s.d;
+    if (ny == 0) return hipSuccess;
+    hipError_t e = launch_zero_f32(y, ny, st);
+    if (e != hipSuccess) return e;
+    a2.C = nullptr;
+    a2.Cd = nullptr;
+    a2.comb_token = row_token;
+    a2.comb_gate = row_gate;
+    a2.Y = y;
+    a2.ldy = s.d;
+  }
   if (a1.E == 0 && !shared) return hipSuccess;
   // routed groups use tail tiles (BM/2 x 2BN) for their last rows
   a1.tail = a2.tail = 1;
@@ -866,6 +929,7 @@ hipError_t launch_grouped_ffn_mxfp8(const moe_shape& s, const uint8_t* xq, const
   }
   hipError_t e = launch_mx_gemm<MX_FC1_BM, MX_FC1_BN, 2, EPI_SWIGLU, 4, 2>(a1, s1, R, st);
   if (e != hipSuccess) return e;
+  if (y) return launch_mx_gemm<MX_FC2_BM, MX_FC2_BN, 1, EPI_COMBINE, 4, 2>(a2, s2, R, st);
   return launch_mx_gemm<MX_FC2_BM, MX_FC2_BN, 1, EPI_STORE, 4, 2>(a2, s2, R, st);
 }
 

@@ -168,6 +168,29 @@ class MoELayer:
             *w.get("ws_up", none), *w.get("ws_down", none), b["y_perm"],
             b["y_shared"], m["ws"], m["ws_bytes"], stream)
 
+    def ffn_mxfp8_combine(self, inp, stream=None):
+        """The MXFP8 grouped FFN with the combine in FC2's epilogue: y
+        straight from the expert GEMMs (needs quantize_weights() and
+        quantize_x())."""
+        if getattr(self, "mx_weights", None) is None:
+            raise RuntimeError("call quantize_weights() before the MXFP8 FFN")
+        b, m, w = self.buf, self._mx_buffers(), self.mx_weights
+        none = (None, None)
+        L.moe_grouped_ffn_mxfp8_combine(
+            self.shape, m["xq"], m["xs"], b["row_token"], b["row_gate"],
+            b["expert_offsets"], *w["w_gate"], *w["w_up"], *w["w_down"],
+            *w.get("ws_gate", none), *w.get("ws_up", none), *w.get("ws_down", none),
+            b["y"], m["ws"], m["ws_bytes"], stream)
+
+    def forward_mxfp8_combined(self, inp, stream=None):
+        """route -> permute (maps only) -> quantise x -> MXFP8 FFN with the
+        combine in FC2, with the cached quantised weights."""
+        self.route(inp, stream)
+        self.permute(inp, stream, maps_only=True)
+        self.quantize_x(inp, stream)
+        self.ffn_mxfp8_combine(inp, stream)
+        return self.buf
+
     def forward_mxfp8(self, inp, stream=None):
         """route -> permute (maps only) -> quantise x -> MXFP8 grouped FFN ->
         combine, with the cached quantised weights."""

@@ -273,3 +273,74 @@ def test_layer_mxfp8_full_size_sampled(name):
     assert_close("y[sample]", out["y"][tt], acc, "bf16")
     del layer, out, inp
     torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------
+# The MXFP8 forward with the combine in FC2's epilogue
+# (moe_grouped_ffn_mxfp8_combine), against grouped_ffn_mxfp8_combine.
+# --------------------------------------------------------------------------
+MX_COMBINE = dict(MX_LAYER)
+MX_COMBINE["mx_skewed_empty_t520"] = MoEConfig("mx_skewed_empty_t520", T=520, d=384, E=32,
+                                               k=2, F=256, zipf_s=1.2)
+
+
+@pytest.mark.parametrize("name", list(MX_COMBINE))
+def test_layer_mxfp8_combined(name):
+    cfg = MX_COMBINE[name]
+    _log(f"[mx combined] {name}")
+    from mixture_experts_layer_logits_amd import MoELayer
+    inp = make_inputs(cfg, device="cuda")
+    layer = MoELayer(cfg)
+    layer.quantize_weights(inp)
+    out = layer.forward_mxfp8_combined(inp)
+    torch.cuda.synchronize()
+    idx, w, amb, same = route_and_check(cfg, inp, out)
+    x = np64(inp["x"])
+    p = O.permute(x, idx, w, cfg.E)
+    sh = None
+    if cfg.F_shared:
+        sh = (x, np64(inp["ws_gate"]), np64(inp["ws_up"]), np64(inp["ws_down"]))
+    ref = O.grouped_ffn_mxfp8_combine(p["x_perm"], p["offsets"], p["token_row"], w,
+                                      np64(inp["w_gate"]), np64(inp["w_up"]),
+                                      np64(inp["w_down"]), sh)
+    ok = ~amb
+    assert_close("y", out["y"][torch.as_tensor(ok).cuda()], ref[ok], "bf16")
+    if cfg.zipf_s > 0:
+        assert (np.diff(p["offsets"]) == 0).any()
+    # k = 2 without a shared expert: two addends per element, bitwise repeatable
+    y1 = out["y"].clone()
+    layer.ffn_mxfp8_combine(inp)
+    torch.cuda.synchronize()
+    if cfg.k <= 2 and not cfg.F_shared:
+        assert torch.equal(out["y"], y1)
+    else:
+        assert_close("y (second run)", out["y"], y1, "f32")
+
+
+def test_layer_mxfp8_combined_full_size_sampled():
+    """Mixtral shape: sampled tokens, each expert they reach evaluated once by
+    the oracle on just their rows, expert outputs kept exact."""
+    cfg = CONFIGS["mixtral_t4096"]
+    _log(f"[mx combined full] {cfg.name}")
+    from mixture_experts_layer_logits_amd import MoELayer
+    inp = make_inputs(cfg, device="cuda")
+    layer = MoELayer(cfg)
+    layer.quantize_weights(inp)
+    out = layer.forward_mxfp8_combined(inp)
+    torch.cuda.synchronize()
+    idx, w, amb, same = route_and_check(cfg, inp, out)
+    toks = np.array([t for t in sample_tokens(cfg.T, 4) if not amb[t]])
+    x = np64(inp["x"][torch.as_tensor(toks, device="cuda")])
+    idx_s, w_s = np.asarray(idx)[toks], np.asarray(w)[toks]
+    acc = np.zeros((len(toks), cfg.d))
+    for e in np.unique(idx_s):
+        sel = np.argwhere(idx_s == e)
+        h = O.swiglu_ffn_mxfp8(x[sel[:, 0]], np64(inp["w_gate"][int(e)]),
+                               np64(inp["w_up"][int(e)]), np64(inp["w_down"][int(e)]))["h"]
+        ye = h @ O.mx_round(np64(inp["w_down"][int(e)])).T
+        for n, (t, j) in enumerate(sel):
+            acc[t] += w_s[t, j] * ye[n]
+    tt = torch.as_tensor(toks, device="cuda")
+    assert_close("y[sample]", out["y"][tt], O.round_f32(acc), "bf16")
+    del layer, out, inp
+    torch.cuda.empty_cache()

@@ -21,7 +21,8 @@
  *  - Tensor pointers are DEVICE pointers owned by the caller; the library
  *    never frees, keeps or allocates memory.  Arrays are row-major and
  *    contiguous.  Outputs must not alias inputs.
- *  - Pointers must be 16-byte aligned.
+ *  - Pointers must be 16-byte aligned (moe_mx_quantize_t relaxes this for
+ *    its outputs, as stated there).
  *  - Everything is asynchronous and ordered on `stream` (a hipStream_t; NULL
  *    is the null stream).  No call synchronises the host, copies device data
  *    to the host, or allocates: per-expert counts stay on the GPU.
@@ -34,8 +35,8 @@
  *  - Results are bitwise deterministic run to run (no floating-point
  *    atomics), with stated exceptions: moe_grouped_ffn_combine and
  *    moe_grouped_ffn_mxfp8_combine, whose fp32 atomic additions are
- *    order-independent only with at most two addends per output element.  The library keeps no mutable
- *    global state.
+ *    order-independent only with at most two addends per output element.
+ *    The library keeps no mutable global state.
  *
  * Dtypes: `dtype` selects the storage type of x, the weights and the
  * materialised intermediates x_perm, h, y_perm, gu_save (MOE_DTYPE_BF16 or

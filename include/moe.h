@@ -127,7 +127,10 @@ int moe_workspace_size(const moe_shape* shape, int op, size_t* bytes);
  *  topk_w [T, k] fp32 out: SOFTMAX renorm=1: softmax over the k selected
  *      logits; renorm=0: full softmax probability.  SIGMOID: s / sum of the k
  *      picked s (renorm=1) or s.
- *  ws: MOE_OP_ROUTE bytes (may be NULL when that is 0). */
+ *  ws: MOE_OP_ROUTE bytes when the logits are computed here (the bf16
+ *      router GEMM splits its contraction when its output tiles are few and
+ *      keeps fp32 partial sums there, added in a fixed order); may be NULL
+ *      when that size is 0 or when logits are an input. */
 int moe_route_topk(const moe_shape* shape, const void* x, const void* w_router,
                    const float* router_bias, float* logits,
                    const float* score_bias, int32_t* topk_idx, float* topk_w,

@@ -47,7 +47,10 @@ size_t ws_bytes_for(const moe_shape& s, int op) {
   const size_t R = (size_t)s.T * s.k;
   const size_t es = esize(s);
   switch (op) {
-    case MOE_OP_ROUTE:
+    case MOE_OP_ROUTE: {   // the split router GEMM's partial sums
+      const int ks = moe::router_ksplit(s);
+      return ks > 1 ? align_up((size_t)ks * s.T * s.E * 4) : 0;
+    }
     case MOE_OP_COMBINE:
       return 0;
     case MOE_OP_PERMUTE: {
@@ -177,10 +180,13 @@ int moe_route_topk(const moe_shape* shape, const void* x, const void* w_router,
   if (!ok_buf(logits, (long long)s.T * s.E * 4) || !ok_buf(topk_idx, (long long)s.T * s.k * 4) ||
       !ok_buf(topk_w, (long long)s.T * s.k * 4) || !ok_buf(score_bias, 0))
     return MOE_ERR_INVALID_ARG;
-  if ((st = check_ws(s, MOE_OP_ROUTE, ws, ws_bytes)) != MOE_OK) return st;
+  // the partial sums are only needed (and the workspace only required)
+  // when the logits are computed here
+  if (compute_logits && (st = check_ws(s, MOE_OP_ROUTE, ws, ws_bytes)) != MOE_OK) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (compute_logits) {
-    if ((st = hip_status(moe::launch_router_logits(s, x, w_router, router_bias, logits, hs))) != MOE_OK)
+    if ((st = hip_status(moe::launch_router_logits(s, x, w_router, router_bias, logits,
+                                                   static_cast<float*>(ws), hs))) != MOE_OK)
       return st;
   }
   return hip_status(moe::launch_topk(s, logits, score_bias, topk_idx, topk_w, hs));

@@ -71,9 +71,10 @@ struct GemmArgs {
   void* GUd;               // FC1 only, or null: the dense group's g | u
   long long ldgud;
   const float* bias;       // EPI_F32_BIAS: added per column, or null
-  // Split-K (EPI_STORE on routed groups only): K is cut into ksplit equal
-  // slices; slice s of every tile writes fp32 partials to
-  // Cpart + s * part_stride + row * N + n, summed later in slice order.
+  // Split-K (EPI_STORE on routed groups, EPI_F32_BIAS on the dense group):
+  // K is cut into ksplit equal slices; slice s of every tile writes fp32
+  // partials (no bias) to Cpart + s * part_stride + row * N + n, summed
+  // later in slice order.
   int ksplit;
   float* Cpart;
   long long part_stride;
@@ -220,8 +221,9 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, TileJob<TIn, TOut
   j.C = static_cast<TOut*>(a.Cd);
   j.GU = static_cast<TOut*>(a.GUd);
   j.ldgu = a.ldgud;
-  j.klen = a.Kd;
-  j.k0 = 0;
+  j.klen = a.Kd / ks;
+  j.k0 = kslice * j.klen;
+  if (ks > 1 && a.Cpart) j.P = a.Cpart + kslice * a.part_stride;
   j.ctok = nullptr;
   j.cgate = nullptr;
   return true;
@@ -649,9 +651,12 @@ gemm_bf16_mfma_kernel(const GemmArgs args) {
           float o[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            o[r] = acc[0][i][j][4 * q + r] + ((args.bias && n + r < job.N) ? args.bias[n + r] : 0.0f);
-          float* dst = job.C + (long long)m * job.ldc + n;
-          if (n + 3 < job.N && (job.ldc & 3) == 0) {
+            o[r] = acc[0][i][j][4 * q + r] +
+                   ((!job.P && args.bias && n + r < job.N) ? args.bias[n + r] : 0.0f);
+          // a split-K slice writes its partial sums (row pitch N), no bias
+          float* dst = job.P ? job.P + (long long)m * job.N + n : job.C + (long long)m * job.ldc + n;
+          const long long ld = job.P ? job.N : job.ldc;
+          if (n + 3 < job.N && (ld & 3) == 0) {
             *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
           } else {
 #pragma unroll

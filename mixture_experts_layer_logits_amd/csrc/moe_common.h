@@ -47,8 +47,10 @@ __device__ __forceinline__ float silu_precise(float g) { return g / (1.0f + expf
 // Launchers implemented in the .hip files.  Each returns hipSuccess or the
 // launch error.  Shapes were validated by the API layer.
 // ---------------------------------------------------------------------------
+// part: router_ksplit(s) * T * E fp32 partial sums when that is above 1.
+int router_ksplit(const moe_shape& s);
 hipError_t launch_router_logits(const moe_shape& s, const void* x, const void* w_router,
-                                const float* router_bias, float* logits,
+                                const float* router_bias, float* logits, float* part,
                                 hipStream_t st);
 hipError_t launch_topk(const moe_shape& s, const float* logits, const float* score_bias,
                        int32_t* topk_idx, float* topk_w, hipStream_t st);

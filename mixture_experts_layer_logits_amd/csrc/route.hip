@@ -13,12 +13,50 @@
 #include <float.h>
 #include <limits.h>
 
+#include <algorithm>
+
 #include "gemm_tiles.h"
 
 namespace moe {
 
+// The router GEMM is as long in K (d) as the expert GEMMs but has few
+// output tiles.  With up to 128 experts it runs 64 x 64 tiles (64 of them at
+// T = 4096, E = 8), whose K loops are latency-bound with only three slices
+// in flight, so it is split in K until there are 512 work items (2 per CU).
+// With more experts, 64-wide tiles would re-read x once per 64 experts (4
+// times at E = 256), so it runs 256 x 256 tiles split in K up to 8 ways
+// towards one item per CU.  Each slice is at least one 32-wide K step.  The
+// split is a pure function of the shape, so results do not depend on the
+// device; slices write fp32 partial sums that a second kernel adds in slice
+// order (then the bias): deterministic.  Measured per router GEMM (+ the
+// partial-sum pass): T = 4096, E = 8: 47 -> 19 us; T = 8192, E = 256, d =
+// 7168: 99 -> 73 us; T = 16384, E = 128, d = 2048 (512 tiles): unsplit, 35 us.
+static bool router_big_tiles(const moe_shape& s) { return s.E > 128; }
+
+int router_ksplit(const moe_shape& s) {
+  if (!(s.dtype == MOE_DTYPE_BF16 && s.d % 64 == 0) || s.T == 0) return 1;
+  const bool big = router_big_tiles(s);
+  const int bm = big ? 256 : 64, bn = big ? 256 : 64;
+  const long long tiles = (long long)cdiv(s.T, bm) * cdiv(s.E, bn);
+  const long long want = big ? 256 : 512;
+  const int most = big ? 8 : 16;
+  int ks = 1;
+  while (ks < most && tiles * ks < want && s.d % (2 * ks * 32) == 0) ks *= 2;
+  return ks;
+}
+
+__global__ void __launch_bounds__(256)
+router_reduce_kernel(const float* __restrict__ part, int ks, long long n, int E,
+                     const float* __restrict__ bias, float* __restrict__ logits) {
+  for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
+    float acc = part[i];
+    for (int sl = 1; sl < ks; ++sl) acc += part[sl * n + i];
+    logits[i] = acc + (bias ? bias[i % E] : 0.0f);
+  }
+}
+
 hipError_t launch_router_logits(const moe_shape& s, const void* x, const void* w_router,
-                                const float* router_bias, float* logits,
+                                const float* router_bias, float* logits, float* part,
                                 hipStream_t st) {
   if (s.T == 0) return hipSuccess;
   GemmArgs a = {};
@@ -34,7 +72,20 @@ hipError_t launch_router_logits(const moe_shape& s, const void* x, const void* w
   a.ldcd = s.E;
   a.bias = router_bias;
   if (s.dtype == MOE_DTYPE_BF16 && s.d % 64 == 0) {
-    return launch_mfma_gemm<64, 64, 1, EPI_F32_BIAS, 2, 2, 0>(a, 0, st);
+    const int ks = router_ksplit(s);
+    if (ks > 1) {
+      a.ksplit = ks;
+      a.Cpart = part;
+      a.part_stride = (long long)s.T * s.E;
+    }
+    hipError_t e = router_big_tiles(s)
+                       ? launch_mfma_gemm<256, 256, 1, EPI_F32_BIAS, 4, 2, 0>(a, 0, st)
+                       : launch_mfma_gemm<64, 64, 1, EPI_F32_BIAS, 2, 2, 0>(a, 0, st);
+    if (e != hipSuccess || ks == 1) return e;
+    const long long n = (long long)s.T * s.E;
+    const int grid = (int)std::min<long long>((n + 255) / 256, 2048);
+    router_reduce_kernel<<<grid, 256, 0, st>>>(part, ks, n, s.E, router_bias, logits);
+    return hipGetLastError();
   } else if (s.dtype == MOE_DTYPE_BF16) {
     const int grid = grid_upper_bound(a, 64, 64, 0);
     gemm_generic_kernel<bf16_t, 1, EPI_F32_BIAS><<<grid, 256, 0, st>>>(a);

@@ -46,7 +46,12 @@ def test_workspace_sizes_scale_with_the_shape():
     s = M.make_shape(c)
     ffn = M.moe_workspace_size(s, L.MOE_OP_FFN)
     assert ffn >= c.T * c.k * c.F * 2      # holds h in bf16
-    assert M.moe_workspace_size(s, L.MOE_OP_ROUTE) == 0
+    # the router GEMM (64 output tiles at this shape) splits K in 8: fp32 partials
+    assert M.moe_workspace_size(s, L.MOE_OP_ROUTE) == 8 * c.T * c.E * 4
+    # 256-expert router: 32 tiles of 256 x 256, split 8 ways
+    assert M.moe_workspace_size(M.make_shape(CONFIGS["deepseek_v3_t8192"]), L.MOE_OP_ROUTE) == \
+        8 * 8192 * 256 * 4
+    assert M.moe_workspace_size(M.make_shape(CONFIGS["tiny_fp32"]), L.MOE_OP_ROUTE) == 0
     assert M.moe_workspace_size(s, L.MOE_OP_COMBINE) == 0
     with pytest.raises(M.MoeError):
         M.moe_workspace_size(s, 9)

@@ -77,8 +77,10 @@ def test_route_topk_from_given_scores(name, over, std, quantum):
     assert torch.equal(lg.cpu(), logits)  # an input stays untouched
 
 
+# bf16 with d % 64 == 0 runs the MFMA kernel, split in K when its tiles are
+# few (64 x 64 tiles for E <= 128, 256 x 256 above); the rest runs the generic kernel
 @pytest.mark.parametrize("dtype,d,E", [(0, 128, 8), (1, 4096, 8), (1, 7168, 256), (1, 200, 24),
-                                       (0, 37, 5)])
+                                       (0, 37, 5), (1, 2048, 128), (1, 512, 96)])
 def test_router_logits_gemm(dtype, d, E):
     _log(f"[router gemm] dtype={dtype} d={d} E={E}")
     M = _lib()
@@ -88,8 +90,10 @@ def test_router_logits_gemm(dtype, d, E):
     logits = torch.empty(cfg.T, E, device="cuda")
     idx = torch.empty(cfg.T, 2, dtype=torch.int32, device="cuda")
     w = torch.empty(cfg.T, 2, device="cuda")
-    M.moe_route_topk(M.make_shape(cfg), inp["x"], inp["w_router"], inp["router_bias"],
-                     logits, None, idx, w)
+    shape = M.make_shape(cfg)
+    ws, n = _ws(M, shape, 0)          # the split router GEMM's partial sums
+    M.moe_route_topk(shape, inp["x"], inp["w_router"], inp["router_bias"],
+                     logits, None, idx, w, ws, n)
     torch.cuda.synchronize()
     ref = O.router_logits(inp["x"], inp["w_router"], inp["router_bias"], "f32")
     # fp32 outputs of an fp32 (or exact bf16-product) accumulation

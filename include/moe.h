@@ -266,7 +266,7 @@ int moe_unpermute_combine(const moe_shape* shape, const void* y_perm,
  *    dx[t] += rnd(dgs . ws_gate + dus . ws_up)[t], added after the routed terms.
  *  x [T, d], ws_gate, ws_up [F_shared, d], ws_down [d, F_shared] dtype and
  *  dws_gate, dws_up [F_shared, d], dws_down [d, F_shared] out (as
- *  shape.wgrad_dtype) are only
+ *  shape.wgrad_dtype; zero when T = 0) are only
  *  touched when F_shared > 0 (may be NULL otherwise); gu_save then holds
  *  R * 2F + T * 2F_shared elements, as moe_grouped_ffn writes it.
  *
@@ -389,8 +389,8 @@ int moe_mx_quantize_t(const void* src, int64_t batches, int32_t rows, int32_t co
  * gather.  The shared expert (F_shared > 0) gets the same over all T tokens,
  * with dy quantised along d.
  *
- *  dy, x_perm, gu_save (required: no recomputation), y_perm, maps, topk_*,
- *      logits, x and every output as in moe_ffn_backward.
+ *  dy, x_perm, gu_save (required unless T = 0: no recomputation), y_perm,
+ *      maps, topk_*, logits, x and every output as in moe_ffn_backward.
  *  w_down_tq [E, F, d], w_down_ts [E, F, d / 32]: w_down quantised along d
  *      (moe_mx_quantize_t with batches E, rows d, cols F, ldq d).
  *  w_gu_tq [E, d, 2F], w_gu_ts [E, d, 2F / 32]: w_gate then w_up quantised

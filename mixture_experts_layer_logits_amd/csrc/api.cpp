@@ -532,7 +532,8 @@ int moe_ffn_backward_mxfp8(const moe_shape* shape, const void* dy, const void* x
       return MOE_ERR_INVALID_ARG;
   }
   if (!ok_buf(dy, (long long)s.T * s.d * 2) || !ok_buf(x_perm, R * s.d * 2) ||
-      gu_save == nullptr || !ok_buf(gu_save, gu_elems * 2) || !ok_buf(y_perm, R * s.d * 2) ||
+      (gu_elems > 0 && gu_save == nullptr) || !ok_buf(gu_save, gu_elems * 2) ||
+      !ok_buf(y_perm, R * s.d * 2) ||
       !ok_buf(expert_offsets, (long long)(s.E + 1) * 4) || !ok_buf(row_token, R * 4) ||
       !ok_buf(token_row, R * 4) || !ok_buf(topk_idx, R * 4) || !ok_buf(topk_w, R * 4) ||
       !ok_buf(logits, (long long)s.T * s.E * 4) || !ok_q(w_down_tq, w_down_ts, wsz) ||

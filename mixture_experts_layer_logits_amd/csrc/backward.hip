@@ -20,6 +20,8 @@
 // tiles of experts without rows run zero K steps and store exact zeros.
 #include <float.h>
 
+#include <algorithm>
+
 #include "gemm_tiles.h"
 
 namespace moe {
@@ -882,6 +884,21 @@ static hipError_t run_backward(const moe_shape& s, BwdArgs& a, const BwdWs& ws, 
   return hipGetLastError();
 }
 
+// Zeroes n 16-bit elements (bf16 weight gradients with no tokens to sum).
+__global__ void __launch_bounds__(256) zero_u16_kernel(uint16_t* __restrict__ p, long long n) {
+  for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n; i += (long long)gridDim.x * 256)
+    p[i] = 0;
+}
+
+// A weight gradient summed over no tokens: zero, in fp32 or bf16.
+static hipError_t zero_wgrad(void* p, long long n, bool bf16, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  if (!bf16) return launch_zero_f32(static_cast<float*>(p), n, st);
+  zero_u16_kernel<<<(int)std::min<long long>((n + 255) / 256, 4096), 256, 0, st>>>(
+      static_cast<uint16_t*>(p), n);
+  return hipGetLastError();
+}
+
 // {0, n}: the row offsets of a single group of n rows.
 __global__ void one_group_offsets_kernel(int32_t* offsets, int n) {
   if (threadIdx.x == 0) {
@@ -974,6 +991,13 @@ hipError_t launch_backward(const moe_shape& s, const void* dy, const void* x_per
   }
   if (e != hipSuccess) return e;
   const bool shared = s.F_shared > 0 && s.T > 0;
+  if (s.F_shared > 0 && s.T == 0) {
+    // no tokens: the shared expert's weight gradients are empty sums
+    const long long n = (long long)s.F_shared * s.d;
+    if ((e = zero_wgrad(dws_gate, n, a.wgrad_bf16, st)) != hipSuccess) return e;
+    if ((e = zero_wgrad(dws_up, n, a.wgrad_bf16, st)) != hipSuccess) return e;
+    if ((e = zero_wgrad(dws_down, n, a.wgrad_bf16, st)) != hipSuccess) return e;
+  }
   if (shared) {
     // The shared expert: one group of all T tokens with gate 1, so dY = dy,
     // its input is x and its saved g | u follow the routed rows in gu_save.

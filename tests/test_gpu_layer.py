@@ -100,6 +100,45 @@ def test_layer_is_bitwise_deterministic():
         assert torch.equal(v, out[k]), k
 
 
+@pytest.mark.parametrize("wgrad", [0, 1], ids=["wgrad_fp32", "wgrad_bf16"])
+def test_layer_no_tokens(wgrad):
+    """T = 0 through every call of the layer (forward through x_perm, fused,
+    with the combine in FC2, and the bf16 and MXFP8 backward).  Nothing of
+    size T exists; the weight gradients, sums over no tokens, are exactly
+    zero for the routed and the shared experts alike."""
+    from mixture_experts_layer_logits_amd import MoELayer
+    cfg = MoEConfig(f"no_tokens_wgrad{wgrad}", T=0, d=256, E=16, k=4, F=256,
+                    F_shared=256, n_groups=4, topk_groups=2, score=SCORE_SIGMOID,
+                    backward=True, wgrad_dtype=wgrad)
+    print(f"[layer no tokens] {cfg.name}", flush=True)
+    inp = make_inputs(cfg, device="cuda")
+    infer = MoELayer(cfg.replace(backward=False))
+    keys = ("dw_gate", "dw_up", "dw_down", "dws_gate", "dws_up", "dws_down")
+    for run in ("forward", "fused", "combined"):
+        if run == "forward":
+            out = infer.forward(inp)
+        elif run == "fused":
+            out = infer.forward(inp, fused=True)
+        else:
+            out = infer.forward_combined(inp)
+        torch.cuda.synchronize()
+        assert out["y"].shape == (0, cfg.d)
+        assert out["expert_offsets"].cpu().tolist() == [0] * (cfg.E + 1)
+    layer = MoELayer(cfg)
+    layer.forward(inp)
+    layer.quantize_weights_t(inp)
+    for bwd in (layer.backward, layer.backward_mxfp8):
+        if layer.grad is None:
+            layer._alloc_grad()
+        for key in keys:
+            layer.grad[key].fill_(float("nan"))
+        g = bwd(inp, inp["dy"])
+        torch.cuda.synchronize()
+        for key in keys:
+            assert torch.all(g[key] == 0), (bwd.__name__, key)
+        assert g["dx"].shape == (0, cfg.d) and g["d_logits"].shape == (0, cfg.E)
+
+
 def test_layer_training_with_shared_expert():
     """Forward (saving g|u of routed and shared rows) then backward of a layer
     with sigmoid group-limited routing and a shared expert, against the

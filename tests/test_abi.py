@@ -94,6 +94,12 @@ def test_calls_reject_null_misaligned_and_small_workspace():
     # a router bias with logits given as input
     st = M.moe_route_topk(s, None, None, p, p, None, p, p, check=False, stream=0)
     assert st == L.MOE_ERR_INVALID_ARG
+    # the bf16 router GEMM split in K needs its partials' workspace
+    cm = M.make_shape(CONFIGS["mixtral_t4096"])
+    need_r = M.moe_workspace_size(cm, L.MOE_OP_ROUTE)
+    for wsp, nb in ((None, 0), (p, need_r - 1)):
+        st = M.moe_route_topk(cm, p, p, None, p, None, p, p, wsp, nb, check=False, stream=0)
+        assert st == L.MOE_ERR_WORKSPACE
     # permute without its workspace
     st = M.moe_permute(s, p, p, p, p, p, p, p, p, None, 0, check=False, stream=0)
     assert st == L.MOE_ERR_WORKSPACE

@@ -96,20 +96,45 @@ hipError_t launch_router_logits(const moe_shape& s, const void* x, const void* w
   return hipGetLastError();
 }
 
-// Wave-wide arg-max: larger key wins, the lower index on equal keys.
-// Lanes without a candidate carry idx == INT_MAX.
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(v, off, 64);
-    const int oi = __shfl_xor(i, off, 64);
-    const bool take = (oi != INT_MAX) &&
-                      (i == INT_MAX || ov > v || (ov == v && oi < i));
-    if (take) {
-      v = ov;
-      i = oi;
-    }
+// Arg-max order: the larger key wins, the lower index on equal keys; lanes
+// without a candidate carry idx == INT_MAX and never win.  The order is
+// total, so any reduction tree finds the same winner.
+__device__ __forceinline__ void argmax_take(float& v, int& i, float ov, int oi) {
+  const bool take = (oi != INT_MAX) && (i == INT_MAX || ov > v || (ov == v && oi < i));
+  if (take) {
+    v = ov;
+    i = oi;
   }
+}
+
+// One step against the lane that the DPP pattern CTRL names (every lane of a
+// row has a source under the patterns used here).
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp(float& v, int& i) {
+  const float ov =
+      __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+  const int oi = __builtin_amdgcn_update_dpp(0, i, CTRL, 0xf, 0xf, false);
+  argmax_take(v, i, ov, oi);
+}
+
+// Wave-wide arg-max, the result in every lane.  Within each 16-lane row the
+// pairs move by DPP (lane ^ 1 and lane ^ 2 by quad permutes, then rotations
+// of the row by 4 and 8), so every lane ends with its row's winner; the four
+// row winners are then read as wave-uniform values.  No LDS traffic, unlike
+// a shuffle through ds_bpermute.  Must be called with every lane active.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  argmax_dpp<0xB1>(v, i);    // quad_perm [1, 0, 3, 2]
+  argmax_dpp<0x4E>(v, i);    // quad_perm [2, 3, 0, 1]
+  argmax_dpp<0x124>(v, i);   // row_ror:4
+  argmax_dpp<0x128>(v, i);   // row_ror:8
+  float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  int ri = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r)
+    argmax_take(rv, ri, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r)),
+                __builtin_amdgcn_readlane(i, 16 * r));
+  v = rv;
+  i = ri;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -223,7 +248,7 @@ topk_kernel(const float* __restrict__ logits, const float* __restrict__ score_bi
         mine = sc[q];
       }
     }
-    const float win_s = __shfl(mine, bi & 63, 64);
+    const float win_s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), bi & 63));
     if (lane == j) {
       my_e = bi;
       my_s = win_s;

@@ -1,17 +1,22 @@
 """Throughput of one GPU's MoE layer (tokens/s) with the grouped-GEMM rate.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--headline-only]
 
 A step is one pass of the whole layer over one batch of seeded synthetic
 tokens already resident in HBM: router GEMM + top-k, permutation, grouped
 SwiGLU FFN (FC1 + FC2, plus the shared expert where the workload has one),
-combine, and the backward where the workload is a training step.  W untimed
-warm-up steps, then K timed steps between two device synchronisations.  Per
-stage, HIP events recorded on the stream the library launches on give the
-mean, median and minimum duration; the grouped FFN stage (the dominant kernel
-pair) is priced against the MI355X roofline.  The bandwidth stages (permute,
-combine) are also timed on their own, after a scratch write that evicts the
-caches and back to back.  The CPU oracle is timed on a bounded sample of the
+combine, and the backward where the workload is a training step.  The
+default workload is the largest configuration, the Qwen3-235B-shape training
+step (forward + backward).  W untimed warm-up steps, then K timed steps
+between two device synchronisations.  Per stage, HIP events recorded on the
+stream the library launches on give the mean, median and minimum duration;
+inside the grouped FFN and backward calls the library records events around
+each main kernel (moe_set_phase_events), and every such kernel is priced
+against the MI355X roofline; the longest one is the line's `roofline`.  The
+bandwidth stages (permute, combine) are also timed on their own, after a
+scratch write that evicts the caches and back to back, beside this box's
+plain device-copy rate.  The CPU oracle is timed on a bounded sample of the
 same workload on the host cores.  Prints one JSON line.
 """
 from __future__ import annotations
@@ -31,11 +36,11 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
-# The grouped FFN's kernel sources; traffic figures recorded in profiles/ are
-# used only while these files are byte-identical to the ones profiled.
-FFN_SOURCES = ("mixture_experts_layer_logits_amd/csrc/ffn.hip",
-               "mixture_experts_layer_logits_amd/csrc/gemm_tiles.h",
-               "mixture_experts_layer_logits_amd/csrc/moe_common.h")
+# Kernel sources per phase; traffic figures recorded in profiles/ are used
+# only while these files are byte-identical to the ones profiled.
+_CSRC = "mixture_experts_layer_logits_amd/csrc/"
+FFN_SOURCES = (_CSRC + "ffn.hip", _CSRC + "gemm_tiles.h", _CSRC + "moe_common.h")
+BWD_SOURCES = (_CSRC + "backward.hip", _CSRC + "gemm_tiles.h", _CSRC + "moe_common.h")
 
 
 def ffn_flops(c):
@@ -57,6 +62,72 @@ def ffn_bytes(c, counts_nonzero):
     if c.backward:
         act += (2 * R * c.F + 2 * c.T * c.F_shared) * b   # gu_save
     return w + act
+
+
+def phase_figures(c, counts_nonzero):
+    """Algorithmic FLOPs and HBM bytes of one launch of each phase kernel
+    (the MOE_PHASE_* kernels of the routed experts), R = T k routed rows,
+    E' = experts with rows, b = storage bytes, wb = weight-gradient bytes:
+      fc1          4 R d F flops; W_g, W_u of E' experts, x_perm read, h
+                   written (+ g | u when training)
+      fc2          2 R F d; W_d of E' experts, h read, y_perm written
+      bwd_dispatch dy and y_perm read, dY_perm written (+ fp32 logits read,
+                   d_logits written)
+      bwd_dh       2 R d F; dY_perm, W_d, g | u read; dg | du and h written
+      bwd_dw_down  2 R d F; dY_perm and h read; dW_down of all E written
+      bwd_dx       4 R F d; dg | du, W_g, W_u read; dX_perm written
+      bwd_dw_gate_up 4 R d F; dg | du and x_perm read; dW_gate, dW_up of all
+                   E written
+      bwd_gather   dX_perm read, fp32 dx written
+    The shared expert's work counts where it shares the launch (fc1, fc2)."""
+    b = 2 if c.dtype == 1 else 4
+    wb = 2 if c.wgrad_dtype == 1 else 4
+    R, T, d, F, E, Fs = c.T * c.k, c.T, c.d, c.F, c.E, c.F_shared
+    En = counts_nonzero
+    f = {}
+    f["fc1"] = (4.0 * R * d * F + 4.0 * T * d * Fs,
+                (2.0 * En * F * d + R * d + R * F + (2 * R * F if c.backward else 0)) * b +
+                ((2.0 * Fs * d + T * d + T * Fs + (2 * T * Fs if c.backward else 0)) * b
+                 if Fs else 0))
+    f["fc2"] = (2.0 * R * F * d + 2.0 * T * Fs * d,
+                (En * d * F + R * F + R * d) * b + ((Fs * d + T * Fs + T * d) * b if Fs else 0))
+    if c.backward:
+        f["bwd_dispatch"] = (2.0 * R * d, (T * d + 2.0 * R * d) * b + 8.0 * T * E + 8.0 * T * c.k)
+        f["bwd_dh"] = (2.0 * R * d * F, (R * d + En * d * F + 2 * R * F + 2 * R * F + R * F) * b)
+        f["bwd_dw_down"] = (2.0 * R * d * F, (R * d + R * F) * b + 1.0 * E * d * F * wb)
+        f["bwd_dx"] = (4.0 * R * F * d, (2.0 * R * F + 2.0 * En * F * d + R * d) * b)
+        f["bwd_dw_gate_up"] = (4.0 * R * d * F, (2.0 * R * F + R * d) * b + 2.0 * E * F * d * wb)
+        f["bwd_gather"] = (1.0 * R * d, R * d * b + 4.0 * T * d)
+    return f
+
+
+# The kernel behind each phase (names as a kernel trace prints them, for the
+# headline bf16 shapes: d and F multiples of 256).
+PHASE_KERNELS = {
+    "fc1": "gemm_bf16_mfma_kernel<256, 128, 2, 1, 4, 2, 1> (FC1 + SwiGLU)",
+    "fc2": "gemm_bf16_mfma_kernel<256, 256, 1, 0, 4, 2, 1> (FC2) + splitk_reduce_kernel",
+    "bwd_dispatch": "bwd_dispatch_kernel<unsigned short>",
+    "bwd_dh": "bwd_dma_kernel<0> (dh + SwiGLU backward)",
+    "bwd_dw_down": "bwd_dma_kernel<2> (dW_down)",
+    "bwd_dx": "bwd_dma_kernel<1> (dX_perm)",
+    "bwd_dw_gate_up": "bwd_dma_kernel<3> (dW_gate | dW_up)",
+    "bwd_gather": "bwd_gather_kernel<unsigned short>",
+}
+
+
+def price(flops, nbytes, ms):
+    """Roofline of one kernel: the bound is the resource whose peak time is
+    longer; achieved = algorithmic work / measured time against that peak."""
+    t = ms / 1e3
+    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        a = flops / t / 1e12
+        return {"bound": "mfma", "achieved": round(a, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(a / PEAK_BF16_TFLOPS, 4)}
+    a = nbytes / t / 1e9
+    return {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(a / PEAK_HBM_GBS, 4)}
 
 
 def permute_bytes(c):
@@ -85,11 +156,11 @@ def sources_digest(paths):
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload):
-    """HBM bytes per moe_grouped_ffn call from the committed FETCH_SIZE /
+def recorded_traffic(workload, kernel="moe_grouped_ffn", sources=FFN_SOURCES):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE /
     WRITE_SIZE summary of this workload, or None when there is none or the
     kernel sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_moe_grouped_ffn_{workload}.md")
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -99,7 +170,7 @@ def recorded_traffic(workload):
                 for kv in line.split()[1:]:
                     key, _, v = kv.partition("=")
                     vals[key] = v
-    if vals.get("sources") != sources_digest(FFN_SOURCES):
+    if vals.get("sources") != sources_digest(sources):
         return None
     try:
         return int(vals["bytes_per_call"])
@@ -170,22 +241,23 @@ def cpu_baseline(cfg, inp, sample_tokens=None, target_s=15.0):
     Without a fixed sample size, passes on growing samples run until one
     takes at least target_s / 2 seconds (or covers the whole workload); the
     last pass is the one reported."""
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_limits
 
-    if sample_tokens:
-        T = min(sample_tokens, cfg.T)
-        dt = _oracle_pass(cfg, inp, T)
-    else:
-        # grow the sample (at most 8x a pass: fixed costs dominate small ones)
-        T = min(cfg.T, 64)
-        dt = _oracle_pass(cfg, inp, T)
-        while dt < target_s / 2 and T < cfg.T:
-            T = min(cfg.T, max(T + 1, int(T * min(8.0, target_s / max(dt, 1e-3)))))
+    # the host cores this process may run on; the oracle's BLAS uses them all
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores, user_api="blas"):
+        if sample_tokens:
+            T = min(sample_tokens, cfg.T)
             dt = _oracle_pass(cfg, inp, T)
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                   if i.get("user_api") == "blas"] or [1])
+        else:
+            # grow the sample (at most 8x a pass: fixed costs dominate small ones)
+            T = min(cfg.T, 64)
+            dt = _oracle_pass(cfg, inp, T)
+            while dt < target_s / 2 and T < cfg.T:
+                T = min(cfg.T, max(T + 1, int(T * min(8.0, target_s / max(dt, 1e-3)))))
+                dt = _oracle_pass(cfg, inp, T)
     kind = "forward+backward" if cfg.backward else "forward"
-    return {"value": round(T / dt, 2), "unit": "tokens/s", "cores": int(threads),
+    return {"value": round(T / dt, 2), "unit": "tokens/s", "cores": int(cores),
             "kind": "oracle", "cpu": cpu_model(),
             "sample": f"first {T} of {cfg.T} tokens of the same workload, whole "
                       f"{kind} layer in the fp64 oracle ({dt:.1f} s)"}
@@ -196,9 +268,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mixtral_t4096")
+    ap.add_argument("--workload", default="qwen3_235b_train_t8192",
+                    help="the Qwen3-235B-shape training step (forward + backward), "
+                         "the largest configuration, by default")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the headline step (no isolated stages, fused, "
+                         "MXFP8 or other variants), so that a kernel trace of the run "
+                         "holds the headline form's kernels alone")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling "
                          "the FETCH_SIZE/WRITE_SIZE counters)")
@@ -215,7 +293,10 @@ def main():
     import numpy as np
     import torch
 
+    import ctypes
+
     from mixture_experts_layer_logits_amd import MoELayer
+    from mixture_experts_layer_logits_amd import _lib as L
     from moe_inputs import CONFIGS, make_inputs
 
     cfg = CONFIGS[args.workload]
@@ -242,23 +323,40 @@ def main():
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
            for _ in range(args.steps)]
+    # Per-kernel events: the library records pair p of a step's array around
+    # phase p's kernels (moe_set_phase_events), on the stream it launches on.
+    nph = 2 * L.MOE_PHASE_COUNT
+    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(nph)]
+           for _ in range(args.steps)]
+    for row in pev:
+        for ev in row:
+            ev.record(stream)          # creates the HIP event behind it
+    parr = [(ctypes.c_void_p * nph)(*[ev.cuda_event for ev in row]) for row in pev]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
+        L.moe_set_phase_events(parr[s])
         step(evs[s])
+    L.moe_set_phase_events(None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
     stage_samples = {st: [evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]
                      for i, st in enumerate(stages)}
     per_stage = {st: float(np.mean(v)) for st, v in stage_samples.items()}
+    phase_ms = {}
+    for p_, name in enumerate(L.PHASE_NAMES):
+        if name.startswith("bwd") and not cfg.backward:
+            continue
+        v = [pev[s][2 * p_].elapsed_time(pev[s][2 * p_ + 1]) for s in range(args.steps)]
+        phase_ms[name] = (float(np.mean(v)), float(np.median(v)), float(np.min(v)))
 
     # The bandwidth stages on their own, each repetition after a 512 MiB
     # scratch write that evicts the L2s and the 256 MB MALL ("flushed"), and
     # back to back with their inputs left in the caches ("cache_resident").
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     isolated = {}
-    for st in ("permute", "combine"):
+    for st in (() if args.headline_only else ("permute", "combine")):
         fn = getattr(layer, st)
         res = {}
         for label, flush in (("flushed", True), ("cache_resident", False)):
@@ -274,13 +372,29 @@ def main():
             torch.cuda.synchronize()
             res[label] = [pev[s_][0].elapsed_time(pev[s_][1]) for s_ in range(args.steps)]
         isolated[st] = res
+    # This box's plain device copy of 1 GiB (read + write), the practical
+    # ceiling of a copy-shaped stage such as permute and combine.
+    copy_gbs = None
+    if not args.headline_only:
+        src = scratch[: 256 << 20]
+        dst = torch.empty_like(src)
+        cev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for _ in range(3):
+            dst.copy_(src)
+        cev[0].record(stream)
+        for _ in range(10):
+            dst.copy_(src)
+        cev[1].record(stream)
+        torch.cuda.synchronize()
+        copy_gbs = 2 * src.numel() * 10 / (cev[0].elapsed_time(cev[1]) / 1e3) / 1e9
+        del src, dst
     del scratch
     torch.cuda.empty_cache()
 
     # The same forward with the permutation fused into FC1's operand load
     # (maps-only permute, rows gathered from x; no x_perm), timed the same way.
     fused = None
-    if not cfg.backward:
+    if not cfg.backward and not args.headline_only:
         def fused_step(ev=None):
             if ev is not None:
                 ev[0].record(stream)
@@ -315,7 +429,7 @@ def main():
     # maps-only permute, then one FFN call that adds each gate-scaled expert
     # output into y (no y_perm, no combine launch).
     combined = None
-    if not cfg.backward:
+    if not cfg.backward and not args.headline_only:
         def comb_step(ev=None):
             if ev is not None:
                 ev[0].record(stream)
@@ -346,7 +460,7 @@ def main():
     # weights quantised once and cached (outside the timed steps, reported
     # on its own), x quantised every step, rows gathered from the quantised x.
     mx = None
-    if (not cfg.backward and cfg.dtype == 1 and
+    if (not cfg.backward and not args.headline_only and cfg.dtype == 1 and
             all(v % 128 == 0 for v in (cfg.d, cfg.F, cfg.F_shared))):
         q0, q1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
         q0.record(stream)
@@ -413,7 +527,7 @@ def main():
     # Training with selective rematerialisation: the forward keeps no g | u
     # and the backward reruns FC1 (same kernels) before its own GEMMs.
     remat = None
-    if cfg.backward:
+    if cfg.backward and not args.headline_only:
         rl = MoELayer(cfg, device=dev, recompute=True)
 
         def remat_step(ev=None):
@@ -503,30 +617,43 @@ def main():
     tokens_per_s = cfg.T / (ms_wall / 1e3)
 
     counts = torch.diff(layer.buf["expert_offsets"]).cpu().numpy()
+    n_nonzero = int((counts > 0).sum())
     flops = ffn_flops(cfg)
     t_ffn = per_stage["ffn"] / 1e3
     tflops = flops / t_ffn / 1e12
-    bytes_ = ffn_bytes(cfg, int((counts > 0).sum()))
-    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
-    t_hbm = bytes_ / (PEAK_HBM_GBS * 1e9)
-    if t_mfma >= t_hbm:
-        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
-    else:
-        gbs = bytes_ / t_ffn / 1e9
-        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
-    roof["traffic"] = recorded_traffic(cfg.name)
-    roof["algorithmic_bytes"] = int(bytes_)
-    roof["kernel"] = ("moe_grouped_ffn: one call = tile schedule, FC1+SwiGLU "
-                      "and FC2 grouped GEMM launches (+ split-K reduce)")
+    bytes_ = ffn_bytes(cfg, n_nonzero)
+    # the forward's grouped FFN call as a whole (FC1 + FC2 and their helpers)
+    ffn_roof = price(flops, bytes_, per_stage["ffn"])
+    ffn_roof["traffic"] = recorded_traffic(cfg.name)
+    ffn_roof["algorithmic_bytes"] = int(bytes_)
+    ffn_roof["kernel"] = ("moe_grouped_ffn: one call = tile schedule, FC1+SwiGLU "
+                          "and FC2 grouped GEMM launches (+ split-K reduce)")
+    # every phase kernel priced on its own; the dominant one (longest mean
+    # launch) is the line's roofline
+    figs = phase_figures(cfg, n_nonzero)
+    kernels = {}
+    for name, (mean, med, mn) in phase_ms.items():
+        fl, nb = figs[name]
+        r = price(fl, nb, mean)
+        r.update({"kernel": PHASE_KERNELS[name], "ms_mean": round(mean, 4),
+                  "ms_median": round(med, 4), "ms_min": round(mn, 4),
+                  "algorithmic_flops": fl, "algorithmic_bytes": int(nb)})
+        kernels[name] = r
+    dom = max(kernels, key=lambda k_: kernels[k_]["ms_mean"])
+    roof = {k_: kernels[dom][k_] for k_ in ("bound", "achieved", "peak", "unit", "frac")}
+    roof["traffic"] = recorded_traffic(cfg.name, dom, BWD_SOURCES if dom.startswith("bwd")
+                                       else FFN_SOURCES)
+    roof.update({"kernel": kernels[dom]["kernel"], "phase": dom,
+                 "ms_per_launch": kernels[dom]["ms_mean"],
+                 "algorithmic_flops": kernels[dom]["algorithmic_flops"],
+                 "algorithmic_bytes": kernels[dom]["algorithmic_bytes"]})
 
-    hbm = {}
+    hbm = {"copy_ceiling_GBs": None if copy_gbs is None else round(copy_gbs, 1)}
     for st, nb in (("permute", permute_bytes(cfg)), ("combine", combine_bytes(cfg))):
         gbs = nb / (per_stage[st] / 1e3) / 1e9
         hbm[st] = {"bytes": int(nb), "GB/s": round(gbs, 1),
                    "frac": round(gbs / PEAK_HBM_GBS, 4)}
-        for label, v in isolated[st].items():
+        for label, v in isolated.get(st, {}).items():
             med = float(np.median(v))
             g = nb / (med / 1e3) / 1e9
             hbm[st][label] = {"ms_median": round(med, 4), "ms_min": round(float(np.min(v)), 4),
@@ -559,6 +686,8 @@ def main():
         "mxfp8_forward": mx,
         "training_variants": remat,
         "roofline": roof,
+        "ffn_roofline": ffn_roof,
+        "kernels": kernels,
         "cpu_baseline": cpu,
         "device": device_record(torch),
     }

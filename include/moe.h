@@ -36,7 +36,8 @@
  *    atomics), with stated exceptions: moe_grouped_ffn_combine and
  *    moe_grouped_ffn_mxfp8_combine, whose fp32 atomic additions are
  *    order-independent only with at most two addends per output element.
- *    The library keeps no mutable global state.
+ *    The library keeps no mutable global state (moe_set_phase_events keeps
+ *    one per-thread pointer for measurement).
  *
  * Dtypes: `dtype` selects the storage type of x, the weights and the
  * materialised intermediates x_perm, h, y_perm, gu_save (MOE_DTYPE_BF16 or
@@ -416,6 +417,37 @@ int moe_ffn_backward_mxfp8(const moe_shape* shape, const void* dy, const void* x
 
 /* Static text for a moe_status value (never NULL). */
 const char* moe_status_string(int status);
+
+/* Measurement aid: the kernels each MOE_PHASE_* names, bracketed by HIP
+ * events on the call's stream, so that a caller can time one kernel inside
+ * a call (the Primus blog times its MoE layer with HIP events; this reaches
+ * inside moe_grouped_ffn and moe_ffn_backward).  The routed experts' kernels
+ * only: the shared expert's own backward launches are not bracketed, and in
+ * the forward it shares FC1's and FC2's launches. */
+enum {
+  MOE_PHASE_FC1 = 0,            /* FC1 + SwiGLU grouped GEMM                   */
+  MOE_PHASE_FC2 = 1,            /* FC2 grouped GEMM (+ its split-K reduce)     */
+  MOE_PHASE_BWD_DISPATCH = 2,   /* dY_perm, d_gate and d_logits                */
+  MOE_PHASE_BWD_DH = 3,         /* dh with the SwiGLU backward                 */
+  MOE_PHASE_BWD_DW_DOWN = 4,    /* dw_down = dY_perm^T . h                     */
+  MOE_PHASE_BWD_DX = 5,         /* dX_perm = dg . w_gate + du . w_up           */
+  MOE_PHASE_BWD_DW_GATE_UP = 6, /* dw_gate | dw_up = [dg | du]^T . x_perm      */
+  MOE_PHASE_BWD_GATHER = 7,     /* dx[t] = sum_j dX_perm[row]                  */
+  MOE_PHASE_COUNT = 8
+};
+
+/* Sets, for the calling thread, the events that later calls of
+ * moe_grouped_ffn and moe_ffn_backward record (moe_ffn_backward_mxfp8: its
+ * two weight-gradient phases): events[2 p] (a hipEvent_t)
+ * just before the kernels of phase p are enqueued and events[2 p + 1] just
+ * after them, for every p with 2 p + 1 < n_events and non-NULL entries.
+ * The array is the caller's and must stay valid until the next call of this
+ * function; n_events = 0 (or events NULL with n_events 0) switches the
+ * recording off, which is the default.  Per-thread state, the library's only
+ * mutable state; calls on other threads are unaffected.  Returns
+ * MOE_ERR_INVALID_ARG for n_events < 0, or for events NULL with
+ * n_events > 0. */
+int moe_set_phase_events(void* const* events, int n_events);
 
 #ifdef __cplusplus
 }

@@ -140,7 +140,15 @@ void carve_backward(const moe_shape& s, Carver& c, moe::BwdWs& bw) {
 
 }  // namespace
 
+thread_local moe::PhaseEvents moe::g_phase_events = {nullptr, 0};
+
 extern "C" {
+
+int moe_set_phase_events(void* const* events, int n_events) {
+  if (n_events < 0 || (n_events > 0 && !events)) return MOE_ERR_INVALID_ARG;
+  moe::g_phase_events = {n_events > 0 ? events : nullptr, n_events};
+  return MOE_OK;
+}
 
 int moe_workspace_size(const moe_shape* shape, int op, size_t* bytes) {
   const int st = check_shape(shape);

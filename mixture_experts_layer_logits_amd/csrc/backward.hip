@@ -869,18 +869,29 @@ static void launch_bwd_gemm(const moe_shape& s, const BwdArgs& a, hipStream_t st
   else bwd_generic_kernel<MODE, T><<<grid, 256, 0, st>>>(a);
 }
 
+// One backward GEMM launch, bracketed by its phase events when `marks`.
+template <int MODE, typename T, int FLAVOR>
+static void launch_bwd_phase(const moe_shape& s, const BwdArgs& a, hipStream_t st, bool marks) {
+  constexpr int PHASE = MODE == BWD_DH ? MOE_PHASE_BWD_DH : MODE == BWD_WD ? MOE_PHASE_BWD_DW_DOWN
+                        : MODE == BWD_DX ? MOE_PHASE_BWD_DX : MOE_PHASE_BWD_DW_GATE_UP;
+  if (marks) phase_mark(PHASE, 0, st);
+  launch_bwd_gemm<MODE, T, FLAVOR>(s, a, st);
+  if (marks) phase_mark(PHASE, 1, st);
+}
+
 template <typename T, int FLAVOR>
-static hipError_t run_backward(const moe_shape& s, BwdArgs& a, const BwdWs& ws, hipStream_t st) {
+static hipError_t run_backward(const moe_shape& s, BwdArgs& a, const BwdWs& ws, hipStream_t st,
+                               bool marks) {
   constexpr int BM = FLAVOR == 2 ? 256 : FLAVOR == 1 ? 128 : 64, BN = BM;
   // tile prefixes of the two row-grouped GEMMs (N = F for dh, N = d for dX)
   schedule_tiles_kernel<<<1, 1024, 0, st>>>(a.offsets, s.E, BM, cdiv(s.F, BN), ws.tiles, BM,
                                             cdiv(s.d, BN), ws.tiles2, 0);
   a.tiles = ws.tiles;
-  launch_bwd_gemm<BWD_DH, T, FLAVOR>(s, a, st);
-  launch_bwd_gemm<BWD_WD, T, FLAVOR>(s, a, st);
+  launch_bwd_phase<BWD_DH, T, FLAVOR>(s, a, st, marks);
+  launch_bwd_phase<BWD_WD, T, FLAVOR>(s, a, st, marks);
   a.tiles = ws.tiles2;
-  launch_bwd_gemm<BWD_DX, T, FLAVOR>(s, a, st);
-  launch_bwd_gemm<BWD_WGU, T, FLAVOR>(s, a, st);
+  launch_bwd_phase<BWD_DX, T, FLAVOR>(s, a, st, marks);
+  launch_bwd_phase<BWD_WGU, T, FLAVOR>(s, a, st, marks);
   return hipGetLastError();
 }
 
@@ -907,27 +918,29 @@ __global__ void one_group_offsets_kernel(int32_t* offsets, int n) {
   }
 }
 
+// marks: bracket the kernels with the phase events (the routed group only).
 static hipError_t run_backward_any(const moe_shape& s, BwdArgs& a, const BwdWs& ws,
-                                   hipStream_t st) {
+                                   hipStream_t st, bool marks) {
   const bool bf = s.dtype == MOE_DTYPE_BF16;
-  if (bf && bwd_uses_dma(s)) return run_backward<bf16_t, 2>(s, a, ws, st);
-  if (bf && bwd_uses_mfma(s)) return run_backward<bf16_t, 1>(s, a, ws, st);
-  if (bf) return run_backward<bf16_t, 0>(s, a, ws, st);
-  return run_backward<float, 0>(s, a, ws, st);
+  if (bf && bwd_uses_dma(s)) return run_backward<bf16_t, 2>(s, a, ws, st, marks);
+  if (bf && bwd_uses_mfma(s)) return run_backward<bf16_t, 1>(s, a, ws, st, marks);
+  if (bf) return run_backward<bf16_t, 0>(s, a, ws, st, marks);
+  return run_backward<float, 0>(s, a, ws, st, marks);
 }
 
 // The weight-gradient GEMMs alone (bf16), after data gradients computed
 // elsewhere (the MXFP8 path) have written h and dg | du.
-static hipError_t run_wgrad_any(const moe_shape& s, const BwdArgs& a, hipStream_t st) {
+static hipError_t run_wgrad_any(const moe_shape& s, const BwdArgs& a, hipStream_t st,
+                                bool marks) {
   if (bwd_uses_dma(s)) {
-    launch_bwd_gemm<BWD_WD, bf16_t, 2>(s, a, st);
-    launch_bwd_gemm<BWD_WGU, bf16_t, 2>(s, a, st);
+    launch_bwd_phase<BWD_WD, bf16_t, 2>(s, a, st, marks);
+    launch_bwd_phase<BWD_WGU, bf16_t, 2>(s, a, st, marks);
   } else if (bwd_uses_mfma(s)) {
-    launch_bwd_gemm<BWD_WD, bf16_t, 1>(s, a, st);
-    launch_bwd_gemm<BWD_WGU, bf16_t, 1>(s, a, st);
+    launch_bwd_phase<BWD_WD, bf16_t, 1>(s, a, st, marks);
+    launch_bwd_phase<BWD_WGU, bf16_t, 1>(s, a, st, marks);
   } else {
-    launch_bwd_gemm<BWD_WD, bf16_t, 0>(s, a, st);
-    launch_bwd_gemm<BWD_WGU, bf16_t, 0>(s, a, st);
+    launch_bwd_phase<BWD_WD, bf16_t, 0>(s, a, st, marks);
+    launch_bwd_phase<BWD_WGU, bf16_t, 0>(s, a, st, marks);
   }
   return hipGetLastError();
 }
@@ -944,6 +957,7 @@ hipError_t launch_backward(const moe_shape& s, const void* dy, const void* x_per
                            const BwdWs& ws, hipStream_t st, const MxBwdWeights* mx) {
   (void)row_token;
   const bool bf = s.dtype == MOE_DTYPE_BF16;
+  phase_mark(MOE_PHASE_BWD_DISPATCH, 0, st);
   if (s.T > 0) {
     if (bf)
       bwd_dispatch_kernel<bf16_t><<<s.T, 256, 0, st>>>(
@@ -956,6 +970,7 @@ hipError_t launch_backward(const moe_shape& s, const void* dy, const void* x_per
           topk_w, logits, s.d, s.E, s.k, s.score, s.renorm, static_cast<float*>(ws.dY), d_gate,
           d_logits);
   }
+  phase_mark(MOE_PHASE_BWD_DISPATCH, 1, st);
   BwdArgs a = {};
   a.E = s.E;
   a.F = s.F;
@@ -985,9 +1000,9 @@ hipError_t launch_backward(const moe_shape& s, const void* dy, const void* x_per
     MxDgrad g = {R, offsets, ws.tiles, ws.tiles2, ws.dyq, ws.dys, mx->wd_tq, mx->wd_ts,
                  gu_save, ws.dgu, ws.h, ws.dguq, ws.dgus, mx->wgu_tq, mx->wgu_ts, ws.dX};
     if ((e = launch_mx_dgrad(s, g, st)) != hipSuccess) return e;
-    e = run_wgrad_any(s, a, st);
+    e = run_wgrad_any(s, a, st, true);
   } else {
-    e = run_backward_any(s, a, ws, st);
+    e = run_backward_any(s, a, ws, st, true);
   }
   if (e != hipSuccess) return e;
   const bool shared = s.F_shared > 0 && s.T > 0;
@@ -1037,11 +1052,12 @@ hipError_t launch_backward(const moe_shape& s, const void* dy, const void* x_per
                    mx->swd_tq, mx->swd_ts, b.gu, ws.s_dgu, ws.s_h, ws.s_dguq, ws.s_dgus,
                    mx->swgu_tq, mx->swgu_ts, ws.s_dX};
       if ((e = launch_mx_dgrad(s2, g, st)) != hipSuccess) return e;
-      if ((e = run_wgrad_any(s2, b, st)) != hipSuccess) return e;
-    } else if ((e = run_backward_any(s2, b, w2, st)) != hipSuccess) {
+      if ((e = run_wgrad_any(s2, b, st, false)) != hipSuccess) return e;
+    } else if ((e = run_backward_any(s2, b, w2, st, false)) != hipSuccess) {
       return e;
     }
   }
+  phase_mark(MOE_PHASE_BWD_GATHER, 0, st);
   if (s.T > 0) {
     if (bf)
       bwd_gather_kernel<bf16_t><<<s.T, 256, 0, st>>>(
@@ -1052,6 +1068,7 @@ hipError_t launch_backward(const moe_shape& s, const void* dy, const void* x_per
           static_cast<const float*>(ws.dX), token_row, s.d, s.k,
           shared ? static_cast<const float*>(ws.s_dX) : nullptr, dx);
   }
+  phase_mark(MOE_PHASE_BWD_GATHER, 1, st);
   return hipGetLastError();
 }
 

@@ -88,10 +88,14 @@ static hipError_t run_generic(const moe_shape& s, GemmArgs& a1, GemmArgs& a2, in
     schedule_tiles_kernel<<<1, 1024, 0, st>>>(a1.offsets, s.E, GEN_BM, cdiv(s.F, GEN_BN),
                                               ws.tiles1, GEN_BM, cdiv(s.d, GEN_BN), ws.tiles2, 0);
   }
+  phase_mark(MOE_PHASE_FC1, 0, st);
   int g1 = grid_upper_bound(a1, GEN_BM, GEN_BN, R);
   if (g1 > 0) gemm_generic_kernel<T, 2, EPI_SWIGLU><<<g1, 256, 0, st>>>(a1);
+  phase_mark(MOE_PHASE_FC1, 1, st);
+  phase_mark(MOE_PHASE_FC2, 0, st);
   int g2 = grid_upper_bound(a2, GEN_BM, GEN_BN, R);
   if (g2 > 0) gemm_generic_kernel<T, 1, EPI2><<<g2, 256, 0, st>>>(a2);
+  phase_mark(MOE_PHASE_FC2, 1, st);
   return hipGetLastError();
 }
 
@@ -224,7 +228,9 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const int3
                                               ws.tiles1, FC2_BM, cdiv(s.d, FC2_BN), ws.tiles2, 1);
   }
   a1.tail = a2.tail = 1;
+  phase_mark(MOE_PHASE_FC1, 0, st);
   hipError_t e = launch_mfma_gemm<FC1_BM, FC1_BN, 2, EPI_SWIGLU, 4, 2, 1>(a1, R, st);
+  phase_mark(MOE_PHASE_FC1, 1, st);
   if (e != hipSuccess) return e;
   const int ks = ffn_fc2_ksplit(s);
   if (ks > 1 && a2.E > 0) {
@@ -232,13 +238,17 @@ hipError_t launch_grouped_ffn(const moe_shape& s, const void* x_perm, const int3
     a2.Cpart = ws.part;
     a2.part_stride = (long long)R * s.d;
   }
+  phase_mark(MOE_PHASE_FC2, 0, st);
   e = launch_mfma_gemm<FC2_BM, FC2_BN, 1, EPI_STORE, 4, 2, 1>(a2, R, st);
-  if (e != hipSuccess || a2.ksplit <= 1) return e;
-  const long long n4 = (long long)R * s.d / 4;
-  const int grid = (int)std::min<long long>((n4 + 255) / 256, 4096);
-  splitk_reduce_kernel<<<grid, 256, 0, st>>>(ws.part, a2.part_stride, ks, n4,
-                                             static_cast<bf16_t*>(y_perm));
-  return hipGetLastError();
+  if (e == hipSuccess && a2.ksplit > 1) {
+    const long long n4 = (long long)R * s.d / 4;
+    const int grid = (int)std::min<long long>((n4 + 255) / 256, 4096);
+    splitk_reduce_kernel<<<grid, 256, 0, st>>>(ws.part, a2.part_stride, ks, n4,
+                                               static_cast<bf16_t*>(y_perm));
+    e = hipGetLastError();
+  }
+  phase_mark(MOE_PHASE_FC2, 1, st);
+  return e;
 }
 
 // The FFN with the combine in FC2's epilogue: y = 0, then FC1 as above, then

@@ -261,10 +261,11 @@ schedule_tiles_kernel(const int32_t* __restrict__ offsets, int E, int bm1, int n
     s2[g] += a2;
     __syncthreads();
   }
-  // inclusive -> exclusive, plus the total at index E
-  if (g <= E) {
-    tiles1[g] = (g == 0) ? 0 : s1[g - 1];
-    if (tiles2) tiles2[g] = (g == 0) ? 0 : s2[g - 1];
+  // inclusive -> exclusive, plus the total at index E (E == 1024 puts that
+  // entry one past the last thread, so the loop gives it to thread 0)
+  for (int i = g; i <= E; i += 1024) {
+    tiles1[i] = (i == 0) ? 0 : s1[i - 1];
+    if (tiles2) tiles2[i] = (i == 0) ? 0 : s2[i - 1];
   }
 }
 }  // namespace

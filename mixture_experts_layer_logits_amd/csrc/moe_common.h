@@ -43,6 +43,21 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return
 __device__ __forceinline__ float silu_fast(float g) { return g / (1.0f + __expf(-g)); }
 __device__ __forceinline__ float silu_precise(float g) { return g / (1.0f + expf(-g)); }
 
+// Events the calling thread asked to have recorded around each MOE_PHASE_*
+// (moe_set_phase_events): ev[2 p] before phase p's kernels, ev[2 p + 1]
+// after them.
+struct PhaseEvents {
+  void* const* ev;
+  int n;
+};
+extern thread_local PhaseEvents g_phase_events;
+
+inline void phase_mark(int phase, int end, hipStream_t st) {
+  const int i = 2 * phase + end;
+  if (i < g_phase_events.n && g_phase_events.ev[i])
+    (void)hipEventRecord(static_cast<hipEvent_t>(g_phase_events.ev[i]), st);
+}
+
 // ---------------------------------------------------------------------------
 // Launchers implemented in the .hip files.  Each returns hipSuccess or the
 // launch error.  Shapes were validated by the API layer.

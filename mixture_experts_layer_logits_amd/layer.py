@@ -51,7 +51,16 @@ class MoELayer:
 
     # ------------------------------------------------------------------
     def route(self, inp, stream=None):
+        """Router scores from x and w_router, or, when inp holds "logits"
+        (fp32 [T, E]), top-k and gates from those given scores."""
         b = self.buf
+        given = inp.get("logits")
+        if given is not None:
+            b["logits"].copy_(given)
+            L.moe_route_topk(self.shape, None, None, None, b["logits"],
+                             inp.get("score_bias"), b["topk_idx"], b["topk_w"],
+                             self.ws, self.ws_bytes, stream)
+            return
         L.moe_route_topk(self.shape, inp["x"], inp["w_router"],
                          inp.get("router_bias"), b["logits"],
                          inp.get("score_bias"), b["topk_idx"], b["topk_w"],

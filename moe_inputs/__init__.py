@@ -211,6 +211,37 @@ def round_robin_topk(T: int, E: int, k: int) -> torch.Tensor:
     return ((t * k + j) % E).to(torch.int32)
 
 
+def weighted_round_robin_topk(T: int, E: int, k: int, weights) -> torch.Tensor:
+    """Deliberately imbalanced round-robin routing: a cyclic schedule lists,
+    in round r = 0, 1, ..., every expert e with weights[e] > r in ascending
+    order; token t takes the k entries of the schedule from position t*k on
+    (cyclically).  Expert e then appears weights[e] times per cycle, so its
+    row count is weights[e] * T*k / len(schedule) when the cycle divides
+    T*k; experts of weight 0 get no rows.  Raises when some window of k
+    consecutive entries repeats an expert (the k picks must be distinct)."""
+    w = [int(v) for v in weights]
+    assert len(w) == E and min(w) >= 0
+    sched = [e for r in range(max(w)) for e in range(E) if w[e] > r]
+    L = len(sched)
+    for p in range(L):
+        win = [sched[(p + j) % L] for j in range(k)]
+        if len(set(win)) != k:
+            raise ValueError("the weighted schedule repeats an expert within k entries")
+    pos = (torch.arange(T, dtype=torch.int64).unsqueeze(1) * k +
+           torch.arange(k, dtype=torch.int64).unsqueeze(0)) % L
+    return torch.as_tensor(sched, dtype=torch.int32)[pos]
+
+
+def planted_logits(topk_idx: torch.Tensor, E: int, seed: int) -> torch.Tensor:
+    """fp32 router scores whose k best entries per token are topk_idx, in
+    that order: background N(0, 0.1^2), pick j set to 8 - j/2."""
+    T, k = topk_idx.shape
+    t = normal((T, E), 0.1, torch.float32, "cpu", child_seed(seed, "logits"))
+    vals = 8.0 - 0.5 * torch.arange(k, dtype=torch.float32)
+    t.scatter_(1, topk_idx.long(), vals.expand(T, k).contiguous())
+    return t
+
+
 def random_topk(T: int, E: int, k: int, seed: int, weights=None) -> torch.Tensor:
     """T rows of k distinct experts in [0, E), drawn without replacement with
     per-expert selection weights (uniform when None; a skewed vector leaves

@@ -53,14 +53,6 @@ def prec_of(cfg):
     return "f32" if cfg.dtype == 0 else "bf16"
 
 
-def oracle_route_from(cfg, inp, logits_gpu):
-    """The oracle's routing from the GPU's fp32 router scores."""
-    return O.route(np64(logits_gpu), cfg.k, cfg.score, cfg.renorm,
-                   cfg.n_groups, cfg.topk_groups,
-                   None if inp.get("score_bias") is None else np64(inp["score_bias"]),
-                   prec_of(cfg))
-
-
 def sample_tokens(T, n):
     if T <= n:
         return np.arange(T)
@@ -128,6 +120,17 @@ def routing_keys(cfg, logits, score_bias):
     return key, gs
 
 
+def key_tolerance(cfg, tol):
+    """How far a selection key can move when the router scores move by tol:
+    softmax keys are the scores themselves; a sigmoid score moves by at most
+    tol / 4 (the slope of the sigmoid) plus its fp32 rounding (half an ulp
+    below 1, on each side), and the biased key s + bias by one more fp32
+    rounding (an ulp below 2)."""
+    if cfg.score == O.SCORE_SOFTMAX:
+        return tol
+    return tol / 4 + 2.0 ** -24 + 2.0 ** -23
+
+
 def ambiguous_tokens(cfg, logits, score_bias, tol, idx):
     """Tokens whose routing could change if the scores moved by tol, judged
     on the oracle's own selection idx: two consecutive picks, or the last
@@ -135,7 +138,7 @@ def ambiguous_tokens(cfg, logits, score_bias, tol, idx):
     the bound (or, with a group limit, the kept and dropped groups are).
     Decided by the oracle alone."""
     key, gs = routing_keys(cfg, logits, score_bias)
-    ktol = tol if cfg.score == O.SCORE_SOFTMAX else tol / 4 + 2.0 ** -24
+    ktol = key_tolerance(cfg, tol)
     T, E = key.shape
     idx = np.asarray(idx, dtype=np.int64)
     sel = np.take_along_axis(key, idx, axis=1)
@@ -155,36 +158,119 @@ def ambiguous_tokens(cfg, logits, score_bias, tol, idx):
     return amb
 
 
-def check_maps_valid(out, idx, E):
-    """Properties every correct permutation has, checked on GPU outputs that
-    may follow a (valid) routing different from the oracle's."""
+def check_maps_valid(out, idx, w, E, x=None):
+    """Properties every correct permutation of the routing (idx, w) has,
+    checked on GPU outputs whether or not that routing equals the oracle's:
+    offsets are the prefix sums of the expert counts; row_token and
+    token_row are inverse maps; slot (t, j) lands inside the segment of
+    expert idx[t, j]; rows of a segment are in ascending token order; the
+    row's gate is the slot's gate bit for bit; x_perm rows are x's rows."""
     idx = np.asarray(idx, dtype=np.int64)
+    w = np.asarray(w, dtype=np.float32)
     T, k = idx.shape
     offs = out["expert_offsets"].cpu().numpy().astype(np.int64)
     counts = np.bincount(idx.reshape(-1), minlength=E)
-    assert np.array_equal(offs, np.concatenate([[0], np.cumsum(counts)]))
-    rt = out["row_token"].cpu().numpy()
-    tr = out["token_row"].cpu().numpy()
-    assert np.array_equal(rt[tr.reshape(-1)], np.repeat(np.arange(T), k))
+    assert np.array_equal(offs, np.concatenate([[0], np.cumsum(counts)])), "offsets"
+    rt = out["row_token"].cpu().numpy().astype(np.int64)
+    tr = out["token_row"].cpu().numpy().astype(np.int64)
+    rg = out["row_gate"].cpu().numpy()
+    R = T * k
+    assert np.all((tr >= 0) & (tr < R)), "token_row out of range"
+    assert np.array_equal(rt[tr.reshape(-1)], np.repeat(np.arange(T), k)), "row_token o token_row"
+    assert np.array_equal(np.sort(tr.reshape(-1)), np.arange(R)), "token_row is not a bijection"
+    assert np.all((offs[idx] <= tr) & (tr < offs[idx + 1])), "slot outside its expert's segment"
+    assert np.array_equal(rg[tr].view(np.uint32), w.view(np.uint32)), "row_gate != topk_w"
     for e in range(E):
         seg = rt[offs[e]:offs[e + 1]]
-        assert np.all(np.diff(seg) > 0)
-        assert np.all((idx[seg] == e).any(axis=1))
+        assert np.all(np.diff(seg) > 0), f"expert {e}: rows not in ascending token order"
+    if x is not None and out.get("x_perm") is not None and R > 0:
+        import torch as _t
+        rows = _t.as_tensor(rt, device=out["x_perm"].device)
+        assert _t.equal(out["x_perm"], x[rows]), "x_perm rows are not x's rows"
 
 
-def route_and_check(cfg, inp, out):
-    """Oracle routing from its own scores; returns (idx, w, ambiguous, same)."""
+def check_routing_valid(cfg, key, gs, ktol, ref_idx, gidx, gw):
+    """Validity of a GPU selection gidx [T, k] (gates gw) on every token,
+    judged by the oracle's own keys (key [T, E], group scores gs or None)
+    within the score bound ktol: k distinct experts; with a group limit, at
+    most topk_groups groups, each scoring within the bound of the oracle's
+    last kept group; inside the groups of its picks, no unpicked expert
+    beats the weakest pick by more than the bound, and (without a group
+    limit) no pick falls below the oracle's k-th key by more than the bound;
+    picks listed in descending key order up to the bound; renormalised gates
+    positive and summing to 1 within fp32 rounding."""
+    T, E = key.shape
+    k = cfg.k
+    gidx = np.asarray(gidx, dtype=np.int64)
+    assert gidx.shape == (T, k)
+    assert np.all((gidx >= 0) & (gidx < E)), "expert index out of range"
+    srt = np.sort(gidx, axis=1)
+    assert np.all(np.diff(srt, axis=1) > 0) if k > 1 else True, "repeated expert in a token"
+    sel = np.take_along_axis(key, gidx, axis=1)
+    if k > 1:
+        assert np.all(sel[:, :-1] >= sel[:, 1:] - 2 * ktol), "picks not in descending key order"
+    allowed = np.ones((T, E), dtype=bool)
+    limited = gs is not None and cfg.topk_groups < cfg.n_groups
+    if limited:
+        G = E // cfg.n_groups
+        grp = gidx // G
+        kept = np.zeros((T, cfg.n_groups), dtype=bool)
+        np.put_along_axis(kept, grp, True, axis=1)
+        assert np.all(kept.sum(axis=1) <= cfg.topk_groups), "picks span too many groups"
+        g_sorted = -np.sort(-gs, axis=1)
+        last_kept = g_sorted[:, cfg.topk_groups - 1]
+        gsel = np.take_along_axis(gs, grp, axis=1)
+        assert np.all(gsel >= last_kept[:, None] - 4 * ktol), "a pick's group is not among the best"
+        allowed = np.repeat(kept, G, axis=1)
+    else:
+        ref_kth = np.take_along_axis(key, np.asarray(ref_idx, dtype=np.int64)[:, -1:], axis=1)[:, 0]
+        assert np.all(sel.min(axis=1) >= ref_kth - 2 * ktol), "a pick lies below the k-th key"
+    rest = np.where(allowed, key, -np.inf)
+    np.put_along_axis(rest, gidx, -np.inf, axis=1)
+    assert np.all(rest.max(axis=1) <= sel.min(axis=1) + 2 * ktol), "an unpicked expert beats a pick"
+    gw = np.asarray(gw, dtype=np.float64)
+    assert np.all(gw > 0), "non-positive gate"
+    if cfg.renorm:
+        assert np.all(np.abs(gw.sum(axis=1) - 1.0) <= 2.0 ** -22 * k), "gates do not sum to 1"
+
+
+def route_and_check(cfg, inp, out, max_ambiguous_frac=0.05):
+    """The oracle routes from its own fp64 router scores; the GPU's routing
+    is then checked against it.
+
+    The GPU's fp32 scores differ from the exact ones by at most
+    err = max |l_gpu - l_oracle|, which must lie within the a-priori bound
+    logit_tolerance.  A token is ambiguous when the oracle's own keys leave a
+    gap of less than 2 err (plus an fp32 rounding) somewhere in its
+    selection: only there may a correct fp32 selection differ.  Unambiguous
+    tokens must match the oracle bit for bit (indices) and to fp32 rounding
+    (gates); every token, ambiguous or not, must hold a valid selection
+    (check_routing_valid).  Returns (idx, w, ambiguous, same)."""
     ref_l = O.router_logits(inp["x"], inp["w_router"], inp.get("router_bias"), "f32")
     assert_close("logits", out["logits"], ref_l, "f32")
+    gl = np64(out["logits"])
+    err = float(np.abs(gl - ref_l).max()) if ref_l.size else 0.0
+    bound = logit_tolerance(cfg.d, ref_l)
+    assert err <= bound, f"router scores off by {err:.3e} > bound {bound:.3e}"
+    tol = err + 2.0 ** -24 * float(np.abs(ref_l).max(initial=0.0))
     sb = inp.get("score_bias")
+    sb = None if sb is None else np64(sb)
     idx, w = O.route(ref_l, cfg.k, cfg.score, cfg.renorm, cfg.n_groups, cfg.topk_groups,
-                     None if sb is None else np64(sb), prec_of(cfg))
-    amb = ambiguous_tokens(cfg, ref_l, None if sb is None else np64(sb),
-                           logit_tolerance(cfg.d, ref_l), idx)
+                     sb, prec_of(cfg))
+    amb = ambiguous_tokens(cfg, ref_l, sb, tol, idx)
     gidx = out["topk_idx"].cpu().numpy()
+    gw = out["topk_w"].cpu().numpy()
     ok = ~amb
     assert_equal_int("topk_idx[unambiguous]", gidx[ok], idx[ok])
-    assert_close("topk_w[unambiguous]", out["topk_w"][torch.as_tensor(ok).cuda()], w[ok], "f32")
+    assert_close("topk_w[unambiguous]", gw[ok], w[ok], "f32")
+    key, gs = routing_keys(cfg, ref_l, sb)
+    ktol = key_tolerance(cfg, tol)
+    check_routing_valid(cfg, key, gs, ktol, idx, gidx, gw)
     same = bool(np.array_equal(gidx, idx))
-    print(f"  ambiguous tokens {int(amb.sum())} of {cfg.T}; routing identical: {same}", flush=True)
+    n_amb = int(amb.sum())
+    print(f"  router score error {err:.2e} (bound {bound:.2e}); ambiguous tokens {n_amb} of "
+          f"{cfg.T}; GPU routing differs on {int((gidx != idx).any(axis=1).sum())}; "
+          f"identical: {same}", flush=True)
+    assert n_amb <= max_ambiguous_frac * max(cfg.T, 1) + 2, \
+        f"{n_amb} ambiguous tokens: the check would cover too little"
     return idx, w, amb, same

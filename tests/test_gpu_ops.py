@@ -177,6 +177,9 @@ FFN_CASES = [
     # N = 384 and d = 256 leave half of the wide tail tiles past N
     ("mfma_tail_classes_splitk", None, 256, None, 1, 384, 0, 1, TAIL_COUNTS),
     ("mfma_tail_classes_shared", None, 512, None, 1, 256, 128, 1, TAIL_COUNTS),
+    # the largest expert count: the tile schedule's total sits at index 1024
+    ("mfma_e1024_t300", 300, 256, 1024, 4, 256, 0, 1, None),
+    ("generic_e1024_t300", 300, 96, 1024, 4, 64, 0, 1, None),
 ]
 
 
@@ -374,6 +377,9 @@ BWD_CASES = [
     ("dma_shared_wgrad_bf16_t300", 300, 256, 16, 4, 256, 1, 1, 1, False, 512, 1),
     ("mfma_skewed_wgrad_bf16_t400", 400, 128, 16, 4, 128, 1, 0, 1, True, 0, 1),
     ("generic_wgrad_bf16_t77", 77, 200, 6, 2, 96, 1, 0, 0, False, 40, 1),
+    # 1024 experts (the largest count): direct-to-LDS and MFMA kernels
+    ("dma_e1024_t300", 300, 256, 1024, 4, 256, 1, 0, 1, False),
+    ("mfma_e1024_t300", 300, 128, 1024, 4, 128, 1, 0, 1, True),
 ]
 
 
@@ -429,11 +435,13 @@ def test_ffn_backward_full_size_sampled(name):
     dy = np64(g["dy"][torch.as_tensor(toks).cuda()])
 
     def dY_rows(rows):
-        """dY_perm for permuted rows: w[t, j] dy[t], rounded to bf16."""
+        """dY_perm for permuted rows, from the oracle's dispatch gradient on
+        just those rows (row i of the result is routed row rows[i])."""
         t = rt[rows]
         j = np.argmax(tr[t] == rows[:, None], axis=1)
         dyt = np64(g["dy"][torch.as_tensor(t).cuda()])
-        return O.round_bf16(w[t, j][:, None] * dyt)
+        n = len(rows)
+        return O.dispatch_grad(dyt, np.arange(n)[:, None], w[t, j][:, None], n, "bf16")
 
     # d_gate and d_logits on sampled tokens
     rows = tr[toks]

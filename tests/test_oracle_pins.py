@@ -48,9 +48,28 @@ def test_round_bf16_ties_to_even_and_fixed_points():
     assert np.array_equal(O.round_bf16(vals), vals)
 
 
-def test_round_f32_matches_numpy_cast():
-    a = np.random.default_rng(2).standard_normal(1000) * 1e3
-    assert np.array_equal(O.round_f32(a), a.astype(np.float32).astype(float))
+def test_round_f32_hand_worked_ties_and_subnormals():
+    """fp32 keeps 24 significant bits: the spacing above 1 is 2^-23 and the
+    smallest subnormal is 2^-149.  Values worked by hand, not by a cast."""
+    # halfway between 1 and 1 + 2^-23: the even neighbour is 1
+    assert O.round_f32(1.0 + 2.0 ** -24) == 1.0
+    # halfway between 1 + 2^-23 (odd) and 1 + 2^-22 (even)
+    assert O.round_f32(1.0 + 3 * 2.0 ** -24) == 1.0 + 2.0 ** -22
+    # just above halfway rounds up
+    assert O.round_f32(1.0 + 2.0 ** -24 + 2.0 ** -40) == 1.0 + 2.0 ** -23
+    # just below halfway rounds down, also for negative values
+    assert O.round_f32(-(1.0 + 2.0 ** -24 - 2.0 ** -40)) == -1.0
+    # between 2 and 4 the spacing doubles: 3 + 2^-23 is halfway, even is 3
+    assert O.round_f32(3.0 + 2.0 ** -23) == 3.0
+    # subnormals: 1.5 * 2^-149 is halfway between 2^-149 (odd) and 2^-148
+    assert O.round_f32(1.5 * 2.0 ** -149) == 2.0 ** -148
+    # 2^-150 is halfway between 0 and 2^-149: the even neighbour is 0
+    assert O.round_f32(2.0 ** -150) == 0.0
+    # 1/3 in fp32 is 11184811 * 2^-25 (0x3eaaaaab)
+    assert O.round_f32(1.0 / 3.0) == 11184811 * 2.0 ** -25
+    # exactly representable values stay
+    vals = np.array([0.5, -1024.75, 2.0 ** -126, 16777215.0])
+    assert np.array_equal(O.round_f32(vals), vals)
 
 
 # --------------------------------------------------------------------------
@@ -495,6 +514,29 @@ def test_zero_row_experts_have_exactly_zero_weight_gradients():
 # --------------------------------------------------------------------------
 # the workloads' input recipe
 # --------------------------------------------------------------------------
+def test_dispatch_grad_rounds_each_scaled_row_to_bf16_once():
+    """dY_perm[token_row[t, j]] = bf16(w[t, j] dy[t]), worked by hand: the
+    product is formed exactly and rounded once, to nearest, ties to even.
+    bf16 keeps 8 significant bits: the spacing is 2^-7 in [1, 2), 2^-6 in
+    [2, 4), 2^-8 in [0.5, 1) and 2^-9 in [0.25, 0.5)."""
+    w13 = 11184811 * 2.0 ** -25                   # fp32(1/3) = 0.3333333432...
+    dy = np.array([[1.0, 3.0, 1.5, -3.0, 2.0, -1.0]])
+    w = np.array([[1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, w13]])
+    tr = np.array([[2, 0, 1]])                    # slot j goes to row tr[j]
+    dY = O.dispatch_grad(dy, tr, w, 3, "bf16")
+    # w = 1 + 2^-8: 1 + 2^-8 and 2 + 2^-7 (and their negatives) are ties that
+    # go to the even neighbour; 3 + 0.75 * 2^-6 and 1.5 + 0.75 * 2^-7 round up
+    assert dY[2].tolist() == [1.0, 3.015625, 1.5078125, -3.015625, 2.0, -1.0]
+    # w = 1 + 3 * 2^-8: 1 + 1.5 * 2^-7 and 2 + 1.5 * 2^-6 are ties whose even
+    # neighbour lies above; 3 + 2.25 * 2^-6 and 1.5 + 2.25 * 2^-7 round down
+    assert dY[0].tolist() == [1.015625, 3.03125, 1.515625, -3.03125, 2.03125, -1.015625]
+    # w = fp32(1/3): 0.3333333433 -> 171 * 2^-9; 1.0000000298 -> 1;
+    # 0.5000000149 -> 0.5; 0.6666666865 -> 171 * 2^-8
+    assert dY[1].tolist() == [0.333984375, 1.0, 0.5, -1.0, 0.66796875, -0.333984375]
+    # unrounded (the fp64 variant) the products differ from these
+    assert O.dispatch_grad(dy, tr, w, 3, "f64")[1][2] != 0.5
+
+
 def test_inputs_are_seeded_and_shaped():
     cfg = CONFIGS["tiny_fp32"]
     a = make_inputs(cfg)

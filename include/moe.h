@@ -161,6 +161,21 @@ int moe_permute(const moe_shape* shape, const void* x, const int32_t* topk_idx,
                 int32_t* row_token, int32_t* token_row, float* row_gate,
                 void* x_perm, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_permute without a workspace, for callers that cannot allocate (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, outputs and results as moe_permute, bit for
+ * bit; its scratch (per-(expert, block of 256 tokens) counts and first rows)
+ * lives in a fixed 2 MiB device array of the library instead, which each GPU
+ * the library runs on holds until the process ends.  Limit:
+ * E * ceil(T / 256) <= 262144 (e.g. T <= 65536 at E = 1024); larger shapes
+ * return MOE_ERR_WORKSPACE before any launch.  Calls on one GPU share that
+ * array: calls that overlap on one GPU (concurrent streams, threads) race and
+ * give undefined maps.  Allocates nothing (no hipMalloc, no hipFree). */
+int moe_permute_noalloc(const moe_shape* shape, const void* x, const int32_t* topk_idx,
+                        const float* topk_w, int32_t* expert_offsets,
+                        int32_t* row_token, int32_t* token_row, float* row_gate,
+                        void* x_perm, void* stream);
+
 /* Grouped SwiGLU expert FFN over ragged, expert-contiguous row ranges, in one
  * launch per GEMM (Primus blog, MegaMoE section: FC1 (gate/up) -> SwiGLU ->
  * FC2 (down)), plus the shared expert over all T tokens when F_shared > 0

@@ -8,7 +8,7 @@ from ._lib import (MoeError, MoeShape, load, make_shape, moe_ffn_backward,  # no
                    moe_grouped_ffn, moe_grouped_ffn_combine, moe_grouped_ffn_mxfp8,
                    moe_grouped_ffn_mxfp8_combine,
                    moe_ffn_backward_mxfp8, moe_mx_quantize, moe_mx_quantize_t,
-                   moe_permute, moe_route_topk, moe_set_phase_events,
+                   moe_permute, moe_permute_noalloc, moe_route_topk, moe_set_phase_events,
                    moe_unpermute_combine,
                    moe_workspace_size, status_string)
 from .layer import MoELayer  # noqa: F401

@@ -35,7 +35,7 @@ EXPORTED = ("moe_workspace_size", "moe_route_topk", "moe_permute",
             "moe_grouped_ffn", "moe_unpermute_combine", "moe_ffn_backward",
             "moe_status_string", "moe_mx_quantize", "moe_grouped_ffn_mxfp8",
             "moe_grouped_ffn_combine", "moe_mx_quantize_t", "moe_ffn_backward_mxfp8",
-            "moe_grouped_ffn_mxfp8_combine", "moe_set_phase_events")
+            "moe_grouped_ffn_mxfp8_combine", "moe_set_phase_events", "moe_permute_noalloc")
 (MOE_PHASE_FC1, MOE_PHASE_FC2, MOE_PHASE_BWD_DISPATCH, MOE_PHASE_BWD_DH,
  MOE_PHASE_BWD_DW_DOWN, MOE_PHASE_BWD_DX, MOE_PHASE_BWD_DW_GATE_UP,
  MOE_PHASE_BWD_GATHER, MOE_PHASE_COUNT) = range(9)
@@ -73,6 +73,7 @@ def load() -> ctypes.CDLL:
     lib.moe_workspace_size.argtypes = [sp, ctypes.c_int, ctypes.POINTER(sz)]
     lib.moe_route_topk.argtypes = [sp] + [vp] * 7 + [vp, sz, vp]
     lib.moe_permute.argtypes = [sp] + [vp] * 8 + [vp, sz, vp]
+    lib.moe_permute_noalloc.argtypes = [sp] + [vp] * 8 + [vp]
     lib.moe_grouped_ffn.argtypes = [sp] + [vp] * 13 + [vp, sz, vp]
     lib.moe_unpermute_combine.argtypes = [sp] + [vp] * 5 + [vp, sz, vp]
     lib.moe_grouped_ffn_combine.argtypes = [sp] + [vp] * 12 + [vp, sz, vp]
@@ -176,6 +177,15 @@ def moe_permute(shape, x, topk_idx, topk_w, expert_offsets, row_token,
         _p(expert_offsets, _I32), _p(row_token, _I32), _p(token_row, _I32),
         _p(row_gate, _F32), _p(x_perm, _act(shape)), _p(ws), ws_bytes, _stream(stream))
     return _check(st, "moe_permute") if check else st
+
+
+def moe_permute_noalloc(shape, x, topk_idx, topk_w, expert_offsets, row_token,
+                        token_row, row_gate, x_perm, stream=None, check=True):
+    st = load().moe_permute_noalloc(
+        ctypes.byref(shape), _p(x, _act(shape)), _p(topk_idx, _I32), _p(topk_w, _F32),
+        _p(expert_offsets, _I32), _p(row_token, _I32), _p(token_row, _I32),
+        _p(row_gate, _F32), _p(x_perm, _act(shape)), _stream(stream))
+    return _check(st, "moe_permute_noalloc") if check else st
 
 
 def moe_grouped_ffn(shape, x_perm, row_token, expert_offsets, w_gate, w_up,

@@ -200,10 +200,11 @@ int moe_route_topk(const moe_shape* shape, const void* x, const void* w_router,
   return hip_status(moe::launch_topk(s, logits, score_bias, topk_idx, topk_w, hs));
 }
 
-int moe_permute(const moe_shape* shape, const void* x, const int32_t* topk_idx,
-                const float* topk_w, int32_t* expert_offsets, int32_t* row_token,
-                int32_t* token_row, float* row_gate, void* x_perm, void* ws, size_t ws_bytes,
-                void* stream) {
+// moe_permute's argument checks (the workspace aside).
+static int check_permute_args(const moe_shape* shape, const void* x, const int32_t* topk_idx,
+                              const float* topk_w, int32_t* expert_offsets,
+                              int32_t* row_token, int32_t* token_row, float* row_gate,
+                              void* x_perm) {
   int st = check_shape(shape);
   if (st != MOE_OK) return st;
   const moe_shape& s = *shape;
@@ -216,6 +217,33 @@ int moe_permute(const moe_shape* shape, const void* x, const int32_t* topk_idx,
       !ok_buf(row_token, R * 4) || !ok_buf(token_row, R * 4) || !ok_buf(row_gate, R * 4) ||
       (rows && !ok_buf(x_perm, R * s.d * es)))
     return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+int moe_permute_noalloc(const moe_shape* shape, const void* x, const int32_t* topk_idx,
+                        const float* topk_w, int32_t* expert_offsets, int32_t* row_token,
+                        int32_t* token_row, float* row_gate, void* x_perm, void* stream) {
+  int st = check_permute_args(shape, x, topk_idx, topk_w, expert_offsets, row_token,
+                              token_row, row_gate, x_perm);
+  if (st != MOE_OK) return st;
+  const moe_shape& s = *shape;
+  if ((long long)s.E * moe::permute_nblk(s) > moe::PERMUTE_NOALLOC_MAX_ENTRIES)
+    return MOE_ERR_WORKSPACE;
+  moe::PermuteWs pw;
+  if ((st = hip_status(moe::permute_noalloc_ws(pw))) != MOE_OK) return st;
+  return hip_status(moe::launch_permute(s, x, topk_idx, topk_w, expert_offsets, row_token,
+                                        token_row, row_gate, x_perm, pw,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int moe_permute(const moe_shape* shape, const void* x, const int32_t* topk_idx,
+                const float* topk_w, int32_t* expert_offsets, int32_t* row_token,
+                int32_t* token_row, float* row_gate, void* x_perm, void* ws, size_t ws_bytes,
+                void* stream) {
+  int st = check_permute_args(shape, x, topk_idx, topk_w, expert_offsets, row_token,
+                              token_row, row_gate, x_perm);
+  if (st != MOE_OK) return st;
+  const moe_shape& s = *shape;
   if ((st = check_ws(s, MOE_OP_PERMUTE, ws, ws_bytes)) != MOE_OK) return st;
   Carver c{static_cast<char*>(ws)};
   const size_t n = (size_t)s.E * moe::permute_nblk(s);

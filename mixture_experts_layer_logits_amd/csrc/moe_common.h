@@ -75,6 +75,11 @@ struct PermuteWs {
   int32_t* blk_base;  // [E * nblk]
 };
 int permute_nblk(const moe_shape& s);
+// The fixed scratch of moe_permute_noalloc: at most this many (expert,
+// block) entries, E * permute_nblk(s).
+constexpr long long PERMUTE_NOALLOC_MAX_ENTRIES = 1LL << 18;
+// Points ws at the current device's fixed scratch (looked up on first use).
+hipError_t permute_noalloc_ws(PermuteWs& ws);
 hipError_t launch_permute(const moe_shape& s, const void* x, const int32_t* topk_idx,
                           const float* topk_w, int32_t* offsets, int32_t* row_token,
                           int32_t* token_row, float* row_gate, void* x_perm,

@@ -23,6 +23,8 @@
 //              destination rows (full-row, 16-byte coalesced stores).  Without
 //              an x_perm buffer this step is skipped: the grouped FFN can read
 //              each row from x through row_token instead.
+#include <mutex>
+
 #include "gemm_tiles.h"
 
 namespace moe {
@@ -227,6 +229,41 @@ hipError_t launch_permute(const moe_shape& s, const void* x, const int32_t* topk
                                                       static_cast<uint8_t*>(x_perm));
   }
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// A fixed scratch area for callers that cannot allocate (moe_permute_noalloc):
+// the per-(expert, block) counts and first rows, 2 x 2^18 int32 (2 MiB).
+// Each GPU holds its own copy for the life of the process; its device
+// address is looked up once per device with that device current, and only
+// that address is ever handed to kernels.  Every entry the kernels read is
+// written earlier in the same call (counts by the count kernel, bases by the
+// scan), so nothing needs clearing; calls that overlap on one GPU race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) int32_t scratch[2 * PERMUTE_NOALLOC_MAX_ENTRIES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t permute_noalloc_ws(PermuteWs& ws) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  ws.blk_cnt = g_scratch_ptr[dev];
+  ws.blk_base = g_scratch_ptr[dev] + PERMUTE_NOALLOC_MAX_ENTRIES;
+  return hipSuccess;
 }
 
 }  // namespace moe

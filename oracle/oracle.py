@@ -346,6 +346,21 @@ def mx_round(a, block=MX_BLOCK):
     return mx_dequantize(q, s, block)
 
 
+def mx_round_rows(a, block=MX_BLOCK):
+    """a [n, c] (one expert's rows) quantized to MXFP8 along its row axis:
+    blocks of `block` consecutive rows starting at the expert's first row,
+    the last block completed with zero rows (the Primus blog's low-precision
+    section pads permuted tokens to the quantization block boundary when the
+    contraction runs over tokens).  Zero rows change no block maximum and
+    contribute nothing to a sum over rows; they are dropped again."""
+    a = as64(a)
+    n = a.shape[0]
+    npad = -(-n // block) * block
+    p = np.zeros((npad,) + a.shape[1:], dtype=F64)
+    p[:n] = a
+    return mx_round(p.T, block).T[:n]
+
+
 def swiglu_ffn_mxfp8(rows, wg, wu, wd):
     """One expert with MXFP8 operands: the rows and the three weights are
     quantized along their contraction dimension (d for FC1, F for FC2), and
@@ -486,7 +501,8 @@ def router_backward(d_gate, topk_idx, topk_w, logits, E, score=SCORE_SOFTMAX,
     return out_f32(prec)(dl)
 
 
-def expert_backward(dYe, xe, gu_e, wg, wu, wd, prec="bf16", mxfp8=False):
+def expert_backward(dYe, xe, gu_e, wg, wu, wd, prec="bf16", mxfp8=False,
+                    mx_wgrad=False):
     """One expert's backward on its rows (dYe [n, d], xe [n, d],
     gu_e [n, 2F]); wg, wu [F, d], wd [d, F].
 
@@ -500,7 +516,13 @@ def expert_backward(dYe, xe, gu_e, wg, wu, wd, prec="bf16", mxfp8=False):
     dY and W_d along d for dh; [dg | du] and [W_g; W_u] along F for dX
     (blocks never straddle g and u: F is a multiple of 32).  dh itself is
     not materialised (exact here); dg, du, h and dX are rounded as above.
-    The weight gradients keep the unquantised operands.
+    The weight gradients keep the unquantised operands unless mx_wgrad.
+
+    mx_wgrad: the two weight-gradient GEMMs take MXFP8 operands too, each
+    quantised along its contraction dimension, the expert's rows
+    (mx_round_rows: 32-row blocks from the expert's first row, the last one
+    padded with zero rows): dY and h for dW_down, [dg | du] and x for
+    dW_gate | dW_up.  Their sums are exact on the dequantised values.
     """
     rnd = rounder(prec)
     gu_e = as64(gu_e)
@@ -523,6 +545,11 @@ def expert_backward(dYe, xe, gu_e, wg, wu, wd, prec="bf16", mxfp8=False):
         dX = rnd(mx_round(dgu) @ mx_round(wgu.T).T)
     else:
         dX = rnd(dgt @ as64(wg) + dut @ as64(wu))
+    if mx_wgrad:
+        xq = mx_round_rows(xe)
+        return dict(dw_down=mx_round_rows(dYe).T @ mx_round_rows(h),
+                    dw_gate=mx_round_rows(dgt).T @ xq, dw_up=mx_round_rows(dut).T @ xq,
+                    dX=dX, dg=dgt, du=dut)
     return dict(dw_down=dYe.T @ h, dw_gate=dgt.T @ xe, dw_up=dut.T @ xe,
                 dX=dX, dg=dgt, du=dut)
 
@@ -550,7 +577,7 @@ def gate_grad(dy, y_perm, token_row):
 
 def ffn_backward(dy, x_perm, gu_save, y_perm, offsets, token_row, topk_idx,
                  topk_w, logits, w_gate, w_up, w_down, score=SCORE_SOFTMAX,
-                 renorm=1, prec="bf16", shared=None, mxfp8=False):
+                 renorm=1, prec="bf16", shared=None, mxfp8=False, mx_wgrad=False):
     """Backward of the layer, from the saved tensors.
 
     The backward mirrors the forward through dispatch/combine duality, with
@@ -561,6 +588,8 @@ def ffn_backward(dy, x_perm, gu_save, y_perm, offsets, token_row, topk_idx,
       d_logits from d_gate through the gate function.
     Weight gradients of experts with no rows are exactly zero.
     mxfp8: the data-gradient GEMMs on MXFP8 operands (expert_backward).
+    mx_wgrad: the weight-gradient GEMMs on MXFP8 operands quantised along
+    each expert's rows, padded per expert (expert_backward).
 
     ``shared`` (optional) = dict(x, gu, ws_gate, ws_up, ws_down) for the
     shared expert applied to every token: it adds ys[t] to y[t] with gate 1, so its
@@ -586,7 +615,7 @@ def ffn_backward(dy, x_perm, gu_save, y_perm, offsets, token_row, topk_idx,
         if b == a:
             continue
         r = expert_backward(dY[a:b], x_perm[a:b], gu[a:b], w_gate[e],
-                            w_up[e], w_down[e], prec, mxfp8)
+                            w_up[e], w_down[e], prec, mxfp8, mx_wgrad)
         dw_down[e], dw_gate[e], dw_up[e] = r["dw_down"], r["dw_gate"], r["dw_up"]
         dX[a:b] = r["dX"]
     dx = np.zeros((T, d), dtype=F64)
@@ -595,7 +624,7 @@ def ffn_backward(dy, x_perm, gu_save, y_perm, offsets, token_row, topk_idx,
     out = {}
     if shared is not None:
         rs = expert_backward(dy, shared["x"], shared["gu"], shared["ws_gate"],
-                             shared["ws_up"], shared["ws_down"], prec, mxfp8)
+                             shared["ws_up"], shared["ws_down"], prec, mxfp8, mx_wgrad)
         dx = dx + rs["dX"]
         out = dict(dws_gate=of32(rs["dw_gate"]), dws_up=of32(rs["dw_up"]),
                    dws_down=of32(rs["dw_down"]), dX_shared=rs["dX"])

@@ -802,3 +802,103 @@ def test_grouped_ffn_mxfp8_combine_by_brute_force():
                         p["token_row"], w)
     assert not np.array_equal(y, unfused)
     assert np.allclose(y, unfused, rtol=2e-2, atol=1e-3)
+
+
+def test_expert_backward_mx_weight_gradients_by_brute_force():
+    """The MXFP8 weight-gradient GEMMs on a tiny expert with Python loops:
+    every operand column quantised along the expert's 37 rows in blocks of
+    32 consecutive rows from the first one (the last block holds 5 rows: its
+    zero padding changes no block maximum), then summed over rows exactly.
+    dY and h for dW_down, dg | du and x for dW_gate | dW_up.  The MX rounding
+    is the brute-force one (table search over torch's E4M3 decoding, frexp
+    exponents); h is recomputed here from the saved g, u."""
+    import math
+    codes = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    table = [(c, float(codes[c])) for c in range(256) if np.isfinite(codes[c]) and codes[c] >= 0]
+    table += [(c, float(codes[c])) for c in range(256) if np.isfinite(codes[c]) and codes[c] < 0]
+    rng = np.random.default_rng(41)
+    n, d, F = 37, 32, 32
+    rb = O.round_bf16
+    dY = rb(rng.standard_normal((n, d)) * np.exp2(rng.integers(-4, 4, (n, 1))))
+    x = rb(rng.standard_normal((n, d)))
+    gu = rb(rng.standard_normal((n, 2 * F)))
+    wg, wu = rb(rng.standard_normal((F, d)) * 0.1), rb(rng.standard_normal((F, d)) * 0.1)
+    wd = rb(rng.standard_normal((d, F)) * 0.1)
+    r = O.expert_backward(dY, x, gu, wg, wu, wd, "bf16", mx_wgrad=True)
+    h = np.array([[float(rb(np.array(gu[t, f] / (1.0 + math.exp(-gu[t, f])) * gu[t, F + f])))
+                   for f in range(F)] for t in range(n)])
+    col = lambda a, j: _mx_round_brute(a[:, j], table)      # one column along the rows
+    qdY = [col(dY, i) for i in range(d)]
+    qh = [col(h, f) for f in range(F)]
+    qx = [col(x, i) for i in range(d)]
+    qdg = [col(r["dg"], f) for f in range(F)]
+    qdu = [col(r["du"], f) for f in range(F)]
+    dw_down = np.array([[sum(qdY[i][t] * qh[f][t] for t in range(n)) for f in range(F)]
+                        for i in range(d)])
+    dw_gate = np.array([[sum(qdg[f][t] * qx[i][t] for t in range(n)) for i in range(d)]
+                        for f in range(F)])
+    dw_up = np.array([[sum(qdu[f][t] * qx[i][t] for t in range(n)) for i in range(d)]
+                      for f in range(F)])
+    for key, want in (("dw_down", dw_down), ("dw_gate", dw_gate), ("dw_up", dw_up)):
+        assert np.allclose(r[key], want, rtol=1e-12, atol=1e-12 * np.abs(want).max()), key
+    # and they differ from the unquantised weight gradients
+    plain = O.expert_backward(dY, x, gu, wg, wu, wd, "bf16")
+    assert not np.allclose(plain["dw_down"], r["dw_down"], rtol=1e-6, atol=0)
+
+
+def test_mx_weight_gradient_blocks_start_at_each_experts_first_row():
+    """ffn_backward with MXFP8 weight gradients quantises each expert's rows
+    on their own (blocks restart at the expert's first row, the last one
+    padded): expert 1's gradients equal expert_backward on its rows alone,
+    and differ from a quantisation whose blocks run on across the previous
+    expert's rows."""
+    rng = np.random.default_rng(43)
+    T, d, E, F = 40, 32, 2, 32
+    rb = O.round_bf16
+    idx = np.array([[0, 1] if t < 24 else [1, 0] for t in range(T)])
+    w = np.full((T, 2), 0.5)
+    idx[30:, :] = [[0, 1]] * 10
+    p = O.permute(None, idx, w, E)
+    counts = np.diff(p["offsets"])
+    assert counts[0] % 32 != 0
+    R = T * 2
+    x_perm = rb(rng.standard_normal((R, d)))
+    gu = rb(rng.standard_normal((R, 2 * F)))
+    y_perm = rb(rng.standard_normal((R, d)))
+    dy = rb(rng.standard_normal((T, d)) * np.exp2(rng.integers(-4, 4, (T, 1))))
+    wg, wu = rb(rng.standard_normal((E, F, d)) * 0.1), rb(rng.standard_normal((E, F, d)) * 0.1)
+    wd = rb(rng.standard_normal((E, d, F)) * 0.1)
+    logits = rng.standard_normal((T, E))
+    out = O.ffn_backward(dy, x_perm, gu, y_perm, p["offsets"], p["token_row"], idx, w, logits,
+                         wg, wu, wd, prec="bf16", mx_wgrad=True)
+    dY = O.dispatch_grad(dy, p["token_row"], w, R, "bf16")
+    a, b = int(p["offsets"][1]), int(p["offsets"][2])
+    alone = O.expert_backward(dY[a:b], x_perm[a:b], gu[a:b], wg[1], wu[1], wd[1], "bf16",
+                              mx_wgrad=True)
+    assert np.array_equal(out["dw_gate"][1], O.round_f32(alone["dw_gate"]))
+    # blocks aligned to the start of all rows instead of expert 1's first row
+    shift = O.mx_round_rows(x_perm)[a:b]
+    assert not np.array_equal(shift, O.mx_round_rows(x_perm[a:b]))
+
+
+def test_mx_weight_gradients_exact_on_mx_representable_operands():
+    """When dY and h are exactly representable in MXFP8 along the rows
+    (block maxima 2, elements in {0, +-1/2, +-1, +-2}) dW_down is unchanged
+    by quantisation, bit for bit; dW_gate, whose dg is not, changes (with
+    g = 0, du = dh silu(0) = 0, so dW_up is zero either way)."""
+    rng = np.random.default_rng(47)
+    n, d, F = 64, 32, 32
+    vals = np.array([0.0, 0.5, -0.5, 1.0, -1.0, 2.0, -2.0])
+    dY = rng.choice(vals, (n, d))
+    dY[::32, :] = 2.0
+    x = O.round_bf16(rng.standard_normal((n, d)))
+    # g = 0 gives h = silu(0) u = 0: h exactly representable for any u
+    gu = np.concatenate([np.zeros((n, F)), O.round_bf16(rng.standard_normal((n, F)))], axis=1)
+    wg, wu = (O.round_bf16(rng.standard_normal((F, d)) * 0.1) for _ in range(2))
+    wd = O.round_bf16(rng.standard_normal((d, F)) * 0.1)
+    assert np.array_equal(O.mx_round_rows(dY), dY)
+    a = O.expert_backward(dY, x, gu, wg, wu, wd, "bf16", mx_wgrad=True)
+    b = O.expert_backward(dY, x, gu, wg, wu, wd, "bf16")
+    assert np.array_equal(a["dw_down"], b["dw_down"])
+    assert not np.array_equal(a["dw_gate"], b["dw_gate"])
+    assert not np.any(a["dw_up"]) and not np.any(b["dw_up"])

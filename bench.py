@@ -611,6 +611,42 @@ def main():
                 "weight_quantize_ms_once": round(q0.elapsed_time(q1), 4)}
             del ml
             torch.cuda.empty_cache()
+            # ... and with the weight-gradient GEMMs in MXFP8 too (operands
+            # quantised along each expert's rows, padded to the block): every
+            # GEMM of the backward on MXFP8 operands
+            ml = MoELayer(cfg.replace(wgrad_mx=1), device=dev)
+            ml.quantize_weights_t(inp)
+            for _ in range(args.warmup):
+                ml.forward(inp)
+                ml.backward_mxfp8(inp, inp["dy"])
+            nph = 2 * L.MOE_PHASE_COUNT
+            xev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 + nph)]
+                   for _ in range(args.steps)]
+            for row in xev:
+                for ev in row:
+                    ev.record(stream)
+            xarr = [(ctypes.c_void_p * nph)(*[ev.cuda_event for ev in row[2:]]) for row in xev]
+            torch.cuda.synchronize()
+            m0 = time.perf_counter()
+            for s_ in range(args.steps):
+                ml.forward(inp)
+                L.moe_set_phase_events(xarr[s_])
+                xev[s_][0].record(stream)
+                ml.backward_mxfp8(inp, inp["dy"])
+                xev[s_][1].record(stream)
+                L.moe_set_phase_events(None)
+            torch.cuda.synchronize()
+            mwall = (time.perf_counter() - m0) * 1e3 / args.steps
+            pms = lambda p_: round(float(np.mean([xev[s_][2 + 2 * p_].elapsed_time(
+                xev[s_][3 + 2 * p_]) for s_ in range(args.steps)])), 4)
+            remat["mxfp8_backward"] = {
+                "ms_per_step": round(mwall, 4), "tokens_per_s": round(cfg.T / (mwall / 1e3), 1),
+                "backward_ms": round(float(np.mean([xev[s_][0].elapsed_time(xev[s_][1])
+                                                    for s_ in range(args.steps)])), 4),
+                "dw_down_ms (token-axis quantise + GEMM)": pms(L.MOE_PHASE_BWD_DW_DOWN),
+                "dw_gate_up_ms (token-axis quantise + GEMM)": pms(L.MOE_PHASE_BWD_DW_GATE_UP)}
+            del ml
+            torch.cuda.empty_cache()
     ms_step = float(np.mean([evs[s][0].elapsed_time(evs[s][-1])
                              for s in range(args.steps)]))
     ms_wall = wall * 1e3 / args.steps

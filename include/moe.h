@@ -93,7 +93,7 @@ enum {
  * F_shared >= 0.  n_groups >= 1 divides E, n_groups <= 64,
  * 1 <= topk_groups <= n_groups, topk_groups * (E / n_groups) >= k; a group
  * limit (n_groups > 1) needs score = MOE_SCORE_SIGMOID.  renorm is 0 or 1.
- * T * k and T * max(d, F) must fit in int32. */
+ * wgrad_mx is 0 or 1.  T * k and T * max(d, F) must fit in int32. */
 typedef struct moe_shape {
   int32_t T, d, E, k, F;
   int32_t F_shared;
@@ -103,6 +103,11 @@ typedef struct moe_shape {
   int32_t dtype;
   int32_t wgrad_dtype;  /* storage of moe_ffn_backward's weight gradients:
                            MOE_DTYPE_F32 (0, the default) or MOE_DTYPE_BF16 */
+  int32_t wgrad_mx;     /* moe_ffn_backward_mxfp8 only: 0 (the default) keeps
+                           its weight-gradient GEMMs in bf16; 1 runs them on
+                           MXFP8 operands quantised along each expert's rows
+                           (its row count padded to a multiple of 128 with
+                           zero rows).  Ignored by every other call. */
 } moe_shape;
 
 /* Bytes of scratch memory `op` (MOE_OP_*) needs for `shape`.  Host-only, no

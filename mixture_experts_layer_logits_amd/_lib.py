@@ -46,7 +46,7 @@ PHASE_NAMES = ("fc1", "fc2", "bwd_dispatch", "bwd_dh", "bwd_dw_down", "bwd_dx",
 class MoeShape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("T", "d", "E", "k", "F", "F_shared", "n_groups",
-                 "topk_groups", "score", "renorm", "dtype", "wgrad_dtype")]
+                 "topk_groups", "score", "renorm", "dtype", "wgrad_dtype", "wgrad_mx")]
 
 
 class MoeError(RuntimeError):
@@ -102,7 +102,8 @@ def make_shape(cfg) -> MoeShape:
     """A moe_shape from an object with the layer's fields (e.g. MoEConfig)."""
     return MoeShape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.F, cfg.F_shared,
                     cfg.n_groups, cfg.topk_groups, cfg.score, cfg.renorm,
-                    cfg.dtype, getattr(cfg, "wgrad_dtype", MOE_DTYPE_F32))
+                    cfg.dtype, getattr(cfg, "wgrad_dtype", MOE_DTYPE_F32),
+                    getattr(cfg, "wgrad_mx", 0))
 
 
 _I32, _F32, _U8 = torch.int32, torch.float32, torch.uint8

@@ -30,6 +30,7 @@ int check_shape(const moe_shape* sp) {
   if (s.renorm != 0 && s.renorm != 1) return MOE_ERR_INVALID_ARG;
   if (s.dtype != MOE_DTYPE_F32 && s.dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
   if (s.wgrad_dtype != MOE_DTYPE_F32 && s.wgrad_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
+  if (s.wgrad_mx != 0 && s.wgrad_mx != 1) return MOE_ERR_INVALID_ARG;
   const long long R = (long long)s.T * s.k;
   const long long wide = std::max<long long>({s.d, s.F, s.F_shared, s.E, 2LL * s.F});
   if (R * wide >= (1LL << 31) || (long long)s.T * wide >= (1LL << 31)) return MOE_ERR_INVALID_ARG;
@@ -41,6 +42,16 @@ int check_shape(const moe_shape* sp) {
 bool ok_buf(const void* p, long long bytes) {
   if (bytes <= 0) return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15) == 0;
   return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15) == 0;
+}
+
+// Rows of the MXFP8 weight gradients' token-axis operands: every expert's
+// row count padded to a multiple of 128 (at most R + 127 E), and the shared
+// expert's T rows padded the same way.
+size_t mx_wgrad_rows(const moe_shape& s) {
+  const size_t R = (size_t)s.T * s.k;
+  const size_t routed = (R + 127 * (size_t)s.E + 127) / 128 * 128;
+  const size_t shared = ((size_t)s.T + 127) / 128 * 128;
+  return std::max(routed, shared);
 }
 
 size_t ws_bytes_for(const moe_shape& s, int op) {
@@ -84,6 +95,15 @@ size_t ws_bytes_for(const moe_shape& s, int op) {
         const size_t T = (size_t)s.T, Fs = (size_t)s.F_shared;
         b += align_up(T * s.d) + align_up(T * s.d / 32) + align_up(T * 2 * Fs) +
              align_up(T * 2 * Fs / 32);
+      }
+      if (s.wgrad_mx) {
+        // padded row offsets, and the two operands of one weight-gradient
+        // GEMM quantised along the padded rows (reused by the next GEMM)
+        const size_t rp = mx_wgrad_rows(s);
+        const size_t ma = std::max<size_t>({(size_t)s.d, 2 * (size_t)s.F, 2 * (size_t)s.F_shared});
+        const size_t mb = std::max<size_t>({(size_t)s.d, (size_t)s.F, (size_t)s.F_shared});
+        b += 2 * align_up((s.E + 1) * 4) + align_up(ma * rp) + align_up(ma * rp / 32) +
+             align_up(mb * rp) + align_up(mb * rp / 32);
       }
       return b;
     }
@@ -552,6 +572,11 @@ int moe_ffn_backward_mxfp8(const moe_shape* shape, const void* dy, const void* x
   const moe_shape& s = *shape;
   if (s.dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
   if (s.d % 128 != 0 || s.F % 128 != 0 || s.F_shared % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  // the MXFP8 weight gradients address their quantised operands with 32-bit offsets
+  if (s.wgrad_mx &&
+      (long long)std::max<long long>({s.d, 2LL * s.F, 2LL * s.F_shared}) *
+              (long long)mx_wgrad_rows(s) >= (1LL << 31))
+    return MOE_ERR_UNSUPPORTED;
   const long long R = (long long)s.T * s.k;
   const long long wsz = (long long)s.E * s.F * s.d;
   const long long wes = s.wgrad_dtype == MOE_DTYPE_BF16 ? 2 : 4;
@@ -593,6 +618,21 @@ int moe_ffn_backward_mxfp8(const moe_shape* shape, const void* dy, const void* x
     bw.s_dys = c.take<uint8_t>(T * s.d / 32);
     bw.s_dguq = c.take<uint8_t>(T * 2 * Fs);
     bw.s_dgus = c.take<uint8_t>(T * 2 * Fs / 32);
+  }
+  bw.poffs = bw.s_poffs = nullptr;
+  bw.wqa = bw.wsa = bw.wqb = bw.wsb = nullptr;
+  bw.wrows = 0;
+  if (s.wgrad_mx) {
+    const size_t rp = mx_wgrad_rows(s);
+    const size_t ma = std::max<size_t>({(size_t)s.d, 2 * (size_t)s.F, 2 * (size_t)s.F_shared});
+    const size_t mb = std::max<size_t>({(size_t)s.d, (size_t)s.F, (size_t)s.F_shared});
+    bw.poffs = c.take<int32_t>((s.E + 1) * 4);
+    bw.s_poffs = c.take<int32_t>((s.E + 1) * 4);
+    bw.wqa = c.take<uint8_t>(ma * rp);
+    bw.wsa = c.take<uint8_t>(ma * rp / 32);
+    bw.wqb = c.take<uint8_t>(mb * rp);
+    bw.wsb = c.take<uint8_t>(mb * rp / 32);
+    bw.wrows = (long long)rp;
   }
   moe::MxBwdWeights mw = {w_down_tq, w_down_ts, w_gu_tq, w_gu_ts,
                           ws_down_tq, ws_down_ts, ws_gu_tq, ws_gu_ts};

@@ -573,7 +573,9 @@ bwd_generic_kernel(const BwdArgs args) {
 // of 64 x 128, direct global->LDS loads into a 4-stage ring of 32-wide K
 // slices).  An operand stored M-contiguous (a column operand) keeps its
 // storage order in LDS: 32 k-rows of 512 bytes, 16-byte chunk c of k-row r at
-// position c ^ 2 (r mod 4).  Its MFMA fragments come from two transposing
+// position c ^ 4 (r mod 4), so that the four k-rows one transposing read
+// touches fill all 64 banks (with c ^ 2 (r mod 4) rows r and r + 1 shared
+// 16 banks: 2-way conflicts on every fragment read).  Its MFMA fragments come from two transposing
 // LDS reads (ds_read_b64_tr_b16): within each 16-lane group, lane j points at
 // k-row kb + j / 4, columns mb + 4 (j mod 4); lane i then receives the four
 // k-values of column mb + i, which is exactly the k-contiguous fragment a
@@ -621,7 +623,7 @@ bwd_dma_kernel(const BwdArgs args) {
     if (col) {
       const int kr = 2 * b + (lane >> 5);        // k-row within the slice
       const int pos = lane & 31;
-      const int c = pos ^ (2 * (kr & 3));
+      const int c = pos ^ (4 * (kr & 3));
       krow_l[j] = kr;
       g_off[j] = (uint32_t)(mn0 + c * 8) * 2u;
     } else {
@@ -658,7 +660,7 @@ bwd_dma_kernel(const BwdArgs args) {
   const int kpos1 = ((2 + (lane >> 5)) ^ sw) << 3;
   // column operand, per lane: k-row part and chunk part of the transposing read
   const int tr_row = (8 * (lane >> 5) + ((lane & 15) >> 2)) * 512;
-  const int tr_swz = 2 * ((lane & 15) >> 2);
+  const int tr_swz = 4 * ((lane & 15) >> 2);
   const int tr_c = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int tr_half = (lane & 1) * 8;
   auto col_frag = [&](const char* op, int kk, int mcol0) -> bf16x8_t {
@@ -945,6 +947,45 @@ static hipError_t run_wgrad_any(const moe_shape& s, const BwdArgs& a, hipStream_
   return hipGetLastError();
 }
 
+// The two weight-gradient GEMMs on MXFP8 operands quantised along each
+// group's rows (the shape's wgrad_mx): dW_down = dY^T . h, then
+// [dW_gate | dW_up] = [dg | du]^T . x, reusing the quantised-operand buffers.
+static hipError_t run_mx_wgrad(const moe_shape& s, const BwdArgs& a, const BwdWs& ws, int groups,
+                               const int32_t* offsets, hipStream_t st, bool marks) {
+  MxWgrad g = {};
+  g.E = groups;
+  g.offsets = offsets;
+  g.poffs = groups == 1 ? ws.s_poffs : ws.poffs;
+  g.qa = ws.wqa;
+  g.sa = ws.wsa;
+  g.qb = ws.wqb;
+  g.sb = ws.wsb;
+  g.wrows = ws.wrows;
+  g.wbf16 = a.wgrad_bf16;
+  g.M = a.d;
+  g.N = a.F;
+  g.A = a.dY;
+  g.B = a.h;
+  g.w0 = a.dw_down;
+  g.w1 = a.dw_down;
+  g.wsplit = a.d;
+  if (marks) phase_mark(MOE_PHASE_BWD_DW_DOWN, 0, st);
+  hipError_t e = launch_mx_wgrad(g, st);
+  if (marks) phase_mark(MOE_PHASE_BWD_DW_DOWN, 1, st);
+  if (e != hipSuccess) return e;
+  g.M = 2 * a.F;
+  g.N = a.d;
+  g.A = a.dgu;
+  g.B = a.x_perm;
+  g.w0 = a.dw_gate;
+  g.w1 = a.dw_up;
+  g.wsplit = a.F;
+  if (marks) phase_mark(MOE_PHASE_BWD_DW_GATE_UP, 0, st);
+  e = launch_mx_wgrad(g, st);
+  if (marks) phase_mark(MOE_PHASE_BWD_DW_GATE_UP, 1, st);
+  return e;
+}
+
 hipError_t launch_backward(const moe_shape& s, const void* dy, const void* x_perm,
                            const void* gu_save, const void* y_perm, const int32_t* offsets,
                            const int32_t* row_token, const int32_t* token_row,
@@ -1000,7 +1041,8 @@ hipError_t launch_backward(const moe_shape& s, const void* dy, const void* x_per
     MxDgrad g = {R, offsets, ws.tiles, ws.tiles2, ws.dyq, ws.dys, mx->wd_tq, mx->wd_ts,
                  gu_save, ws.dgu, ws.h, ws.dguq, ws.dgus, mx->wgu_tq, mx->wgu_ts, ws.dX};
     if ((e = launch_mx_dgrad(s, g, st)) != hipSuccess) return e;
-    e = run_wgrad_any(s, a, st, true);
+    e = s.wgrad_mx ? run_mx_wgrad(s, a, ws, s.E, offsets, st, true)
+                   : run_wgrad_any(s, a, st, true);
   } else {
     e = run_backward_any(s, a, ws, st, true);
   }
@@ -1052,7 +1094,9 @@ hipError_t launch_backward(const moe_shape& s, const void* dy, const void* x_per
                    mx->swd_tq, mx->swd_ts, b.gu, ws.s_dgu, ws.s_h, ws.s_dguq, ws.s_dgus,
                    mx->swgu_tq, mx->swgu_ts, ws.s_dX};
       if ((e = launch_mx_dgrad(s2, g, st)) != hipSuccess) return e;
-      if ((e = run_wgrad_any(s2, b, st, false)) != hipSuccess) return e;
+      if ((e = s.wgrad_mx ? run_mx_wgrad(s2, b, ws, 1, ws.s_offsets, st, false)
+                          : run_wgrad_any(s2, b, st, false)) != hipSuccess)
+        return e;
     } else if ((e = run_backward_any(s2, b, w2, st, false)) != hipSuccess) {
       return e;
     }

@@ -40,8 +40,11 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 // EPI_COMBINE: no C; each result row is scaled by its row's gate and added
 // (fp32 atomics) into Y at its token's row.  EPI_DSWIGLU (MXFP8 kernel
-// only): the SwiGLU backward of the result dh.
-enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_F32_BIAS = 2, EPI_COMBINE = 3, EPI_DSWIGLU = 4 };
+// only): the SwiGLU backward of the result dh.  EPI_WGRAD (MXFP8 kernel
+// only): a weight gradient, one fixed tile grid per group whose K is the
+// group's padded row count.
+enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_F32_BIAS = 2, EPI_COMBINE = 3, EPI_DSWIGLU = 4,
+       EPI_WGRAD = 5 };
 
 struct GemmArgs {
   // routed groups (E == 0: none)
@@ -85,6 +88,8 @@ struct GemmArgs {
   const float* comb_gate;
   float* Y;
   long long ldy;
+  // EPI_WGRAD: rows of each group's output (the A operand's rows)
+  int Mw;
 };
 
 // One tile's work, with typed base pointers already offset to the group.

@@ -157,6 +157,26 @@ struct MxDgrad {
   void* dX;                      // [rows, d] bf16 out
 };
 hipError_t launch_mx_dgrad(const moe_shape& s, const MxDgrad& g, hipStream_t st);
+// The weight-gradient GEMM dW[e] = A_e^T . B_e over each group's rows on
+// MXFP8 operands quantised along the rows (padded per group to 128 rows):
+// A [rows, M] and B [rows, N] bf16, row-grouped by `offsets` (E groups);
+// output rows m < wsplit go to w0 [E][wsplit][N], the rest to w1
+// [E][M - wsplit][N], fp32 or bf16 (wbf16).  poffs [E + 1] receives the
+// padded offsets; qa/sa and qb/sb hold the quantised operands (wrows padded
+// rows each).
+struct MxWgrad {
+  int E, M, N;
+  const int32_t* offsets;
+  int32_t* poffs;
+  const void* A;
+  const void* B;
+  uint8_t *qa, *sa, *qb, *sb;
+  long long wrows;
+  void* w0;
+  void* w1;
+  int wsplit, wbf16;
+};
+hipError_t launch_mx_wgrad(const MxWgrad& g, hipStream_t st);
 
 hipError_t launch_combine(const moe_shape& s, const void* y_perm, const int32_t* token_row,
                           const float* topk_w, const void* y_shared, float* y,
@@ -181,6 +201,15 @@ struct BwdWs {
   uint8_t *dguq, *dgus;     // [R, 2F], [R, 2F / 32]
   uint8_t *s_dyq, *s_dys;   // [T, d], [T, d / 32]: dy for the shared expert
   uint8_t *s_dguq, *s_dgus; // [T, 2 F_shared], [T, 2 F_shared / 32]
+  // MXFP8 weight gradients (shape.wgrad_mx) only: padded row offsets of
+  // the routed experts and of the shared expert's one group, and the two
+  // operands of one weight-gradient GEMM quantised along the padded rows
+  // ([rows of the output, wrows] codes and [.., wrows / 32] scales)
+  int32_t* poffs;           // [E + 1]
+  int32_t* s_poffs;         // [E + 1] (two used)
+  uint8_t *wqa, *wsa;       // A operand
+  uint8_t *wqb, *wsb;       // B operand
+  long long wrows;          // padded rows allocated (a multiple of 128)
 };
 // The quantised weights the MXFP8 data gradients read.
 struct MxBwdWeights {

@@ -235,6 +235,12 @@ struct MxBwd {
   bf16_t* dgu;
   bf16_t* h;
   int F;
+  // EPI_WGRAD: rows m < wsplit of group g go to w0 + (g wsplit + m) N,
+  // the others to w1 + (g (M - wsplit) + m - wsplit) N; fp32, or bf16 when
+  // wbf16
+  void* w0;
+  void* w1;
+  int wsplit, wbf16;
 };
 
 // The shape of one tile class: CLS 0 is BM x BN with WM x WN waves and a
@@ -286,7 +292,10 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& args, const MxScales& sc
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WNC, wn = wave % WNC;
   const bool live = job.m0 + wm * WTM < job.rows;
-  const int kb = job.K / 32;                    // scale bytes per operand row
+  // scale bytes per operand row: the rows of both operands are lda codes
+  // long (lda = K except in the weight gradients, whose operand rows hold
+  // every group's padded rows and each tile reads its group's K of them)
+  const int kb = (int)(job.lda / 32);
   // SG = 8: scale group g covers K blocks 16 g .. 16 g + 15 (steps 8 g ..
   // 8 g + 7), read as the 16 bytes from sg_start(g); the last group's
   // window ends at the row's end (kb >= 16 here), so no read passes it.
@@ -332,7 +341,7 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& args, const MxScales& sc
     } else {
       const int rb = row - BMC;
       src = (rb < BNC) ? job.B0 : job.B1;
-      ld = job.K;
+      ld = (int)job.lda;                                // both operands' row stride
       rbase = job.n0 + (rb < BNC ? rb : rb - BNC);
       rlimit = job.N;
     }
@@ -598,12 +607,17 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& args, const MxScales& sc
       }
     }
   };
-  if (!live) {
-    k_loop(std::false_type{});
-    if constexpr (EPI == EPI_DSWIGLU || EPI == EPI_COMBINE) barrier();   // the staged epilogue's
-    return;
+  // A weight gradient of a group without rows runs zero K steps and stores
+  // exact zeros (KT is uniform over the workgroup: every wave skips the same
+  // loop and its barriers).
+  if (EPI != EPI_WGRAD || KT > 0) {
+    if (!live) {
+      k_loop(std::false_type{});
+      if constexpr (EPI == EPI_DSWIGLU || EPI == EPI_COMBINE) barrier();   // the staged epilogue's
+      return;
+    }
+    k_loop(std::true_type{});
   }
-  k_loop(std::true_type{});
 
   if constexpr (EPI == EPI_COMBINE) {
     // The combine folded into FC2: per 32-row half, this wave's 32 x 128 fp32
@@ -743,6 +757,39 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& args, const MxScales& sc
     return;
   }
 
+  if constexpr (EPI == EPI_WGRAD) {
+    // a weight gradient: 4 consecutive fp32 (or bf16) values per lane and
+    // 32-column block, straight from the accumulators; the group is job.row0
+    const int Mrest = job.rows - bw.wsplit;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int m = job.m0 + wm * WTM + i * 32 + frag_row;
+      if (!live || m >= job.rows) continue;
+      const long long row = m < bw.wsplit
+                                ? ((long long)job.row0 * bw.wsplit + m) * job.N
+                                : ((long long)job.row0 * Mrest + (m - bw.wsplit)) * job.N;
+      void* base = m < bw.wsplit ? bw.w0 : bw.w1;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int nblk = job.n0 + wn * WTN + j * 32;
+        if (nblk >= job.N) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = nblk + 8 * q + 4 * hsel;
+          const f32x16_t& Cv = acc[0][i][j];
+          if (bw.wbf16)
+            *reinterpret_cast<uint2*>(static_cast<bf16_t*>(base) + row + n) =
+                make_uint2(pack_bf16x2(Cv[4 * q], Cv[4 * q + 1]),
+                           pack_bf16x2(Cv[4 * q + 2], Cv[4 * q + 3]));
+          else
+            *reinterpret_cast<float4*>(static_cast<float*>(base) + row + n) =
+                make_float4(Cv[4 * q], Cv[4 * q + 1], Cv[4 * q + 2], Cv[4 * q + 3]);
+        }
+      }
+    }
+    return;
+  }
+
   // Epilogue.  Lane owns row m = .. + (lane % 32) and, for register v,
   // column n = .. + 8 (v / 4) + 4 (lane / 32) + v % 4.
 #pragma unroll
@@ -834,6 +881,175 @@ hipError_t launch_mx_gemm(const GemmArgs& a, const MxScales& sc, int R, hipStrea
     gemm_mx_kernel<BM, BN, NB, EPI, WM, WN, 8, 1><<<grid, 64 * WM * WN, 0, st>>>(a, sc, bw);
   else
     gemm_mx_kernel<BM, BN, NB, EPI, WM, WN, 1, 1><<<grid, 64 * WM * WN, 0, st>>>(a, sc, bw);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// MXFP8 weight gradients (Primus blog, low-precision section: the permuted
+// tokens are padded to the quantisation block boundary).  A weight gradient
+// contracts over an expert's rows, so its operands are quantised along the
+// rows, in 32-row blocks from the expert's first row.  Each expert's row
+// count is padded to a multiple of 128 (the GEMM's scale granularity: one
+// scale dword per row covers two 64-value steps) with zero rows, which
+// change no block maximum and add nothing to the sums.
+//
+//   pad_offsets:   poffs[e] = sum over e' < e of the padded row counts
+//   quantize_tok:  src [R, C] bf16 (rows grouped by offsets) -> codes
+//                  [C, ldq] and scales [C, ldq / 32]: padded row P of
+//                  expert e is source row offsets[e] + P - poffs[e] when
+//                  that row is the expert's, else zero
+//   wgrad GEMM:    per expert, dW[e][m, n] = sum_k A_q[m, k] B_q[n, k]
+//                  over its padded rows k, on the scaled MFMA
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(1024)
+pad_offsets_kernel(const int32_t* __restrict__ offsets, int E, int32_t* __restrict__ poffs) {
+  __shared__ int s[1024];
+  const int g = threadIdx.x;
+  int v = 0;
+  if (g < E) {
+    const int c = offsets[g + 1] - offsets[g];
+    v = (c + 127) / 128 * 128;
+  }
+  s[g] = v;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int a = (g >= off) ? s[g - off] : 0;
+    __syncthreads();
+    s[g] += a;
+    __syncthreads();
+  }
+  for (int i = g; i <= E; i += 1024) poffs[i] = (i == 0) ? 0 : s[i - 1];
+}
+
+// A workgroup takes 32 padded rows x 64 columns through LDS; 4 lanes per
+// column quantise 8 rows each (as mx_quantize_t_kernel does for weights).
+// Row blocks past poffs[E] exit: the GEMM reads only the padded rows of
+// each expert.
+__global__ void __launch_bounds__(256)
+mx_quantize_tok_kernel(const bf16_t* __restrict__ src, int cols,
+                       const int32_t* __restrict__ offsets, const int32_t* __restrict__ poffs,
+                       int E, long long ldq, uint8_t* __restrict__ q, uint8_t* __restrict__ sq) {
+  __shared__ float tile[32][65];
+  const int P0 = blockIdx.y * 32, c0 = blockIdx.x * 64;
+  if (P0 >= poffs[E]) return;
+  // the expert of padded row P0: largest e with poffs[e] <= P0
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (poffs[mid] <= P0) lo = mid; else hi = mid - 1;
+  }
+  const int r0 = offsets[lo] + (P0 - poffs[lo]);
+  const int rend = offsets[lo + 1];
+  for (int i = threadIdx.x; i < 32 * 64; i += 256) {
+    const int rr = i >> 6, cc = i & 63;
+    const int c = c0 + cc, r = r0 + rr;
+    tile[rr][cc] = (c < cols && r < rend) ? to_f32<bf16_t>(src[(long long)r * cols + c]) : 0.0f;
+  }
+  __syncthreads();
+  const int cc = threadIdx.x >> 2, part = threadIdx.x & 3;
+  float v[8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    v[p] = tile[8 * part + p][cc];
+    amax = fmaxf(amax, fabsf(v[p]));
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+  const int sx = mx_scale_exp(amax);
+  const float inv = mx_inv_scale(sx);
+  uint32_t lo32 = 0, hi32 = 0;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    lo32 |= e4m3_code(v[p] * inv) << (8 * p);
+    hi32 |= e4m3_code(v[4 + p] * inv) << (8 * p);
+  }
+  const int c = c0 + cc;
+  if (c < cols) {
+    *reinterpret_cast<uint2*>(q + (long long)c * ldq + P0 + 8 * part) = make_uint2(lo32, hi32);
+    if (part == 0) sq[(long long)c * (ldq / 32) + P0 / 32] = (uint8_t)(sx + 127);
+  }
+}
+
+// Weight-gradient tiles: per expert a fixed grid of ceil(Mw / BM) x
+// ceil(N / BN) tiles, row tiles adjacent; each XCD walks a contiguous range.
+// A and B are the quantised operands (rows of lda padded-row codes); a
+// tile's K is its expert's padded row count, starting at poffs[e].
+template <int BM, int BN>
+__device__ __forceinline__ bool decode_wgrad_tile(const GemmArgs& a,
+                                                  TileJob<uint8_t, bf16_t>& j) {
+  const int mt = cdiv(a.Mw, BM), nt = cdiv(a.N, BN);
+  const int total = a.E * mt * nt;
+  const int per = (total + 7) >> 3, slot = blockIdx.x >> 3;
+  if (slot >= per) return false;
+  const int lid = (blockIdx.x & 7) * per + slot;
+  if (lid >= total) return false;
+  const int g = lid / (mt * nt), r = lid - g * (mt * nt);
+  const int p0 = a.offsets[g];
+  j.m0 = (r % mt) * BM;
+  j.n0 = (r / mt) * BN;
+  j.A = static_cast<const uint8_t*>(a.A) + p0;
+  j.lda = a.lda;
+  j.gather = nullptr;
+  j.rows = a.Mw;
+  j.B0 = static_cast<const uint8_t*>(a.B0) + p0;
+  j.B1 = nullptr;
+  j.N = a.N;
+  j.K = a.offsets[g + 1] - p0;
+  j.k0 = 0;
+  j.klen = j.K;
+  j.C = nullptr;
+  j.ldc = a.N;
+  j.GU = nullptr;
+  j.ldgu = 0;
+  j.P = nullptr;
+  j.cls = 0;
+  j.dense = 0;
+  j.row0 = g;                 // EPI_WGRAD: the expert
+  j.ctok = nullptr;
+  j.cgate = nullptr;
+  return true;
+}
+
+template <int BM, int BN, int WM, int WN>
+__global__ void __launch_bounds__(64 * WM * WN)
+gemm_mx_wgrad_kernel(const GemmArgs args, const MxScales sc, const MxBwd bw) {
+  using S0 = MxShape<BM, BN, 1, WM, WN, 1, 0>;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[S0::RING];
+  __shared__ __attribute__((aligned(1024))) uint8_t sring[S0::SRING + 64];
+  TileJob<uint8_t, bf16_t> job;
+  if (!decode_wgrad_tile<BM, BN>(args, job)) return;
+  mx_tile<BM, BN, 1, EPI_WGRAD, WM, WN, 1, 0>(args, sc, bw, job, ring, sring);
+}
+
+hipError_t launch_mx_wgrad(const MxWgrad& g, hipStream_t st) {
+  if (g.E == 0) return hipSuccess;
+  pad_offsets_kernel<<<1, 1024, 0, st>>>(g.offsets, g.E, g.poffs);
+  const unsigned yb = (unsigned)(g.wrows / 32);
+  mx_quantize_tok_kernel<<<dim3(cdiv(g.M, 64), yb), 256, 0, st>>>(
+      static_cast<const bf16_t*>(g.A), g.M, g.offsets, g.poffs, g.E, g.wrows, g.qa, g.sa);
+  mx_quantize_tok_kernel<<<dim3(cdiv(g.N, 64), yb), 256, 0, st>>>(
+      static_cast<const bf16_t*>(g.B), g.N, g.offsets, g.poffs, g.E, g.wrows, g.qb, g.sb);
+  GemmArgs a = {};
+  MxScales sc = {};
+  a.E = g.E;
+  a.offsets = g.poffs;
+  a.A = g.qa;
+  a.lda = g.wrows;
+  a.B0 = g.qb;
+  a.N = g.N;
+  a.K = 0;
+  a.Mw = g.M;
+  sc.A = g.sa;
+  sc.B0 = g.sb;
+  MxBwd bw = {};
+  bw.w0 = g.w0;
+  bw.w1 = g.w1;
+  bw.wsplit = g.wsplit;
+  bw.wbf16 = g.wbf16;
+  const long long tiles = (long long)g.E * cdiv(g.M, MX_FC2_BM) * cdiv(g.N, MX_FC2_BN);
+  const int grid = (int)(((tiles + 7) / 8) * 8);
+  gemm_mx_wgrad_kernel<MX_FC2_BM, MX_FC2_BN, 4, 2><<<grid, 512, 0, st>>>(a, sc, bw);
   return hipGetLastError();
 }
 

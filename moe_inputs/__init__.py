@@ -61,6 +61,7 @@ class MoEConfig:
     renorm: int = 1             # renormalise the k gates over the selected set
     dtype: int = DTYPE_BF16
     wgrad_dtype: int = DTYPE_F32    # storage of the weight gradients
+    wgrad_mx: int = 0               # MXFP8 backward: weight gradients in MXFP8 too
     x_std: float = 1.0
     w_std: float = 0.02
     router_std: float = 0.02

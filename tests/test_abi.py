@@ -62,7 +62,7 @@ BAD_SHAPES = [
     dict(T=-1), dict(n_groups=3), dict(n_groups=2, topk_groups=3),
     dict(n_groups=8, topk_groups=1, k=8, E=32),  # 1 group of 4 experts < k
     dict(n_groups=2, score=0), dict(score=5), dict(renorm=2), dict(dtype=3),
-    dict(k=65, E=128), dict(wgrad_dtype=2),
+    dict(k=65, E=128), dict(wgrad_dtype=2), dict(wgrad_mx=2),
 ]
 
 

@@ -165,11 +165,64 @@ def test_ffn_backward_mxfp8(case):
         assert (counts == 0).any()
 
 
-def test_ffn_backward_mxfp8_full_size_sampled():
+MXW_CASES = [
+    # name, T, d, E, k, F, score, renorm, skew, F_shared, wgrad_dtype: the
+    # MXFP8 weight gradients (operands quantised along each expert's rows,
+    # padded to 128); row counts that are no multiple of 32
+    ("mxw_softmax_t300", 300, 256, 8, 2, 256, 0, 1, False, 0, 0),
+    # the shared expert's 300 rows pad to 384; sigmoid scores
+    ("mxw_shared_sigmoid_t300", 300, 256, 16, 4, 256, 1, 1, False, 256, 0),
+    # empty experts: zero K steps, exactly zero gradients
+    ("mxw_skewed_empty_t400", 400, 128, 16, 4, 128, 0, 1, True, 0, 0),
+    # d = F = 384: the last row and column tiles half past the output;
+    # bf16 weight gradients
+    ("mxw_d384_shared_wgrad_bf16_t500", 500, 384, 12, 4, 384, 0, 1, True, 128, 1),
+    # about 500 rows per expert: several 128-row blocks, 8 K steps
+    ("mxw_long_k_t1000", 1000, 256, 4, 2, 256, 0, 1, False, 0, 0),
+]
+
+
+@pytest.mark.parametrize("case", MXW_CASES, ids=[c[0] for c in MXW_CASES])
+def test_ffn_backward_mxfp8_weight_gradients(case):
+    name, T, d, E, k, F, score, renorm, skew, Fs, wgrad = case
+    _log(f"[backward mxfp8 wgrad] {name}")
+    M = _lib()
+    cfg = MoEConfig(name, T=T, d=d, E=E, k=k, F=F, F_shared=Fs, score=score,
+                    renorm=renorm, backward=True, wgrad_dtype=wgrad, wgrad_mx=1)
+    inp = make_inputs(cfg, device="cuda")
+    g = _bwd_inputs(cfg, skew)
+    out = run_bwd_mx(M, cfg, inp, g)
+    shared = None
+    if Fs:
+        shared = dict(x=np64(inp["x"]), gu=np64(g["gu_s"]), ws_gate=np64(inp["ws_gate"]),
+                      ws_up=np64(inp["ws_up"]), ws_down=np64(inp["ws_down"]))
+    ref = O.ffn_backward(g["dy"], g["x_perm"], g["gu"], g["y_perm"], g["p"]["offsets"],
+                         g["p"]["token_row"], g["idx"], g["w"], g["logits"],
+                         np64(inp["w_gate"]), np64(inp["w_up"]), np64(inp["w_down"]),
+                         score, renorm, "bf16", shared=shared, mxfp8=True, mx_wgrad=True)
+    keys = ["d_gate", "d_logits", "dx", "dw_gate", "dw_up", "dw_down"]
+    if Fs:
+        keys += ["dws_gate", "dws_up", "dws_down"]
+    for key in keys:
+        assert_close(key, out[key], ref[key], "bf16")
+    counts = np.diff(g["p"]["offsets"])
+    for e in range(E):
+        for key in ("dw_gate", "dw_up", "dw_down"):
+            if counts[e] == 0:
+                assert torch.all(out[key][e] == 0), (key, e)
+            else:      # each expert on its own (a wrong block would hide in the whole)
+                assert_close(f"{key}[{e}]", out[key][e], ref[key][e], "bf16")
+    if skew:
+        assert (counts == 0).any()
+
+
+@pytest.mark.parametrize("wgrad_mx", [0, 1], ids=["bf16_wgrad", "mxfp8_wgrad"])
+def test_ffn_backward_mxfp8_full_size_sampled(wgrad_mx):
     """The Qwen3-235B training shape: sampled tokens for dx, d_gate and
-    d_logits; three whole experts for the weight gradients."""
-    cfg = CONFIGS["qwen3_235b_train_t8192"]
-    _log(f"[backward mxfp8 full] {cfg.name}")
+    d_logits; three whole experts for the weight gradients (bf16, or MXFP8
+    along each expert's padded rows)."""
+    cfg = CONFIGS["qwen3_235b_train_t8192"].replace(wgrad_mx=wgrad_mx)
+    _log(f"[backward mxfp8 full] {cfg.name} wgrad_mx={wgrad_mx}")
     M = _lib()
     inp = make_inputs(cfg, device="cuda")
     g = _bwd_inputs(cfg)
@@ -181,16 +234,20 @@ def test_ffn_backward_mxfp8_full_size_sampled():
     tt = torch.as_tensor(toks).cuda()
 
     def dY_rows(rows):
+        """dY_perm of routed rows, from the oracle's dispatch gradient on
+        just those rows."""
         t = rt[rows]
         j = np.argmax(tr[t] == rows[:, None], axis=1)
         dyt = np64(g["dy"][torch.as_tensor(t).cuda()])
-        return O.round_bf16(w[t, j][:, None] * dyt)
+        n = len(rows)
+        return O.dispatch_grad(dyt, np.arange(n)[:, None], w[t, j][:, None], n, "bf16")
 
     def expert(e, rows):
         rr = torch.as_tensor(rows).cuda()
         return O.expert_backward(dY_rows(rows), g["x_perm"][rr], g["gu"][rr],
                                  np64(inp["w_gate"][e]), np64(inp["w_up"][e]),
-                                 np64(inp["w_down"][e]), "bf16", mxfp8=True)
+                                 np64(inp["w_down"][e]), "bf16", mxfp8=True,
+                                 mx_wgrad=bool(wgrad_mx))
 
     rows = tr[toks].reshape(-1)
     ex = np.searchsorted(p["offsets"], rows, side="right") - 1

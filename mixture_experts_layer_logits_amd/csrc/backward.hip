@@ -845,6 +845,329 @@ bwd_dma_kernel(const BwdArgs args) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Weight gradients as a persistent kernel.  Each expert's tiles have a short
+// K (its row count: about 512 rows in a Qwen3-235B-shape step), so a
+// workgroup per tile spent more time starting, waiting for its first slice
+// and draining its epilogue than in its K loop (per-tile timestamps: 3.7 us
+// to the first slice, a 15 us K loop, a 4.6 us epilogue, 1.7 us between
+// workgroups).  Here one workgroup per CU walks a run of tiles, and the
+// stream of K slices continues across tiles: the next tile's first slices
+// load during the current tile's last steps and its epilogue.
+//
+// The epilogue therefore cannot stage its results in the ring (which holds
+// those slices): each wave has 4 KiB of its own, one 32 x 32 fp32 block at a
+// time, rows of 128 bytes with 16-byte chunk c of row r at c ^ ((r >> 1) & 7),
+// which is conflict-free for both the accumulator-layout writes and the
+// row-contiguous reads; each store instruction covers 8 rows x 128 bytes.
+//
+// vmcnt counts loads and stores in issue order, so a wait for a slice
+// issued before an epilogue's stores need not wait for them, while a wait
+// for one issued after them does: each wave counts the memory operations it
+// issued after the slice it waits for.
+// ---------------------------------------------------------------------------
+template <int MODE>
+__global__ void __launch_bounds__(512)
+bwd_wgrad_kernel(const BwdArgs args) {
+  static_assert(MODE == BWD_WD || MODE == BWD_WGU, "weight gradients only");
+  constexpr int BM = 256, BN = 256, BK = 32, WN = 2;
+  constexpr int WTM = 64, WTN = 128, MI = WTM / 32, NJ = WTN / 32;
+  constexpr int OPB = BM * BK * 2;              // bytes of one operand per stage (16 KiB)
+  constexpr int STAGE = OPB;                    // bf16 elements per stage (A then B)
+  constexpr int BPW = 4;                        // 1 KiB load blocks per wave per slice
+  constexpr int NST = MI * NJ * 4;              // global stores per wave per epilogue
+  __shared__ __attribute__((aligned(1024))) bf16_t ring[4 * STAGE];
+  __shared__ __attribute__((aligned(1024))) float stg[8][32 * 32];
+
+  const int Mtot = MODE == BWD_WD ? args.d : 2 * args.F;
+  const int Ntot = MODE == BWD_WD ? args.F : args.d;
+  const int mt = cdiv(Mtot, BM), nt = cdiv(Ntot, BN);
+  const int total = args.E * mt * nt;
+  // XCD x (workgroups are dealt to the 8 XCDs round-robin) takes a contiguous
+  // range of the tile list; its workgroups interleave over that range, so
+  // the tiles running at one time on an XCD are neighbours sharing operands
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslot = gridDim.x >> 3;
+  const int per = (total + 7) >> 3;
+  const int t_begin = xcd * per + slot;
+  const int t_end = min(total, (xcd + 1) * per);
+  if (t_begin >= t_end) return;                 // uniform: no tiles for this workgroup
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const bool load_a = wave < 4;
+  const int blk0 = (wave & 3) * BPW;
+  const int lds_op = load_a ? 0 : OPB;
+  const long long lda = MODE == BWD_WD ? args.d : 2LL * args.F;   // A: dY or dg | du rows
+  const long long ldb = MODE == BWD_WD ? args.F : (long long)args.d;   // B: h or x_perm rows
+  const long long ld = load_a ? lda : ldb;
+  const bf16_t* opnd = static_cast<const bf16_t*>(
+      load_a ? (MODE == BWD_WD ? args.dY : args.dgu) : (MODE == BWD_WD ? args.h : args.x_perm));
+  // per lane, block j of a slice holds k-row 2 (blk0 + j) + lane / 32 and the
+  // 16-byte column chunk (lane % 32) ^ 4 (k-row % 4) (computed where used:
+  // arrays of them indexed in a loop the compiler keeps rolled go to scratch)
+
+  // ---- the slice stream: tile t_begin + i nslot, its K slices in order,
+  // tiles without rows skipped -------------------------------------------
+  // The expert offsets are read through the constant address space with a
+  // scalar index: scalar loads, counted by lgkmcnt.  As vector loads the
+  // compiler's own wait for them would be a vmcnt(0) that drains every DMA
+  // in flight (it cannot see the loads issued in inline assembly).
+  const __attribute__((address_space(4))) int32_t* offs =
+      (const __attribute__((address_space(4))) int32_t*)args.offsets;
+  auto offset_of = [&](int e) { return offs[__builtin_amdgcn_readfirstlane(e)]; };
+  // The issue cursor: tile is_t (decoded only when the cursor reaches it),
+  // slice is_s of its is_KT.  Within a tile a lane's DMA offsets stay fixed
+  // (column chunk and k-row within the slice) and the scalar base advances
+  // by one slice per issue; only a last, partial slice clamps its k-rows.
+  int is_t = t_begin, is_s = 0, is_K = 0, is_KT = 0;
+  const char* is_base = nullptr;                // k-row 32 is_s of the tile's operand block
+  uint32_t goff0 = 0, goff1 = 0, goff2 = 0, goff3 = 0;
+  int is_mn0 = 0;
+  const uint32_t slice_bytes = (uint32_t)(BK * ld * 2);
+  auto lane_off = [&](int j, int mn0, int kmax) {
+    const int krs = 2 * (blk0 + j) + (lane >> 5);
+    const int ccol = (lane & 31) ^ (4 * (krs & 3));
+    const int kr = krs < kmax ? krs : kmax - 1;
+    return (uint32_t)(mn0 + ccol * 8) * 2u + (uint32_t)(kr * (int)ld) * 2u;
+  };
+  auto load_issue_tile = [&]() {                // from is_t on, the next tile with rows
+    for (; is_t < t_end; is_t += nslot) {
+      const int e = is_t / (mt * nt), r = is_t - e * (mt * nt);
+      const int row0 = offset_of(e);
+      is_K = offset_of(e + 1) - row0;
+      if (is_K == 0) continue;
+      is_KT = cdiv(is_K, BK);
+      is_mn0 = load_a ? (r % mt) * BM : (r / mt) * BN;
+      // wave-uniform values the compiler cannot prove uniform: scalar copies
+      is_base = uniform_ptr(opnd + (long long)row0 * ld);
+      goff0 = lane_off(0, is_mn0, BK);
+      goff1 = lane_off(1, is_mn0, BK);
+      goff2 = lane_off(2, is_mn0, BK);
+      goff3 = lane_off(3, is_mn0, BK);
+      return;
+    }
+  };
+  load_issue_tile();
+  int issued = 0;                               // slices issued so far
+  // `issued` at the last three epilogues (-1: none): an epilogue's stores
+  // are younger than slice g exactly when it ran with issued > g
+  int ep0 = -1, ep1 = -1, ep2 = -1;
+  const uint32_t lds_wave = (uint32_t)(uintptr_t)MOE_AS_LDS(reinterpret_cast<char*>(ring)) +
+                            (uint32_t)(lds_op + blk0 * 1024);
+  auto issue_one = [&]() {
+    if (is_t >= t_end) return;
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_wave + (uint32_t)(issued & 3) * (STAGE * 2));
+    uint32_t o0 = goff0, o1 = goff1, o2 = goff2, o3 = goff3;
+    if (__builtin_amdgcn_readfirstlane((is_s + 1) * BK > is_K)) {
+      // a partial last slice: k-rows past the tile's end read its last row
+      // (their A values are zeroed before use)
+      const int kmax = is_K - is_s * BK;
+      o0 = lane_off(0, is_mn0, kmax);
+      o1 = lane_off(1, is_mn0, kmax);
+      o2 = lane_off(2, is_mn0, kmax);
+      o3 = lane_off(3, is_mn0, kmax);
+    }
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(lds0), "v"(o0), "s"(is_base) : "memory");
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(lds0 + 1024), "v"(o1), "s"(is_base) : "memory");
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(lds0 + 2048), "v"(o2), "s"(is_base) : "memory");
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(lds0 + 3072), "v"(o3), "s"(is_base) : "memory");
+    ++issued;
+    if (++is_s == is_KT) {
+      is_s = 0;
+      is_t += nslot;
+      load_issue_tile();
+    } else {
+      is_base = is_base + slice_bytes;
+    }
+  };
+  // waits until this wave's loads of slice g have landed, leaving every
+  // younger operation in flight: the slices issued after it, and the stores
+  // of the epilogues since (counting at most three: a smaller count than
+  // the true one only waits longer)
+  auto wait_for = [&](int g) {
+    const int ys = issued - 1 - g;
+    const int ye = (ep0 > g ? 1 : 0) + (ep1 > g ? 1 : 0) + (ep2 > g ? 1 : 0);
+    if (ye == 0) {                              // inside a tile: the common case
+      if (ys >= 2) wait_vmcnt<2 * BPW>();
+      else if (ys == 1) wait_vmcnt<BPW>();
+      else wait_vmcnt<0>();
+      return;
+    }
+    const int y = ys * BPW + ye * NST;
+    if (y >= NST + 3 * BPW) wait_vmcnt<NST + 3 * BPW>();
+    else if (y >= NST + 2 * BPW) wait_vmcnt<NST + 2 * BPW>();
+    else if (y >= NST + BPW) wait_vmcnt<NST + BPW>();
+    else if (y >= NST) wait_vmcnt<NST>();
+    else if (y >= 2 * BPW) wait_vmcnt<2 * BPW>();
+    else if (y >= BPW) wait_vmcnt<BPW>();
+    else wait_vmcnt<0>();
+  };
+
+  // ---- fragments (as bwd_dma_kernel: both operands are column operands) --
+  const int frag_row = lane & 31;
+  const int tr_row = (8 * (lane >> 5) + ((lane & 15) >> 2)) * 512;
+  const int tr_swz = 4 * ((lane & 15) >> 2);
+  const int tr_c = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tr_half = (lane & 1) * 8;
+  auto col_frag = [&](const char* op, int kk, int mcol0) -> bf16x8_t {
+    const int c = (tr_c + (mcol0 >> 3)) ^ tr_swz;
+    const char* p = op + kk * 16 * 512 + tr_row + (c << 4) + tr_half;
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t*)MOE_AS_LDS(p));
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t*)MOE_AS_LDS(p + 4 * 512));
+    const auto v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8_t, v);
+  };
+  auto load_frags = [&](const bf16_t* stage, int kk, bf16x8_t (&af)[MI], bf16x8_t (&bfr)[NJ]) {
+    const char* sa = reinterpret_cast<const char*>(stage);
+    const char* sb = sa + OPB;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) af[i] = col_frag(sa, kk, wm * WTM + i * 32);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) bfr[j] = col_frag(sb, kk, wn * WTN + j * 32);
+  };
+  f32x16_t acc[MI][NJ];
+  auto mma = [&](const bf16x8_t (&af)[MI], const bf16x8_t (&bfr)[NJ]) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+  };
+  auto mask_tail = [&](bf16x8_t (&af)[MI], int s, int kk, int K) {
+    const int k0 = s * BK + kk * 16 + 8 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (k0 + e >= K) af[i][e] = (__bf16)0.0f;
+  };
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  constexpr int NREAD = 2 * MI + 2 * NJ;        // LDS reads per half-step
+  auto interleave = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, NREAD - (MI * NJ - 1), 0);
+#pragma unroll
+    for (int r = 0; r < MI * NJ - 1; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  };
+
+  // ---- the epilogue: one 32 x 32 block at a time through the wave's 4 KiB
+  float* sw = stg[wave];
+  auto epilogue = [&](int e_, int m0_, int n0_) {
+    // The tile's output block, from scalars the compiler cannot see through:
+    // otherwise it hoists the 32 store addresses out of the K loop and keeps
+    // them live across it (spilling).  Tiles never straddle dW_gate and
+    // dW_up (F is a multiple of 256 here).
+    uint32_t e = __builtin_amdgcn_readfirstlane(e_);
+    uint32_t m0 = __builtin_amdgcn_readfirstlane(m0_);
+    uint32_t n0 = __builtin_amdgcn_readfirstlane(n0_);
+    asm volatile("" : "+s"(e), "+s"(m0), "+s"(n0));
+    const bool up = MODE == BWD_WGU && (int)m0 >= args.F;
+    const long long per_e = (long long)(MODE == BWD_WD ? args.d : args.F) * Ntot;
+    const long long blk = (long long)e * per_e +
+                          (long long)((int)m0 - (up ? args.F : 0) + wm * WTM) * Ntot +
+                          (int)n0 + wn * WTN;
+    void* const wbase = MODE == BWD_WD ? args.dw_down : (up ? args.dw_up : args.dw_gate);
+    static_for<MI * NJ>([&](auto ijc) __attribute__((always_inline)) {
+        constexpr int i = decltype(ijc)::value / NJ, j = decltype(ijc)::value % NJ;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ch = 2 * q + (lane >> 5);
+          const int pos = ch ^ ((frag_row >> 1) & 7);
+          *reinterpret_cast<float4*>(sw + frag_row * 32 + pos * 4) =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                          acc[i][j][4 * q + 3]);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int r = (lane >> 3) + 8 * t, ch = lane & 7;
+          const float4 v4 = *reinterpret_cast<const float4*>(sw + r * 32 + ((ch ^ ((r >> 1) & 7)) * 4));
+          const long long o = blk + (long long)(i * 32 + r) * Ntot + j * 32 + ch * 4;
+          // fp32 gradients (the largest write of the backward) bypass L2 so
+          // they do not evict the operand slices other tiles still read;
+          // the bf16 form is half the bytes and measures faster cached.
+          if (args.wgrad_bf16) {
+            *reinterpret_cast<uint2*>(static_cast<bf16_t*>(wbase) + o) =
+                make_uint2(pack_bf16x2(v4.x, v4.y), pack_bf16x2(v4.z, v4.w));
+          } else {
+            typedef float f4_t __attribute__((ext_vector_type(4)));
+            const f4_t q = {v4.x, v4.y, v4.z, v4.w};
+            __builtin_nontemporal_store(q, reinterpret_cast<f4_t*>(static_cast<float*>(wbase) + o));
+          }
+        }
+    });
+    ep2 = ep1;
+    ep1 = ep0;
+    ep0 = issued;
+  };
+
+  // ---- the tiles ----------------------------------------------------------
+  for (int j = 0; j < 3; ++j) issue_one();
+  int consumed = 0;                             // slices consumed so far
+  bf16x8_t af0[MI], af1[MI], bf0[NJ], bf1[NJ];
+  for (int t = t_begin; t < t_end; t += nslot) {
+    const int e = t / (mt * nt), r = t - e * (mt * nt);
+    const int m0 = (r % mt) * BM, n0 = (r / mt) * BN;
+    const int K = offset_of(e + 1) - offset_of(e);
+    const int KT = cdiv(K, BK);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j2 = 0; j2 < NJ; ++j2)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j2][v] = 0.0f;
+    if (KT > 0) {
+      // the tile's first slice: landed and visible to every wave
+      wait_for(consumed);
+      barrier();
+      load_frags(ring + (consumed & 3) * STAGE, 0, af0, bf0);
+      const bool tail = (K % BK) != 0;
+      for (int s = 0; s < KT; ++s, ++consumed) {
+        const bf16_t* cur = ring + (consumed & 3) * STAGE;
+        const bf16_t* nxt = ring + ((consumed + 1) & 3) * STAGE;
+        const bool last = s == KT - 1;
+        const bool tail_step = __builtin_amdgcn_readfirstlane(tail && last);
+        if (tail_step) mask_tail(af0, s, 0, K);
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags(cur, 1, af1, bf1);
+        mma(af0, bf0);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+        if (consumed + 1 < issued) wait_for(consumed + 1);
+        barrier();
+        issue_one();                            // slice consumed + 3, of this tile or a later one
+        if (tail_step) mask_tail(af1, s, 1, K);
+        __builtin_amdgcn_sched_barrier(0);
+        // (in the tile's last step these read the next slice in the stream,
+        // or a stale stage: one code path for every step, since a branch
+        // here made the compiler copy the accumulators through scratch; the
+        // next tile reads its first fragments again after its barrier)
+        load_frags(nxt, 0, af0, bf0);
+        mma(af1, bf1);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    epilogue(e, m0, n0);
+  }
+  wait_vmcnt<0>();
+}
+
 static bool bwd_uses_dma(const moe_shape& s) {
   return s.dtype == MOE_DTYPE_BF16 && s.d % 256 == 0 && s.F % 256 == 0;
 }
@@ -853,9 +1176,35 @@ static bool bwd_uses_mfma(const moe_shape& s) {
   return s.dtype == MOE_DTYPE_BF16 && s.d % 128 == 0 && s.F % 128 == 0;
 }
 
+// Compute units of the current device (cached per device; the persistent
+// weight-gradient kernel launches one workgroup per CU).
+static int device_cus() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 // FLAVOR: 0 generic, 1 MFMA with register transposes, 2 direct-to-LDS MFMA
+// (the weight gradients persistent, one workgroup per CU)
 template <int MODE, typename T, int FLAVOR>
 static void launch_bwd_gemm(const moe_shape& s, const BwdArgs& a, hipStream_t st) {
+  if constexpr (FLAVOR == 2 && (MODE == BWD_WD || MODE == BWD_WGU)) {
+    if (s.E > 0) {
+      const long long tiles = MODE == BWD_WD ? (long long)s.E * cdiv(s.d, 256) * cdiv(s.F, 256)
+                                             : (long long)s.E * cdiv(2 * s.F, 256) * cdiv(s.d, 256);
+      const long long cap = ((tiles + 7) / 8) * 8;
+      const int grid = (int)std::min<long long>(cap, device_cus() / 8 * 8);
+      bwd_wgrad_kernel<MODE><<<grid, 512, 0, st>>>(a);
+    }
+    return;
+  }
   constexpr int BM = FLAVOR == 2 ? 256 : FLAVOR == 1 ? 128 : 64;
   constexpr int BN = BM;
   const long long R = (long long)s.T * s.k;

@@ -29,10 +29,23 @@
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "moe_common.h"
 
 namespace moe {
+
+// fn(integral_constant<int, 0>{}), ..., fn(integral_constant<int, N - 1>{}):
+// a loop the compiler cannot leave rolled (a rolled loop over accumulator
+// blocks indexes them at run time and moves them to scratch memory).
+template <typename Fn, int... I>
+__device__ __forceinline__ void static_for_impl(Fn& fn, std::integer_sequence<int, I...>) {
+  (fn(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& fn) {
+  static_for_impl(fn, std::make_integer_sequence<int, N>{});
+}
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));

@@ -48,15 +48,6 @@ __device__ __forceinline__ uint32_t opaque_u32(uint32_t v) {
 // by here.
 __device__ __forceinline__ void use_acc(const f32x16_t& a) { asm volatile("" ::"v"(a)); }
 
-// fn(integral_constant<int, 0>{}), ..., fn(integral_constant<int, N - 1>{}).
-template <typename Fn, int... I>
-__device__ __forceinline__ void static_for_impl(Fn& fn, std::integer_sequence<int, I...>) {
-  (fn(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename Fn>
-__device__ __forceinline__ void static_for(Fn&& fn) {
-  static_for_impl(fn, std::make_integer_sequence<int, N>{});
-}
 
 // FC1: 256 rows x (128 gate + 128 up) columns; FC2: 256 x 256; 8 waves.
 constexpr int MX_FC1_BM = 256, MX_FC1_BN = 128;

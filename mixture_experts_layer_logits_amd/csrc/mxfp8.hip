@@ -912,16 +912,19 @@ pad_offsets_kernel(const int32_t* __restrict__ offsets, int E, int32_t* __restri
   for (int i = g; i <= E; i += 1024) poffs[i] = (i == 0) ? 0 : s[i - 1];
 }
 
-// A workgroup takes 32 padded rows x 64 columns through LDS; 4 lanes per
-// column quantise 8 rows each (as mx_quantize_t_kernel does for weights).
-// Row blocks past poffs[E] exit: the GEMM reads only the padded rows of
-// each expert.
+// A workgroup takes 128 padded rows x 64 columns (one expert's rows: the
+// padded counts are multiples of 128) through LDS, 16-byte loads of whole
+// 128-byte row segments; thread (block b, column c) then quantises the 32
+// rows of block b of column c, so each column's 128 codes leave as one full
+// 128-byte line written by four neighbouring threads.  Callers pass cols a
+// multiple of 8.  Row blocks past poffs[E] exit: the GEMM reads only the
+// padded rows of each expert.
 __global__ void __launch_bounds__(256)
 mx_quantize_tok_kernel(const bf16_t* __restrict__ src, int cols,
                        const int32_t* __restrict__ offsets, const int32_t* __restrict__ poffs,
                        int E, long long ldq, uint8_t* __restrict__ q, uint8_t* __restrict__ sq) {
-  __shared__ float tile[32][65];
-  const int P0 = blockIdx.y * 32, c0 = blockIdx.x * 64;
+  __shared__ bf16_t tile[128][64 + 8];          // rows of 144 bytes: 16-byte aligned
+  const int P0 = blockIdx.y * 128, c0 = blockIdx.x * 64;
   if (P0 >= poffs[E]) return;
   // the expert of padded row P0: largest e with poffs[e] <= P0
   int lo = 0, hi = E - 1;
@@ -931,34 +934,40 @@ mx_quantize_tok_kernel(const bf16_t* __restrict__ src, int cols,
   }
   const int r0 = offsets[lo] + (P0 - poffs[lo]);
   const int rend = offsets[lo + 1];
-  for (int i = threadIdx.x; i < 32 * 64; i += 256) {
-    const int rr = i >> 6, cc = i & 63;
-    const int c = c0 + cc, r = r0 + rr;
-    tile[rr][cc] = (c < cols && r < rend) ? to_f32<bf16_t>(src[(long long)r * cols + c]) : 0.0f;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int rr = (tid >> 3) + 32 * u, ch = tid & 7;
+    const int r = r0 + rr, c = c0 + 8 * ch;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);      // rows past the expert and columns past cols: 0
+    if (r < rend && c < cols) v = *reinterpret_cast<const uint4*>(src + (long long)r * cols + c);
+    *reinterpret_cast<uint4*>(&tile[rr][8 * ch]) = v;
   }
   __syncthreads();
-  const int cc = threadIdx.x >> 2, part = threadIdx.x & 3;
-  float v[8];
+  const int cc = tid & 63, b = tid >> 6;
+  float v[32];
   float amax = 0.0f;
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    v[p] = tile[8 * part + p][cc];
+  for (int p = 0; p < 32; ++p) {
+    v[p] = to_f32<bf16_t>(tile[32 * b + p][cc]);
     amax = fmaxf(amax, fabsf(v[p]));
   }
-  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
   const int sx = mx_scale_exp(amax);
   const float inv = mx_inv_scale(sx);
-  uint32_t lo32 = 0, hi32 = 0;
+  uint32_t w[8];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    lo32 |= e4m3_code(v[p] * inv) << (8 * p);
-    hi32 |= e4m3_code(v[4 + p] * inv) << (8 * p);
+  for (int g = 0; g < 8; ++g) {
+    uint32_t x = 0;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) x |= e4m3_code(v[4 * g + p] * inv) << (8 * p);
+    w[g] = x;
   }
   const int c = c0 + cc;
   if (c < cols) {
-    *reinterpret_cast<uint2*>(q + (long long)c * ldq + P0 + 8 * part) = make_uint2(lo32, hi32);
-    if (part == 0) sq[(long long)c * (ldq / 32) + P0 / 32] = (uint8_t)(sx + 127);
+    uint4* dst = reinterpret_cast<uint4*>(q + (long long)c * ldq + P0 + 32 * b);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    sq[(long long)c * (ldq / 32) + P0 / 32 + b] = (uint8_t)(sx + 127);
   }
 }
 
@@ -1016,7 +1025,7 @@ gemm_mx_wgrad_kernel(const GemmArgs args, const MxScales sc, const MxBwd bw) {
 hipError_t launch_mx_wgrad(const MxWgrad& g, hipStream_t st) {
   if (g.E == 0) return hipSuccess;
   pad_offsets_kernel<<<1, 1024, 0, st>>>(g.offsets, g.E, g.poffs);
-  const unsigned yb = (unsigned)(g.wrows / 32);
+  const unsigned yb = (unsigned)(g.wrows / 128);   // wrows: a multiple of 128
   mx_quantize_tok_kernel<<<dim3(cdiv(g.M, 64), yb), 256, 0, st>>>(
       static_cast<const bf16_t*>(g.A), g.M, g.offsets, g.poffs, g.E, g.wrows, g.qa, g.sa);
   mx_quantize_tok_kernel<<<dim3(cdiv(g.N, 64), yb), 256, 0, st>>>(

@@ -108,9 +108,9 @@ PHASE_KERNELS = {
     "fc2": "gemm_bf16_mfma_kernel<256, 256, 1, 0, 4, 2, 1> (FC2) + splitk_reduce_kernel",
     "bwd_dispatch": "bwd_dispatch_kernel<unsigned short>",
     "bwd_dh": "bwd_dma_kernel<0> (dh + SwiGLU backward)",
-    "bwd_dw_down": "bwd_dma_kernel<2> (dW_down)",
+    "bwd_dw_down": "bwd_wgrad_kernel<2> (dW_down, persistent)",
     "bwd_dx": "bwd_dma_kernel<1> (dX_perm)",
-    "bwd_dw_gate_up": "bwd_dma_kernel<3> (dW_gate | dW_up)",
+    "bwd_dw_gate_up": "bwd_wgrad_kernel<3> (dW_gate | dW_up, persistent)",
     "bwd_gather": "bwd_gather_kernel<unsigned short>",
 }
 

@@ -254,11 +254,18 @@ struct BwdJob {
   int M_valid, N_valid, K;    // rows of A valid in this tile's group (row modes)
   int m0, n0;
   int row0, e;
+  int cls;                    // 0: BM x BN tile, 1: BM/2 x 2BN tail tile (TAIL decode)
 };
 
-template <int MODE, int BM, int BN, typename T>
+// TAIL (dh and dX of the direct-to-LDS kernel): the tile list was built
+// with tail tiles (schedule_tiles_kernel, tail = 1).  As in the forward's
+// decode, column tiles go in pairs: the expert's full row tiles of columns
+// 2p and 2p + 1, then its tail tile (the last <= BM/2 rows) over the same
+// 2 BN columns, which finds that weight strip still in L2.
+template <int MODE, int BM, int BN, typename T, bool TAIL = false>
 __device__ __forceinline__ bool bwd_decode(const BwdArgs& a, BwdJob<T>& j) {
   const int bid = blockIdx.x;
+  j.cls = 0;
   if (MODE == BWD_DH || MODE == BWD_DX) {
     const int total = a.tiles[a.E];
     const int per = (total + 7) >> 3, slot = bid >> 3;
@@ -272,9 +279,27 @@ __device__ __forceinline__ bool bwd_decode(const BwdArgs& a, BwdJob<T>& j) {
     }
     const int g = lo;
     const int row0 = a.offsets[g], rows = a.offsets[g + 1] - row0;
-    const int mt = cdiv(rows, BM), r = lid - a.tiles[g];
-    j.m0 = (r % mt) * BM;
-    j.n0 = (r / mt) * BN;
+    const int r = lid - a.tiles[g];
+    if (!TAIL) {
+      const int mt = cdiv(rows, BM);
+      j.m0 = (r % mt) * BM;
+      j.n0 = (r / mt) * BN;
+    } else {
+      const int mt = group_full_rows(rows, BM, 1);
+      const int ht = (mt * BM < rows) ? 1 : 0;
+      const int nt = cdiv(MODE == BWD_DH ? a.F : a.d, BN);
+      const int per = 2 * mt + ht;
+      const int p = r / per, q = r - p * per;
+      const int pair_cols = (nt - 2 * p) < 2 ? (nt - 2 * p) : 2;
+      if (q < pair_cols * mt) {
+        j.m0 = (q % mt) * BM;
+        j.n0 = (2 * p + q / mt) * BN;
+      } else {
+        j.cls = 1;
+        j.m0 = mt * BM;
+        j.n0 = p * 2 * BN;
+      }
+    }
     j.row0 = row0;
     j.e = g;
     j.M_valid = rows;
@@ -569,87 +594,111 @@ bwd_generic_kernel(const BwdArgs args) {
 }
 
 // ---------------------------------------------------------------------------
-// Backward GEMMs on the forward kernel's structure (256 x 256 tiles, 8 waves
-// of 64 x 128, direct global->LDS loads into a 4-stage ring of 32-wide K
-// slices).  An operand stored M-contiguous (a column operand) keeps its
-// storage order in LDS: 32 k-rows of 512 bytes, 16-byte chunk c of k-row r at
-// position c ^ 4 (r mod 4), so that the four k-rows one transposing read
-// touches fill all 64 banks (with c ^ 2 (r mod 4) rows r and r + 1 shared
-// 16 banks: 2-way conflicts on every fragment read).  Its MFMA fragments come from two transposing
-// LDS reads (ds_read_b64_tr_b16): within each 16-lane group, lane j points at
-// k-row kb + j / 4, columns mb + 4 (j mod 4); lane i then receives the four
-// k-values of column mb + i, which is exactly the k-contiguous fragment a
-// row operand gives with one 16-byte read.  Weight-gradient tiles have
-// K = rows of the expert; the last slice's k-rows past K hold clamped data
-// and are zeroed in the A fragments before use.
+// dh and dX on the forward kernel's structure (256 x 256 tiles, 8 waves of
+// 64 x 128, direct global->LDS loads into a 4-stage ring of 32-wide K
+// slices).  The row operand (dY_perm for dh, dg | du for dX) is read as the
+// forward reads its rows.  The weights are the column operand: stored
+// N-contiguous, they keep that order in LDS, 32 k-rows of 512 bytes (256
+// columns), 16-byte chunk c of k-row r at position c ^ 4 (r mod 4), so the
+// four k-rows one transposing read touches fill all 64 banks (with
+// c ^ 2 (r mod 4), rows r and r + 1 shared 16 banks).  Its MFMA fragments
+// come from two transposing LDS reads (ds_read_b64_tr_b16): within each
+// 16-lane group, lane j points at k-row kb + j / 4, columns mb + 4 (j mod 4);
+// lane i then receives the four k-values of column mb + i, the k-contiguous
+// fragment a row operand gives with one 16-byte read.
+//
+// Tail tiles, as in the forward: an expert whose last t rows number at most
+// 128 gets 128-row x 512-column tiles for them instead of half-empty
+// 256-row tiles (Qwen3-235B shape: 23% of the MFMA work was padding rows
+// with 256-row tiles only, 12% with tail tiles).  Their waves are laid out
+// 2 x 4, each keeping its 64 x 128 block; a stage then holds the two
+// 256-column halves of the weights (16 KiB each) and 128 operand rows
+// (8 KiB), 40 KiB, and each wave loads 5 blocks of 1 KiB instead of 4.
+// Columns past N (an odd number of 256-column tiles) are clamped on load
+// and never stored.
 // ---------------------------------------------------------------------------
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 template <int MODE>
 __global__ void __launch_bounds__(512)
 bwd_dma_kernel(const BwdArgs args) {
-  constexpr int BM = 256, BN = 256, BK = 32, WM = 4, WN = 2;
-  constexpr int WTM = BM / WM, WTN = BN / WN, MI = WTM / 32, NJ = WTN / 32;
-  constexpr bool A_COL = (MODE == BWD_WD || MODE == BWD_WGU);
-  constexpr int OPB = BM * BK * 2;              // bytes of one operand per stage (16 KiB)
-  constexpr int STAGE = 2 * OPB / 2;            // elements per stage (A then B)
-  constexpr int BPW = 4;                        // 1 KiB load blocks per wave per stage
+  static_assert(MODE == BWD_DH || MODE == BWD_DX, "dh and dX only");
+  constexpr int BM = 256, BN = 256, BK = 32, WTM = 64, WTN = 128;
+  constexpr int MI = WTM / 32, NJ = WTN / 32;
+  constexpr int OPB = BM * BK * 2;              // bytes of 256 rows or columns per stage (16 KiB)
+  constexpr int STAGE_B = OPB * 5 / 2;          // bytes per stage: 40 KiB (a tail tile's)
+  constexpr int STAGE = STAGE_B / 2;            // ... in bf16 elements
+  constexpr int BPWX = 5;                       // 1 KiB load blocks per wave per stage, at most
   __shared__ __attribute__((aligned(1024))) bf16_t st0[STAGE];
   __shared__ __attribute__((aligned(1024))) bf16_t st1[STAGE];
   __shared__ __attribute__((aligned(1024))) bf16_t st2[STAGE];
   __shared__ __attribute__((aligned(1024))) bf16_t st3[STAGE];
 
   BwdJob<bf16_t> job;
-  if (!bwd_decode<MODE, BM, BN>(args, job)) return;
+  if (!bwd_decode<MODE, BM, BN, bf16_t, true>(args, job)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WN, wn = wave % WN;
+  const bool tail = __builtin_amdgcn_readfirstlane(job.cls) != 0;
+  const int wn_count = tail ? 4 : 2;
+  const int wm = wave / wn_count, wn = wave % wn_count;
   const int K = job.K;
   const int KT = cdiv(K, BK);
+  // byte offsets within a stage: full tiles hold A (256 rows) then B (256
+  // columns); tail tiles B's two halves, then A (128 rows)
+  const int bpw = tail ? 5 : 4;
+  const int a_off = tail ? 2 * OPB : 0;
+  const int b_off = tail ? (wn >> 1) * OPB : OPB;
+  const int bcol0 = (tail ? (wn & 1) : wn) * WTN;   // this wave's first column within its B half
 
-  // ---- loads: waves 0-3 fill A (16 blocks), waves 4-7 fill B ------------
-  const bool load_a = wave < 4;
-  const int blk0 = (wave & 3) * BPW;            // first block within the operand
-  const bool col = load_a ? A_COL : true;       // B is a column operand in every mode
-  const bf16_t* src0 = load_a ? job.A : job.B0;
-  const bf16_t* src1 = load_a ? job.A : job.B1; // DX: rows k >= kswitch read B1
-  const long long ld = load_a ? job.lda : job.ldb;
-  const int mn0 = load_a ? job.m0 : job.n0;
-  uint32_t g_off[BPW];                          // byte offsets, k-independent part
-  int krow_l[BPW];                              // column operands: k-row of this lane
+  // ---- loads: block gb = wave * bpw + j of the stage ----------------------
+  // full: gb < 16 A rows 16 gb.., else B block gb - 16; tail: gb < 8 A rows
+  // 16 gb.., else B half (gb - 8) / 16, block (gb - 8) % 16.  A row blocks
+  // hold 16 rows x 64 bytes, B blocks two k-rows x 512 bytes.
+  const int n_a = tail ? 8 : 16;
+  uint32_t g_off[BPWX];                         // byte offsets, k-independent part
+  int krow_l[BPWX];                             // B blocks: k-row of this lane (-1: an A block)
+  uint32_t lds_b[BPWX];                         // byte offset of the block in a stage
 #pragma unroll
-  for (int j = 0; j < BPW; ++j) {
-    const int b = blk0 + j;
-    if (col) {
-      const int kr = 2 * b + (lane >> 5);        // k-row within the slice
-      const int pos = lane & 31;
-      const int c = pos ^ (4 * (kr & 3));
-      krow_l[j] = kr;
-      g_off[j] = (uint32_t)(mn0 + c * 8) * 2u;
-    } else {
-      int r = mn0 + 16 * b + (lane >> 2);        // row operand (A of DH / DX)
+  for (int j = 0; j < BPWX; ++j) {
+    const int gb = wave * bpw + (j < bpw ? j : bpw - 1);
+    if (gb < n_a) {
+      int r = job.m0 + 16 * gb + (lane >> 2);
       r = r < job.M_valid ? r : job.M_valid - 1;
       const int c = (lane & 3) ^ swz(lane >> 2);
-      krow_l[j] = 0;
-      g_off[j] = (uint32_t)(r * (int)ld + c * 8) * 2u;
+      krow_l[j] = -1;
+      g_off[j] = (uint32_t)(r * (int)job.lda + c * 8) * 2u;
+      lds_b[j] = (uint32_t)(a_off + gb * 1024);
+    } else {
+      const int bb = gb - n_a;                   // 0..15 (full) or 0..31 (tail)
+      const int half = bb >> 4, blk = bb & 15;
+      const int kr = 2 * blk + (lane >> 5);
+      const int c = (lane & 31) ^ (4 * (kr & 3));
+      int col = job.n0 + half * BN + c * 8;
+      col = col < job.N_valid - 8 ? col : job.N_valid - 8;   // never stored
+      krow_l[j] = kr;
+      g_off[j] = (uint32_t)col * 2u;
+      lds_b[j] = (uint32_t)((tail ? 0 : OPB) + bb * 1024);
     }
   }
-  const int lds_op = load_a ? 0 : OPB;           // byte offset of the operand in a stage
-  auto dma = [&](bf16_t* stage, int k0) {
-    const bf16_t* srcb = (k0 >= job.kswitch) ? src1 : src0;
-    const char* base = reinterpret_cast<const char*>(srcb) + (col ? 0 : (size_t)k0 * 2);
+  auto dma = [&](bf16_t* stage, int k0, auto nblk_c) {
+    constexpr int NBLK = decltype(nblk_c)::value;
+    const bf16_t* srcb = (k0 >= job.kswitch) ? job.B1 : job.B0;
+    const char* base_a = reinterpret_cast<const char*>(job.A) + (size_t)k0 * 2;
+    const char* base_b = reinterpret_cast<const char*>(srcb);
+    const uint32_t st_lds = (uint32_t)(uintptr_t)MOE_AS_LDS(reinterpret_cast<char*>(stage));
 #pragma unroll
-    for (int j = 0; j < BPW; ++j) {
-      uint32_t off = g_off[j];
-      if (col) {
+    for (int j = 0; j < NBLK; ++j) {
+      const uint32_t lds = st_lds + lds_b[j];
+      if (krow_l[j] < 0) {
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :: "s"(lds), "v"(g_off[j]), "s"(base_a) : "memory");
+      } else {
         int kr = k0 + krow_l[j];
-        kr = kr < K ? kr : K - 1;                 // clamp the tail (zeroed later)
-        off += (uint32_t)(kr * (int)ld) * 2u;
+        kr = kr < K ? kr : K - 1;
+        const uint32_t off = g_off[j] + (uint32_t)(kr * (int)job.ldb) * 2u;
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :: "s"(lds), "v"(off), "s"(base_b) : "memory");
       }
-      const uint32_t lds = (uint32_t)(uintptr_t)MOE_AS_LDS(reinterpret_cast<char*>(stage) + lds_op +
-                                                           (blk0 + j) * 1024);
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                   :: "s"(lds), "v"(off), "s"(base) : "memory");
     }
   };
 
@@ -674,19 +723,15 @@ bwd_dma_kernel(const BwdArgs args) {
     return __builtin_bit_cast(bf16x8_t, v);
   };
   auto load_frags = [&](const bf16_t* stage, int kk, bf16x8_t (&af)[MI], bf16x8_t (&bfr)[NJ]) {
-    const char* sa = reinterpret_cast<const char*>(stage);
-    const char* sb = sa + OPB;
+    const char* sa = reinterpret_cast<const char*>(stage) + a_off;
+    const char* sb = reinterpret_cast<const char*>(stage) + b_off;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-      if constexpr (A_COL) {
-        af[i] = col_frag(sa, kk, wm * WTM + i * 32);
-      } else {
-        const int off = (wm * WTM + i * 32 + frag_row) * BK + (kk ? kpos1 : kpos0);
-        af[i] = *reinterpret_cast<const bf16x8_t*>(reinterpret_cast<const bf16_t*>(sa) + off);
-      }
+      const int off = (wm * WTM + i * 32 + frag_row) * BK + (kk ? kpos1 : kpos0);
+      af[i] = *reinterpret_cast<const bf16x8_t*>(reinterpret_cast<const bf16_t*>(sa) + off);
     }
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) bfr[j] = col_frag(sb, kk, wn * WTN + j * 32);
+    for (int j = 0; j < NJ; ++j) bfr[j] = col_frag(sb, kk, bcol0 + j * 32);
   };
   f32x16_t acc[MI][NJ];
 #pragma unroll
@@ -702,15 +747,6 @@ bwd_dma_kernel(const BwdArgs args) {
       for (int j = 0; j < NJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
   };
-  // zero the k-values >= K held by this lane in sub-step kk of slice s
-  auto mask_tail = [&](bf16x8_t (&af)[MI], int s, int kk) {
-    const int k0 = s * BK + kk * 16 + 8 * (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (k0 + e >= K) af[i][e] = (__bf16)0.0f;
-  };
   auto barrier = [&]() {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
@@ -718,19 +754,11 @@ bwd_dma_kernel(const BwdArgs args) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto wait_slice = [&](int ready, int issued) {
-    const int younger = issued - 1 - ready;
-    if (younger >= 2) wait_vmcnt<2 * BPW>();
-    else if (younger == 1) wait_vmcnt<BPW>();
-    else wait_vmcnt<0>();
-  };
-  const bool tail = A_COL && (K % BK) != 0;
-  bf16x8_t af0[MI], af1[MI], bf0[NJ], bf1[NJ];
   // Fragment reads spread between the MFMAs of each half-step (the first
   // reads of a half go ahead of its first MFMA, then one read per MFMA).
   // The last step also reads the (unused) next stage so that reads and
-  // MFMAs stay in one block; the tail masks are applied before each block.
-  constexpr int NREAD = (A_COL ? 2 * MI : MI) + 2 * NJ;   // LDS reads per half-step
+  // MFMAs stay in one block.
+  constexpr int NREAD = MI + 2 * NJ;            // LDS reads per half-step
   auto interleave = [&]() {
     __builtin_amdgcn_sched_group_barrier(0x100, NREAD - (MI * NJ - 1), 0);
 #pragma unroll
@@ -740,56 +768,67 @@ bwd_dma_kernel(const BwdArgs args) {
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   };
-  auto step = [&](const bf16_t* cur, const bf16_t* next, bf16_t* refill, int s) {
-    if (tail && s == KT - 1) mask_tail(af0, s, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_frags(cur, 1, af1, bf1);
-    mma(af0, bf0);
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
-    if (s + 1 < KT) wait_slice(s + 1, s + 3 < KT ? s + 3 : KT);
-    barrier();
-    if (s + 3 < KT) dma(refill, (s + 3) * BK);
-    if (tail && s == KT - 1) mask_tail(af1, s, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    load_frags(next, 0, af0, bf0);
-    mma(af1, bf1);
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  if (KT > 0) {
-    dma(st0, 0);
-    if (KT > 1) dma(st1, BK);
-    if (KT > 2) dma(st2, 2 * BK);
-    wait_slice(0, KT < 3 ? KT : 3);
-    barrier();
-    load_frags(st0, 0, af0, bf0);
-    int kt = 0;
-    for (; kt + 4 <= KT; kt += 4) {
-      step(st0, st1, st3, kt);
-      step(st1, st2, st0, kt + 1);
-      step(st2, st3, st1, kt + 2);
-      step(st3, st0, st2, kt + 3);
+  // The K loop exists once per load-block count (4 or 5 per wave): the
+  // vmcnt waits count this wave's loads per slice.
+  auto k_loop = [&](auto nblk_c) {
+    constexpr int NBLK = decltype(nblk_c)::value;
+    auto wait_slice = [&](int ready, int issued) {
+      const int younger = issued - 1 - ready;
+      if (younger >= 2) wait_vmcnt<2 * NBLK>();
+      else if (younger == 1) wait_vmcnt<NBLK>();
+      else wait_vmcnt<0>();
+    };
+    bf16x8_t af0[MI], af1[MI], bf0[NJ], bf1[NJ];
+    auto step = [&](const bf16_t* cur, const bf16_t* next, bf16_t* refill, int s) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_frags(cur, 1, af1, bf1);
+      mma(af0, bf0);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + 1 < KT) wait_slice(s + 1, s + 3 < KT ? s + 3 : KT);
+      barrier();
+      if (s + 3 < KT) dma(refill, (s + 3) * BK, nblk_c);
+      __builtin_amdgcn_sched_barrier(0);
+      load_frags(next, 0, af0, bf0);
+      mma(af1, bf1);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (KT > 0) {
+      dma(st0, 0, nblk_c);
+      if (KT > 1) dma(st1, BK, nblk_c);
+      if (KT > 2) dma(st2, 2 * BK, nblk_c);
+      wait_slice(0, KT < 3 ? KT : 3);
+      barrier();
+      load_frags(st0, 0, af0, bf0);
+      int kt = 0;
+      for (; kt + 4 <= KT; kt += 4) {
+        step(st0, st1, st3, kt);
+        step(st1, st2, st0, kt + 1);
+        step(st2, st3, st1, kt + 2);
+        step(st3, st0, st2, kt + 3);
+      }
+      if (kt < KT) step(st0, st1, st3, kt);
+      if (kt + 1 < KT) step(st1, st2, st0, kt + 1);
+      if (kt + 2 < KT) step(st2, st3, st1, kt + 2);
     }
-    if (kt < KT) step(st0, st1, st3, kt);
-    if (kt + 1 < KT) step(st1, st2, st0, kt + 1);
-    if (kt + 2 < KT) step(st2, st3, st1, kt + 2);
-  }
+  };
+  if (tail) k_loop(std::integral_constant<int, 5>{});
+  else k_loop(std::integral_constant<int, 4>{});
 
   {
     // Outputs go out through LDS: in the accumulator layout a store
     // instruction scatters 16-byte pieces over 32 rows (which cost several
-    // times their bytes in write traffic for the bf16 outputs, and store
-    // issue time for the fp32 weight gradients: 7.9 -> 7.3 ms for the
-    // Qwen3-235B backward once staged); re-read row-contiguous, every 16 (DX)
-    // or 32 (DH, and the weight gradients) lanes write whole runs of one row.
-    // The ring is free once every wave has passed this barrier; each wave
-    // stages through its own 16 KiB.
+    // times their bytes in write traffic); re-read row-contiguous, every 16
+    // (DX) or 32 (DH) lanes write whole runs of one row.  The ring is free
+    // once every wave has passed this barrier; each wave stages through its
+    // own 16 KiB (the first 32 KiB of each stage).
     barrier();
     char* buf = reinterpret_cast<char*>((wave >> 1) == 0 ? st0 : (wave >> 1) == 1 ? st1
                                         : (wave >> 1) == 2 ? st2 : st3) + (wave & 1) * 16384;
     const int rbase = job.m0 + wm * WTM;          // first row of this wave (within the group)
     const int cbase = job.n0 + wn * WTN;          // first column of this wave
+    if (cbase >= job.N_valid) return;             // a tail tile's columns past N
     if constexpr (MODE == BWD_DX) {
       // 64 rows x 128 bf16 columns; 16-byte chunk c of row r at c ^ (r mod 16)
 #pragma unroll
@@ -814,11 +853,9 @@ bwd_dma_kernel(const BwdArgs args) {
           *reinterpret_cast<uint4*>(out + (long long)(rbase + r) * args.d + ch * 8) = v;
       }
     } else {
-      // dh (or a weight gradient) in fp32, 32 rows x 128 columns per pass;
-      // 16-byte chunk c of row r at c ^ r.  Each lane then owns 4
-      // consecutive columns of one row: for dh it applies the SwiGLU
-      // backward with coalesced g, u loads and stores, for a weight gradient
-      // it stores them.
+      // dh in fp32, 32 rows x 128 columns per pass; 16-byte chunk c of row r
+      // at c ^ r.  Each lane then owns 4 consecutive columns of one row and
+      // applies the SwiGLU backward with coalesced g, u loads and stores.
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
 #pragma unroll
@@ -1203,21 +1240,22 @@ static void launch_bwd_gemm(const moe_shape& s, const BwdArgs& a, hipStream_t st
       const int grid = (int)std::min<long long>(cap, device_cus() / 8 * 8);
       bwd_wgrad_kernel<MODE><<<grid, 512, 0, st>>>(a);
     }
-    return;
+  } else {
+    constexpr int BM = FLAVOR == 2 ? 256 : FLAVOR == 1 ? 128 : 64;
+    constexpr int BN = BM;
+    const long long R = (long long)s.T * s.k;
+    // (with tail tiles a group's tiles are at most its 256-row tiles' count)
+    long long tiles;
+    if (MODE == BWD_DH) tiles = (cdiv((int)R, BM) + s.E) * (long long)cdiv(s.F, BN);
+    else if (MODE == BWD_DX) tiles = (cdiv((int)R, BM) + s.E) * (long long)cdiv(s.d, BN);
+    else if (MODE == BWD_WD) tiles = (long long)s.E * cdiv(s.d, BM) * cdiv(s.F, BN);
+    else tiles = (long long)s.E * cdiv(2 * s.F, BM) * cdiv(s.d, BN);
+    const int grid = (int)(((tiles + 7) / 8) * 8);
+    if (grid == 0) return;
+    if constexpr (FLAVOR == 2) bwd_dma_kernel<MODE><<<grid, 512, 0, st>>>(a);
+    else if constexpr (FLAVOR == 1) bwd_mfma_kernel<MODE><<<grid, 256, 0, st>>>(a);
+    else bwd_generic_kernel<MODE, T><<<grid, 256, 0, st>>>(a);
   }
-  constexpr int BM = FLAVOR == 2 ? 256 : FLAVOR == 1 ? 128 : 64;
-  constexpr int BN = BM;
-  const long long R = (long long)s.T * s.k;
-  long long tiles;
-  if (MODE == BWD_DH) tiles = (cdiv((int)R, BM) + s.E) * (long long)cdiv(s.F, BN);
-  else if (MODE == BWD_DX) tiles = (cdiv((int)R, BM) + s.E) * (long long)cdiv(s.d, BN);
-  else if (MODE == BWD_WD) tiles = (long long)s.E * cdiv(s.d, BM) * cdiv(s.F, BN);
-  else tiles = (long long)s.E * cdiv(2 * s.F, BM) * cdiv(s.d, BN);
-  const int grid = (int)(((tiles + 7) / 8) * 8);
-  if (grid == 0) return;
-  if constexpr (FLAVOR == 2) bwd_dma_kernel<MODE><<<grid, 512, 0, st>>>(a);
-  else if constexpr (FLAVOR == 1) bwd_mfma_kernel<MODE><<<grid, 256, 0, st>>>(a);
-  else bwd_generic_kernel<MODE, T><<<grid, 256, 0, st>>>(a);
 }
 
 // One backward GEMM launch, bracketed by its phase events when `marks`.
@@ -1236,7 +1274,7 @@ static hipError_t run_backward(const moe_shape& s, BwdArgs& a, const BwdWs& ws, 
   constexpr int BM = FLAVOR == 2 ? 256 : FLAVOR == 1 ? 128 : 64, BN = BM;
   // tile prefixes of the two row-grouped GEMMs (N = F for dh, N = d for dX)
   schedule_tiles_kernel<<<1, 1024, 0, st>>>(a.offsets, s.E, BM, cdiv(s.F, BN), ws.tiles, BM,
-                                            cdiv(s.d, BN), ws.tiles2, 0);
+                                            cdiv(s.d, BN), ws.tiles2, FLAVOR == 2 ? 1 : 0);
   a.tiles = ws.tiles;
   launch_bwd_phase<BWD_DH, T, FLAVOR>(s, a, st, marks);
   launch_bwd_phase<BWD_WD, T, FLAVOR>(s, a, st, marks);

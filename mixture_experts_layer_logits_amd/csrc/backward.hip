@@ -903,6 +903,21 @@ bwd_dma_kernel(const BwdArgs args) {
 // for one issued after them does: each wave counts the memory operations it
 // issued after the slice it waits for.
 // ---------------------------------------------------------------------------
+// Tile r of an expert's mt x nt weight-gradient grid: m-tiles go in groups
+// of gm (the last may be smaller); within a group m runs fastest, then n, and
+// the n direction alternates from group to group.  The tiles that run
+// together on an XCD then form a gm x (slots / gm) block of the grid, and
+// consecutive blocks share one operand's columns (a serpentine), which the
+// XCD's L2 still holds.
+__device__ __forceinline__ void wgrad_tile_mn(int r, int mt, int nt, int gm, int& mi, int& ni) {
+  const int gi = r / (gm * nt);
+  const int q = r - gi * gm * nt;
+  const int gsz = min(gm, mt - gi * gm);
+  const int nq = q / gsz;
+  mi = gi * gm + (q - nq * gsz);
+  ni = (gi & 1) ? nt - 1 - nq : nq;
+}
+
 template <int MODE>
 __global__ void __launch_bounds__(512)
 bwd_wgrad_kernel(const BwdArgs args) {
@@ -924,6 +939,10 @@ bwd_wgrad_kernel(const BwdArgs args) {
   // range of the tile list; its workgroups interleave over that range, so
   // the tiles running at one time on an XCD are neighbours sharing operands
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslot = gridDim.x >> 3;
+  // m-group size: the largest power of two with gm^2 <= nslot mt / nt, which
+  // makes the block of concurrent tiles about as wide in m as in n
+  int gm = 1;
+  while (2 * gm <= mt && 4 * gm * gm * nt <= nslot * mt) gm *= 2;
   const int per = (total + 7) >> 3;
   const int t_begin = xcd * per + slot;
   const int t_end = min(total, (xcd + 1) * per);
@@ -975,7 +994,9 @@ bwd_wgrad_kernel(const BwdArgs args) {
       is_K = offset_of(e + 1) - row0;
       if (is_K == 0) continue;
       is_KT = cdiv(is_K, BK);
-      is_mn0 = load_a ? (r % mt) * BM : (r / mt) * BN;
+      int mi, ni;
+      wgrad_tile_mn(r, mt, nt, gm, mi, ni);
+      is_mn0 = load_a ? mi * BM : ni * BN;
       // wave-uniform values the compiler cannot prove uniform: scalar copies
       is_base = uniform_ptr(opnd + (long long)row0 * ld);
       goff0 = lane_off(0, is_mn0, BK);
@@ -1159,7 +1180,9 @@ bwd_wgrad_kernel(const BwdArgs args) {
   bf16x8_t af0[MI], af1[MI], bf0[NJ], bf1[NJ];
   for (int t = t_begin; t < t_end; t += nslot) {
     const int e = t / (mt * nt), r = t - e * (mt * nt);
-    const int m0 = (r % mt) * BM, n0 = (r / mt) * BN;
+    int mi, ni;
+    wgrad_tile_mn(r, mt, nt, gm, mi, ni);
+    const int m0 = mi * BM, n0 = ni * BN;
     const int K = offset_of(e + 1) - offset_of(e);
     const int KT = cdiv(K, BK);
 #pragma unroll

@@ -242,28 +242,50 @@ def test_layer_mxfp8_forward(name):
     assert_close("y", out["y"][torch.as_tensor(ok).cuda()], ref_y[ok], "bf16")
 
 
+# sampled tokens per full-size shape: the oracle's cost is one weight
+# quantisation per expert reached (about 3 s at the DeepSeek-V3 shape, 11 s
+# at Mixtral's), so the 8-expert Mixtral shape takes many more tokens
+MX_FULL_SAMPLE = {"deepseek_v3_t8192": 4, "mixtral_t4096": 32}
+
+
 @pytest.mark.parametrize("name", ["deepseek_v3_t8192", "mixtral_t4096"])
 def test_layer_mxfp8_full_size_sampled(name):
-    """Full-size MXFP8 forward on a few sampled tokens: the oracle runs each
-    expert those tokens reach once, on just their rows."""
+    """Full-size MXFP8 forward: sampled tokens (y_perm rows, y_shared, y), and
+    every row of two whole experts (the heaviest and the median one by the
+    oracle's counts; compared when the routing matches the oracle's bit for
+    bit, so that the oracle's own permutation names the rows).  The oracle
+    runs each expert it needs once, on just the rows needed."""
     cfg = CONFIGS[name]
     _log(f"[mx layer full] {name}")
     inp, layer, out = _mx_layer(cfg)
     idx, w, amb, same = route_and_check(cfg, inp, out)
-    toks = np.array([t for t in sample_tokens(cfg.T, 4) if not amb[t]])
-    x = np64(inp["x"][torch.as_tensor(toks, device="cuda")])
+    toks = np.array([t for t in sample_tokens(cfg.T, MX_FULL_SAMPLE[name]) if not amb[t]])
+    p = O.permute(None, idx, w, cfg.E)
+    counts = np.diff(p["offsets"])
+    order = np.argsort(-counts, kind="stable")
+    whole = [int(order[0]), int(order[np.count_nonzero(counts) // 2])] if same else []
+    _log(f"  {len(toks)} sampled tokens; whole experts {whole} "
+         f"({[int(counts[e]) for e in whole]} rows)")
+    x_all = inp["x"]
     idx_s, w_s = np.asarray(idx)[toks], np.asarray(w)[toks]
     y_rows = np.zeros((len(toks), cfg.k, cfg.d))
-    for e in np.unique(idx_s):
+    for e in sorted(set(np.unique(idx_s).tolist()) | set(whole)):
         sel = np.argwhere(idx_s == e)
-        y_rows[sel[:, 0], sel[:, 1]] = O.swiglu_ffn_mxfp8(
-            x[sel[:, 0]], np64(inp["w_gate"][int(e)]), np64(inp["w_up"][int(e)]),
-            np64(inp["w_down"][int(e)]))["y"]
+        a, b = int(p["offsets"][e]), int(p["offsets"][e + 1])
+        seg = p["row_token"][a:b] if e in whole else np.zeros(0, dtype=np.int64)
+        rows_t = np.concatenate([toks[sel[:, 0]], seg]).astype(np.int64)
+        xe = np64(x_all[torch.as_tensor(rows_t, device="cuda")])
+        ye = O.swiglu_ffn_mxfp8(xe, np64(inp["w_gate"][e]), np64(inp["w_up"][e]),
+                                np64(inp["w_down"][e]))["y"]
+        y_rows[sel[:, 0], sel[:, 1]] = ye[:len(sel)]
+        if e in whole:
+            assert_close(f"y_perm[expert {e}]", out["y_perm"][a:b], ye[len(sel):], "bf16")
     tt = torch.as_tensor(toks, device="cuda")
     rows = out["token_row"][tt].reshape(-1).long()
     assert_close("y_perm[sample]", out["y_perm"][rows], y_rows.reshape(-1, cfg.d), "bf16")
     acc = np.zeros((len(toks), cfg.d))
     if cfg.F_shared:
+        x = np64(x_all[tt])
         ys = O.swiglu_ffn_mxfp8(x, np64(inp["ws_gate"]), np64(inp["ws_up"]),
                                 np64(inp["ws_down"]))["y"]
         assert_close("y_shared[sample]", out["y_shared"][tt], ys, "bf16")
@@ -329,7 +351,7 @@ def test_layer_mxfp8_combined_full_size_sampled():
     out = layer.forward_mxfp8_combined(inp)
     torch.cuda.synchronize()
     idx, w, amb, same = route_and_check(cfg, inp, out)
-    toks = np.array([t for t in sample_tokens(cfg.T, 4) if not amb[t]])
+    toks = np.array([t for t in sample_tokens(cfg.T, 32) if not amb[t]])
     x = np64(inp["x"][torch.as_tensor(toks, device="cuda")])
     idx_s, w_s = np.asarray(idx)[toks], np.asarray(w)[toks]
     acc = np.zeros((len(toks), cfg.d))

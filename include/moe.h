@@ -93,7 +93,9 @@ enum {
  * F_shared >= 0.  n_groups >= 1 divides E, n_groups <= 64,
  * 1 <= topk_groups <= n_groups, topk_groups * (E / n_groups) >= k; a group
  * limit (n_groups > 1) needs score = MOE_SCORE_SIGMOID.  renorm is 0 or 1.
- * wgrad_mx is 0 or 1.  T * k and T * max(d, F) must fit in int32. */
+ * wgrad_mx is 0 or 1.  T * k, T * max(d, 2F, F_shared, E) and F * d must
+ * be below 2^31 (R * d itself is not bounded: routed rows are addressed
+ * with 64-bit offsets). */
 typedef struct moe_shape {
   int32_t T, d, E, k, F;
   int32_t F_shared;

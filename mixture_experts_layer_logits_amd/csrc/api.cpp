@@ -31,9 +31,14 @@ int check_shape(const moe_shape* sp) {
   if (s.dtype != MOE_DTYPE_F32 && s.dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
   if (s.wgrad_dtype != MOE_DTYPE_F32 && s.wgrad_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
   if (s.wgrad_mx != 0 && s.wgrad_mx != 1) return MOE_ERR_INVALID_ARG;
+  // Row indices are int32.  Arrays of R routed rows are addressed with
+  // 64-bit row offsets (the tile kernels fold each load block's first row
+  // into a 64-bit base), so only arrays indexed by absolute token row in
+  // 32 bits (x gathered by the fused permutation, logits) and one expert's
+  // weight matrix bound the products.
   const long long R = (long long)s.T * s.k;
   const long long wide = std::max<long long>({s.d, s.F, s.F_shared, s.E, 2LL * s.F});
-  if (R * wide >= (1LL << 31) || (long long)s.T * wide >= (1LL << 31)) return MOE_ERR_INVALID_ARG;
+  if (R >= (1LL << 31) || (long long)s.T * wide >= (1LL << 31)) return MOE_ERR_INVALID_ARG;
   if ((long long)s.F * s.d >= (1LL << 31)) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
@@ -572,11 +577,8 @@ int moe_ffn_backward_mxfp8(const moe_shape* shape, const void* dy, const void* x
   const moe_shape& s = *shape;
   if (s.dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
   if (s.d % 128 != 0 || s.F % 128 != 0 || s.F_shared % 128 != 0) return MOE_ERR_UNSUPPORTED;
-  // the MXFP8 weight gradients address their quantised operands with 32-bit offsets
-  if (s.wgrad_mx &&
-      (long long)std::max<long long>({s.d, 2LL * s.F, 2LL * s.F_shared}) *
-              (long long)mx_wgrad_rows(s) >= (1LL << 31))
-    return MOE_ERR_UNSUPPORTED;
+  // the MXFP8 weight gradients' padded row count is an int32
+  if (s.wgrad_mx && (long long)mx_wgrad_rows(s) >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
   const long long R = (long long)s.T * s.k;
   const long long wsz = (long long)s.E * s.F * s.d;
   const long long wes = s.wgrad_dtype == MOE_DTYPE_BF16 ? 2 : 4;

@@ -658,15 +658,21 @@ bwd_dma_kernel(const BwdArgs args) {
   uint32_t g_off[BPWX];                         // byte offsets, k-independent part
   int krow_l[BPWX];                             // B blocks: k-row of this lane (-1: an A block)
   uint32_t lds_b[BPWX];                         // byte offset of the block in a stage
+  // A blocks: the block's first row folded into a 64-bit base, so a lane's
+  // 32-bit offset spans at most 16 rows whatever the group's size
+  const char* a_base[BPWX];
 #pragma unroll
   for (int j = 0; j < BPWX; ++j) {
     const int gb = wave * bpw + (j < bpw ? j : bpw - 1);
     if (gb < n_a) {
-      int r = job.m0 + 16 * gb + (lane >> 2);
+      const int rb = job.m0 + 16 * gb;
+      const int r0 = rb < job.M_valid ? rb : job.M_valid - 1;
+      int r = rb + (lane >> 2);
       r = r < job.M_valid ? r : job.M_valid - 1;
       const int c = (lane & 3) ^ swz(lane >> 2);
       krow_l[j] = -1;
-      g_off[j] = (uint32_t)(r * (int)job.lda + c * 8) * 2u;
+      g_off[j] = (uint32_t)((r - r0) * (int)job.lda + c * 8) * 2u;
+      a_base[j] = uniform_ptr(job.A + (long long)r0 * job.lda);
       lds_b[j] = (uint32_t)(a_off + gb * 1024);
     } else {
       const int bb = gb - n_a;                   // 0..15 (full) or 0..31 (tail)
@@ -677,19 +683,20 @@ bwd_dma_kernel(const BwdArgs args) {
       col = col < job.N_valid - 8 ? col : job.N_valid - 8;   // never stored
       krow_l[j] = kr;
       g_off[j] = (uint32_t)col * 2u;
+      a_base[j] = nullptr;
       lds_b[j] = (uint32_t)((tail ? 0 : OPB) + bb * 1024);
     }
   }
   auto dma = [&](bf16_t* stage, int k0, auto nblk_c) {
     constexpr int NBLK = decltype(nblk_c)::value;
     const bf16_t* srcb = (k0 >= job.kswitch) ? job.B1 : job.B0;
-    const char* base_a = reinterpret_cast<const char*>(job.A) + (size_t)k0 * 2;
     const char* base_b = reinterpret_cast<const char*>(srcb);
     const uint32_t st_lds = (uint32_t)(uintptr_t)MOE_AS_LDS(reinterpret_cast<char*>(stage));
 #pragma unroll
     for (int j = 0; j < NBLK; ++j) {
       const uint32_t lds = st_lds + lds_b[j];
       if (krow_l[j] < 0) {
+        const char* base_a = a_base[j] + (size_t)k0 * 2;
         asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                      :: "s"(lds), "v"(g_off[j]), "s"(base_a) : "memory");
       } else {

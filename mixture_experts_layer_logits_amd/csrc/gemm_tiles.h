@@ -378,7 +378,11 @@ gemm_bf16_mfma_kernel(const GemmArgs args) {
   // of the operand that block belongs to and fetches the logical chunk that
   // belongs at position l % 4.
   const int dma_c = (lane & 3) ^ swz(lane >> 2);
-  uint32_t g_off[BPWX];   // byte offsets from the block's operand base (< 2^31)
+  // Each block's first row is folded into its 64-bit base, so a lane's
+  // 32-bit offset spans at most 16 rows whatever the operand's size.  Rows
+  // gathered from x keep the absolute token row (T d < 2^31, checked by the
+  // API).
+  uint32_t g_off[BPWX];
   const char* g_base[BPWX];
 #pragma unroll
   for (int j = 0; j < BPWX; ++j) {
@@ -399,10 +403,16 @@ gemm_bf16_mfma_kernel(const GemmArgs args) {
     }
     int r = rbase + (lane >> 2);
     r = r < rlimit ? r : rlimit - 1;                    // clamp: never stored
-    // fused permutation: a routed row comes straight from its token's row
-    if (row < bmc && job.gather) r = job.gather[r];
-    g_off[j] = (uint32_t)(r * ld + dma_c * 8) * 2u;
-    g_base[j] = uniform_ptr(src);
+    if (row < bmc && job.gather) {
+      // fused permutation: a routed row comes straight from its token's row
+      r = job.gather[r];
+      g_off[j] = (uint32_t)(r * ld + dma_c * 8) * 2u;
+      g_base[j] = uniform_ptr(src);
+    } else {
+      const int r0 = rbase < rlimit ? rbase : rlimit - 1;   // the block's first (clamped) row
+      g_off[j] = (uint32_t)((r - r0) * ld + dma_c * 8) * 2u;
+      g_base[j] = uniform_ptr(src + (long long)r0 * ld);
+    }
   }
   // Issued as inline assembly so that only the explicit vmcnt waits below
   // order these loads (the compiler cannot tell the four stages apart across

@@ -338,9 +338,17 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& args, const MxScales& sc
     }
     int r = rbase + (lane >> 2);
     r = r < rlimit ? r : rlimit - 1;                    // clamp: never stored
-    if (row < BMC && job.gather) r = job.gather[r];
-    g_off[j] = (uint32_t)(r * ld + dma_c * 16);
-    g_base[j] = uniform_ptr(src);
+    if (row < BMC && job.gather) {
+      // gathered token rows keep their absolute offset (T d < 2^31)
+      r = job.gather[r];
+      g_off[j] = (uint32_t)(r * ld + dma_c * 16);
+      g_base[j] = uniform_ptr(src);
+    } else {
+      // the block's first (clamped) row folded into the 64-bit base
+      const int r0 = rbase < rlimit ? rbase : rlimit - 1;
+      g_off[j] = (uint32_t)((r - r0) * ld + dma_c * 16);
+      g_base[j] = uniform_ptr(src + (long long)r0 * ld);
+    }
   }
   // Scale loads: block b = wave * SPW + j (the last block again where the
   // waves have more loads than there are blocks) covers stage rows 64 b ..
@@ -366,10 +374,17 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& args, const MxScales& sc
       rlimit = job.N;
     }
     int r = rbase < rlimit ? rbase : rlimit - 1;
-    if (blk0 < BMC && job.gather) r = job.gather[r];
-    s_off[j] = (uint32_t)(r * kb);
     s_lds[j] = (uint32_t)blk * 64 * SSTR;
-    s_base[j] = uniform_ptr(src);
+    if (blk0 < BMC && job.gather) {
+      r = job.gather[r];
+      s_off[j] = (uint32_t)(r * kb);
+      s_base[j] = uniform_ptr(src);
+    } else {
+      const int rb0 = blk0 < BMC ? job.m0 + blk0 : job.n0 + (blk0 - BMC - ((blk0 - BMC) < BNC ? 0 : BNC));
+      const int r0 = rb0 < rlimit ? rb0 : rlimit - 1;   // the block's first (clamped) row
+      s_off[j] = (uint32_t)((r - r0) * kb);
+      s_base[j] = uniform_ptr(src + (long long)r0 * kb);
+    }
   }
   // Slice kt: its scale loads (SG = 1, or the first slice of a group), then
   // its data loads (inline assembly, so that only the explicit vmcnt waits

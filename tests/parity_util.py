@@ -274,3 +274,52 @@ def route_and_check(cfg, inp, out, max_ambiguous_frac=0.05):
     assert n_amb <= max_ambiguous_frac * max(cfg.T, 1) + 2, \
         f"{n_amb} ambiguous tokens: the check would cover too little"
     return idx, w, amb, same
+
+
+def oracle_sampled_backward(cfg, inp, p, idx, w, logits, toks, experts):
+    """Oracle gradients for sampled tokens (dx, d_gate, d_logits) and whole
+    experts (dW), each expert evaluated on just the rows needed.  Every
+    routed row r of token t, slot j: x_perm[r] = x[t], g | u from the
+    oracle's FC1 on x[t], dY_perm[r] = w[t, j] dy[t] (dispatch_grad)."""
+    prec = prec_of(cfg)
+    rnd = O.rounder(prec)
+    wg, wu, wd = inp["w_gate"], inp["w_up"], inp["w_down"]
+    tr, rt = p["token_row"], p["row_token"]
+
+    def rows_of(tokens, slots, e):
+        """x, saved g | u, y_perm and dY_perm of the routed rows (t, j)."""
+        x = np64(inp["x"][torch.as_tensor(tokens, device="cuda")])
+        f = O.swiglu_ffn(x, np64(wg[e]), np64(wu[e]), np64(wd[e]), prec)
+        gu = np.concatenate([rnd(f["g"]), rnd(f["u"])], axis=1)
+        dy = np64(inp["dy"][torch.as_tensor(tokens, device="cuda")])
+        n = len(tokens)
+        dY = O.dispatch_grad(dy, np.arange(n)[:, None], w[tokens, slots][:, None], n, prec)
+        return x, gu, f["y"], dY, dy
+
+    T, k = len(toks), cfg.k
+    dX = np.zeros((T, k, cfg.d))
+    yp = np.zeros((T, k, cfg.d))
+    for e in np.unique(idx[toks]):
+        ti, sj = np.nonzero(idx[toks] == e)
+        x, gu, y, dY, _ = rows_of(toks[ti], sj, int(e))
+        r = O.expert_backward(dY, x, gu, np64(wg[int(e)]), np64(wu[int(e)]),
+                              np64(wd[int(e)]), prec)
+        dX[ti, sj] = r["dX"]
+        yp[ti, sj] = y
+    dy_s = np64(inp["dy"][torch.as_tensor(toks, device="cuda")])
+    d_gate = O.gate_grad(dy_s, yp.reshape(T * k, cfg.d), np.arange(T * k).reshape(T, k))
+    d_logits = O.router_backward(d_gate, idx[toks], w[toks], logits[toks], cfg.E,
+                                 cfg.score, cfg.renorm, prec)
+    of32 = O.out_f32(prec)
+    out = dict(dx=of32(dX.sum(axis=1)), d_gate=of32(d_gate), d_logits=d_logits, dw={})
+    for e in experts:
+        a, b = int(p["offsets"][e]), int(p["offsets"][e + 1])
+        tokens = rt[a:b].astype(np.int64)
+        slots = np.argmax(tr[tokens] == np.arange(a, b)[:, None], axis=1)
+        if b == a:
+            out["dw"][e] = None
+            continue
+        x, gu, _, dY, _ = rows_of(tokens, slots, e)
+        r = O.expert_backward(dY, x, gu, np64(wg[e]), np64(wu[e]), np64(wd[e]), prec)
+        out["dw"][e] = {key: of32(r[key]) for key in ("dw_gate", "dw_up", "dw_down")}
+    return out

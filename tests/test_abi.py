@@ -63,6 +63,9 @@ BAD_SHAPES = [
     dict(n_groups=8, topk_groups=1, k=8, E=32),  # 1 group of 4 experts < k
     dict(n_groups=2, score=0), dict(score=5), dict(renorm=2), dict(dtype=3),
     dict(k=65, E=128), dict(wgrad_dtype=2), dict(wgrad_mx=2),
+    # T k >= 2^31 routed rows; T d >= 2^31 (x indexed by token in 32 bits);
+    # F d >= 2^31 (one expert's weights)
+    dict(T=1 << 28, k=8, E=8), dict(T=1 << 20, d=1 << 11), dict(F=1 << 16, d=1 << 15),
 ]
 
 
@@ -75,6 +78,17 @@ def test_bad_shapes_are_rejected(bad):
     n = ctypes.c_size_t(0)
     assert L.load().moe_workspace_size(ctypes.byref(s), 0, ctypes.byref(n)) == \
         L.MOE_ERR_INVALID_ARG
+
+
+def test_routed_rows_beyond_int32_elements_are_accepted():
+    """R d itself is not bounded (routed rows are addressed with 64-bit
+    offsets): a DeepSeek-V3-width step of 40000 tokens at k = 8 has
+    R d = 2.29e9 > 2^31 and is a valid shape."""
+    c = CONFIGS["tiny_fp32"].replace(T=40000, d=7168, E=32, k=8, F=256, dtype=1)
+    assert c.T * c.k * c.d >= 1 << 31
+    s = M.make_shape(c)
+    n = ctypes.c_size_t(0)
+    assert L.load().moe_workspace_size(ctypes.byref(s), 0, ctypes.byref(n)) == L.MOE_OK
 
 
 def _fake(addr=0x100000):

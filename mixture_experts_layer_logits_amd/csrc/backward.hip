@@ -889,6 +889,21 @@ bwd_dma_kernel(const BwdArgs args) {
   }
 }
 
+// Tile r of an expert's mt x nt weight-gradient grid: m-tiles go in groups
+// of gm (the last may be smaller); within a group m runs fastest, then n, and
+// the n direction alternates from group to group.  The tiles that run
+// together on an XCD then form a gm x (slots / gm) block of the grid, and
+// consecutive blocks share one operand's columns (a serpentine), which the
+// XCD's L2 still holds.
+__device__ __forceinline__ void wgrad_tile_mn(int r, int mt, int nt, int gm, int& mi, int& ni) {
+  const int gi = r / (gm * nt);
+  const int q = r - gi * gm * nt;
+  const int gsz = min(gm, mt - gi * gm);
+  const int nq = q / gsz;
+  mi = gi * gm + (q - nq * gsz);
+  ni = (gi & 1) ? nt - 1 - nq : nq;
+}
+
 // ---------------------------------------------------------------------------
 // Weight gradients as a persistent kernel.  Each expert's tiles have a short
 // K (its row count: about 512 rows in a Qwen3-235B-shape step), so a
@@ -910,21 +925,6 @@ bwd_dma_kernel(const BwdArgs args) {
 // for one issued after them does: each wave counts the memory operations it
 // issued after the slice it waits for.
 // ---------------------------------------------------------------------------
-// Tile r of an expert's mt x nt weight-gradient grid: m-tiles go in groups
-// of gm (the last may be smaller); within a group m runs fastest, then n, and
-// the n direction alternates from group to group.  The tiles that run
-// together on an XCD then form a gm x (slots / gm) block of the grid, and
-// consecutive blocks share one operand's columns (a serpentine), which the
-// XCD's L2 still holds.
-__device__ __forceinline__ void wgrad_tile_mn(int r, int mt, int nt, int gm, int& mi, int& ni) {
-  const int gi = r / (gm * nt);
-  const int q = r - gi * gm * nt;
-  const int gsz = min(gm, mt - gi * gm);
-  const int nq = q / gsz;
-  mi = gi * gm + (q - nq * gsz);
-  ni = (gi & 1) ? nt - 1 - nq : nq;
-}
-
 template <int MODE>
 __global__ void __launch_bounds__(512)
 bwd_wgrad_kernel(const BwdArgs args) {
@@ -1073,7 +1073,7 @@ bwd_wgrad_kernel(const BwdArgs args) {
     else wait_vmcnt<0>();
   };
 
-  // ---- fragments (as bwd_dma_kernel: both operands are column operands) --
+  // ---- fragments: both operands are column operands (read transposed) ---
   const int frag_row = lane & 31;
   const int tr_row = (8 * (lane >> 5) + ((lane & 15) >> 2)) * 512;
   const int tr_swz = 4 * ((lane & 15) >> 2);

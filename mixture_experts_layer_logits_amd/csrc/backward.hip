@@ -946,10 +946,13 @@ bwd_wgrad_kernel(const BwdArgs args) {
   // range of the tile list; its workgroups interleave over that range, so
   // the tiles running at one time on an XCD are neighbours sharing operands
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslot = gridDim.x >> 3;
-  // m-group size: the largest power of two with gm^2 <= nslot mt / nt, which
-  // makes the block of concurrent tiles about as wide in m as in n
-  int gm = 1;
-  while (2 * gm <= mt && 4 * gm * gm * nt <= nslot * mt) gm *= 2;
+  // m-groups: mt split evenly into the group count nearest mt / sqrt(nslot
+  // mt / nt), which makes the block of concurrent tiles about as wide in m
+  // as in n (Qwen3-235B shape: groups of 6 of dW_gate|up's 12 m-tiles, 2.36
+  // -> 2.33 ms against the 4 of a power-of-two rule; 8 of dW_down's 16)
+  const float gm_target = sqrtf((float)nslot * (float)mt / (float)nt);
+  const int n_groups = max(1, (int)lrintf((float)mt / gm_target));
+  const int gm = (mt + n_groups - 1) / n_groups;
   const int per = (total + 7) >> 3;
   const int t_begin = xcd * per + slot;
   const int t_end = min(total, (xcd + 1) * per);

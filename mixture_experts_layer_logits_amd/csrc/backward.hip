@@ -860,31 +860,85 @@ bwd_dma_kernel(const BwdArgs args) {
           *reinterpret_cast<uint4*>(out + (long long)(rbase + r) * args.d + ch * 8) = v;
       }
     } else {
-      // dh in fp32, 32 rows x 128 columns per pass; 16-byte chunk c of row r
-      // at c ^ r.  Each lane then owns 4 consecutive columns of one row and
-      // applies the SwiGLU backward with coalesced g, u loads and stores.
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
+      // dh in fp32, 32 rows x 128 columns per block; 16-byte chunk c of row r
+      // at c ^ r.  Each lane then owns 4 consecutive columns of one row per
+      // pass and applies the SwiGLU backward with coalesced g, u loads and
+      // dg, du, h stores.  The 32 passes go in groups of 4, and a group's g, u
+      // loads are issued before the previous group's stores: vmcnt counts
+      // loads and stores in issue order, so a load issued after a store
+      // would wait for that store too.
+      constexpr int GR = 4, NGRP = 2 * 32 / (2 * GR);   // 8 groups of 4 passes
+      const int ch = lane & 31;
+      const long long F = args.F;
+      const bf16_t* gu_e = static_cast<const bf16_t*>(args.gu) + (long long)job.row0 * 2 * F;
+      bf16_t* dgu_e = static_cast<bf16_t*>(args.out_dgu) + (long long)job.row0 * 2 * F;
+      bf16_t* h_e = static_cast<bf16_t*>(args.out_h) + (long long)job.row0 * F;
+      auto stage_block = [&](int i) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int ch = j * 8 + 2 * q + (lane >> 5);
-            *reinterpret_cast<float4*>(buf + frag_row * 512 + ((ch ^ frag_row) << 4)) =
+            const int c = j * 8 + 2 * q + (lane >> 5);
+            *reinterpret_cast<float4*>(buf + frag_row * 512 + ((c ^ frag_row) << 4)) =
                 make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                             acc[i][j][4 * q + 3]);
           }
+      };
+      // pass t of block i: row 2 t + lane / 32 of the block
+      auto row_of = [&](int grp, int u) { return rbase + (grp >> 2) * 32 + 2 * ((grp & 3) * GR + u) + (lane >> 5); };
+      uint2 gq[2][GR], uq[2][GR];
+      auto load_gu = [&](int grp, uint2 (&g)[GR], uint2 (&uu)[GR]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const int r = 2 * t + (lane >> 5), ch = lane & 31;
-          const float4 d4 = *reinterpret_cast<const float4*>(buf + r * 512 + ((ch ^ r) << 4));
-          const int m = rbase + i * 32 + r;
+        for (int u = 0; u < GR; ++u) {
+          const int m = row_of(grp, u);
+          const int mc = m < job.M_valid ? m : job.M_valid - 1;   // read a valid row, store none
+          const bf16_t* pg = gu_e + (long long)mc * 2 * F + cbase + 4 * ch;
+          g[u] = *reinterpret_cast<const uint2*>(pg);
+          uu[u] = *reinterpret_cast<const uint2*>(pg + F);
+        }
+      };
+      stage_block(0);
+      load_gu(0, gq[0], uq[0]);
+      static_for<NGRP>([&](auto gc) __attribute__((always_inline)) {
+        constexpr int grp = decltype(gc)::value;
+        if constexpr (grp + 1 < NGRP) load_gu(grp + 1, gq[(grp + 1) & 1], uq[(grp + 1) & 1]);
+        float4 d4[GR];
+#pragma unroll
+        for (int u = 0; u < GR; ++u) {
+          const int r = 2 * ((grp & 3) * GR + u) + (lane >> 5);
+          d4[u] = *reinterpret_cast<const float4*>(buf + r * 512 + ((ch ^ r) << 4));
+        }
+        // the next block reuses the staging buffer after this group's reads
+        if constexpr (grp == NGRP / 2 - 1) stage_block(1);
+#pragma unroll
+        for (int u = 0; u < GR; ++u) {
+          const int m = row_of(grp, u);
           if (m < job.M_valid) {
-            const float v[4] = {d4.x, d4.y, d4.z, d4.w};
-            bwd_store4<MODE, bf16_t>(args, job, m, cbase + 4 * ch, v, false);
+            const float v[4] = {d4[u].x, d4[u].y, d4[u].z, d4[u].w};
+            const uint32_t gw[2] = {gq[grp & 1][u].x, gq[grp & 1][u].y};
+            const uint32_t uw[2] = {uq[grp & 1][u].x, uq[grp & 1][u].y};
+            float dg[4], du[4], hh[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t gb = gw[q >> 1], ub = uw[q >> 1];
+              const float g = __uint_as_float((q & 1) ? (gb & 0xffff0000u) : (gb << 16));
+              const float uv = __uint_as_float((q & 1) ? (ub & 0xffff0000u) : (ub << 16));
+              const float sg = 1.0f / (1.0f + __expf(-g));
+              const float sl = g * sg;
+              dg[q] = v[q] * uv * sg * (1.0f + g * (1.0f - sg));
+              du[q] = v[q] * sl;
+              hh[q] = sl * uv;
+            }
+            const long long o = (long long)m * 2 * F + cbase + 4 * ch;
+            *reinterpret_cast<uint2*>(dgu_e + o) =
+                make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+            *reinterpret_cast<uint2*>(dgu_e + o + F) =
+                make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+            *reinterpret_cast<uint2*>(h_e + (long long)m * F + cbase + 4 * ch) =
+                make_uint2(pack_bf16x2(hh[0], hh[1]), pack_bf16x2(hh[2], hh[3]));
           }
         }
-      }
+      });
     }
   }
 }
@@ -1151,34 +1205,50 @@ bwd_wgrad_kernel(const BwdArgs args) {
                           (long long)((int)m0 - (up ? args.F : 0) + wm * WTM) * Ntot +
                           (int)n0 + wn * WTN;
     void* const wbase = MODE == BWD_WD ? args.dw_down : (up ? args.dw_up : args.dw_gate);
-    static_for<MI * NJ>([&](auto ijc) __attribute__((always_inline)) {
-        constexpr int i = decltype(ijc)::value / NJ, j = decltype(ijc)::value % NJ;
+    // Per 32 x 32 block: the four staging writes, then the four row reads,
+    // then the four global stores, so the reads return together and each
+    // store waits only for its own.  The staging buffer is reused by the
+    // next block without a wait (a wave's LDS operations complete in order).
+    // The output type is one uniform branch around the whole loop.
+    auto blocks = [&](auto store4) __attribute__((always_inline)) {
+      static_for<MI * NJ>([&](auto ijc) __attribute__((always_inline)) {
+          constexpr int i = decltype(ijc)::value / NJ, j = decltype(ijc)::value % NJ;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int ch = 2 * q + (lane >> 5);
-          const int pos = ch ^ ((frag_row >> 1) & 7);
-          *reinterpret_cast<float4*>(sw + frag_row * 32 + pos * 4) =
-              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                          acc[i][j][4 * q + 3]);
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int r = (lane >> 3) + 8 * t, ch = lane & 7;
-          const float4 v4 = *reinterpret_cast<const float4*>(sw + r * 32 + ((ch ^ ((r >> 1) & 7)) * 4));
-          const long long o = blk + (long long)(i * 32 + r) * Ntot + j * 32 + ch * 4;
-          // fp32 gradients (the largest write of the backward) bypass L2 so
-          // they do not evict the operand slices other tiles still read;
-          // the bf16 form is half the bytes and measures faster cached.
-          if (args.wgrad_bf16) {
-            *reinterpret_cast<uint2*>(static_cast<bf16_t*>(wbase) + o) =
-                make_uint2(pack_bf16x2(v4.x, v4.y), pack_bf16x2(v4.z, v4.w));
-          } else {
-            typedef float f4_t __attribute__((ext_vector_type(4)));
-            const f4_t q = {v4.x, v4.y, v4.z, v4.w};
-            __builtin_nontemporal_store(q, reinterpret_cast<f4_t*>(static_cast<float*>(wbase) + o));
+          for (int q = 0; q < 4; ++q) {
+            const int ch = 2 * q + (lane >> 5);
+            const int pos = ch ^ ((frag_row >> 1) & 7);
+            *reinterpret_cast<float4*>(sw + frag_row * 32 + pos * 4) =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                            acc[i][j][4 * q + 3]);
           }
-        }
-    });
+          float4 v4[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int r = (lane >> 3) + 8 * t, ch = lane & 7;
+            v4[t] = *reinterpret_cast<const float4*>(sw + r * 32 + ((ch ^ ((r >> 1) & 7)) * 4));
+          }
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int r = (lane >> 3) + 8 * t, ch = lane & 7;
+            store4(blk + (long long)(i * 32 + r) * Ntot + j * 32 + ch * 4, v4[t]);
+          }
+      });
+    };
+    if (args.wgrad_bf16) {
+      // bf16 gradients: half the bytes, and faster through L2 than around it
+      blocks([&](long long o, const float4& v) __attribute__((always_inline)) {
+        *reinterpret_cast<uint2*>(static_cast<bf16_t*>(wbase) + o) =
+            make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+      });
+    } else {
+      // fp32 gradients (the largest write of the backward) bypass L2 so they
+      // do not evict the operand slices other tiles still read
+      blocks([&](long long o, const float4& v) __attribute__((always_inline)) {
+        typedef float f4_t __attribute__((ext_vector_type(4)));
+        const f4_t q = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(q, reinterpret_cast<f4_t*>(static_cast<float*>(wbase) + o));
+      });
+    }
     ep2 = ep1;
     ep1 = ep0;
     ep0 = issued;

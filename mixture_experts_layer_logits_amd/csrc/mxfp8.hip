@@ -700,19 +700,34 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& args, const MxScales& sc
               make_float4(D[4 * q], D[4 * q + 1], D[4 * q + 2], D[4 * q + 3]);
         }
       });
+      // The 16 passes go in groups of 4; a group's g, u loads are issued
+      // before the previous group's stores (vmcnt counts loads and stores in
+      // issue order: a load issued after a store would wait for it too).
+      // Rows and columns past the tile read a valid element and store none.
+      const int ch = lane & 31, n = cbase + 4 * ch;
+      const int nc = n < job.N ? n : job.N - 4;   // N is a multiple of 32
+      uint2 gqs[2][4], uqs[2][4];
+      auto load_gu = [&](int grp, uint2 (&gq4)[4], uint2 (&uq4)[4]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const int r = 2 * t + hsel, ch = lane & 31;
+        for (int u = 0; u < 4; ++u) {
+          const int m = job.m0 + wm * WTM + i * 32 + 2 * (4 * grp + u) + hsel;
+          const long long rg = (long long)job.row0 + (m < job.rows ? m : job.rows - 1);
+          gq4[u] = *reinterpret_cast<const uint2*>(bw.gu + rg * 2 * F + nc);
+          uq4[u] = *reinterpret_cast<const uint2*>(bw.gu + rg * 2 * F + F + nc);
+        }
+      };
+      load_gu(0, gqs[0], uqs[0]);
+      static_for<4>([&](auto gc) __attribute__((always_inline)) {
+      constexpr int grp = decltype(gc)::value;
+      if constexpr (grp + 1 < 4) load_gu(grp + 1, gqs[(grp + 1) & 1], uqs[(grp + 1) & 1]);
+#pragma unroll
+      for (int pu = 0; pu < 4; ++pu) {
+        const int r = 2 * (4 * grp + pu) + hsel;
         const float4 d4 = *reinterpret_cast<const float4*>(buf + r * 512 + ((ch ^ r) << 4));
         const int m = job.m0 + wm * WTM + i * 32 + r;
-        const int n = cbase + 4 * ch;
-        const bool ok = m < job.rows && n < job.N;   // N is a multiple of 32
+        const bool ok = m < job.rows && n < job.N;
         const long long rg = (long long)job.row0 + m;
-        uint2 gq = make_uint2(0u, 0u), uq = make_uint2(0u, 0u);
-        if (ok) {
-          gq = *reinterpret_cast<const uint2*>(bw.gu + rg * 2 * F + n);
-          uq = *reinterpret_cast<const uint2*>(bw.gu + rg * 2 * F + F + n);
-        }
+        const uint2 gq = gqs[grp & 1][pu], uq = uqs[grp & 1][pu];
         const float dh[4] = {d4.x, d4.y, d4.z, d4.w};
         const uint32_t gw[2] = {gq.x, gq.y}, uw[2] = {uq.x, uq.y};
         float dg[4], du[4], hh[4];
@@ -759,6 +774,7 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& args, const MxScales& sc
           }
         }
       }
+      });
     });
     return;
   }

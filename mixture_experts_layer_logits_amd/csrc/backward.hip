@@ -14,10 +14,14 @@
 //
 // The GEMMs take each operand either K-contiguous ("row" operands, as in the
 // forward) or M-contiguous ("column" operands: a weight read against its
-// storage order, or activations contracted over rows).  Column operands are
-// transposed in registers on their way to LDS, so the MFMA fragment reads
-// are the same 16-byte row reads as in the forward kernel.  Weight-gradient
-// tiles of experts without rows run zero K steps and store exact zeros.
+// storage order, or activations contracted over rows).  The direct-to-LDS
+// kernels (d and F multiples of 256: bwd_dma_kernel for dh and dX, the
+// persistent bwd_wgrad_kernel for the weight gradients) keep column
+// operands in storage order in LDS and build their MFMA fragments with the
+// transposing LDS read (ds_read_b64_tr_b16).  The MFMA kernel for other
+// shapes transposes them in registers on their way to LDS and reads 16-byte
+// rows as the forward kernel does.  Weight-gradient tiles of experts without
+// rows run zero K steps and store exact zeros.
 #include <float.h>
 
 #include <algorithm>

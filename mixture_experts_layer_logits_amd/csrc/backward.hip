@@ -162,24 +162,41 @@ bwd_dispatch_kernel(const T* __restrict__ dy, const T* __restrict__ y_perm,
 // b6: dx[t] = sum_j dX_perm[token_row[t, j]] (fp32, fixed order), then
 // + dX_shared[t] when the layer has a shared expert (dXs non-null).
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, int JB>
 __global__ void __launch_bounds__(256)
 bwd_gather_kernel(const T* __restrict__ dX, const int32_t* __restrict__ token_row, int d, int k,
                   const T* __restrict__ dXs, float* __restrict__ dx) {
   const int t = blockIdx.x;
   const int32_t* rows = token_row + (long long)t * k;
   if (sizeof(T) == 2 && d % 8 == 0) {
+    // batches of JB rows as straight-line code: the row loads unconditional
+    // (a slot past k reads row 0, unused), then the sums in the order j = 0,
+    // 1, ..., k-1; a load under a branch, or added where it was loaded, was
+    // waited for on its own.  A token's rows are uniform over the workgroup.
     const bf16_t* X = reinterpret_cast<const bf16_t*>(dX);
     for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
       float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int j = 0; j < k; ++j) {
-        const int r = rows[j];
-        if (r < 0) continue;
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(X + (long long)r * d + c);
+      for (int j0 = 0; j0 < k; j0 += JB) {
+        u32x4_t raw[JB];
+        int r[JB];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] += __uint_as_float(v[q] << 16);
-          acc[2 * q + 1] += __uint_as_float(v[q] & 0xffff0000u);
+        for (int jj = 0; jj < JB; ++jj) {
+          r[jj] = j0 + jj < k ? rows[j0 + jj] : -1;
+          raw[jj] = *reinterpret_cast<const u32x4_t*>(X + (long long)(r[jj] < 0 ? 0 : r[jj]) * d + c);
+        }
+        float v[JB][8];
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v[jj][2 * q] = __uint_as_float(raw[jj][q] << 16);
+            v[jj][2 * q + 1] = __uint_as_float(raw[jj][q] & 0xffff0000u);
+          }
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj) {
+          if (r[jj] < 0) continue;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] += v[jj][i];
         }
       }
       if (dXs) {
@@ -1598,11 +1615,13 @@ hipError_t launch_backward(const moe_shape& s, const void* dy, const void* x_per
   phase_mark(MOE_PHASE_BWD_GATHER, 0, st);
   if (s.T > 0) {
     if (bf)
-      bwd_gather_kernel<bf16_t><<<s.T, 256, 0, st>>>(
-          static_cast<const bf16_t*>(ws.dX), token_row, s.d, s.k,
-          shared ? static_cast<const bf16_t*>(ws.s_dX) : nullptr, dx);
+      with_gather_batch(s.k, [&](auto jb) {
+        bwd_gather_kernel<bf16_t, decltype(jb)::value><<<s.T, 256, 0, st>>>(
+            static_cast<const bf16_t*>(ws.dX), token_row, s.d, s.k,
+            shared ? static_cast<const bf16_t*>(ws.s_dX) : nullptr, dx);
+      });
     else
-      bwd_gather_kernel<float><<<s.T, 256, 0, st>>>(
+      bwd_gather_kernel<float, 1><<<s.T, 256, 0, st>>>(
           static_cast<const float*>(ws.dX), token_row, s.d, s.k,
           shared ? static_cast<const float*>(ws.s_dX) : nullptr, dx);
   }

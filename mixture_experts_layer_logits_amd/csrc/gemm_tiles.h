@@ -138,6 +138,16 @@ __host__ __device__ inline int group_full_rows(int rows, int bm, int tail) {
 
 __host__ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// Batch size of a per-token gather over its k routed rows (combine, dx):
+// fn(integral_constant<int, B>) with B the largest of 1, 2, 4, 8 not above k.
+template <typename Fn>
+inline void with_gather_batch(int k, Fn&& fn) {
+  if (k >= 8) fn(std::integral_constant<int, 8>{});
+  else if (k >= 4) fn(std::integral_constant<int, 4>{});
+  else if (k >= 2) fn(std::integral_constant<int, 2>{});
+  else fn(std::integral_constant<int, 1>{});
+}
+
 // Upper bound of the tile count, known on the host (a multiple of 8).
 inline int grid_upper_bound(const GemmArgs& a, int BM, int BN, int R) {
   long long t = 0;

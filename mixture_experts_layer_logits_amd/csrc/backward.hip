@@ -35,7 +35,7 @@ bool backward_supported(const moe_shape&) { return true; }
 // ---------------------------------------------------------------------------
 // b1 + b7: one workgroup per token.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, int JB>
 __global__ void __launch_bounds__(256)
 bwd_dispatch_kernel(const T* __restrict__ dy, const T* __restrict__ y_perm,
                     const int32_t* __restrict__ token_row, const int32_t* __restrict__ topk_idx,
@@ -50,43 +50,74 @@ bwd_dispatch_kernel(const T* __restrict__ dy, const T* __restrict__ y_perm,
   const int lane = tid & 63, wave = tid >> 6;
   __shared__ float s_part[64][4];
   const bool vec = (sizeof(T) == 2) && (d % 8 == 0);
-  for (int j = 0; j < k; ++j) {
-    const int r = token_row[(long long)t * k + j];
-    const float w = topk_w[(long long)t * k + j];
-    float part = 0.0f;
-    if (r >= 0) {
-      if (vec) {
-        // 8 bf16 per thread and step: one 16-byte load of dy and y_perm,
-        // one 16-byte store of w * dy
-        const bf16_t* dyb = reinterpret_cast<const bf16_t*>(dyt);
-        const bf16_t* ypb = reinterpret_cast<const bf16_t*>(y_perm) + (long long)r * d;
-        bf16_t* dYb = reinterpret_cast<bf16_t*>(dY) + (long long)r * d;
-        for (int c = tid * 8; c < d; c += 256 * 8) {
-          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(dyb + c);
-          const u32x4_t yv = *reinterpret_cast<const u32x4_t*>(ypb + c);
+  if (vec) {
+    // The token's rows in batches of JB (the largest of 1, 2, 4, 8 not above
+    // k).  Per 8-column run a thread loads dy once and the batch's y_perm
+    // rows unconditionally (a slot past k reads row 0, unused), then forms
+    // each row's products and its 16-byte store of w * dy: the loads of a
+    // run are not waited for one by one, nor behind the previous row's
+    // stores.  Each row's partial dot product runs over the thread's runs in
+    // ascending order, as it would one row at a time.
+    const bf16_t* dyb = reinterpret_cast<const bf16_t*>(dyt);
+    for (int j0 = 0; j0 < k; j0 += JB) {
+      int r[JB];
+      float w[JB], part[JB];
+#pragma unroll
+      for (int jj = 0; jj < JB; ++jj) {
+        const bool in = j0 + jj < k;
+        r[jj] = in ? token_row[(long long)t * k + j0 + jj] : -1;
+        w[jj] = in ? topk_w[(long long)t * k + j0 + jj] : 0.0f;
+        part[jj] = 0.0f;
+      }
+      for (int c = tid * 8; c < d; c += 256 * 8) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(dyb + c);
+        u32x4_t yv[JB];
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj)
+          yv[jj] = *reinterpret_cast<const u32x4_t*>(
+              reinterpret_cast<const bf16_t*>(y_perm) + (long long)(r[jj] < 0 ? 0 : r[jj]) * d + c);
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj) {
+          if (r[jj] < 0) continue;
           u32x4_t o;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float g0 = __uint_as_float(a[q] << 16), g1 = __uint_as_float(a[q] & 0xffff0000u);
-            const float y0 = __uint_as_float(yv[q] << 16), y1 = __uint_as_float(yv[q] & 0xffff0000u);
-            part = fmaf(g0, y0, part);
-            part = fmaf(g1, y1, part);
-            o[q] = pack_bf16x2(w * g0, w * g1);
+            const float y0 = __uint_as_float(yv[jj][q] << 16), y1 = __uint_as_float(yv[jj][q] & 0xffff0000u);
+            part[jj] = fmaf(g0, y0, part[jj]);
+            part[jj] = fmaf(g1, y1, part[jj]);
+            o[q] = pack_bf16x2(w[jj] * g0, w[jj] * g1);
           }
-          *reinterpret_cast<u32x4_t*>(dYb + c) = o;
+          *reinterpret_cast<u32x4_t*>(reinterpret_cast<bf16_t*>(dY) + (long long)r[jj] * d + c) = o;
         }
-      } else {
+      }
+      // wave reductions (fixed butterfly order), partials combined below
+#pragma unroll
+      for (int jj = 0; jj < JB; ++jj) {
+        if (j0 + jj >= k) continue;
+        float pv = part[jj];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) pv += __shfl_xor(pv, off, 64);
+        if (lane == 0) s_part[j0 + jj][wave] = pv;
+      }
+    }
+  } else {
+    for (int j = 0; j < k; ++j) {
+      const int r = token_row[(long long)t * k + j];
+      const float w = topk_w[(long long)t * k + j];
+      float part = 0.0f;
+      if (r >= 0) {
         for (int c = tid; c < d; c += 256) {
           const float g = to_f32<T>(dyt[c]);
           dY[(long long)r * d + c] = from_f32<T>(w * g);
           part = fmaf(g, to_f32<T>(y_perm[(long long)r * d + c]), part);
         }
       }
-    }
-    // wave reduction (fixed butterfly order), partials combined below
+      // wave reduction (fixed butterfly order), partials combined below
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
-    if (lane == 0) s_part[j][wave] = part;
+      for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+      if (lane == 0) s_part[j][wave] = part;
+    }
   }
   __syncthreads();
   if (tid < k) {
@@ -1512,12 +1543,14 @@ hipError_t launch_backward(const moe_shape& s, const void* dy, const void* x_per
   phase_mark(MOE_PHASE_BWD_DISPATCH, 0, st);
   if (s.T > 0) {
     if (bf)
-      bwd_dispatch_kernel<bf16_t><<<s.T, 256, 0, st>>>(
-          static_cast<const bf16_t*>(dy), static_cast<const bf16_t*>(y_perm), token_row, topk_idx,
-          topk_w, logits, s.d, s.E, s.k, s.score, s.renorm, static_cast<bf16_t*>(ws.dY), d_gate,
-          d_logits);
+      with_gather_batch(s.k, [&](auto jb) {
+        bwd_dispatch_kernel<bf16_t, decltype(jb)::value><<<s.T, 256, 0, st>>>(
+            static_cast<const bf16_t*>(dy), static_cast<const bf16_t*>(y_perm), token_row,
+            topk_idx, topk_w, logits, s.d, s.E, s.k, s.score, s.renorm,
+            static_cast<bf16_t*>(ws.dY), d_gate, d_logits);
+      });
     else
-      bwd_dispatch_kernel<float><<<s.T, 256, 0, st>>>(
+      bwd_dispatch_kernel<float, 1><<<s.T, 256, 0, st>>>(
           static_cast<const float*>(dy), static_cast<const float*>(y_perm), token_row, topk_idx,
           topk_w, logits, s.d, s.E, s.k, s.score, s.renorm, static_cast<float*>(ws.dY), d_gate,
           d_logits);

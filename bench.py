@@ -102,17 +102,23 @@ def phase_figures(c, counts_nonzero):
 
 
 # The kernel behind each phase (names as a kernel trace prints them, for the
-# headline bf16 shapes: d and F multiples of 256).
+# headline bf16 shapes: d and F multiples of 256; {jb} is the row batch of
+# the per-token gathers, the largest of 1, 2, 4, 8 not above k).
 PHASE_KERNELS = {
     "fc1": "gemm_bf16_mfma_kernel<256, 128, 2, 1, 4, 2, 1> (FC1 + SwiGLU)",
     "fc2": "gemm_bf16_mfma_kernel<256, 256, 1, 0, 4, 2, 1> (FC2) + splitk_reduce_kernel",
-    "bwd_dispatch": "bwd_dispatch_kernel<unsigned short>",
+    "bwd_dispatch": "bwd_dispatch_kernel<unsigned short, {jb}>",
     "bwd_dh": "bwd_dma_kernel<0> (dh + SwiGLU backward)",
     "bwd_dw_down": "bwd_wgrad_kernel<2> (dW_down, persistent)",
     "bwd_dx": "bwd_dma_kernel<1> (dX_perm)",
     "bwd_dw_gate_up": "bwd_wgrad_kernel<3> (dW_gate | dW_up, persistent)",
-    "bwd_gather": "bwd_gather_kernel<unsigned short>",
+    "bwd_gather": "bwd_gather_kernel<unsigned short, {jb}>",
 }
+
+
+def phase_kernel(name, k):
+    jb = 8 if k >= 8 else 4 if k >= 4 else 2 if k >= 2 else 1
+    return PHASE_KERNELS[name].replace("{jb}", str(jb))
 
 
 def price(flops, nbytes, ms):
@@ -671,7 +677,7 @@ def main():
     for name, (mean, med, mn) in phase_ms.items():
         fl, nb = figs[name]
         r = price(fl, nb, mean)
-        r.update({"kernel": PHASE_KERNELS[name], "ms_mean": round(mean, 4),
+        r.update({"kernel": phase_kernel(name, cfg.k), "ms_mean": round(mean, 4),
                   "ms_median": round(med, 4), "ms_min": round(mn, 4),
                   "algorithmic_flops": fl, "algorithmic_bytes": int(nb)})
         kernels[name] = r

@@ -277,8 +277,13 @@ def test_grouped_ffn(case):
 # --------------------------------------------------------------------------
 # moe_unpermute_combine on synthetic rows
 # --------------------------------------------------------------------------
+# The vector kernel gathers a token's rows in batches of 1, 2, 4 or 8 (the
+# largest not above k): k = 1, 2, 4 fill their batches, k = 5 and 12 leave
+# padding slots in a second batch, and the fp32 case takes the same path.
 @pytest.mark.parametrize("T,d,E,k,shared,dtype", [(1000, 512, 8, 2, False, 1), (333, 96, 16, 4, True, 1),
-                                                  (100, 20, 5, 3, True, 0), (50, 13, 4, 2, False, 1)])
+                                                  (100, 20, 5, 3, True, 0), (50, 13, 4, 2, False, 1),
+                                                  (120, 64, 4, 1, False, 1), (200, 64, 16, 5, True, 1),
+                                                  (150, 256, 32, 12, False, 1), (90, 40, 8, 3, True, 0)])
 def test_unpermute_combine(T, d, E, k, shared, dtype):
     _log(f"[combine] T={T} d={d} k={k} shared={shared}")
     M = _lib()
@@ -377,6 +382,10 @@ BWD_CASES = [
     ("dma_shared_wgrad_bf16_t300", 300, 256, 16, 4, 256, 1, 1, 1, False, 512, 1),
     ("mfma_skewed_wgrad_bf16_t400", 400, 128, 16, 4, 128, 1, 0, 1, True, 0, 1),
     ("generic_wgrad_bf16_t77", 77, 200, 6, 2, 96, 1, 0, 0, False, 40, 1),
+    # k above one gather batch (the dispatch gradient and the dx gather take
+    # a token's rows 8 at a time) and k = 5 (a batch of 4, then a padded one)
+    ("dma_k12_t150", 150, 256, 32, 12, 256, 1, 0, 1, False),
+    ("mfma_k5_t200", 200, 128, 16, 5, 128, 1, 0, 1, True),
     # 1024 experts (the largest count): direct-to-LDS and MFMA kernels
     ("dma_e1024_t300", 300, 256, 1024, 4, 256, 1, 0, 1, False),
     ("mfma_e1024_t300", 300, 128, 1024, 4, 128, 1, 0, 1, True),

@@ -919,7 +919,9 @@ bwd_dma_kernel(const BwdArgs args) {
       // loads are issued before the previous group's stores: vmcnt counts
       // loads and stores in issue order, so a load issued after a store
       // would wait for that store too.
-      constexpr int GR = 4, NGRP = 2 * 32 / (2 * GR);   // 8 groups of 4 passes
+      // GR passes per group, GPB groups per 32-row block, MI blocks
+      constexpr int GR = 4, GPB = 16 / GR, NGRP = MI * GPB;
+      static_assert(MI == 2, "the second block is staged halfway");
       const int ch = lane & 31;
       const long long F = args.F;
       const bf16_t* gu_e = static_cast<const bf16_t*>(args.gu) + (long long)job.row0 * 2 * F;
@@ -937,7 +939,9 @@ bwd_dma_kernel(const BwdArgs args) {
           }
       };
       // pass t of block i: row 2 t + lane / 32 of the block
-      auto row_of = [&](int grp, int u) { return rbase + (grp >> 2) * 32 + 2 * ((grp & 3) * GR + u) + (lane >> 5); };
+      auto row_of = [&](int grp, int u) {
+        return rbase + (grp / GPB) * 32 + 2 * ((grp % GPB) * GR + u) + (lane >> 5);
+      };
       uint2 gq[2][GR], uq[2][GR];
       auto load_gu = [&](int grp, uint2 (&g)[GR], uint2 (&uu)[GR]) __attribute__((always_inline)) {
 #pragma unroll
@@ -957,11 +961,11 @@ bwd_dma_kernel(const BwdArgs args) {
         float4 d4[GR];
 #pragma unroll
         for (int u = 0; u < GR; ++u) {
-          const int r = 2 * ((grp & 3) * GR + u) + (lane >> 5);
+          const int r = 2 * ((grp % GPB) * GR + u) + (lane >> 5);
           d4[u] = *reinterpret_cast<const float4*>(buf + r * 512 + ((ch ^ r) << 4));
         }
         // the next block reuses the staging buffer after this group's reads
-        if constexpr (grp == NGRP / 2 - 1) stage_block(1);
+        if constexpr (grp == GPB - 1) stage_block(1);
 #pragma unroll
         for (int u = 0; u < GR; ++u) {
           const int m = row_of(grp, u);

@@ -718,62 +718,62 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& args, const MxScales& sc
       };
       load_gu(0, gqs[0], uqs[0]);
       static_for<4>([&](auto gc) __attribute__((always_inline)) {
-      constexpr int grp = decltype(gc)::value;
-      if constexpr (grp + 1 < 4) load_gu(grp + 1, gqs[(grp + 1) & 1], uqs[(grp + 1) & 1]);
+        constexpr int grp = decltype(gc)::value;
+        if constexpr (grp + 1 < 4) load_gu(grp + 1, gqs[(grp + 1) & 1], uqs[(grp + 1) & 1]);
 #pragma unroll
-      for (int pu = 0; pu < 4; ++pu) {
-        const int r = 2 * (4 * grp + pu) + hsel;
-        const float4 d4 = *reinterpret_cast<const float4*>(buf + r * 512 + ((ch ^ r) << 4));
-        const int m = job.m0 + wm * WTM + i * 32 + r;
-        const bool ok = m < job.rows && n < job.N;
-        const long long rg = (long long)job.row0 + m;
-        const uint2 gq = gqs[grp & 1][pu], uq = uqs[grp & 1][pu];
-        const float dh[4] = {d4.x, d4.y, d4.z, d4.w};
-        const uint32_t gw[2] = {gq.x, gq.y}, uw[2] = {uq.x, uq.y};
-        float dg[4], du[4], hh[4];
-        float ag = 0.0f, au = 0.0f;
+        for (int pu = 0; pu < 4; ++pu) {
+          const int r = 2 * (4 * grp + pu) + hsel;
+          const float4 d4 = *reinterpret_cast<const float4*>(buf + r * 512 + ((ch ^ r) << 4));
+          const int m = job.m0 + wm * WTM + i * 32 + r;
+          const bool ok = m < job.rows && n < job.N;
+          const long long rg = (long long)job.row0 + m;
+          const uint2 gq = gqs[grp & 1][pu], uq = uqs[grp & 1][pu];
+          const float dh[4] = {d4.x, d4.y, d4.z, d4.w};
+          const uint32_t gw[2] = {gq.x, gq.y}, uw[2] = {uq.x, uq.y};
+          float dg[4], du[4], hh[4];
+          float ag = 0.0f, au = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t gb = gw[e >> 1], ub = uw[e >> 1];
-          const float g = __uint_as_float((e & 1) ? (gb & 0xffff0000u) : (gb << 16));
-          const float u = __uint_as_float((e & 1) ? (ub & 0xffff0000u) : (ub << 16));
-          const float sg = 1.0f / (1.0f + __expf(-g));
-          const float sl = g * sg;
-          // rounded to bf16 here, so the quantised blocks see the stored values
-          dg[e] = bf16_round(dh[e] * u * sg * (1.0f + g * (1.0f - sg)));
-          du[e] = bf16_round(dh[e] * sl);
-          hh[e] = sl * u;
-          ag = fmaxf(ag, fabsf(dg[e]));
-          au = fmaxf(au, fabsf(du[e]));
-        }
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t gb = gw[e >> 1], ub = uw[e >> 1];
+            const float g = __uint_as_float((e & 1) ? (gb & 0xffff0000u) : (gb << 16));
+            const float u = __uint_as_float((e & 1) ? (ub & 0xffff0000u) : (ub << 16));
+            const float sg = 1.0f / (1.0f + __expf(-g));
+            const float sl = g * sg;
+            // rounded to bf16 here, so the quantised blocks see the stored values
+            dg[e] = bf16_round(dh[e] * u * sg * (1.0f + g * (1.0f - sg)));
+            du[e] = bf16_round(dh[e] * sl);
+            hh[e] = sl * u;
+            ag = fmaxf(ag, fabsf(dg[e]));
+            au = fmaxf(au, fabsf(du[e]));
+          }
 #pragma unroll
-        for (int x = 1; x < 8; x <<= 1) {
-          ag = fmaxf(ag, __shfl_xor(ag, x, 64));
-          au = fmaxf(au, __shfl_xor(au, x, 64));
-        }
-        const int sgx = mx_scale_exp(ag), sux = mx_scale_exp(au);
-        const float ig = mx_inv_scale(sgx), iu = mx_inv_scale(sux);
-        uint32_t cg = 0, cu = 0;
+          for (int x = 1; x < 8; x <<= 1) {
+            ag = fmaxf(ag, __shfl_xor(ag, x, 64));
+            au = fmaxf(au, __shfl_xor(au, x, 64));
+          }
+          const int sgx = mx_scale_exp(ag), sux = mx_scale_exp(au);
+          const float ig = mx_inv_scale(sgx), iu = mx_inv_scale(sux);
+          uint32_t cg = 0, cu = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          cg |= e4m3_code(dg[e] * ig) << (8 * e);
-          cu |= e4m3_code(du[e] * iu) << (8 * e);
-        }
-        if (ok) {
-          bf16_t* dgp = bw.dgu + rg * 2 * F + n;
-          *reinterpret_cast<uint2*>(dgp) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
-          *reinterpret_cast<uint2*>(dgp + F) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
-          *reinterpret_cast<uint2*>(bw.h + rg * F + n) =
-              make_uint2(pack_bf16x2(hh[0], hh[1]), pack_bf16x2(hh[2], hh[3]));
-          uint8_t* cp = job.C + (long long)m * job.ldc + n;
-          *reinterpret_cast<uint32_t*>(cp) = cg;
-          *reinterpret_cast<uint32_t*>(cp + F) = cu;
-          if ((lane & 7) == 0) {
-            sC[(long long)m * (job.ldc / 32) + n / 32] = (uint8_t)(sgx + 127);
-            sC[(long long)m * (job.ldc / 32) + (F + n) / 32] = (uint8_t)(sux + 127);
+          for (int e = 0; e < 4; ++e) {
+            cg |= e4m3_code(dg[e] * ig) << (8 * e);
+            cu |= e4m3_code(du[e] * iu) << (8 * e);
+          }
+          if (ok) {
+            bf16_t* dgp = bw.dgu + rg * 2 * F + n;
+            *reinterpret_cast<uint2*>(dgp) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+            *reinterpret_cast<uint2*>(dgp + F) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+            *reinterpret_cast<uint2*>(bw.h + rg * F + n) =
+                make_uint2(pack_bf16x2(hh[0], hh[1]), pack_bf16x2(hh[2], hh[3]));
+            uint8_t* cp = job.C + (long long)m * job.ldc + n;
+            *reinterpret_cast<uint32_t*>(cp) = cg;
+            *reinterpret_cast<uint32_t*>(cp + F) = cu;
+            if ((lane & 7) == 0) {
+              sC[(long long)m * (job.ldc / 32) + n / 32] = (uint8_t)(sgx + 127);
+              sC[(long long)m * (job.ldc / 32) + (F + n) / 32] = (uint8_t)(sux + 127);
+            }
           }
         }
-      }
       });
     });
     return;

@@ -43,7 +43,8 @@ __device__ __forceinline__ void cvt8(const Raw8<float>& r, float (&v)[8]) {
 // One workgroup per token; each thread owns runs of 8 columns (d % 8 == 0).
 // The k gathered rows go in batches of JB (1, 2, 4 or 8, the largest not
 // above k).  A batch is straight-line code: its JB row loads are issued
-// unconditionally (a slot past k reads row 0, and its value is not used),
+// unconditionally (a slot past k, or one without a row, reads row 0, and
+// its value is not used),
 // then converted, then accumulated in the order j = 0, 1, ..., k-1.  Loads
 // under a branch, or converted where they were loaded, were each waited for
 // on their own.  A token's rows are uniform over the workgroup.

@@ -138,7 +138,8 @@ __host__ __device__ inline int group_full_rows(int rows, int bm, int tail) {
 
 __host__ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
-// Batch size of a per-token gather over its k routed rows (combine, dx):
+// Batch size of a per-token gather over its k routed rows (combine, the
+// dispatch gradient, dx):
 // fn(integral_constant<int, B>) with B the largest of 1, 2, 4, 8 not above k.
 template <typename Fn>
 inline void with_gather_batch(int k, Fn&& fn) {

@@ -44,10 +44,10 @@ __device__ __forceinline__ void cvt8(const Raw8<float>& r, float (&v)[8]) {
 // The k gathered rows go in batches of JB (1, 2, 4 or 8, the largest not
 // above k).  A batch is straight-line code: its JB row loads are issued
 // unconditionally (a slot past k, or one without a row, reads row 0, and
-// its value is not used),
-// then converted, then accumulated in the order j = 0, 1, ..., k-1.  Loads
-// under a branch, or converted where they were loaded, were each waited for
-// on their own.  A token's rows are uniform over the workgroup.
+// its value is not used), then converted, then accumulated in the order
+// j = 0, 1, ..., k-1.  Loads under a branch, or converted where they were
+// loaded, were each waited for on their own.  A token's rows are uniform
+// over the workgroup.
 template <typename T, int JB>
 __global__ void __launch_bounds__(256)
 combine_vec_kernel(const T* __restrict__ y_perm, const int32_t* __restrict__ token_row,
